@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule forward kernel on one MI355X.
+
+One "step" is one gdn_fwd call over one batch of the wide-head workload
+(B=4, H=16, T=4096, dk=dv=128, bf16 q/k/v/out, fp32 g/beta, fp32 state with
+h0 ~ N(0, 0.02), chunk 64), inputs already resident in HBM.  Four complete
+input/output sets (about 1.1 GB) are rotated so that the 256 MB last-level
+cache cannot serve a step from the previous one.
+
+Prints ONE JSON line: tokens/s over the timed steps, the roofline of the
+kernel (algorithmic HBM bytes per launch / mean launch time measured with
+HIP events on the launch stream, against the 8 TB/s HBM3E peak), and the
+FP64 oracle timed on the host cores on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "gated-delta-rule fwd tokens/s + achieved HBM GB/s (% roofline), 1 MI355X"
+KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc", "gdn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wide_head.json")
+
+
+def algorithmic_bytes(wl: synth.Workload, has_h0: bool) -> int:
+    """Minimum HBM traffic of one call: read q, k, v, g, beta once, write out
+    once, read h0 (if given) and write hT once."""
+    s = 2 if wl.dtype == "bf16" else 4
+    per_token_head = (2 * wl.dk + 2 * wl.dv) * s + 2 * 4
+    state = wl.B * wl.H * wl.dk * wl.dv * 4
+    return wl.tokens * wl.H * per_token_head + state * (2 if has_h0 else 1)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(inp: synth.Inputs):
+    """The FP64 oracle on the host cores over the whole workload."""
+    import oracle
+
+    a = [inp.as_f64(n) for n in ("q", "k", "v", "g", "beta", "h0")]
+    cores = os.cpu_count() or 1
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.fwd_seq(*a, cu_seqlens=inp.cu_seqlens, nthreads=cores)
+    dt = time.perf_counter() - t0
+    wl = inp.wl
+    return {"value": wl.tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload ({wl.B * wl.H} chains x {wl.T} tokens), "
+                      f"{dt:.2f} s wall on {cores} threads"}
+
+
+def parity_sample(inp, out, hT):
+    """Sampled-chain check against the oracle before any number is reported."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from hip_case import TOL, compare
+
+    eo, eh = compare(inp, out, hT, chains=[0, inp.wl.B * inp.wl.H - 1])
+    tol = TOL[inp.wl.dtype]
+    if not (eo <= tol and eh <= tol):
+        raise SystemExit(f"parity check failed: rel err out {eo:.3e} hT {eh:.3e} > {tol}")
+    return eo, eh
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="wide_head", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-parity", action="store_true", help="skip the sampled parity check")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); chains shard across GPUs with no communication, "
+              "so there is no multi-GPU step to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_deltanet_recurrence_delta_amd as gdn
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from hip_case import device_inputs
+
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.generate(wl)
+    sets = []
+    for _ in range(max(1, args.sets)):
+        d = device_inputs(inp)
+        d["out"] = torch.empty(d["v"].shape, dtype=d["v"].dtype, device="cuda")
+        d["hT"] = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+        sets.append(d)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    # Validate once through the checked wrapper, then time the raw C entry
+    # point with pre-extracted pointers so host overhead stays off the clock.
+    for d in sets:
+        gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
+                chunk=wl.chunk, out=d["out"], hT=d["hT"], stream=stream)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    dtype_code = gdn.GDN_BF16 if wl.dtype == "bf16" else gdn.GDN_F32
+    B = len(inp.cu_seqlens) - 1 if inp.cu_seqlens is not None else wl.B
+    T = int(inp.cu_seqlens[-1]) if inp.cu_seqlens is not None else wl.T
+    calls = [tuple(ptr(d[n]) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens", "out", "hT"))
+             for d in sets]
+    raw = gdn.load().gdn_fwd
+    sh = stream.cuda_stream
+
+    def step(i):
+        rc = raw(*calls[i % len(calls)], B, T, wl.H, wl.dk, wl.dv, sh, dtype_code, wl.chunk)
+        if rc != 0:
+            raise SystemExit(f"gdn_fwd failed with status {rc}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    errs = None
+    if not args.no_parity:
+        errs = parity_sample(inp, sets[0]["out"], sets[0]["hT"])
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = wl.tokens
+    alg = algorithmic_bytes(wl, inp.h0 is not None)
+    mean_launch_s = float(launch_ms.mean()) / 1e3
+    achieved = alg / mean_launch_s / 1e9
+    traffic = measured_traffic() if args.workload == "wide_head" else None
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                "beta=sigmoid(N(0,1)), g=-softplus(N(%g,1)))" % wl.g_mean,
+        "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} dk={wl.dk} dv={wl.dv} "
+                               f"{wl.dtype} chunk={wl.chunk}" + (" varlen" if wl.varlen else ""),
+                   "tokens_per_step": tokens, "rotated_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg, "mean_launch_us": mean_launch_s * 1e6,
+                     "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
+                     "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
+                     "p90_us": float(np.percentile(launch_ms, 90)) * 1e3},
+    }
+    if errs is not None:
+        rec["parity"] = {"rel_err_out": errs[0], "rel_err_hT": errs[1], "chains": "first and last"}
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

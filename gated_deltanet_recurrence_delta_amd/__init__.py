@@ -1,0 +1,134 @@
+"""MI355X (gfx950) gated-delta-rule forward pass.
+
+Python face of the C ABI in ``include/gdn.h`` (``libgdn.so``): argument
+marshalling only.  Every step of the computation runs in the HIP kernel; if
+the library is missing this raises instead of falling back to anything else.
+
+The rule (HyMo "Model Architecture Walkthrough", sections 5.2.1-5.2.2):
+S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+o_t = S_t q_t, alpha_t = exp(g_t).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["gdn_fwd", "fwd", "GdnError", "lib_path", "load", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+_lib = None
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gdn_fwd failed ({status}): {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdn.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise OSError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m gated_deltanet_recurrence_delta_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.gdn_fwd.restype = I
+        lib.gdn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I]
+        lib.gdn_strerror.restype = ctypes.c_char_p
+        lib.gdn_strerror.argtypes = [I]
+        lib.gdn_version.restype = I
+        lib.gdn_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def version() -> int:
+    return load().gdn_version()
+
+
+def strerror(status: int) -> str:
+    return load().gdn_strerror(status).decode()
+
+
+def gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
+            stream, dtype, chunk) -> int:
+    """Raw C call with integer pointers (0 = NULL).  Returns the status."""
+    return load().gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT,
+                          int(B), int(T), int(H), int(dk), int(dv),
+                          stream, int(dtype), int(chunk))
+
+
+def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
+        out=None, hT=None, stream=None):
+    """Gated-delta-rule forward on torch device tensors.
+
+    q, k: (B,T,H,dk); v: (B,T,H,dv); g, beta: (B,T,H) float32 (packed:
+    drop B and pass int32 ``cu_seqlens`` of length B+1).  q/k/v share one
+    dtype, float32 or bfloat16.  h0: (B,H,dk,dv) float32 or None.
+    Returns (out, hT); out has q's dtype, hT is float32.  Runs on the
+    current stream (or ``stream``), asynchronously.
+    """
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dtype = GDN_BF16
+    elif q.dtype == torch.float32:
+        dtype = GDN_F32
+    else:
+        raise TypeError(f"q/k/v dtype must be float32 or bfloat16, got {q.dtype}")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    for name, t in (("g", g), ("beta", beta)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    tensors = [q, k, v, g, beta] + [x for x in (h0, cu_seqlens, out, hT) if x is not None]
+    dev = q.device
+    for t in tensors:
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        if q.dim() != 3:
+            raise ValueError("packed q must be (T, H, dk)")
+        T, H, dk = q.shape
+        B = cu_seqlens.numel() - 1
+        if B < 0:
+            raise ValueError("cu_seqlens must have at least one entry")
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be (B, T, H, dk)")
+        B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape[:-1]) != tuple(q.shape[:-1]):
+        raise ValueError("q, k, v shapes disagree")
+    if tuple(g.shape) != tuple(q.shape[:-1]) or tuple(beta.shape) != tuple(q.shape[:-1]):
+        raise ValueError("g/beta must have q's shape without the last dimension")
+    if h0 is not None and (h0.dtype != torch.float32 or tuple(h0.shape) != (B, H, dk, dv)):
+        raise ValueError("h0 must be float32 (B, H, dk, dv)")
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if hT is None:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    rc = gdn_fwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(h0), ptr(cu_seqlens),
+                 ptr(out), ptr(hT), B, T, H, dk, dv, stream.cuda_stream, dtype, chunk)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT

@@ -1,0 +1,104 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated-delta-rule forward library.
+ *
+ * The operation (per head, per sequence):
+ *
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   o_t = S_t q_t,                 alpha_t = exp(g_t),
+ *
+ * the delta rule "change = rate x (target - prediction) x input" of HyMo's
+ * "Model Architecture Walkthrough", section 5.2.2, with rate beta_t, target
+ * v_t, input (write key) k_t and prediction alpha_t S_{t-1} k_t, after the
+ * per-head scalar decay exp(g_t) of sections 5.2.1 and 5.3.1 of that page.
+ * The read o_t uses the state after the step's write (section 5.2.1 reads
+ * H_t); no 1/sqrt(dk) scale is applied.  The tensor layout follows the
+ * pages' kernel interface: q, k are (B,T,H,dk), v and out are (B,T,H,dv),
+ * g and beta are (B,T,H) ("Optimization Quartet", section 3.2 and the
+ * wrapper of section 3.3), math in fp32, output in the caller's dtype.
+ *
+ * All pointers are DEVICE pointers on the current HIP device unless stated.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GDN_OK 0
+#define GDN_ERR_INVALID_ARG (-1) /* null required pointer, bad size, bad dtype/chunk */
+#define GDN_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for      */
+#define GDN_ERR_LAUNCH (-3)      /* the HIP launch itself failed                      */
+
+/* Storage dtype of q, k, v and out. */
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/*
+ * gdn_fwd -- forward pass of the gated delta rule, chunkwise-parallel form.
+ *
+ * Dense mode (cu_seqlens == NULL): B sequences of T tokens each.
+ *   q, k : (B, T, H, dk)   dtype         row-major, contiguous
+ *   v    : (B, T, H, dv)   dtype
+ *   g    : (B, T, H)       float32       natural-log decay, alpha = exp(g)
+ *   beta : (B, T, H)       float32       write strength
+ *   out  : (B, T, H, dv)   dtype         written; rounded to nearest even for bf16
+ *
+ * Packed mode (cu_seqlens != NULL): B sequences packed back to back,
+ *   T = total tokens; q, k, v, g, beta, out drop the leading B dimension
+ *   ((T, H, .) and (T, H)).  cu_seqlens is a DEVICE int32 array of B+1
+ *   non-decreasing offsets with cu_seqlens[0] == 0 and cu_seqlens[B] == T;
+ *   sequence n is tokens [cu_seqlens[n], cu_seqlens[n+1]).  Each sequence is
+ *   an independent recurrence with its own initial and final state; chunks
+ *   restart at each sequence start.  These device-side preconditions are not
+ *   checked (checking would need a device read); violating them is undefined.
+ *
+ * State, both modes:
+ *   h0   : (B, H, dk, dv)  float32, or NULL for a zero initial state.
+ *   hT   : (B, H, dk, dv)  float32, written with the final state.
+ *   hT[b,h,i,j] = S[j,i]: i runs over the key dimension, j over the value
+ *   dimension (the pages' hidden state is (key dim) x (value dim)).
+ *   hT may alias h0 exactly (in-place state update); out must not alias
+ *   any input.  A sequence of length 0 gets hT = h0 (or zeros).
+ *
+ * Sizes: B >= 0, T >= 0, H >= 1.  dk, dv in {32, 64, 128}.
+ * dtype: GDN_F32 or GDN_BF16.
+ * chunk: tokens per chunk; 0 selects 64 for GDN_BF16 and 16 for GDN_F32.
+ *        GDN_BF16 accepts 32 and 64; GDN_F32 accepts 16 and 32, and 64 when
+ *        dk == 32 (larger fp32 tiles exceed the 160 KB of LDS).  The result
+ *        does not depend on the chunk length beyond floating-point rounding.
+ * stream: a hipStream_t (NULL = the null stream).
+ *
+ * Pointers: q, k, v, g, beta and out are required when T > 0 and may be
+ * NULL when T == 0 (no tokens); hT is required when B > 0.
+ *
+ * Behaviour: validates every host-side argument first; on any error returns
+ * a negative status, launches nothing and leaves the outputs untouched.  On
+ * success the work is queued on `stream` and the call returns GDN_OK
+ * immediately; results are valid once the stream has been synchronised.
+ * The caller owns all buffers; the library allocates no device memory,
+ * keeps no pointer after returning and holds no global mutable state
+ * (re-entrant, thread-safe).  Identical inputs give bitwise-identical
+ * outputs (no atomics, fixed reduction order).  Arithmetic: bf16 operands
+ * with fp32 accumulation for GDN_BF16, fp32 throughout for GDN_F32; the
+ * state is carried in fp32.  Non-finite inputs propagate.
+ */
+int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* h0, const int32_t* cu_seqlens,
+            void* out, float* hT, int B, int T, int H, int dk, int dv,
+            void* stream, int dtype, int chunk);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* gdn_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

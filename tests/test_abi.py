@@ -1,0 +1,87 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_recurrence_delta_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, INVALID, UNSUPPORTED, LAUNCH = 0, -1, -2, -3
+# Non-null dummy host addresses: validation never dereferences them.
+P = 0x1000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    assert _declared_functions() == ["gdn_fwd", "gdn_strerror", "gdn_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gdn.lib_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert gdn.version() == 100
+    for code in (OK, INVALID, UNSUPPORTED, LAUNCH, 12345):
+        assert isinstance(gdn.strerror(code), str) and gdn.strerror(code)
+
+
+def _call(**kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, out=P, hT=P,
+             B=1, T=8, H=1, dk=32, dv=32, stream=None, dtype=1, chunk=64)
+    a.update(kw)
+    return gdn.gdn_fwd(**a)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "out", "hT"])
+def test_null_required_pointer(name):
+    assert _call(**{name: 0}) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=0), dict(dk=0), dict(dv=-4),
+                                dict(dtype=2), dict(dtype=-1), dict(chunk=48), dict(chunk=128),
+                                dict(chunk=-64)])
+def test_invalid_sizes(kw):
+    assert _call(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(dk=16), dict(dv=256), dict(dk=96), dict(dtype=1, chunk=16),
+                                dict(dtype=0, chunk=64, dk=128)])
+def test_unsupported(kw):
+    assert _call(**kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "out"])
+def test_token_pointers_may_be_null_without_tokens(name):
+    # No chains (B == 0) and no tokens: success without a launch.
+    assert _call(**{name: 0, "T": 0, "B": 0, "hT": 0}) == OK
+
+
+def test_state_pointer_required_with_chains():
+    assert _call(hT=0, T=0) == INVALID
+
+
+def test_empty_batch_is_a_no_op():
+    # B == 0: nothing to launch, nothing touched, success.
+    assert _call(B=0) == OK
+    assert _call(B=0, cu_seqlens=P, T=0) == OK
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 1, 32)
+    g = torch.zeros(1, 4, 1)
+    with pytest.raises(ValueError):
+        gdn.fwd(q, q, q, g, g)

@@ -1,0 +1,213 @@
+"""HIP path vs the FP64 oracle, element by element, through the C ABI.
+
+Tolerances (infinity-norm relative error per output tensor, out and hT
+separately): 1e-4 for float32 storage, 2e-2 for bfloat16 storage with fp32
+accumulation.  Index handling (packing, chunk boundaries, causality,
+aliasing, determinism) is checked bit for bit against other GPU runs.
+"""
+import numpy as np
+import pytest
+
+import synth
+from hip_case import TOL, compare, dev, device_inputs, host_f64, run_hip
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, chains=None, chunk=None):
+    out, hT = run_hip(inp, chunk=chunk)
+    eo, eh = compare(inp, out, hT, chains)
+    tol = TOL[inp.wl.dtype]
+    print(f"{inp.wl.name}: rel err out {eo:.3e} hT {eh:.3e} (tol {tol:g})", flush=True)
+    assert eo <= tol and eh <= tol, (eo, eh)
+    return out, hT
+
+
+# ------------------------------------------------------------ full oracle --
+
+def test_tiny_workload():
+    _check(synth.generate(synth.WORKLOADS["tiny"]))
+
+
+SMALL = [
+    # (dtype, B, T, H, dk, dv, chunk, h0_std)
+    ("f32", 2, 200, 3, 32, 32, 16, 0.3),
+    ("f32", 1, 77, 2, 64, 32, 32, 0.3),
+    ("f32", 1, 90, 2, 128, 64, 32, 0.0),
+    ("f32", 1, 130, 2, 32, 128, 64, 0.5),
+    ("bf16", 2, 200, 3, 128, 128, 64, 0.3),
+    ("bf16", 1, 333, 2, 128, 128, 32, 0.0),
+    ("bf16", 3, 150, 2, 32, 32, 64, 0.3),
+    ("bf16", 2, 97, 2, 64, 64, 64, 0.3),
+    ("bf16", 1, 129, 3, 32, 128, 64, 0.2),
+    ("bf16", 1, 129, 3, 128, 32, 32, 0.2),
+    ("bf16", 1, 10, 4, 128, 128, 64, 0.5),
+    ("bf16", 1, 1, 2, 128, 128, 64, 0.5),
+    ("f32", 1, 1, 2, 32, 32, 16, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_shapes(case):
+    dtype, B, T, H, dk, dv, chunk, h0 = case
+    wl = synth.custom(name="small", seed=100 + SMALL.index(case), B=B, T=T, H=H, dk=dk, dv=dv,
+                      dtype=dtype, chunk=chunk, h0_std=h0)
+    _check(synth.generate(wl))
+
+
+def test_slow_decay_keeps_h0_visible():
+    """Slow decay so that h0 still shows in hT after many chunks."""
+    wl = synth.custom(name="slow", seed=21, B=2, T=300, H=2, dk=128, dv=128, dtype="bf16",
+                      chunk=64, h0_std=1.0, g_mean=-4.0)
+    _check(synth.generate(wl))
+
+
+def test_many_workgroups():
+    """More work items than compute units: several dispatch rounds."""
+    wl = synth.custom(name="wide", seed=22, B=6, T=70, H=16, dk=128, dv=128, dtype="bf16",
+                      chunk=64, h0_std=0.1)
+    _check(synth.generate(wl))
+
+
+@pytest.mark.parametrize("dtype,chunk", [("f32", 16), ("f32", 32), ("bf16", 32), ("bf16", 64)])
+def test_chunk_lengths_agree(dtype, chunk):
+    wl = synth.custom(name="chunks", seed=23, B=1, T=250, H=2, dk=32, dv=32, dtype=dtype,
+                      chunk=chunk, h0_std=0.2)
+    _check(synth.generate(wl))
+
+
+def test_packed_small():
+    wl = synth.custom(name="packed", seed=24, H=3, dk=128, dv=128, dtype="bf16", chunk=64,
+                      seq_lens=[65, 0, 1, 64, 200, 3, 0])
+    _check(synth.generate(wl))
+
+
+def test_packed_f32():
+    wl = synth.custom(name="packed32", seed=25, H=2, dk=32, dv=32, dtype="f32", chunk=16,
+                      h0_std=0.4, seq_lens=[17, 0, 33, 1, 16])
+    _check(synth.generate(wl))
+
+
+# ------------------------------------------------------- full-size workloads --
+
+SAMPLES = {
+    "small_state": [0, 37, 77, 127],
+    "wide_head": [0, 21, 42, 63],
+    "varlen": [0, 16 * 5 + 3, 16 * 17 + 9, 16 * 31 + 15],
+    "long_context": [0, 9],
+}
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_full_workload_sampled_chains(name):
+    """Full size, the benchmark's launch; the oracle checks sampled chains."""
+    inp = synth.generate(synth.WORKLOADS[name])
+    _check(inp, chains=SAMPLES[name])
+
+
+# ----------------------------------------------------------- bit-exactness --
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_packed_equals_per_sequence_bitwise():
+    lens = [100, 0, 64, 1, 129, 63]
+    wl = synth.custom(name="pk", seed=31, H=2, dk=128, dv=128, dtype="bf16", chunk=64,
+                      seq_lens=lens)
+    inp = synth.generate(wl)
+    d = device_inputs(inp)
+    h0 = torch.randn(len(lens), 2, 128, 128, device="cuda") * 0.1
+    d["h0"] = h0
+    out, hT = run_hip(inp, d=d)
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        one = dict(q=d["q"][s:e][None].contiguous(), k=d["k"][s:e][None].contiguous(),
+                   v=d["v"][s:e][None].contiguous(), g=d["g"][s:e][None].contiguous(),
+                   beta=d["beta"][s:e][None].contiguous(), h0=h0[n:n + 1].contiguous(),
+                   cu_seqlens=None)
+        o1, h1 = run_hip(inp, d=one)
+        assert torch.equal(_bits(out[s:e]), _bits(o1[0])), f"sequence {n} out"
+        assert torch.equal(_bits(hT[n]), _bits(h1[0])), f"sequence {n} hT"
+
+
+def test_causality_bitwise():
+    wl = synth.custom(name="causal", seed=32, B=1, T=256, H=2, dk=128, dv=128, dtype="bf16",
+                      chunk=64, h0_std=0.2)
+    inp = synth.generate(wl)
+    d = device_inputs(inp)
+    out, _ = run_hip(inp, d=d)
+    t = 100
+    d2 = {k: (v.clone() if v is not None else None) for k, v in d.items()}
+    for name in ("q", "k", "v"):
+        d2[name][:, t + 1:] = torch.randn_like(d2[name][:, t + 1:].float()).to(d2[name].dtype)
+    d2["g"][:, t + 1:] = -torch.rand_like(d2["g"][:, t + 1:])
+    d2["beta"][:, t + 1:] = torch.rand_like(d2["beta"][:, t + 1:])
+    out2, _ = run_hip(inp, d=d2)
+    assert torch.equal(_bits(out[:, : t + 1]), _bits(out2[:, : t + 1]))
+    assert not torch.equal(out[:, t + 1:], out2[:, t + 1:])
+
+
+@pytest.mark.parametrize("split", [64, 128, 192])
+def test_split_at_chunk_boundary_bitwise(split):
+    wl = synth.custom(name="split", seed=33, B=2, T=256, H=2, dk=128, dv=128, dtype="bf16",
+                      chunk=64, h0_std=0.3)
+    inp = synth.generate(wl)
+    d = device_inputs(inp)
+    out, hT = run_hip(inp, d=d)
+    part = lambda lo, hi, h0: dict(
+        q=d["q"][:, lo:hi].contiguous(), k=d["k"][:, lo:hi].contiguous(),
+        v=d["v"][:, lo:hi].contiguous(), g=d["g"][:, lo:hi].contiguous(),
+        beta=d["beta"][:, lo:hi].contiguous(), h0=h0, cu_seqlens=None)
+    oa, ha = run_hip(inp, d=part(0, split, d["h0"]))
+    ob, hb = run_hip(inp, d=part(split, 256, ha))
+    assert torch.equal(_bits(torch.cat([oa, ob], dim=1)), _bits(out))
+    assert torch.equal(_bits(hb), _bits(hT))
+
+
+def test_deterministic():
+    inp = synth.generate(synth.custom(name="det", seed=34, B=2, T=300, H=4, dk=128, dv=128,
+                                      dtype="bf16", chunk=64, h0_std=0.1))
+    d = device_inputs(inp)
+    o1, h1 = run_hip(inp, d=d)
+    o2, h2 = run_hip(inp, d=d)
+    assert torch.equal(_bits(o1), _bits(o2)) and torch.equal(_bits(h1), _bits(h2))
+
+
+def test_hT_may_alias_h0():
+    inp = synth.generate(synth.custom(name="alias", seed=35, B=2, T=130, H=2, dk=64, dv=64,
+                                      dtype="bf16", chunk=64, h0_std=0.5))
+    d = device_inputs(inp)
+    o1, h1 = run_hip(inp, d=d)
+    state = d["h0"].clone()
+    d["h0"] = state
+    o2, h2 = run_hip(inp, d=d, hT=state)
+    assert h2.data_ptr() == state.data_ptr()
+    assert torch.equal(_bits(o1), _bits(o2)) and torch.equal(_bits(h1), _bits(state))
+
+
+def test_empty_inputs():
+    # T == 0 (dense): hT = h0; zero-length packed sequences keep their h0.
+    inp = synth.generate(synth.custom(name="empty", seed=36, B=2, T=0, H=2, dk=32, dv=32,
+                                      dtype="bf16", chunk=64, h0_std=0.5))
+    out, hT = run_hip(inp)
+    assert out.numel() == 0
+    assert torch.equal(hT, dev(inp.h0))
+    inp = synth.generate(synth.custom(name="empty2", seed=37, H=2, dk=32, dv=32, dtype="bf16",
+                                      chunk=64, seq_lens=[0, 0, 5]))
+    d = device_inputs(inp)
+    d["h0"] = torch.randn(3, 2, 32, 32, device="cuda")
+    out, hT = run_hip(inp, d=d)
+    assert torch.equal(hT[:2], d["h0"][:2])
+
+
+def test_rejects_bad_args_without_launch():
+    import gated_deltanet_recurrence_delta_amd as gdn
+
+    inp = synth.generate(synth.custom(name="bad", seed=38, B=1, T=8, H=1, dk=32, dv=32,
+                                      dtype="bf16", chunk=64))
+    d = device_inputs(inp)
+    with pytest.raises(gdn.GdnError):
+        gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=16)
