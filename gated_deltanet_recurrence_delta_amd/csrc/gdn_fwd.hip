@@ -23,16 +23,16 @@
 //     M   <- Gam_C M + K^T diag(w) U
 //
 // Work decomposition: one workgroup per (chain, 32-wide value tile).  Value
-// columns never mix in the rule, so tiles are independent.  Per workgroup:
-//   * "value" waves (DVT/16 of them) each own 16 state columns: they keep M
-//     in MFMA accumulators for the whole sequence and run the state-
-//     dependent part of every chunk (K M, X, Tinv X, O, the state update);
-//   * two "prep" waves run one chunk ahead and build everything that does
-//     not depend on the state: the decay vectors, Tinv (Gram matrix, 16x16
-//     diagonal inverses on the VALU, block merges on the MFMA) and the
-//     masked decayed Q K^T;
-//   * all waves stage the next chunk's K and Q from HBM through registers
-//     into a triple-buffered, XOR-swizzled LDS ring.
+// columns never mix in the rule, so tiles are independent.  Per workgroup,
+// a three-stage pipeline over chunks (one LDS barrier per stage step):
+//   * the Gram wave loads chunk c+1 from HBM into registers while it stages
+//     chunk c (K, Q and this tile's V) into LDS, forms the decay vectors,
+//     the off-diagonal blocks of A and the masked decayed Q K^T;
+//   * one step later the solve wave forms the diagonal blocks of A and Tinv
+//     (16x16 diagonal inverses on the VALU, block merges on the MFMA);
+//   * one step after that the value waves (DVT/16 of them, 16 state columns
+//     each, M held in MFMA accumulators for the whole sequence) run the
+//     state-dependent part: K M, X, Tinv X, O, the state update.
 // One barrier per chunk.  No atomics: results are deterministic.
 //
 // Operand conventions: a 16x16xSLAB MFMA "fragment" gives every lane
@@ -193,6 +193,44 @@ __device__ static inline typename Mma<TI>::frag acc_frag(const f32x4* a, int s) 
   }
 }
 
+// ------------------------------------------------------------ cross-lane
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane
+// row with DPP row shifts, then the row totals are added across rows.  The
+// order of additions is fixed, so every call gives the same bits.
+__device__ static inline float wave_prefix_sum(float x, int lane) {
+  // DPP row_shr:n is control code 0x110 + n; lanes shifted in from outside
+  // the row read 0 (bound_ctrl).
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const float off = lane < 16 ? 0.f : (lane < 32 ? r0 : (lane < 48 ? r0 + r1 : (r0 + r1) + r2));
+  return x + off;
+}
+
+// Barrier that orders LDS only.  Waves share nothing through global memory
+// inside the kernel, so outstanding global loads and stores may stay in
+// flight across it.
+__device__ static inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Transposing LDS read (gfx950): within each 16-lane group, destination
+// lane i, element k receives element (i & 3) of the 8 bytes addressed by
+// source lane (i >> 2) + 4k.
+__device__ static inline bf16x4 lds_read_tr(const char* base, int off) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)(base + off));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 // ------------------------------------------------------------ configuration
 
 template <typename TI, int DK, int DVT, int C>
@@ -205,29 +243,31 @@ struct Cfg {
   static constexpr int NKB = DK / 16;     // 16-row key blocks of the state
   static constexpr int NKS = DK / SLAB;   // key slabs
   static constexpr int NDV = DVT / 16;    // value waves
-  static constexpr int NW = NDV + 2;      // + two prep waves
+  static constexpr int W_S = NDV;         // solve wave
+  static constexpr int W_G = NDV + 1;     // Gram / loader wave
+  static constexpr int NW = NDV + 2;
   static constexpr int NT = 64 * NW;
   static_assert(C % SLAB == 0 && DK % SLAB == 0 && DVT % 16 == 0, "shape");
   static_assert(NB <= 4, "chunk of at most 64 tokens");
 
   static constexpr int KQ_BYTES = C * DK * S;
+  static constexpr int V_BYTES = C * DVT * S;
   static constexpr int CC_BYTES = C * C * S;
-  static constexpr int VEC_BYTES = 3 * C * 4;  // beta, Gam, w
-  static constexpr int AD_STRIDE = 260;        // floats per padded 16x16 block
-  static constexpr int OFF_K = 0;                           // [3] K chunks
-  static constexpr int OFF_Q = OFF_K + 3 * KQ_BYTES;        // [3] Q chunks
-  static constexpr int OFF_T = OFF_Q + 3 * KQ_BYTES;        // [2] Tinv
-  static constexpr int OFF_P = OFF_T + 2 * CC_BYTES;        // [2] masked decayed Q K^T
-  static constexpr int OFF_VEC = OFF_P + 2 * CC_BYTES;      // [2] per-token vectors
-  static constexpr int OFF_A = OFF_VEC + 2 * VEC_BYTES;     // A, off-diagonal blocks
-  static constexpr int OFF_TT = OFF_A + CC_BYTES;           // Tinv^T
-  static constexpr int OFF_AD = OFF_TT + CC_BYTES;          // A diagonal blocks, fp32
+  static constexpr int VEC_BYTES = 4 * C * 4;  // beta, gamma, exp(gamma), exp(gamma_C - gamma)
+  static constexpr int AD_STRIDE = 260;        // floats per padded 16x16 fp32 block
+  static constexpr int OFF_K = 0;                         // [3] K ring
+  static constexpr int OFF_V = OFF_K + 3 * KQ_BYTES;      // [3] V ring (this tile's columns)
+  static constexpr int OFF_A = OFF_V + 3 * V_BYTES;       // [2] A, off-diagonal blocks
+  static constexpr int OFF_P = OFF_A + 2 * CC_BYTES;      // [3] masked decayed Q K^T
+  static constexpr int OFF_T = OFF_P + 3 * CC_BYTES;      // [2] Tinv
+  static constexpr int OFF_TT = OFF_T + 2 * CC_BYTES;     // [1] Tinv^T (solve wave only)
+  static constexpr int OFF_VEC = OFF_TT + CC_BYTES;       // [3] per-token vectors
+  static constexpr int OFF_AD = OFF_VEC + 3 * VEC_BYTES;  // [1] A diagonal blocks, fp32
   static constexpr int LDS = OFF_AD + NB * AD_STRIDE * 4;
 
-  // Staging of one K or Q chunk: 16-byte granules per thread.
-  static constexpr int GRK = DK * S / 16;   // granules per token row
-  static constexpr int NG = C * GRK;
-  static constexpr int NPT = (NG + NT - 1) / NT;
+  // Solve-wave staging of this tile's V: 16-byte granules per lane.
+  static constexpr int GRV = DVT * S / 16;  // granules per v token row (this tile)
+  static constexpr int NPV = (C * GRV + 63) / 64;
 };
 
 struct Params {
@@ -252,20 +292,28 @@ __device__ static inline int xcd_remap(int bid, int n) {
   return xcd * q + (xcd < r ? xcd : r) + slot;
 }
 
+// Chunk c flows through three stages, one per loop iteration, with one
+// LDS barrier between iterations:
+//   iteration c   : Gram wave  -- stage K of chunk c into LDS, decay
+//                   vectors, off-diagonal A blocks, P (its K and Q
+//                   fragments were loaded two iterations earlier);
+//                   solve wave -- stage this tile's V of chunk c into LDS;
+//   iteration c+1 : solve wave -- diagonal A blocks, Tinv;
+//   iteration c+2 : value waves -- the state-dependent products.
 template <typename TI, int DK, int DVT, int C>
 __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const Params p) {
   using CF = Cfg<TI, DK, DVT, C>;
   using MM = Mma<TI>;
   using F = typename MM::frag;
   using SK = Swz<TI, DK>;
+  using SV = Swz<TI, DVT>;
   constexpr int SLAB = CF::SLAB, E = CF::E, BPS = CF::BPS;
   constexpr int NB = CF::NB, NTS = CF::NTS, NKB = CF::NKB, NKS = CF::NKS, NDV = CF::NDV;
 
   __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q4 = lane >> 4, n16 = lane & 15;
 
   const int item = xcd_remap(blockIdx.x, p.nwg);
@@ -282,51 +330,41 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
     len = p.T;
   }
   const int NC = (len + C - 1) / C;
+  const int NIT = NC > 0 ? NC + 2 : 0;
   const long kq_stride = (long)H * DK * CF::S;  // bytes between tokens in q/k
+  const long v_stride = (long)H * p.dv * CF::S;
   const char* qbase = p.q + hh * (long)DK * CF::S;
   const char* kbase = p.k + hh * (long)DK * CF::S;
+  const char* vbase = p.v + ((long)hh * p.dv + tile * DVT) * CF::S;
+  auto clamp_tok = [&](int t) { return t < len ? t : len - 1; };
 
-  // ---------------------------------------------------- K/Q staging
-  uint4 stK[CF::NPT], stQ[CF::NPT];
-  auto stage_load = [&](int c) {
+  auto kbuf = [&](int c) { return smem + CF::OFF_K + (c % 3) * CF::KQ_BYTES; };
+  auto vbuf = [&](int c) { return smem + CF::OFF_V + (c % 3) * CF::V_BYTES; };
+  auto abuf = [&](int c) { return smem + CF::OFF_A + (c & 1) * CF::CC_BYTES; };
+  auto pbuf = [&](int c) { return smem + CF::OFF_P + (c % 3) * CF::CC_BYTES; };
+  auto tbuf = [&](int c) { return smem + CF::OFF_T + (c & 1) * CF::CC_BYTES; };
+  auto vecb = [&](int c) { return reinterpret_cast<float*>(smem + CF::OFF_VEC + (c % 3) * CF::VEC_BYTES); };
+
+  // Q or K fragments of chunk c straight from global memory: fragment
+  // (tb, s) of lane (n16, q4) is row 16 tb + n16, key positions
+  // s*SLAB + E*q4 .. +E-1 (16 bytes).
+  auto load_frags = [&](const char* base, int c, F (&f)[NB][NKS]) {
 #pragma unroll
-    for (int i = 0; i < CF::NPT; ++i) {
-      const int gi = tid + CF::NT * i;
-      if (CF::NG % CF::NT == 0 || gi < CF::NG) {
-        const int row = gi / CF::GRK, gc = gi % CF::GRK;
-        int t = c * C + row;
-        t = t < len ? t : len - 1;
-        const long off = (rowbase + t) * kq_stride + gc * 16;
-        stK[i] = *reinterpret_cast<const uint4*>(kbase + off);
-        stQ[i] = *reinterpret_cast<const uint4*>(qbase + off);
-      }
+    for (int tb = 0; tb < NB; ++tb) {
+      const long row = rowbase + clamp_tok(c * C + 16 * tb + n16);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        f[tb][s] = *reinterpret_cast<const F*>(base + row * kq_stride + (s * SLAB + E * q4) * CF::S);
     }
   };
-  auto stage_store = [&](int c) {
-    char* sk = smem + CF::OFF_K + (c % 3) * CF::KQ_BYTES;
-    char* sq = smem + CF::OFF_Q + (c % 3) * CF::KQ_BYTES;
-#pragma unroll
-    for (int i = 0; i < CF::NPT; ++i) {
-      const int gi = tid + CF::NT * i;
-      if (CF::NG % CF::NT == 0 || gi < CF::NG) {
-        const int row = gi / CF::GRK, gc = gi % CF::GRK;
-        lds_st<uint4>(sk, SK::goff(row, gc), stK[i]);
-        lds_st<uint4>(sq, SK::goff(row, gc), stQ[i]);
-      }
-    }
-  };
-
-  if (NC > 0) {
-    stage_load(0);
-    stage_store(0);
-  }
-  __syncthreads();
 
   if (wave < NDV) {
-    // =========================================================== value wave
+    // =========================================================== value waves
     const int dvcol = tile * DVT + wave * 16 + n16;  // this lane's state column
     const long sbase = (long)chain * DK * p.dv;      // h0/hT slab of this chain
-    // Accumulator block b, element e holds M[key(b, 4q+e)][dvcol].
+    // Accumulator block b, element e holds M[key(b, 4q+e)][dvcol].  For bf16
+    // the key order makes two stacked blocks a fragment with natural key
+    // positions and lets one transposing read fetch four keys.
     auto key_of = [&](int b, int r) -> int {
       if constexpr (BPS == 2) {
         return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3);
@@ -341,50 +379,83 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
       for (int e = 0; e < 4; ++e)
         Macc[b][e] = p.h0 ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + dvcol] : 0.f;
     }
-    const char* vbase = p.v + ((long)hh * p.dv + dvcol) * CF::S;
-    const long v_stride = (long)H * p.dv * CF::S;
-    float Vr[NB][4];
-    auto load_v = [&](int c) {
+
+    // One step: chunk c = it - 2 with its Q fragments in `qcur`; Q of chunk
+    // c+1 is fetched into `qnxt` for the next step.
+    auto step = [&](int it, F (&qcur)[NB][NKS], F (&qnxt)[NB][NKS]) {
+      const int c = it - 2;
+      if (c + 1 >= 0 && c + 1 < NC) load_frags(qbase, c + 1, qnxt);
+      if (c >= 0) {
+        const char* sk = kbuf(c);
+        const char* sv = vbuf(c);
+        const char* st = tbuf(c);
+        const char* sp = pbuf(c);
+        const float* vec = vecb(c);
+
+        // LDS reads for the first products: K fragments and V.
+        F Kf[NB][NKS];
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb)
+        for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          int t = c * C + 16 * tb + 4 * q4 + e;
-          t = t < len ? t : len - 1;
-          Vr[tb][e] = to_f(*reinterpret_cast<const TI*>(vbase + (rowbase + t) * v_stride));
+          for (int s = 0; s < NKS; ++s) Kf[tb][s] = frag_nat<TI, DK>(sk, 16 * tb + n16, s * SLAB, q4);
+        // V in accumulator layout: Vc[tb][e] = V[16 tb + 4 q + e][16 wave + n16].
+        f32x4 Vc[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          if constexpr (sizeof(TI) == 2) {
+            const int src = lane & 15;
+            const bf16x4 r = lds_read_tr(sv, SV::off(16 * tb + 4 * q4 + (src >> 2), 16 * wave + 4 * (src & 3)));
+            Vc[tb] = f32x4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              Vc[tb][e] = lds_ld<float>(sv, SV::off(16 * tb + 4 * q4 + e, 16 * wave + n16));
+          }
         }
-    };
-    if (NC > 0) load_v(0);
-
-    for (int it = 0; it <= NC; ++it) {
-      if (it + 1 < NC) stage_load(it + 1);
-      if (it >= 1) {
-        const int c = it - 1;
-        const char* sk = smem + CF::OFF_K + (c % 3) * CF::KQ_BYTES;
-        const char* sq = smem + CF::OFF_Q + (c % 3) * CF::KQ_BYTES;
-        const char* st = smem + CF::OFF_T + (c & 1) * CF::CC_BYTES;
-        const char* sp = smem + CF::OFF_P + (c & 1) * CF::CC_BYTES;
-        const float* vec = reinterpret_cast<const float*>(smem + CF::OFF_VEC + (c & 1) * CF::VEC_BYTES);
-
-        // State as MFMA fragments (key positions in natural order).
         F Mf[NKS];
 #pragma unroll
         for (int s = 0; s < NKS; ++s) Mf[s] = acc_frag<TI>(Macc, s);
 
-        // Y = K M ; X = beta (V - Gam Y)
-        f32x4 X[NB];
+        // Y = K M
+        f32x4 Y[NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
           f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < NKS; ++s)
-            y = MM::mma(frag_nat<TI, DK>(sk, 16 * tb + n16, s * SLAB, q4), Mf[s], y);
-          const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + 16 * tb + 4 * q4);
-          const f32x4 gm = *reinterpret_cast<const f32x4*>(vec + C + 16 * tb + 4 * q4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) X[tb][e] = bt[e] * (Vr[tb][e] - gm[e] * y[e]);
+          for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[tb][s], Mf[s], y);
+          Y[tb] = y;
         }
-        if (c + 1 < NC) load_v(c + 1);
+
+        // LDS reads for the later products: Tinv, P.
+        F Tf[NB][NTS], Pf[NB][NTS];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int s = 0; s <= (16 * tb + 15) / SLAB; ++s) {
+            Tf[tb][s] = frag_pi<TI, C>(st, 16 * tb + n16, s * SLAB, q4);
+            Pf[tb][s] = frag_pi<TI, C>(sp, 16 * tb + n16, s * SLAB, q4);
+          }
+
+        // O^T, first part: (M^T Q^T) diag(Gam); independent of Y, fills the
+        // MFMA pipe while X is formed.
+        f32x4 O[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) o = MM::mma(Mf[s], qcur[tb][s], o);
+          O[tb] = o;
+        }
+
+        // X = beta (V - Gam Y)
+        f32x4 X[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + 16 * tb + 4 * q4);
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(vec + 2 * C + 16 * tb + 4 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) X[tb][e] = bt[e] * (Vc[tb][e] - gm[e] * Y[tb][e]);
+        }
         F Xf[NTS];
 #pragma unroll
         for (int s = 0; s < NTS; ++s) Xf[s] = acc_frag<TI>(X, s);
@@ -395,16 +466,36 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
         for (int tb = 0; tb < NB; ++tb) {
           f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s <= (16 * tb + 15) / SLAB; ++s)
-            u = MM::mma(frag_pi<TI, C>(st, 16 * tb + n16, s * SLAB, q4), Xf[s], u);
+          for (int s = 0; s <= (16 * tb + 15) / SLAB; ++s) u = MM::mma(Tf[tb][s], Xf[s], u);
           U[tb] = u;
         }
+
+        // Transposed K for the state update (tokens along the contraction).
+        F KT[NKB][NTS];
+#pragma unroll
+        for (int b = 0; b < NKB; ++b)
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) {
+            if constexpr (BPS == 2) {
+              // Two transposing reads: tokens 32s + 4q + k and 32s + 16 + 4q + k
+              // of keys key_of(b, n16).
+              const int src = lane & 15;
+              const int key0 = 32 * (b >> 1) + 8 * (src & 3) + 4 * (b & 1);
+              const bf16x4 lo = lds_read_tr(sk, SK::off(32 * s + 4 * q4 + (src >> 2), key0));
+              const bf16x4 hi = lds_read_tr(sk, SK::off(32 * s + 16 + 4 * q4 + (src >> 2), key0));
+              KT[b][s] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < E; ++e) KT[b][s][e] = lds_ld<TI>(sk, SK::off(s * 16 + 4 * q4 + e, key_of(b, n16)));
+            }
+          }
+
         F Uf[NTS], Wf[NTS];
         {
           f32x4 WU[NB];
 #pragma unroll
           for (int tb = 0; tb < NB; ++tb) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(vec + 2 * C + 16 * tb + 4 * q4);
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(vec + 3 * C + 16 * tb + 4 * q4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) WU[tb][e] = wv[e] * U[tb][e];
           }
@@ -415,19 +506,27 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
           }
         }
 
-        // O^T = (M^T Q^T) diag(Gam) + U^T P^T, one 16-token block at a time.
+        // M <- Gam_C M + K^T diag(w) U
+        const float gC = vec[2 * C + C - 1];
+#pragma unroll
+        for (int b = 0; b < NKB; ++b) {
+          f32x4 m = Macc[b];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m[e] *= gC;
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) m = MM::mma(KT[b][s], Wf[s], m);
+          Macc[b] = m;
+        }
+
+        // O^T, second part: + U^T P^T; store.
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
-          f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < NKS; ++s)
-            o = MM::mma(Mf[s], frag_nat<TI, DK>(sq, 16 * tb + n16, s * SLAB, q4), o);
-          const float gcol = vec[C + 16 * tb + n16];
+          f32x4 o = O[tb];
+          const float gcol = vec[2 * C + 16 * tb + n16];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] *= gcol;
 #pragma unroll
-          for (int s = 0; s <= (16 * tb + 15) / SLAB; ++s)
-            o = MM::mma(Uf[s], frag_pi<TI, C>(sp, 16 * tb + n16, s * SLAB, q4), o);
+          for (int s = 0; s <= (16 * tb + 15) / SLAB; ++s) o = MM::mma(Uf[s], Pf[tb][s], o);
           const int t = c * C + 16 * tb + n16;
           if (t < len) {
             char* dst = p.out + (((rowbase + t) * H + hh) * (long)p.dv + tile * DVT + wave * 16 + 4 * q4) * CF::S;
@@ -438,35 +537,14 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
             }
           }
         }
-
-        // M <- Gam_C M + K^T diag(w) U
-        const float gC = vec[C + C - 1];
-#pragma unroll
-        for (int b = 0; b < NKB; ++b) {
-          f32x4 m = Macc[b];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) m[e] *= gC;
-          const int key = key_of(b, n16);
-#pragma unroll
-          for (int s = 0; s < NTS; ++s) {
-            F a;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-              int tok;
-              if constexpr (BPS == 2) {
-                tok = s * 32 + 16 * (e >> 2) + 4 * q4 + (e & 3);
-              } else {
-                tok = s * 16 + 4 * q4 + e;
-              }
-              a[e] = lds_ld<TI>(sk, SK::off(tok, key));
-            }
-            m = MM::mma(a, Wf[s], m);
-          }
-          Macc[b] = m;
-        }
       }
-      if (it + 1 < NC) stage_store(it + 1);
-      __syncthreads();
+      lds_barrier();
+    };
+
+    F qa[NB][NKS], qb[NB][NKS];
+    for (int it = 0; it < NIT; it += 2) {
+      step(it, qa, qb);
+      if (it + 1 < NIT) step(it + 1, qb, qa);
     }
 
 #pragma unroll
@@ -474,177 +552,247 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + dvcol] = Macc[b][e];
-  } else {
-    // ============================================================ prep waves
-    const bool p0 = wave == NDV;
-    float gv = 0.f, bv = 0.f;
-    auto load_gb = [&](int c) {
-      gv = 0.f;
-      bv = 0.f;
-      const int t = c * C + lane;
-      if (lane < C && t < len) {
-        const long idx = (rowbase + t) * H + hh;
-        gv = p.g[idx];
-        bv = p.beta[idx];
+
+  } else if (wave == CF::W_S) {
+    // ============================================================ solve wave
+    // Also stages this tile's V two chunks ahead.
+    auto load_v = [&](int c, uint4 (&st)[CF::NPV]) {
+#pragma unroll
+      for (int i = 0; i < CF::NPV; ++i) {
+        const int gi = lane + 64 * i;
+        if ((C * CF::GRV) % 64 == 0 || gi < C * CF::GRV) {
+          const int row = gi / CF::GRV, gc = gi % CF::GRV;
+          st[i] = *reinterpret_cast<const uint4*>(vbase + (rowbase + clamp_tok(c * C + row)) * v_stride + gc * 16);
+        }
       }
     };
-    if (NC > 0) load_gb(0);
-
-    for (int it = 0; it <= NC; ++it) {
-      if (it + 1 < NC) stage_load(it + 1);
+    auto step = [&](int it, uint4 (&vcur)[CF::NPV]) {
       if (it < NC) {
-        const int c = it;
-        const char* sk = smem + CF::OFF_K + (c % 3) * CF::KQ_BYTES;
-        const char* sq = smem + CF::OFF_Q + (c % 3) * CF::KQ_BYTES;
-        char* st = smem + CF::OFF_T + (c & 1) * CF::CC_BYTES;
-        char* sp = smem + CF::OFF_P + (c & 1) * CF::CC_BYTES;
-        float* vec = reinterpret_cast<float*>(smem + CF::OFF_VEC + (c & 1) * CF::VEC_BYTES);
-
-        // In-chunk cumulative log-decay (inclusive scan over the lanes).
-        float gam = gv;
+        char* sv = vbuf(it);
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float y = __shfl_up(gam, d, 64);
-          if (lane >= d) gam += y;
+        for (int i = 0; i < CF::NPV; ++i) {
+          const int gi = lane + 64 * i;
+          if ((C * CF::GRV) % 64 == 0 || gi < C * CF::GRV) lds_st<uint4>(sv, SV::goff(gi / CF::GRV, gi % CF::GRV), vcur[i]);
         }
-        const float bet = bv;
-        if (c + 1 < NC) load_gb(c + 1);
+        if (it + 2 < NC) load_v(it + 2, vcur);
+      }
+      const int c = it - 1;
+      if (c >= 0 && c < NC) {
+        const char* sk = kbuf(c);
+        const char* sa = abuf(c);
+        char* st = tbuf(c);
+        char* stt = smem + CF::OFF_TT;
+        float* sad = reinterpret_cast<float*>(smem + CF::OFF_AD);
+        const float* vec = vecb(c);
 
-        // Per-lane decay of the 16-token block rows (i = 16*bi + n16) and
-        // of the accumulator rows (j = 16*bj + 4*q4 + e).
-        float gi[NB], bi_[NB], gj[NB][4];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          gi[b] = __shfl(gam, 16 * b + n16, 64);
-          bi_[b] = __shfl(bet, 16 * b + n16, 64);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) gj[b][e] = __shfl(gam, 16 * b + 4 * q4 + e, 64);
-        }
-
+        // Diagonal blocks of A: beta_i (K K^T)_ij exp(gamma_i - gamma_j), j < i.
         F Kf[NB][NKS];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int s = 0; s < NKS; ++s) Kf[b][s] = frag_nat<TI, DK>(sk, 16 * b + n16, s * SLAB, q4);
+        float gi[NB], bi[NB];
+        f32x4 gj[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          gi[b] = vec[C + 16 * b + n16];
+          bi[b] = vec[16 * b + n16];
+          gj[b] = *reinterpret_cast<const f32x4*>(vec + C + 16 * b + 4 * q4);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) a = MM::mma(Kf[b][s], Kf[b][s], a);
+          // a[e] = (K K^T)[i = 16 b + n16][j = 16 b + 4 q4 + e]
+          f32x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool keep = 4 * q4 + e < n16;
+            r[e] = keep ? bi[b] * a[e] * __expf(gi[b] - gj[b][e]) : 0.f;
+          }
+          *reinterpret_cast<f32x4*>(sad + b * CF::AD_STRIDE + 16 * n16 + 4 * q4) = r;
+        }
 
-        if (!p0) {
-          // ---- prep wave 1: per-token vectors and P = masked decayed Q K^T
-          const float gC = __shfl(gam, C - 1, 64);
-          if (lane < C) {
-            vec[lane] = bet;
-            vec[C + lane] = __expf(gam);
-            vec[2 * C + lane] = __expf(gC - gam);
+        // Diagonal 16x16 blocks of Tinv: forward substitution in fp32.  Lane
+        // (block q4, column n16) computes column n16 of its block's inverse;
+        // the rows of A it needs are all loaded before the substitution.
+        if (q4 < NB) {
+          const float* ad = sad + q4 * CF::AD_STRIDE;
+          f32x4 arow[16][4];
+#pragma unroll
+          for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int l4 = 0; l4 < i; l4 += 4) arow[i][l4 >> 2] = *reinterpret_cast<const f32x4*>(ad + 16 * i + l4);
+          __builtin_amdgcn_sched_barrier(0);
+          float tc[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float s = (i == n16) ? 1.f : 0.f;
+#pragma unroll
+            for (int l = 0; l + 1 < i; ++l) s -= arow[i][l >> 2][l & 3] * tc[l];
+            if (i > 0) s -= arow[i][(i - 1) >> 2][(i - 1) & 3] * tc[i - 1];
+            tc[i] = s;
           }
+          const int base = 16 * q4;
 #pragma unroll
-          for (int b1 = 0; b1 < NB; ++b1) {  // row block of P (token i)
-            F Qf[NKS];
+          for (int i = 0; i < 16; ++i) st1<TI, C>(st, base + i, base + n16, tc[i]);
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) Qf[s] = frag_nat<TI, DK>(sq, 16 * b1 + n16, s * SLAB, q4);
+          for (int i = 0; i < 16; i += 4)
+            st4<TI, C>(stt, base + n16, base + i, f32x4{tc[i], tc[i + 1], tc[i + 2], tc[i + 3]});
+        }
+        if constexpr (BPS == 2) {
 #pragma unroll
-            for (int b2 = 0; b2 <= b1; ++b2) {  // column block (token j)
-              f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int s = 0; s < NKS; ++s) a = MM::mma(Kf[b2][s], Qf[s], a);
-              // a[e] = (Q K^T)[i = 16 b1 + n16][j = 16 b2 + 4 q4 + e]
-              f32x4 r;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const bool keep = (16 * b2 + 4 * q4 + e) <= (16 * b1 + n16);
-                const float d = keep ? gi[b1] - gj[b2][e] : 0.f;
-                r[e] = keep ? a[e] * __expf(d) : 0.f;
-              }
-              st4<TI, C>(sp, 16 * b1 + n16, 16 * b2 + 4 * q4, r);
-            }
-            if (BPS == 2 && (b1 & 1) == 0 && b1 + 1 < NB)
-              st4<TI, C>(sp, 16 * b1 + n16, 16 * (b1 + 1) + 4 * q4, f32x4{0.f, 0.f, 0.f, 0.f});
-          }
-        } else {
-          // ---- prep wave 0: A, then Tinv = (I + A)^{-1}
-          char* sa = smem + CF::OFF_A;
-          char* stt = smem + CF::OFF_TT;
-          float* sad = reinterpret_cast<float*>(smem + CF::OFF_AD);
-#pragma unroll
-          for (int b1 = 0; b1 < NB; ++b1) {
-#pragma unroll
-            for (int b2 = 0; b2 <= b1; ++b2) {
-              f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int s = 0; s < NKS; ++s) a = MM::mma(Kf[b2][s], Kf[b1][s], a);
-              // a[e] = (K K^T)[i = 16 b1 + n16][j = 16 b2 + 4 q4 + e]
-              f32x4 r;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const bool keep = (16 * b2 + 4 * q4 + e) < (16 * b1 + n16);
-                const float d = keep ? gi[b1] - gj[b2][e] : 0.f;
-                r[e] = keep ? bi_[b1] * a[e] * __expf(d) : 0.f;
-              }
-              if (b2 == b1) {
-                *reinterpret_cast<f32x4*>(sad + b1 * CF::AD_STRIDE + 16 * n16 + 4 * q4) = r;
-              } else {
-                st4<TI, C>(sa, 16 * b1 + n16, 16 * b2 + 4 * q4, r);
-              }
-            }
-          }
+          for (int b1 = 0; b1 + 1 < NB; b1 += 2)
+            st4<TI, C>(st, 16 * b1 + n16, 16 * (b1 + 1) + 4 * q4, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
 
-          // Diagonal 16x16 blocks: forward substitution on the VALU in fp32.
-          // Lane (block q4, column n16) computes column n16 of the inverse.
-          if (q4 < NB) {
-            const float* ad = sad + q4 * CF::AD_STRIDE;
-            float tc[16];
+        // Off-diagonal blocks, by distance from the diagonal:
+        //   Tinv_ij = -Tinv_ii * sum_{j <= l < i} A_il Tinv_lj.
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float s = (i == n16) ? 1.f : 0.f;
+        for (int d = 1; d < NB; ++d) {
+          f32x4 R[NB];
 #pragma unroll
-              for (int l4 = 0; l4 < i; l4 += 4) {
-                const f32x4 arow = *reinterpret_cast<const f32x4*>(ad + 16 * i + l4);
+          for (int i = d; i < NB; ++i) {
+            const int j = i - d;
+            const int L = 16 * d;
+            f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                  if (l4 + u < i) s -= arow[u] * tc[l4 + u];
-              }
-              tc[i] = s;
+            for (int s = 0; s * SLAB < L; ++s) {
+              const bool valid = s * SLAB + E * q4 < L;
+              const F fa = valid ? frag_nat<TI, C>(sa, 16 * i + n16, 16 * j + s * SLAB, q4) : MM::zero();
+              const F fb = valid ? frag_nat<TI, C>(stt, 16 * j + n16, 16 * j + s * SLAB, q4) : MM::zero();
+              r = MM::mma(fa, fb, r);
             }
-            const int base = 16 * q4;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st1<TI, C>(st, base + i, base + n16, tc[i]);
-#pragma unroll
-            for (int i = 0; i < 16; i += 4)
-              st4<TI, C>(stt, base + n16, base + i, f32x4{tc[i], tc[i + 1], tc[i + 2], tc[i + 3]});
+            R[i] = r;  // R[row 16 i + 4 q4 + e][col 16 j + n16]
           }
-          if constexpr (BPS == 2) {
 #pragma unroll
-            for (int b1 = 0; b1 + 1 < NB; b1 += 2)
-              st4<TI, C>(st, 16 * b1 + n16, 16 * (b1 + 1) + 4 * q4, f32x4{0.f, 0.f, 0.f, 0.f});
-          }
-
-          // Off-diagonal blocks: Tinv_ij = -Tinv_ii * sum_{j<=l<i} A_il Tinv_lj.
+          for (int i = d; i < NB; ++i) {
+            const int j = i - d;
+            f32x4 o = MM::mma(frag_pi1<TI, C>(st, 16 * i + n16, 16 * i, q4), MM::from_acc1(R[i]),
+                              f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int i = 1; i < NB; ++i) {
-#pragma unroll
-            for (int j = 0; j < i; ++j) {
-              const int L = 16 * (i - j);
-              f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int s = 0; s * SLAB < L; ++s) {
-                const bool valid = s * SLAB + E * q4 < L;
-                const F fa = valid ? frag_nat<TI, C>(sa, 16 * i + n16, 16 * j + s * SLAB, q4) : MM::zero();
-                const F fb = valid ? frag_nat<TI, C>(stt, 16 * j + n16, 16 * j + s * SLAB, q4) : MM::zero();
-                r = MM::mma(fa, fb, r);
-              }
-              // r[e] = R[row 16 i + 4 q4 + e][col 16 j + n16]
-              f32x4 o = MM::mma(frag_pi1<TI, C>(st, 16 * i + n16, 16 * i, q4), MM::from_acc1(r),
-                                f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                o[e] = -o[e];
-                st1<TI, C>(st, 16 * i + 4 * q4 + e, 16 * j + n16, o[e]);
-              }
-              st4<TI, C>(stt, 16 * j + n16, 16 * i + 4 * q4, o);
+            for (int e = 0; e < 4; ++e) {
+              o[e] = -o[e];
+              st1<TI, C>(st, 16 * i + 4 * q4 + e, 16 * j + n16, o[e]);
             }
+            st4<TI, C>(stt, 16 * j + n16, 16 * i + 4 * q4, o);
           }
         }
       }
-      if (it + 1 < NC) stage_store(it + 1);
-      __syncthreads();
+      lds_barrier();
+    };
+
+    uint4 va[CF::NPV], vb[CF::NPV];
+    if (NC > 0) load_v(0, va);
+    if (NC > 1) load_v(1, vb);
+    for (int it = 0; it < NIT; it += 2) {
+      step(it, va);
+      if (it + 1 < NIT) step(it + 1, vb);
+    }
+  } else {
+    // ===================================================== Gram / loader wave
+    // K and Q fragments (and g, beta) are fetched two chunks ahead into one
+    // of two register sets and used straight from registers.
+    auto load_gb = [&](int c, float& sg, float& sb) {
+      sg = 0.f;
+      sb = 0.f;
+      const int t = c * C + lane;
+      if (lane < C && t < len) {
+        const long idx = (rowbase + t) * H + hh;
+        sg = p.g[idx];
+        sb = p.beta[idx];
+      }
+    };
+    auto step = [&](int it, F (&Kc)[NB][NKS], F (&Qc)[NB][NKS], float& sg, float& sb) {
+      const int c = it;
+      if (c < NC) {
+        char* sk = kbuf(c);
+        char* sa = abuf(c);
+        char* sp = pbuf(c);
+        float* vec = vecb(c);
+        // Stage K of chunk c for the solve and value waves.
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) lds_st<F>(sk, SK::off(16 * tb + n16, s * SLAB + E * q4), Kc[tb][s]);
+
+        // In-chunk cumulative log-decay and the per-token vectors.
+        const float gam = wave_prefix_sum(sg, lane);
+        const float bet = sb;
+        const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), C - 1));
+        if (lane < C) {
+          vec[lane] = bet;
+          vec[C + lane] = gam;
+          vec[2 * C + lane] = __expf(gam);
+          vec[3 * C + lane] = __expf(gC - gam);
+        }
+        float gi[NB], bi[NB];
+        f32x4 gj[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          gi[b] = vec[C + 16 * b + n16];
+          bi[b] = vec[16 * b + n16];
+          gj[b] = *reinterpret_cast<const f32x4*>(vec + C + 16 * b + 4 * q4);
+        }
+
+#pragma unroll
+        for (int b1 = 0; b1 < NB; ++b1) {
+#pragma unroll
+          for (int b2 = 0; b2 <= b1; ++b2) {
+            // Decay exp(gamma_i - gamma_j), i = 16 b1 + n16, j = 16 b2 + 4 q4 + e,
+            // shared by A (j < i) and P (j <= i); zero above the diagonal.
+            f32x4 dec;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool keep = b2 < b1 || 4 * q4 + e <= n16;
+              dec[e] = keep ? __expf(gi[b1] - gj[b2][e]) : 0.f;
+            }
+            f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) pq = MM::mma(Kc[b2][s], Qc[b1][s], pq);
+            // pq[e] = (Q K^T)[i][j]
+            f32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = pq[e] * dec[e];
+            st4<TI, C>(sp, 16 * b1 + n16, 16 * b2 + 4 * q4, r);
+            if (b2 < b1) {  // off-diagonal block of A (the solve wave forms the diagonal ones)
+              f32x4 kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int s = 0; s < NKS; ++s) kk = MM::mma(Kc[b2][s], Kc[b1][s], kk);
+              f32x4 ra;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ra[e] = bi[b1] * kk[e] * dec[e];
+              st4<TI, C>(sa, 16 * b1 + n16, 16 * b2 + 4 * q4, ra);
+            }
+          }
+          if (BPS == 2 && (b1 & 1) == 0 && b1 + 1 < NB)
+            st4<TI, C>(sp, 16 * b1 + n16, 16 * (b1 + 1) + 4 * q4, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        if (c + 2 < NC) {
+          load_frags(kbase, c + 2, Kc);
+          load_frags(qbase, c + 2, Qc);
+          load_gb(c + 2, sg, sb);
+        }
+      }
+      lds_barrier();
+    };
+
+    F ka[NB][NKS], qa_[NB][NKS], kb[NB][NKS], qb_[NB][NKS];
+    float ga = 0.f, ba = 0.f, gb = 0.f, bb = 0.f;
+    if (NC > 0) {
+      load_frags(kbase, 0, ka);
+      load_frags(qbase, 0, qa_);
+      load_gb(0, ga, ba);
+    }
+    if (NC > 1) {
+      load_frags(kbase, 1, kb);
+      load_frags(qbase, 1, qb_);
+      load_gb(1, gb, bb);
+    }
+    for (int it = 0; it < NIT; it += 2) {
+      step(it, ka, qa_, ga, ba);
+      if (it + 1 < NIT) step(it + 1, kb, qb_, gb, bb);
     }
   }
 }
@@ -665,9 +813,6 @@ int by_chunk(const Params& p, int nwg, hipStream_t s, int chunk) {
   } else {
     if (chunk == 16) return launch<TI, DK, 32, 16>(p, nwg, s);
     if (chunk == 32) return launch<TI, DK, 32, 32>(p, nwg, s);
-    if constexpr (DK == 32) {
-      if (chunk == 64) return launch<TI, DK, 32, 64>(p, nwg, s);
-    }
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -700,7 +845,7 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   if ((dk != 32 && dk != 64 && dk != 128) || (dv != 32 && dv != 64 && dv != 128))
     return GDN_ERR_UNSUPPORTED;
   if (dtype == GDN_BF16 && chunk == 16) return GDN_ERR_UNSUPPORTED;
-  if (dtype == GDN_F32 && chunk == 64 && dk != 32) return GDN_ERR_UNSUPPORTED;
+  if (dtype == GDN_F32 && chunk == 64) return GDN_ERR_UNSUPPORTED;
   const int ntile = dv / 32;
   const long nwg_l = (long)B * H * ntile;
   if (nwg_l > 0x7fffffffL) return GDN_ERR_INVALID_ARG;

@@ -67,9 +67,9 @@ extern "C" {
  * Sizes: B >= 0, T >= 0, H >= 1.  dk, dv in {32, 64, 128}.
  * dtype: GDN_F32 or GDN_BF16.
  * chunk: tokens per chunk; 0 selects 64 for GDN_BF16 and 16 for GDN_F32.
- *        GDN_BF16 accepts 32 and 64; GDN_F32 accepts 16 and 32, and 64 when
- *        dk == 32 (larger fp32 tiles exceed the 160 KB of LDS).  The result
- *        does not depend on the chunk length beyond floating-point rounding.
+ *        GDN_BF16 accepts 32 and 64; GDN_F32 accepts 16 and 32 (64-token
+ *        fp32 tiles exceed the 160 KB of LDS).  The result does not depend
+ *        on the chunk length beyond floating-point rounding.
  * stream: a hipStream_t (NULL = the null stream).
  *
  * Pointers: q, k, v, g, beta and out are required when T > 0 and may be

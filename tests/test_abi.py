@@ -58,7 +58,7 @@ def test_invalid_sizes(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(dk=16), dict(dv=256), dict(dk=96), dict(dtype=1, chunk=16),
-                                dict(dtype=0, chunk=64, dk=128)])
+                                dict(dtype=0, chunk=64, dk=128), dict(dtype=0, chunk=64, dk=32)])
 def test_unsupported(kw):
     assert _call(**kw) == UNSUPPORTED
 

@@ -35,7 +35,7 @@ SMALL = [
     ("f32", 2, 200, 3, 32, 32, 16, 0.3),
     ("f32", 1, 77, 2, 64, 32, 32, 0.3),
     ("f32", 1, 90, 2, 128, 64, 32, 0.0),
-    ("f32", 1, 130, 2, 32, 128, 64, 0.5),
+    ("f32", 1, 130, 2, 32, 128, 32, 0.5),
     ("bf16", 2, 200, 3, 128, 128, 64, 0.3),
     ("bf16", 1, 333, 2, 128, 128, 32, 0.0),
     ("bf16", 3, 150, 2, 32, 32, 64, 0.3),
