@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "gated-delta-rule fwd tokens/s + achieved HBM GB/s (% roofline), 1 MI355X"
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc", "gdn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wide_head.json")
+COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
 
 
 def algorithmic_bytes(wl: synth.Workload, has_h0: bool) -> int:
@@ -98,6 +99,9 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-parity", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run three plain 256 MiB device-to-device copies, whose HBM "
+                         "counter readings calibrate the kernel's FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -143,6 +147,15 @@ def main():
         rc = raw(*calls[i % len(calls)], B, T, wl.H, wl.dk, wl.dv, sh, dtype_code, wl.chunk)
         if rc != 0:
             raise SystemExit(f"gdn_fwd failed with status {rc}")
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)
