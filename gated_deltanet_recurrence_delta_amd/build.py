@@ -15,6 +15,15 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed-fp32 VALU forms stay off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results stay in VGPRs: the state, Gram and output products are
+    # all post-processed on the VALU, and accumulators in AGPRs would cost a
+    # copy per element each way
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # no implicit multiply-add fusion: code that is inlined in more than one
+    # place (prologue and loop, unrolled loop halves) must round identically
+    # for results to be bitwise reproducible across chunk positions; the
+    # kernels spell out every fused multiply-add they want
+    "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
           const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + 16 * tb + 4 * q4);
           const f32x4 gm = *reinterpret_cast<const f32x4*>(vec + 2 * C + 16 * tb + 4 * q4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) X[tb][e] = bt[e] * (Vc[tb][e] - gm[e] * Y[tb][e]);
+          for (int e = 0; e < 4; ++e) X[tb][e] = bt[e] * __builtin_fmaf(-gm[e], Y[tb][e], Vc[tb][e]);
         }
         F Xf[NTS];
 #pragma unroll
@@ -630,8 +630,8 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
           for (int i = 0; i < 16; ++i) {
             float s = (i == n16) ? 1.f : 0.f;
 #pragma unroll
-            for (int l = 0; l + 1 < i; ++l) s -= arow[i][l >> 2][l & 3] * tc[l];
-            if (i > 0) s -= arow[i][(i - 1) >> 2][(i - 1) & 3] * tc[i - 1];
+            for (int l = 0; l + 1 < i; ++l) s = __builtin_fmaf(-arow[i][l >> 2][l & 3], tc[l], s);
+            if (i > 0) s = __builtin_fmaf(-arow[i][(i - 1) >> 2][(i - 1) & 3], tc[i - 1], s);
             tc[i] = s;
           }
           const int base = 16 * q4;
@@ -797,6 +797,663 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
   }
 }
 
+// ======================================================================
+// bf16 kernel
+//
+// Same chunk algebra, reorganised for bf16 so that every global access goes
+// through a per-sequence buffer descriptor (rows past the sequence end read
+// as zero and stores past it are dropped, so the ragged tail needs no
+// special code), q, k and this tile's v land in LDS by direct buffer-to-LDS
+// copies, and the triangular solve needs no serial block merges.  One
+// workgroup per (chain, 32-column value tile), four waves, one LDS barrier
+// per step:
+//
+//   loader wave (step c): copies q, k, v of chunk c+1 into the LDS rings;
+//       g and beta of chunk c+1 -> per-token vectors; inverses of the 16x16
+//       diagonal blocks of (I + A) of chunk c (fp32 forward substitution,
+//       one lane per column) once the Gram wave has published them.
+//   Gram wave (step c): diagonal blocks of A (published first, LDS flag),
+//       then the off-diagonal blocks of A.
+//   state wave (step c+1): Y = K M, X = beta V - beta Gam Y, U by block
+//       forward substitution U_b = Tbb^-1 (X_b - sum_{j<b} A_bj U_j), the
+//       update M <- Gam_C M + K^T diag(w) U; publishes U and the bf16 state.
+//   output wave (step c+1): diag(Gam) Q M and the masked decayed
+//       P = (Q K^T) * D of chunk c in registers; at step c+2 it adds P U and
+//       stores the chunk.
+//
+// The decay exp(gamma_i - gamma_j) of an off-diagonal block (rows in block
+// b1, columns in an earlier block) is the product of two factors through
+// the first token of block b1, exp(gamma_i - gamma_{16 b1}) and
+// exp(gamma_{16 b1} - gamma_j); for g <= 0 both are at most 1, so neither
+// overflows.  Diagonal blocks use the direct exponential.
+//
+// LDS layouts (all chosen so that every fragment read is one instruction
+// from a per-lane base register plus a compile-time offset):
+//   q/k tiles: rows of 2*DK bytes, 16-byte granules XOR-permuted by row;
+//   v tiles:   rows of 64 bytes, granules XOR-permuted by row;
+//   C x C tile (A and the inverted diagonal blocks): rows of 2*C bytes;
+//       inside each 32-column slab the columns are stored in the order
+//       {0-3, 16-19, 4-7, 20-23, ...} so that the eight positions a lane
+//       holds in a 16x16x32 fragment are contiguous; granules XOR-permuted.
+// ======================================================================
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Granule permutation of a q/k row (GR granules of 16 bytes): distinct low
+// three bits over any 8 consecutive rows, so the 16 lanes of a fragment read
+// (16 consecutive rows, one granule each) hit distinct bank groups.
+template <int GR>
+__device__ static inline int swz_kq(int r) {
+  if constexpr (GR >= 8) return 2 * (r & 3) + ((r >> 2) & 1);
+  else return (r >> 1) & 3;  // two 64-byte rows share a 128-byte bank line
+}
+__device__ static inline int swz_v(int r) { return r & 2; }
+template <int C>
+__device__ static inline int swz_cc(int r) {
+  if constexpr (C == 64) return r & 7;
+  else return (r >> 1) & 3;
+}
+
+template <int DK, int C>
+struct Cfg16 {
+  static constexpr int DVT = 32, NCB = 2;  // value columns per workgroup, 16-column blocks
+  static constexpr int NB = C / 16, NTS = C / 32, NKB = DK / 16, NKS = DK / 32;
+  static constexpr int KQ_ROWB = DK * 2, V_ROWB = 64, CC_ROWB = C * 2;
+  static constexpr int GR = KQ_ROWB / 16;
+  static constexpr int KQ_BYTES = C * KQ_ROWB, V_BYTES = C * V_ROWB, CC_BYTES = C * CC_ROWB;
+  static constexpr int UF_BYTES = NCB * NTS * 1024;  // U fragments, fragment-major
+  static constexpr int MF_BYTES = NCB * NKS * 1024;  // state fragments, fragment-major
+  // Per-token vectors (fp32, C each): beta, lambda = gamma*log2(e), Gam,
+  // w = exp(gamma_C - gamma), beta*Gam, exp(gamma_t - gamma at the start of
+  // t's block), and for b = 1..NB-1, exp(gamma_{16 b} - gamma_t) (t < 16 b).
+  static constexpr int F_BETA = 0, F_LAM = 1, F_GAM = 2, F_W = 3, F_BG = 4, F_ER = 5;
+  static constexpr int NF = 5 + NB;
+  static constexpr int AD_ROW = 20, AD_BLK = 16 * AD_ROW;  // fp32 diagonal blocks, padded rows
+  static constexpr int KQ_INS = KQ_BYTES / 1024, V_INS = V_BYTES / 1024;  // copies per chunk
+  static constexpr int KQ_RPI = 1024 / KQ_ROWB, V_RPI = 1024 / V_ROWB;    // rows per copy
+  static constexpr int LDS = 6 * KQ_BYTES + 3 * V_BYTES + 2 * CC_BYTES + 2 * UF_BYTES + 2 * MF_BYTES +
+                             3 * NF * C * 4 + NB * AD_BLK * 4 + 16;
+  static_assert(NB >= 2 && NB <= 4 && NKS >= 1 && GR >= 4, "shape");
+};
+
+// Wait until the LDS word `f` holds at least v.  The read is issued from
+// inline assembly so that the compiler does not make it wait for this
+// wave's outstanding copies into LDS (which never touch the flag).
+__device__ static inline void flag_wait_lds(const int* f, int v) {
+  const unsigned addr = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) int*)f;
+  for (;;) {
+    int x;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+    if (__builtin_amdgcn_readfirstlane(x) >= v) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+__device__ static inline void flag_release(int* f, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at
+// lds + 16 * lane.  (Kept out of the kernel body: the host compilation pass
+// does not accept this builtin inside a kernel and would drop its stub.)
+__device__ static inline void copy_to_lds(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ static inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ static inline bf16x4 cvt4(f32x4 v) {
+  return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
+// Raw buffer descriptor over [base, base + bytes); accesses at or past the
+// end read zero and write nothing.
+__device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+template <typename V>
+__device__ static inline V lds_at(const char* p) { return *reinterpret_cast<const V*>(p); }
+
+template <int DK, int C>
+__global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
+  using CF = Cfg16<DK, C>;
+  using MM = Mma<__bf16>;
+  using F = bf16x8;
+  constexpr int NB = CF::NB, NTS = CF::NTS, NKB = CF::NKB, NKS = CF::NKS, NCB = CF::NCB, NF = CF::NF;
+  constexpr int GR = CF::GR, KQR = CF::KQ_ROWB, CCR = CF::CC_ROWB;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // Separate LDS objects: the loader wave's own LDS accesses (flag, diagonal
+  // blocks, Tbb, vectors) never alias its in-flight copies (q, k, v).
+  __shared__ __attribute__((aligned(16))) char sK[3 * CF::KQ_BYTES];
+  __shared__ __attribute__((aligned(16))) char sQ[3 * CF::KQ_BYTES];
+  __shared__ __attribute__((aligned(16))) char sV[3 * CF::V_BYTES];
+  __shared__ __attribute__((aligned(16))) char sAT[2 * CF::CC_BYTES];
+  __shared__ __attribute__((aligned(16))) char sUF[2 * CF::UF_BYTES];
+  __shared__ __attribute__((aligned(16))) char sMF[2 * CF::MF_BYTES];
+  __shared__ __attribute__((aligned(16))) float sVEC[3 * NF * C];
+  __shared__ __attribute__((aligned(16))) float sAD[NB * CF::AD_BLK];
+  __shared__ int sFLAG[4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4, n16 = lane & 15;
+
+  const int item = xcd_remap(blockIdx.x, p.nwg);
+  const int chain = __builtin_amdgcn_readfirstlane(item / p.ntile);
+  const int tile = __builtin_amdgcn_readfirstlane(item % p.ntile);
+  const int H = p.H;
+  const int bseq = chain / H, hh = chain % H;
+  long rowbase;
+  int len;
+  if (p.cu) {
+    rowbase = p.cu[bseq];
+    len = p.cu[bseq + 1] - p.cu[bseq];
+  } else {
+    rowbase = (long)bseq * p.T;
+    len = p.T;
+  }
+  rowbase = __builtin_amdgcn_readfirstlane((int)rowbase);
+  len = __builtin_amdgcn_readfirstlane(len);
+  const int NC = (len + C - 1) / C;
+  const int NIT = NC > 0 ? NC + 2 : 0;
+  const long kq_stride = (long)H * DK * 2;  // bytes between tokens in q/k
+  const long v_stride = (long)H * p.dv * 2;  // bytes between tokens in v/out
+  auto vec_of = [&](int c) { return sVEC + (c % 3) * NF * C; };
+
+  // Lane-constant parts of the fragment addresses.
+  // q/k fragment (row 16 tb + n16, natural slab s): base[s] + 16*KQR*tb.
+  int kq_frag[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) kq_frag[s] = n16 * KQR + 16 * ((4 * s + q4) ^ swz_kq<GR>(n16));
+  // C x C fragment (row 16 b + n16, slab s) and the Gram wave's 4-wide
+  // stores (slab s, half): base[s] + 16*CCR*b (+ 8 for the second half).
+  int cc_frag[NTS];
+#pragma unroll
+  for (int s = 0; s < NTS; ++s) cc_frag[s] = n16 * CCR + 16 * ((4 * s + q4) ^ swz_cc<C>(n16));
+
+  if (wave == 0) {
+    // ========================================================== loader wave
+    // Copy i of a chunk writes LDS bytes [1024 i, 1024 i + 1024): lane l
+    // fills granule l % GR of row i*RPI + l/GR with the logical granule
+    // (l % GR) ^ swz(row).  The same offsets serve q and k.
+    int kq_src[CF::KQ_INS], v_src[CF::V_INS];
+#pragma unroll
+    for (int i = 0; i < CF::KQ_INS; ++i) {
+      const int r = i * CF::KQ_RPI + lane / GR;
+      kq_src[i] = (int)(r * kq_stride) + 16 * ((lane % GR) ^ swz_kq<GR>(r));
+    }
+#pragma unroll
+    for (int i = 0; i < CF::V_INS; ++i) {
+      const int r = i * CF::V_RPI + lane / 4;
+      v_src[i] = (int)(r * v_stride) + 16 * ((lane & 3) ^ swz_v(r));
+    }
+    // g and beta: lane t < C reads token t of the chunk; other lanes read
+    // past any descriptor's end (zero).
+    const int gb_src = lane < C ? lane * H * 4 : 0x7ffffff0;
+    // Diagonal-block inverse: lane (block q4, column n16) writes row n16 of
+    // Tbb^T (= column n16 of Tbb): four 4-wide pieces.
+    int t_dst[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = 16 * q4 + n16;
+      t_dst[m] = r * CCR + 16 * ((4 * (q4 >> 1) + m) ^ swz_cc<C>(r)) + 8 * (q4 & 1);
+    }
+
+    auto issue = [&](int c, float& sg, float& sb) {
+      const long row0 = rowbase + (long)c * C;
+      const long left = (long)(len - c * C);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0 * kq_stride + hh * DK * 2, left * kq_stride);
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + row0 * kq_stride + hh * DK * 2, left * kq_stride);
+      const __amdgpu_buffer_rsrc_t rv =
+          make_rsrc(p.v + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, left * v_stride);
+      const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + row0 * H + hh, left * H * 4);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0 * H + hh, left * H * 4);
+      sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, gb_src, 0, 0));
+      sb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, gb_src, 0, 0));
+      char* dk = sK + (c % 3) * CF::KQ_BYTES;
+      char* dq = sQ + (c % 3) * CF::KQ_BYTES;
+      char* dv = sV + (c % 3) * CF::V_BYTES;
+#pragma unroll
+      for (int i = 0; i < CF::KQ_INS; ++i) {
+        copy_to_lds(rk, dk + i * 1024, kq_src[i]);
+        copy_to_lds(rq, dq + i * 1024, kq_src[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < CF::V_INS; ++i)
+        copy_to_lds(rv, dv + i * 1024, v_src[i]);
+    };
+    auto make_vec = [&](int c, float sg, float sb) {
+      float* vec = vec_of(c);
+      const float lam = wave_prefix_sum(sg * kLog2e, lane);
+      const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), C - 1));
+      float lb[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) lb[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 16 * b));
+      if (lane < C) {
+        const int blk = lane >> 4;
+        float lown = lb[0];
+#pragma unroll
+        for (int b = 1; b < NB; ++b) lown = blk == b ? lb[b] : lown;
+        const float gam = exp2_fast(lam);
+        vec[CF::F_BETA * C + lane] = sb;
+        vec[CF::F_LAM * C + lane] = lam;
+        vec[CF::F_GAM * C + lane] = gam;
+        vec[CF::F_W * C + lane] = exp2_fast(lamC - lam);
+        vec[CF::F_BG * C + lane] = sb * gam;
+        vec[CF::F_ER * C + lane] = exp2_fast(lam - lown);
+#pragma unroll
+        for (int b = 1; b < NB; ++b) vec[(CF::F_ER + b) * C + lane] = lane < 16 * b ? exp2_fast(lb[b] - lam) : 0.f;
+      }
+    };
+
+    if (lane == 0) sFLAG[0] = 0;
+    if (NC > 0) {
+      float sg, sb;
+      issue(0, sg, sb);
+      make_vec(0, sg, sb);
+    }
+    lds_barrier();
+
+    for (int it = 0; it < NIT; ++it) {
+      float sg = 0.f, sb = 0.f;
+      const bool more = it + 1 < NC;
+      if (more) issue(it + 1, sg, sb);
+      if (it < NC) {
+        // Inverse of each 16x16 diagonal block of (I + A): lane (block q4,
+        // column n16) runs forward substitution down the block's rows.
+        flag_wait_lds(&sFLAG[0], it + 1);
+        if (q4 < NB) {
+          const float* A = sAD + q4 * CF::AD_BLK;
+          f32x4 arow[16][4];
+#pragma unroll
+          for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int l4 = 0; l4 < i; l4 += 4) arow[i][l4 >> 2] = *reinterpret_cast<const f32x4*>(A + i * CF::AD_ROW + l4);
+          __builtin_amdgcn_sched_barrier(0);
+          float tc[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float s = (i == n16) ? 1.f : 0.f;
+#pragma unroll
+            for (int l = 0; l + 1 < i; ++l) s = __builtin_fmaf(-arow[i][l >> 2][l & 3], tc[l], s);
+            if (i > 0) s = __builtin_fmaf(-arow[i][(i - 1) >> 2][(i - 1) & 3], tc[i - 1], s);
+            tc[i] = s;
+          }
+          char* sat = sAT + (it & 1) * CF::CC_BYTES;
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            lds_st<bf16x4>(sat, t_dst[m],
+                           bf16x4{(__bf16)tc[4 * m], (__bf16)tc[4 * m + 1], (__bf16)tc[4 * m + 2], (__bf16)tc[4 * m + 3]});
+        }
+      }
+      if (more) make_vec(it + 1, sg, sb);
+      lds_barrier();
+    }
+  } else if (wave == 1) {
+    // ============================================================ Gram wave
+    lds_barrier();
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it;
+      if (c < NC) {
+        const char* sk = sK + (c % 3) * CF::KQ_BYTES;
+        const float* vec = vec_of(c);
+        char* sat = sAT + (c & 1) * CF::CC_BYTES;
+        F Kf[NB][NKS];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) Kf[b][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * b);
+        // A block result: lane (n16, q4) holds row i = 16 b1 + n16 and
+        // columns j = 16 b2 + 4 q4 + e.
+        float li[NB], bi[NB], eri[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          li[b] = vec[CF::F_LAM * C + 16 * b + n16];
+          bi[b] = vec[CF::F_BETA * C + 16 * b + n16];
+          eri[b] = vec[CF::F_ER * C + 16 * b + n16];
+        }
+        // Diagonal blocks (j < i), published first for the loader wave.
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const f32x4 lj = *reinterpret_cast<const f32x4*>(vec + CF::F_LAM * C + 16 * b + 4 * q4);
+          f32x4 kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) kk = MM::mma(Kf[b][s], Kf[b][s], kk);
+          f32x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = 4 * q4 + e < n16 ? bi[b] * kk[e] * exp2_fast(li[b] - lj[e]) : 0.f;
+          *reinterpret_cast<f32x4*>(sAD + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
+        }
+        flag_release(&sFLAG[0], c + 1);
+        // Off-diagonal blocks.
+#pragma unroll
+        for (int b1 = 1; b1 < NB; ++b1)
+#pragma unroll
+          for (int b2 = 0; b2 < b1; ++b2) {
+            const f32x4 ec = *reinterpret_cast<const f32x4*>(vec + (CF::F_ER + b1) * C + 16 * b2 + 4 * q4);
+            f32x4 kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) kk = MM::mma(Kf[b2][s], Kf[b1][s], kk);
+            const float sc = bi[b1] * eri[b1];
+            f32x4 ra;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ra[e] = sc * kk[e] * ec[e];
+            lds_st<bf16x4>(sat, cc_frag[b2 >> 1] + 16 * CCR * b1 + 8 * (b2 & 1), cvt4(ra));
+          }
+      }
+      lds_barrier();
+    }
+  } else if (wave == 2) {
+    // =========================================================== state wave
+    const long sbase = (long)chain * DK * p.dv;
+    const int col0 = tile * CF::DVT;
+    // Accumulator block b, element e of column block cb holds
+    // M[key(b, 4q + e)][col0 + 16 cb + n16]; two stacked blocks form a
+    // fragment with natural key positions.
+    auto key_of = [&](int b, int r) { return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3); };
+    f32x4 Macc[NKB][NCB];
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Macc[b][cb][e] = p.h0 ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col0 + 16 * cb + n16] : 0.f;
+
+    // Transposing reads.  K^T: rows 32 s + 16 hi + 4 q4 + (src >> 2), the
+    // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 (b&1) .. +3.
+    const int src = lane & 15;
+    int kt_base[(NKB + 1) / 2];
+#pragma unroll
+    for (int bh = 0; bh < (NKB + 1) / 2; ++bh) {
+      const int r = 4 * q4 + (src >> 2);
+      kt_base[bh] = r * KQR + 16 * ((4 * bh + (src & 3)) ^ swz_kq<GR>(r));
+    }
+    // V in accumulator layout: rows 16 tb + 4 q4 + (src >> 2), columns
+    // 16 cb + 4 (src & 3) .. +3.
+    int v_base[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int r = 4 * q4 + (src >> 2);
+      v_base[cb] = r * CF::V_ROWB + 16 * ((2 * cb + ((src & 3) >> 1)) ^ swz_v(r)) + 8 * (src & 1);
+    }
+    // Tbb (transposing read of Tbb^T): rows 16 b + 4 q4 + (src >> 2),
+    // columns 16 b + 4 (src & 3) .. +3.
+    int t_base[NTS];
+#pragma unroll
+    for (int bh = 0; bh < NTS; ++bh) {
+      const int r = 4 * q4 + (src >> 2);
+      t_base[bh] = r * CCR + 16 * ((4 * bh + (src & 3)) ^ swz_cc<C>(r));
+    }
+
+    F Mf[NKS][NCB];
+    auto publish_state = [&](int slot) {
+      char* mf = sMF + slot * CF::MF_BYTES;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          Mf[s][cb] = MM::from_acc(Macc[2 * s][cb], Macc[2 * s + 1][cb]);
+          lds_st<F>(mf, ((cb * NKS + s) * 64 + lane) * 16, Mf[s][cb]);
+        }
+    };
+    publish_state(0);
+    lds_barrier();
+
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it - 1;
+      if (c >= 0 && c < NC) {
+        const char* sk = sK + (c % 3) * CF::KQ_BYTES;
+        const char* sv = sV + (c % 3) * CF::V_BYTES;
+        const char* sat = sAT + (c & 1) * CF::CC_BYTES;
+        const float* vec = vec_of(c);
+
+        // Operands that do not depend on the state.
+        F Kf[NB][NKS];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) Kf[tb][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * tb);
+        F Tf[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x4 t = lds_read_tr(sat, t_base[b >> 1] + 16 * CCR * b + 8 * (b & 1));
+          F f{};
+          f[0] = t[0]; f[1] = t[1]; f[2] = t[2]; f[3] = t[3];
+          Tf[b] = f;
+        }
+        // Row blocks of A left of the diagonal as pi-order fragments; where
+        // the slab's upper half is the diagonal block the matching operand
+        // half is zero.
+        F Af[NB][NTS];
+#pragma unroll
+        for (int b = 1; b < NB; ++b)
+#pragma unroll
+          for (int s = 0; 32 * s < 16 * b; ++s) Af[b][s] = lds_at<F>(sat + cc_frag[s] + 16 * CCR * b);
+        bf16x4 Vr[NB][NCB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) Vr[tb][cb] = lds_read_tr(sv, v_base[cb] + 16 * CF::V_ROWB * tb);
+
+        // Y = K M
+        f32x4 Y[NB][NCB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[tb][s], Mf[s][cb], y);
+            Y[tb][cb] = y;
+          }
+
+        // X = beta V - beta Gam Y
+        f32x4 X[NB][NCB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + CF::F_BETA * C + 16 * tb + 4 * q4);
+          const f32x4 bg = *reinterpret_cast<const f32x4*>(vec + CF::F_BG * C + 16 * tb + 4 * q4);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) X[tb][cb][e] = __builtin_fmaf(-bg[e], Y[tb][cb][e], bt[e] * (float)Vr[tb][cb][e]);
+        }
+
+        // U_b = Tbb (X_b - sum_{j<b} A_bj U_j)
+        f32x4 U[NB][NCB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 x = X[b][cb];
+            if (b > 0) {
+              f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int s = 0; 32 * s < 16 * b; ++s) {
+                const F ub = 32 * s + 16 < 16 * b ? MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb])
+                                                  : MM::from_acc1(U[2 * s][cb]);
+                r = MM::mma(Af[b][s], ub, r);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] -= r[e];
+            }
+            U[b][cb] = MM::mma(Tf[b], MM::from_acc1(x), f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+
+        // Publish U for the output wave; W = diag(w) U for the update.
+        char* uf = sUF + (c & 1) * CF::UF_BYTES;
+        F Wf[NTS][NCB];
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 4 * q4);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 16 + 4 * q4);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            lds_st<F>(uf, ((cb * NTS + s) * 64 + lane) * 16, MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb]));
+            f32x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] = w0[e] * U[2 * s][cb][e];
+              b[e] = w1[e] * U[2 * s + 1][cb][e];
+            }
+            Wf[s][cb] = MM::from_acc(a, b);
+          }
+        }
+
+        // M <- Gam_C M + K^T diag(w) U; K^T by transposing reads with tokens
+        // in pi order to match the W fragments.
+        const float gC = vec[CF::F_GAM * C + C - 1];
+#pragma unroll
+        for (int b = 0; b < NKB; ++b) {
+          F KT[NTS];
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) {
+            const char* kb = sk + kt_base[b >> 1] + 8 * (b & 1) + 32 * s * KQR;
+            const bf16x4 lo = lds_read_tr(kb, 0);
+            const bf16x4 hi = lds_read_tr(kb, 16 * KQR);
+            KT[s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 m = Macc[b][cb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] *= gC;
+#pragma unroll
+            for (int s = 0; s < NTS; ++s) m = MM::mma(KT[s], Wf[s][cb], m);
+            Macc[b][cb] = m;
+          }
+        }
+        publish_state((c + 1) & 1);
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col0 + 16 * cb + n16] = Macc[b][cb][e];
+  } else {
+    // ========================================================== output wave
+    // Output rows: lane (token 16 tb + n16, columns 16 cb + 4 q4 .. +3).
+    int o_off[NB];
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) o_off[tb] = (int)((16 * tb + n16) * v_stride) + 8 * q4;
+    lds_barrier();
+    // One step: finish chunk it-2 (+ P U, store); then for chunk it-1
+    // diag(Gam) Q M and P = (Q K^T) * D, kept in registers.
+    auto step = [&](int it, F (&Pc)[NB][NTS], F (&Pn)[NB][NTS], f32x4 (&Ofin)[NB][NCB], f32x4 (&Onew)[NB][NCB]) {
+      const int c2 = it - 2, c1 = it - 1;
+      if (c2 >= 0 && c2 < NC) {
+        const char* uf = sUF + (c2 & 1) * CF::UF_BYTES;
+        F Uf[NTS][NCB];
+#pragma unroll
+        for (int s = 0; s < NTS; ++s)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) Uf[s][cb] = lds_at<F>(uf + ((cb * NTS + s) * 64 + lane) * 16);
+        const long row0 = rowbase + (long)c2 * C;
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(p.out + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, (long)(len - c2 * C) * v_stride);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 o = Ofin[tb][cb];
+#pragma unroll
+            for (int s = 0; s <= (16 * tb + 15) / 32; ++s) o = MM::mma(Uf[s][cb], Pc[tb][s], o);
+            const bf16x4 ob = cvt4(o);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro, o_off[tb] + 32 * cb, 0, 0);
+          }
+      }
+      if (c1 >= 0 && c1 < NC) {
+        const char* sq = sQ + (c1 % 3) * CF::KQ_BYTES;
+        const char* sk = sK + (c1 % 3) * CF::KQ_BYTES;
+        const char* mf = sMF + (c1 & 1) * CF::MF_BYTES;
+        const float* vec = vec_of(c1);
+        F Qf[NB][NKS];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) Qf[tb][s] = lds_at<F>(sq + kq_frag[s] + 16 * KQR * tb);
+        F Mf[NKS][NCB];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) Mf[s][cb] = lds_at<F>(mf + ((cb * NKS + s) * 64 + lane) * 16);
+        // O^T = (M^T Q^T) diag(Gam): lane (token 16 tb + n16, q4) holds
+        // columns 16 cb + 4 q4 + e.
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          const float gcol = vec[CF::F_GAM * C + 16 * tb + n16];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) o = MM::mma(Mf[s][cb], Qf[tb][s], o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] *= gcol;
+            Onew[tb][cb] = o;
+          }
+        }
+        // P: lane (n16, q4) of block (b1, b2) holds row i = 16 b1 + n16 and
+        // columns j = 16 b2 + 4 q4 + e, which is the pi-order B operand of
+        // P U for slab b2 >> 1.
+        F Kf[NB][NKS];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) Kf[b][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * b);
+#pragma unroll
+        for (int b1 = 0; b1 < NB; ++b1) {
+          const float li = vec[CF::F_LAM * C + 16 * b1 + n16];
+          const float eri = vec[CF::F_ER * C + 16 * b1 + n16];
+          f32x4 pb[NB];
+#pragma unroll
+          for (int b2 = 0; b2 <= b1; ++b2) {
+            f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) pq = MM::mma(Kf[b2][s], Qf[b1][s], pq);
+            if (b2 < b1) {
+              const f32x4 ec = *reinterpret_cast<const f32x4*>(vec + (CF::F_ER + b1) * C + 16 * b2 + 4 * q4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pb[b2][e] = pq[e] * (eri * ec[e]);
+            } else {
+              const f32x4 lj = *reinterpret_cast<const f32x4*>(vec + CF::F_LAM * C + 16 * b1 + 4 * q4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pb[b2][e] = 4 * q4 + e <= n16 ? pq[e] * exp2_fast(li - lj[e]) : 0.f;
+            }
+          }
+#pragma unroll
+          for (int s = 0; 32 * s <= 16 * b1; ++s)
+            Pn[b1][s] = 2 * s + 1 <= b1 ? MM::from_acc(pb[2 * s], pb[2 * s + 1]) : MM::from_acc1(pb[2 * s]);
+        }
+      }
+      lds_barrier();
+    };
+    F P0[NB][NTS], P1[NB][NTS];
+    f32x4 O0[NB][NCB], O1[NB][NCB];
+    for (int it = 0; it < NIT; it += 2) {
+      step(it, P1, P0, O1, O0);
+      if (it + 1 < NIT) step(it + 1, P0, P1, O0, O1);
+    }
+  }
+}
+
+template <int DK, int C>
+int launch16(const Params& p, int nwg, hipStream_t stream) {
+  static_assert(Cfg16<DK, C>::LDS <= 160 * 1024, "LDS budget");
+  hipLaunchKernelGGL((gdn_bf16_kernel<DK, C>), dim3(nwg), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 template <typename TI, int DK, int DVT, int C>
 int launch(const Params& p, int nwg, hipStream_t stream) {
   using CF = Cfg<TI, DK, DVT, C>;
@@ -808,8 +1465,8 @@ int launch(const Params& p, int nwg, hipStream_t stream) {
 template <typename TI, int DK>
 int by_chunk(const Params& p, int nwg, hipStream_t s, int chunk) {
   if constexpr (sizeof(TI) == 2) {
-    if (chunk == 64) return launch<TI, DK, 32, 64>(p, nwg, s);
-    if (chunk == 32) return launch<TI, DK, 32, 32>(p, nwg, s);
+    if (chunk == 64) return launch16<DK, 64>(p, nwg, s);
+    if (chunk == 32) return launch16<DK, 32>(p, nwg, s);
   } else {
     if (chunk == 16) return launch<TI, DK, 32, 16>(p, nwg, s);
     if (chunk == 32) return launch<TI, DK, 32, 32>(p, nwg, s);
