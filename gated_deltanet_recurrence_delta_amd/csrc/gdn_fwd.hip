@@ -53,6 +53,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------ operand traits
 
@@ -1070,19 +1071,31 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
         flag_wait_lds(&sFLAG[0], it + 1);
         if (q4 < NB) {
           const float* A = sAD + q4 * CF::AD_BLK;
-          f32x4 arow[16][4];
+          // Row i holds columns 0..i-1: whole 4-wide pieces, then a 2- and/or
+          // 1-wide piece, so every value read is used.
+          float ar[16][16];
 #pragma unroll
-          for (int i = 1; i < 16; ++i)
+          for (int i = 1; i < 16; ++i) {
+            const float* row = A + i * CF::AD_ROW;
 #pragma unroll
-            for (int l4 = 0; l4 < i; l4 += 4) arow[i][l4 >> 2] = *reinterpret_cast<const f32x4*>(A + i * CF::AD_ROW + l4);
-          __builtin_amdgcn_sched_barrier(0);
+            for (int l = 0; l + 4 <= i; l += 4) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(row + l);
+              ar[i][l] = v[0]; ar[i][l + 1] = v[1]; ar[i][l + 2] = v[2]; ar[i][l + 3] = v[3];
+            }
+            const int l0 = i & ~3;
+            if (i & 2) {
+              const f32x2 v = *reinterpret_cast<const f32x2*>(row + l0);
+              ar[i][l0] = v[0]; ar[i][l0 + 1] = v[1];
+            }
+            if (i & 1) ar[i][i - 1] = row[i - 1];
+          }
           float tc[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             float s = (i == n16) ? 1.f : 0.f;
 #pragma unroll
-            for (int l = 0; l + 1 < i; ++l) s = __builtin_fmaf(-arow[i][l >> 2][l & 3], tc[l], s);
-            if (i > 0) s = __builtin_fmaf(-arow[i][(i - 1) >> 2][(i - 1) & 3], tc[i - 1], s);
+            for (int l = 0; l + 1 < i; ++l) s = __builtin_fmaf(-ar[i][l], tc[l], s);
+            if (i > 0) s = __builtin_fmaf(-ar[i][i - 1], tc[i - 1], s);
             tc[i] = s;
           }
           char* sat = sAT + (it & 1) * CF::CC_BYTES;
@@ -1214,12 +1227,14 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
         const char* sat = sAT + (c & 1) * CF::CC_BYTES;
         const float* vec = vec_of(c);
 
-        // Operands that do not depend on the state.
-        F Kf[NB][NKS];
+        // Operands that do not depend on the state.  K is read one row block
+        // ahead of its use to keep the live register set small.
+        F Kf[2][NKS];
+        auto read_k = [&](int tb) {
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) Kf[tb][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * tb);
+          for (int s = 0; s < NKS; ++s) Kf[tb & 1][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * tb);
+        };
+        read_k(0);
         F Tf[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -1242,37 +1257,26 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) Vr[tb][cb] = lds_read_tr(sv, v_base[cb] + 16 * CF::V_ROWB * tb);
 
-        // Y = K M
-        f32x4 Y[NB][NCB];
+        // Row block b: Y_b = K_b M, X_b = beta V_b - beta Gam Y_b and
+        // U_b = Tbb (X_b - sum_{j<b} A_bj U_j), one block at a time so that
+        // the products of block b+1 can fill the latency of block b's solve.
+        f32x4 U[NB][NCB];
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
+        for (int b = 0; b < NB; ++b) {
+          if (b + 1 < NB) read_k(b + 1);
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + CF::F_BETA * C + 16 * b + 4 * q4);
+          const f32x4 bg = *reinterpret_cast<const f32x4*>(vec + CF::F_BG * C + 16 * b + 4 * q4);
+          f32x4 x[NCB];
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[tb][s], Mf[s][cb], y);
-            Y[tb][cb] = y;
+            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[b & 1][s], Mf[s][cb], y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[cb][e] = __builtin_fmaf(-bg[e], y[e], bt[e] * (float)Vr[b][cb][e]);
           }
-
-        // X = beta V - beta Gam Y
-        f32x4 X[NB][NCB];
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-          const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + CF::F_BETA * C + 16 * tb + 4 * q4);
-          const f32x4 bg = *reinterpret_cast<const f32x4*>(vec + CF::F_BG * C + 16 * tb + 4 * q4);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) X[tb][cb][e] = __builtin_fmaf(-bg[e], Y[tb][cb][e], bt[e] * (float)Vr[tb][cb][e]);
-        }
-
-        // U_b = Tbb (X_b - sum_{j<b} A_bj U_j)
-        f32x4 U[NB][NCB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            f32x4 x = X[b][cb];
             if (b > 0) {
               f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1282,10 +1286,31 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
                 r = MM::mma(Af[b][s], ub, r);
               }
 #pragma unroll
-              for (int e = 0; e < 4; ++e) x[e] -= r[e];
+              for (int e = 0; e < 4; ++e) x[cb][e] -= r[e];
             }
-            U[b][cb] = MM::mma(Tf[b], MM::from_acc1(x), f32x4{0.f, 0.f, 0.f, 0.f});
+            U[b][cb] = MM::mma(Tf[b], MM::from_acc1(x[cb]), f32x4{0.f, 0.f, 0.f, 0.f});
           }
+        }
+
+        // K^T for the update (transposing reads, tokens in pi order to match
+        // the W fragments); Gam_C M and W are formed while they arrive.
+        F KT[NKB][NTS];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) {
+            const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
+            const bf16x4 lo = lds_read_tr(p0, 0);
+            const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
+            KT[kb][s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        const float gC = vec[CF::F_GAM * C + C - 1];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Macc[kb][cb][e] *= gC;
 
         // Publish U for the output wave; W = diag(w) U for the update.
         char* uf = sUF + (c & 1) * CF::UF_BYTES;
@@ -1307,29 +1332,16 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
           }
         }
 
-        // M <- Gam_C M + K^T diag(w) U; K^T by transposing reads with tokens
-        // in pi order to match the W fragments.
-        const float gC = vec[CF::F_GAM * C + C - 1];
+        // M <- Gam_C M + K^T diag(w) U
 #pragma unroll
-        for (int b = 0; b < NKB; ++b) {
-          F KT[NTS];
-#pragma unroll
-          for (int s = 0; s < NTS; ++s) {
-            const char* kb = sk + kt_base[b >> 1] + 8 * (b & 1) + 32 * s * KQR;
-            const bf16x4 lo = lds_read_tr(kb, 0);
-            const bf16x4 hi = lds_read_tr(kb, 16 * KQR);
-            KT[s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
+        for (int b = 0; b < NKB; ++b)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             f32x4 m = Macc[b][cb];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) m[e] *= gC;
-#pragma unroll
-            for (int s = 0; s < NTS; ++s) m = MM::mma(KT[s], Wf[s][cb], m);
+            for (int s = 0; s < NTS; ++s) m = MM::mma(KT[b][s], Wf[s][cb], m);
             Macc[b][cb] = m;
           }
-        }
         publish_state((c + 1) & 1);
       }
       lds_barrier();
