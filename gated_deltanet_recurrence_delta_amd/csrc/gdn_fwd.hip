@@ -804,23 +804,31 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
 // Same chunk algebra, reorganised for bf16 so that every global access goes
 // through a per-sequence buffer descriptor (rows past the sequence end read
 // as zero and stores past it are dropped, so the ragged tail needs no
-// special code), q, k and this tile's v land in LDS by direct buffer-to-LDS
-// copies, and the triangular solve needs no serial block merges.  One
-// workgroup per (chain, 32-column value tile), four waves, one LDS barrier
-// per step:
+// special code) and q, k and this tile's v land in LDS by direct
+// buffer-to-LDS copies.  The correction is split into a state-independent
+// and a state-dependent part:
 //
-//   loader wave (step c): copies q, k, v of chunk c+1 into the LDS rings;
-//       g and beta of chunk c+1 -> per-token vectors; inverses of the 16x16
-//       diagonal blocks of (I + A) of chunk c (fp32 forward substitution,
-//       one lane per column) once the Gram wave has published them.
-//   Gram wave (step c): diagonal blocks of A (published first, LDS flag),
-//       then the off-diagonal blocks of A.
-//   state wave (step c+1): Y = K M, X = beta V - beta Gam Y, U by block
-//       forward substitution U_b = Tbb^-1 (X_b - sum_{j<b} A_bj U_j), the
-//       update M <- Gam_C M + K^T diag(w) U; publishes U and the bf16 state.
-//   output wave (step c+1): diag(Gam) Q M and the masked decayed
-//       P = (Q K^T) * D of chunk c in registers; at step c+2 it adds P U and
-//       stores the chunk.
+//     U = Tinv diag(beta) V - Tinv diag(beta Gam) K M = u + T' Y,
+//     u = Tinv diag(beta) V,   T' = -Tinv diag(beta Gam),   Y = K M,
+//
+// so that only Y, one triangular product and the update remain in the
+// chunk-to-chunk recurrence.  One workgroup per (chain, 32-column value
+// tile), six waves, one LDS barrier per step:
+//
+//   loader wave (step c): copies k, v of chunk c+1 and q of chunk c into
+//       the LDS rings; g and beta of chunk c+1 -> per-token vectors.
+//   Gram wave (step c): diagonal blocks of A of chunk c (fp32, published
+//       first, LDS flag), then the off-diagonal blocks (bf16, second flag).
+//   solve wave (step c): inverses of the 16x16 diagonal blocks of (I + A)
+//       (fp32 forward substitution, one lane per column), then block
+//       forward substitution of (I + A) [R_T | R_u] = [diag(beta) |
+//       diag(beta) V] on the MFMA; publishes T' = -R_T diag(Gam) and
+//       u = R_u.
+//   state wave (step c+1): Y = K M, U = u + T' Y, publishes U (LDS flag),
+//       the update M <- Gam_C M + K^T diag(w) U, publishes the bf16 state.
+//   two output waves (step c+1), each owning half of the chunk's 16-row
+//       blocks: diag(Gam) Q M and the masked decayed P = (Q K^T) * D of
+//       chunk c, then (once U is published) P U, and the stores.
 //
 // The decay exp(gamma_i - gamma_j) of an off-diagonal block (rows in block
 // b1, columns in an earlier block) is the product of two factors through
@@ -832,10 +840,14 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
 // from a per-lane base register plus a compile-time offset):
 //   q/k tiles: rows of 2*DK bytes, 16-byte granules XOR-permuted by row;
 //   v tiles:   rows of 64 bytes, granules XOR-permuted by row;
-//   C x C tile (A and the inverted diagonal blocks): rows of 2*C bytes;
-//       inside each 32-column slab the columns are stored in the order
-//       {0-3, 16-19, 4-7, 20-23, ...} so that the eight positions a lane
-//       holds in a 16x16x32 fragment are contiguous; granules XOR-permuted.
+//   A tile (off-diagonal blocks of A and the inverted diagonal blocks):
+//       rows of 2*C bytes; inside each 32-column slab the columns are
+//       stored in the order {0-3, 16-19, 4-7, 20-23, ...} so that the eight
+//       positions a lane holds in a 16x16x32 fragment are contiguous;
+//   T'^T tile: rows of 2*C bytes in natural column order (read with
+//       transposing reads); both C x C tiles XOR-permute granules by row;
+//   u: fp32 accumulator blocks, U and the state: bf16 fragments, all
+//       stored lane-major so that each lane reads 16 contiguous bytes.
 // ======================================================================
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -864,19 +876,38 @@ struct Cfg16 {
   static constexpr int KQ_ROWB = DK * 2, V_ROWB = 64, CC_ROWB = C * 2;
   static constexpr int GR = KQ_ROWB / 16;
   static constexpr int KQ_BYTES = C * KQ_ROWB, V_BYTES = C * V_ROWB, CC_BYTES = C * CC_ROWB;
-  static constexpr int UF_BYTES = NCB * NTS * 1024;  // U fragments, fragment-major
-  static constexpr int MF_BYTES = NCB * NKS * 1024;  // state fragments, fragment-major
+  static constexpr int UF_BYTES = NCB * NTS * 1024;  // U, bf16 fragments
+  static constexpr int UU_BYTES = NB * NCB * 1024;   // u, fp32 accumulator blocks
+  static constexpr int MF_BYTES = NCB * NKS * 1024;  // state, bf16 fragments
   // Per-token vectors (fp32, C each): beta, lambda = gamma*log2(e), Gam,
-  // w = exp(gamma_C - gamma), beta*Gam, exp(gamma_t - gamma at the start of
-  // t's block), and for b = 1..NB-1, exp(gamma_{16 b} - gamma_t) (t < 16 b).
-  static constexpr int F_BETA = 0, F_LAM = 1, F_GAM = 2, F_W = 3, F_BG = 4, F_ER = 5;
-  static constexpr int NF = 5 + NB;
-  static constexpr int AD_ROW = 20, AD_BLK = 16 * AD_ROW;  // fp32 diagonal blocks, padded rows
+  // w = exp(gamma_C - gamma), exp(gamma_t - gamma at the start of t's
+  // block), and for b = 1..NB-1, exp(gamma_{16 b} - gamma_t) (t < 16 b).
+  static constexpr int F_BETA = 0, F_LAM = 1, F_GAM = 2, F_W = 3, F_ER = 4;
+  static constexpr int NF = 4 + NB;
+  // fp32 diagonal blocks: padded rows, and blocks 4 banks apart so that the
+  // four blocks' rows are read without bank conflicts.
+  static constexpr int AD_ROW = 20, AD_BLK = 16 * AD_ROW + 4;
   static constexpr int KQ_INS = KQ_BYTES / 1024, V_INS = V_BYTES / 1024;  // copies per chunk
   static constexpr int KQ_RPI = 1024 / KQ_ROWB, V_RPI = 1024 / V_ROWB;    // rows per copy
-  static constexpr int LDS = 6 * KQ_BYTES + 3 * V_BYTES + 2 * CC_BYTES + 2 * UF_BYTES + 2 * MF_BYTES +
-                             3 * NF * C * 4 + NB * AD_BLK * 4 + 16;
+  // Wave roles.  Waves w and w + 4 share a SIMD: the state wave shares
+  // with the loader, the T solve wave has its SIMD to itself.
+  static constexpr int W_S = 0, W_OA = 1, W_OB = 2, W_X = 3, W_L = 4, W_G = 5, W_XU = 6, NW = 7;
+  // Output wave o owns row blocks own_tb(o, 0..NOWN-1): {0, 3} and {1, 2}
+  // for four blocks (equal MFMA work), {0} and {1} for two.
+  static constexpr int NOWN = NB == 4 ? 2 : 1;
+  __host__ __device__ static constexpr int own_tb(int o, int i) { return NB == 4 ? (i == 0 ? o : 3 - o) : o; }
+  // Ring depths: k is copied two steps ahead of the Gram wave and read
+  // until the state and output waves finish the chunk two steps later; v
+  // is copied two steps ahead of the u solve.
+  static constexpr int NKR = 5, NVR = 3;
+  static constexpr int LDS = NKR * KQ_BYTES + NVR * V_BYTES + 3 * CC_BYTES + UU_BYTES + MF_BYTES + UF_BYTES +
+                             4 * NF * C * 4 + 2 * NB * AD_BLK * 4 + 32;
   static_assert(NB >= 2 && NB <= 4 && NKS >= 1 && GR >= 4, "shape");
+};
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
 };
 
 // Wait until the LDS word `f` holds at least v.  The read is issued from
@@ -921,29 +952,38 @@ template <typename V>
 __device__ static inline V lds_at(const char* p) { return *reinterpret_cast<const V*>(p); }
 
 template <int DK, int C>
-__global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
+__global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
   using CF = Cfg16<DK, C>;
+  static_assert(64 * CF::NW == 448, "launch bounds");
   using MM = Mma<__bf16>;
   using F = bf16x8;
   constexpr int NB = CF::NB, NTS = CF::NTS, NKB = CF::NKB, NKS = CF::NKS, NCB = CF::NCB, NF = CF::NF;
   constexpr int GR = CF::GR, KQR = CF::KQ_ROWB, CCR = CF::CC_ROWB;
   constexpr float kLog2e = 1.4426950408889634f;
 
-  // Separate LDS objects: the loader wave's own LDS accesses (flag, diagonal
-  // blocks, Tbb, vectors) never alias its in-flight copies (q, k, v).
-  __shared__ __attribute__((aligned(16))) char sK[3 * CF::KQ_BYTES];
-  __shared__ __attribute__((aligned(16))) char sQ[3 * CF::KQ_BYTES];
-  __shared__ __attribute__((aligned(16))) char sV[3 * CF::V_BYTES];
+  // Separate LDS objects: the loader wave's own LDS accesses (flags,
+  // vectors) never alias its in-flight copies (q, k, v).
+  __shared__ __attribute__((aligned(16))) char sK[CF::NKR * CF::KQ_BYTES];
+  __shared__ __attribute__((aligned(16))) char sV[CF::NVR * CF::V_BYTES];
   __shared__ __attribute__((aligned(16))) char sAT[2 * CF::CC_BYTES];
-  __shared__ __attribute__((aligned(16))) char sUF[2 * CF::UF_BYTES];
-  __shared__ __attribute__((aligned(16))) char sMF[2 * CF::MF_BYTES];
-  __shared__ __attribute__((aligned(16))) float sVEC[3 * NF * C];
-  __shared__ __attribute__((aligned(16))) float sAD[NB * CF::AD_BLK];
-  __shared__ int sFLAG[4];
+  __shared__ __attribute__((aligned(16))) char sTP[CF::CC_BYTES];
+  __shared__ __attribute__((aligned(16))) char sUU[CF::UU_BYTES];
+  __shared__ __attribute__((aligned(16))) char sMF[CF::MF_BYTES];
+  __shared__ __attribute__((aligned(16))) char sUF[CF::UF_BYTES];
+  __shared__ __attribute__((aligned(16))) float sVEC[4 * NF * C];
+  __shared__ __attribute__((aligned(16))) float sAD[2 * NB * CF::AD_BLK];
+  // Flags, each holding chunk index + 1:
+  //   [0] U published (state -> output waves);
+  //   [1] diagonal-block inverses published (T -> u solve wave);
+  //   [2] T' and u read (state -> solve waves, which then overwrite them);
+  //   [3], [4] state read by output wave 0 / 1 (-> state wave, which then
+  //   publishes the next state over it).
+  __shared__ int sFLAG[8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q4 = lane >> 4, n16 = lane & 15;
+  const int src = lane & 15;  // source lane of a transposing read
 
   const int item = xcd_remap(blockIdx.x, p.nwg);
   const int chain = __builtin_amdgcn_readfirstlane(item / p.ntile);
@@ -965,24 +1005,24 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
   const int NIT = NC > 0 ? NC + 2 : 0;
   const long kq_stride = (long)H * DK * 2;  // bytes between tokens in q/k
   const long v_stride = (long)H * p.dv * 2;  // bytes between tokens in v/out
-  auto vec_of = [&](int c) { return sVEC + (c % 3) * NF * C; };
+  auto vec_of = [&](int c) { return sVEC + (c & 3) * NF * C; };
 
   // Lane-constant parts of the fragment addresses.
   // q/k fragment (row 16 tb + n16, natural slab s): base[s] + 16*KQR*tb.
   int kq_frag[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) kq_frag[s] = n16 * KQR + 16 * ((4 * s + q4) ^ swz_kq<GR>(n16));
-  // C x C fragment (row 16 b + n16, slab s) and the Gram wave's 4-wide
+  // A-tile fragment (row 16 b + n16, slab s) and the Gram wave's 4-wide
   // stores (slab s, half): base[s] + 16*CCR*b (+ 8 for the second half).
   int cc_frag[NTS];
 #pragma unroll
   for (int s = 0; s < NTS; ++s) cc_frag[s] = n16 * CCR + 16 * ((4 * s + q4) ^ swz_cc<C>(n16));
 
-  if (wave == 0) {
+  if (wave == CF::W_L) {
     // ========================================================== loader wave
     // Copy i of a chunk writes LDS bytes [1024 i, 1024 i + 1024): lane l
     // fills granule l % GR of row i*RPI + l/GR with the logical granule
-    // (l % GR) ^ swz(row).  The same offsets serve q and k.
+    // (l % GR) ^ swz(row).
     int kq_src[CF::KQ_INS], v_src[CF::V_INS];
 #pragma unroll
     for (int i = 0; i < CF::KQ_INS; ++i) {
@@ -997,37 +1037,36 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
     // g and beta: lane t < C reads token t of the chunk; other lanes read
     // past any descriptor's end (zero).
     const int gb_src = lane < C ? lane * H * 4 : 0x7ffffff0;
-    // Diagonal-block inverse: lane (block q4, column n16) writes row n16 of
-    // Tbb^T (= column n16 of Tbb): four 4-wide pieces.
-    int t_dst[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int r = 16 * q4 + n16;
-      t_dst[m] = r * CCR + 16 * ((4 * (q4 >> 1) + m) ^ swz_cc<C>(r)) + 8 * (q4 & 1);
-    }
 
-    auto issue = [&](int c, float& sg, float& sb) {
+    // Every load and copy below is issued unconditionally: a chunk past the
+    // end gets empty descriptors (its loads read zeros and its copies fill
+    // ring slots no live chunk occupies), so each step issues the same
+    // number of memory operations and one counted wait per step leaves
+    // exactly that step's operations in flight.
+    auto load_gb = [&](int c, float& sg, float& sb) {
       const long row0 = rowbase + (long)c * C;
-      const long left = (long)(len - c * C);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0 * kq_stride + hh * DK * 2, left * kq_stride);
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + row0 * kq_stride + hh * DK * 2, left * kq_stride);
-      const __amdgpu_buffer_rsrc_t rv =
-          make_rsrc(p.v + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, left * v_stride);
+      const long left = c < NC ? (long)(len - c * C) : 0;
       const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + row0 * H + hh, left * H * 4);
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0 * H + hh, left * H * 4);
       sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, gb_src, 0, 0));
       sb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, gb_src, 0, 0));
-      char* dk = sK + (c % 3) * CF::KQ_BYTES;
-      char* dq = sQ + (c % 3) * CF::KQ_BYTES;
-      char* dv = sV + (c % 3) * CF::V_BYTES;
+    };
+    auto issue_k = [&](int c) {
+      const long row0 = rowbase + (long)c * C;
+      const long left = c < NC ? (long)(len - c * C) : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0 * kq_stride + hh * DK * 2, left * kq_stride);
+      char* dk = sK + (c % CF::NKR) * CF::KQ_BYTES;
 #pragma unroll
-      for (int i = 0; i < CF::KQ_INS; ++i) {
-        copy_to_lds(rk, dk + i * 1024, kq_src[i]);
-        copy_to_lds(rq, dq + i * 1024, kq_src[i]);
-      }
+      for (int i = 0; i < CF::KQ_INS; ++i) copy_to_lds(rk, dk + i * 1024, kq_src[i]);
+    };
+    auto issue_v = [&](int c) {
+      const long row0 = rowbase + (long)c * C;
+      const long left = c < NC ? (long)(len - c * C) : 0;
+      const __amdgpu_buffer_rsrc_t rv =
+          make_rsrc(p.v + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, left * v_stride);
+      char* dv = sV + (c % CF::NVR) * CF::V_BYTES;
 #pragma unroll
-      for (int i = 0; i < CF::V_INS; ++i)
-        copy_to_lds(rv, dv + i * 1024, v_src[i]);
+      for (int i = 0; i < CF::V_INS; ++i) copy_to_lds(rv, dv + i * 1024, v_src[i]);
     };
     auto make_vec = [&](int c, float sg, float sb) {
       float* vec = vec_of(c);
@@ -1041,81 +1080,64 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
         float lown = lb[0];
 #pragma unroll
         for (int b = 1; b < NB; ++b) lown = blk == b ? lb[b] : lown;
-        const float gam = exp2_fast(lam);
         vec[CF::F_BETA * C + lane] = sb;
         vec[CF::F_LAM * C + lane] = lam;
-        vec[CF::F_GAM * C + lane] = gam;
+        vec[CF::F_GAM * C + lane] = exp2_fast(lam);
         vec[CF::F_W * C + lane] = exp2_fast(lamC - lam);
-        vec[CF::F_BG * C + lane] = sb * gam;
         vec[CF::F_ER * C + lane] = exp2_fast(lam - lown);
 #pragma unroll
         for (int b = 1; b < NB; ++b) vec[(CF::F_ER + b) * C + lane] = lane < 16 * b ? exp2_fast(lb[b] - lam) : 0.f;
       }
     };
 
-    if (lane == 0) sFLAG[0] = 0;
-    if (NC > 0) {
-      float sg, sb;
-      issue(0, sg, sb);
-      make_vec(0, sg, sb);
-    }
-    lds_barrier();
+    // Wait until at most the current step's loads and copies are in flight
+    // and this wave's LDS stores are done, then join the barrier.  (A plain
+    // LDS fence here would also wait for the copies just issued.)
+    constexpr int NOPS = CF::KQ_INS + CF::V_INS + 2;
+    static_assert(NOPS < 64, "vmcnt range");
+    constexpr int WAIT_NOPS = (NOPS & 15) | ((NOPS >> 4) << 14) | (7 << 4);  // vmcnt(NOPS) lgkmcnt(0)
+    auto step_barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(WAIT_NOPS);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
 
-    for (int it = 0; it < NIT; ++it) {
-      float sg = 0.f, sb = 0.f;
-      const bool more = it + 1 < NC;
-      if (more) issue(it + 1, sg, sb);
-      if (it < NC) {
-        // Inverse of each 16x16 diagonal block of (I + A): lane (block q4,
-        // column n16) runs forward substitution down the block's rows.
-        flag_wait_lds(&sFLAG[0], it + 1);
-        if (q4 < NB) {
-          const float* A = sAD + q4 * CF::AD_BLK;
-          // Row i holds columns 0..i-1: whole 4-wide pieces, then a 2- and/or
-          // 1-wide piece, so every value read is used.
-          float ar[16][16];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) {
-            const float* row = A + i * CF::AD_ROW;
-#pragma unroll
-            for (int l = 0; l + 4 <= i; l += 4) {
-              const f32x4 v = *reinterpret_cast<const f32x4*>(row + l);
-              ar[i][l] = v[0]; ar[i][l + 1] = v[1]; ar[i][l + 2] = v[2]; ar[i][l + 3] = v[3];
-            }
-            const int l0 = i & ~3;
-            if (i & 2) {
-              const f32x2 v = *reinterpret_cast<const f32x2*>(row + l0);
-              ar[i][l0] = v[0]; ar[i][l0 + 1] = v[1];
-            }
-            if (i & 1) ar[i][i - 1] = row[i - 1];
-          }
-          float tc[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float s = (i == n16) ? 1.f : 0.f;
-#pragma unroll
-            for (int l = 0; l + 1 < i; ++l) s = __builtin_fmaf(-ar[i][l], tc[l], s);
-            if (i > 0) s = __builtin_fmaf(-ar[i][i - 1], tc[i - 1], s);
-            tc[i] = s;
-          }
-          char* sat = sAT + (it & 1) * CF::CC_BYTES;
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            lds_st<bf16x4>(sat, t_dst[m],
-                           bf16x4{(__bf16)tc[4 * m], (__bf16)tc[4 * m + 1], (__bf16)tc[4 * m + 2], (__bf16)tc[4 * m + 3]});
-        }
-      }
-      if (more) make_vec(it + 1, sg, sb);
-      lds_barrier();
+    if (lane < 8) sFLAG[lane] = 0;
+    float g0 = 0.f, b0 = 0.f, g1 = 0.f, b1 = 0.f;
+    if (NIT > 0) {
+      load_gb(0, g0, b0);
+      issue_k(0);
+      make_vec(0, g0, b0);
+      issue_v(0);
+      load_gb(1, g1, b1);
+      issue_k(1);
     }
-  } else if (wave == 1) {
+    step_barrier();  // k of chunk 0 has landed
+
+    // Step it: v of chunk it+1 and k of chunk it+2 (two steps ahead of
+    // their first readers), g and beta of chunk it+2, and the vectors of
+    // chunk it+1 from the g and beta loaded one step earlier.
+    auto step = [&](int it, float& gu, float& bu, float& gl, float& bl) {
+      load_gb(it + 2, gl, bl);
+      issue_v(it + 1);
+      issue_k(it + 2);
+      if (it + 1 < NC) make_vec(it + 1, gu, bu);
+      step_barrier();
+    };
+    for (int it = 0; it < NIT; it += 2) {
+      step(it, g1, b1, g0, b0);
+      if (it + 1 < NIT) step(it + 1, g0, b0, g1, b1);
+    }
+  } else if (wave == CF::W_G) {
     // ============================================================ Gram wave
     lds_barrier();
     for (int it = 0; it < NIT; ++it) {
       const int c = it;
       if (c < NC) {
-        const char* sk = sK + (c % 3) * CF::KQ_BYTES;
+        const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
         const float* vec = vec_of(c);
+        float* ad = sAD + (c & 1) * NB * CF::AD_BLK;
         char* sat = sAT + (c & 1) * CF::CC_BYTES;
         F Kf[NB][NKS];
 #pragma unroll
@@ -1131,7 +1153,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
           bi[b] = vec[CF::F_BETA * C + 16 * b + n16];
           eri[b] = vec[CF::F_ER * C + 16 * b + n16];
         }
-        // Diagonal blocks (j < i), published first for the loader wave.
+        // Diagonal blocks (j < i), fp32.
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const f32x4 lj = *reinterpret_cast<const f32x4*>(vec + CF::F_LAM * C + 16 * b + 4 * q4);
@@ -1141,9 +1163,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
           f32x4 r;
 #pragma unroll
           for (int e = 0; e < 4; ++e) r[e] = 4 * q4 + e < n16 ? bi[b] * kk[e] * exp2_fast(li[b] - lj[e]) : 0.f;
-          *reinterpret_cast<f32x4*>(sAD + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
+          *reinterpret_cast<f32x4*>(ad + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
         }
-        flag_release(&sFLAG[0], c + 1);
         // Off-diagonal blocks.
 #pragma unroll
         for (int b1 = 1; b1 < NB; ++b1)
@@ -1162,7 +1183,198 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
       }
       lds_barrier();
     }
-  } else if (wave == 2) {
+  } else if (wave == CF::W_X || wave == CF::W_XU) {
+    // ========================================================= solve waves
+    // Diagonal-block inverse: lane (block q4, column n16) writes row n16 of
+    // Tbb^T (= column n16 of Tbb): four 4-wide pieces.
+    int t_dst[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = 16 * q4 + n16;
+      t_dst[m] = r * CCR + 16 * ((4 * (q4 >> 1) + m) ^ swz_cc<C>(r)) + 8 * (q4 & 1);
+    }
+    // Tbb as an MFMA row operand (transposing read of Tbb^T): rows
+    // 16 b + 4 q4 + (src >> 2), columns 16 b + 4 (src & 3) .. +3.
+    int t_base[NTS];
+#pragma unroll
+    for (int bh = 0; bh < NTS; ++bh) {
+      const int r = 4 * q4 + (src >> 2);
+      t_base[bh] = r * CCR + 16 * ((4 * bh + (src & 3)) ^ swz_cc<C>(r));
+    }
+    // V in accumulator layout: rows 16 tb + 4 q4 + (src >> 2), columns
+    // 16 cb + 4 (src & 3) .. +3.
+    int v_base[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int r = 4 * q4 + (src >> 2);
+      v_base[cb] = r * CF::V_ROWB + 16 * ((2 * cb + ((src & 3) >> 1)) ^ swz_v(r)) + 8 * (src & 1);
+    }
+    // T'^T store: row j = 16 col + n16, columns 16 b + 4 q4 .. +3.
+    auto tp_off = [&](int b, int col) {
+      const int j = 16 * col + n16;
+      return j * CCR + 16 * ((2 * b + (q4 >> 1)) ^ swz_cc<C>(j)) + 8 * (q4 & 1);
+    };
+    const bf16x4 z4 = {};
+    auto cat = [](bf16x4 lo, bf16x4 hi) { return F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; };
+
+    // Row block b of (I + A) R = X: R_b = Tbb (X_b - sum_{j<b} A_bj R_j).
+    // The T wave solves for X = diag(beta) (lower blocks only) and publishes
+    // T' = -R diag(Gam); the u wave solves for X = diag(beta) V and
+    // publishes u = R.  Each result block is rounded to bf16 once and reused
+    // as the B operand of every later row block.
+    auto solve_wave = [&](auto rc) {
+      constexpr bool TW = decltype(rc)::value == 0;
+      lds_barrier();
+      for (int it = 0; it < NIT; ++it) {
+        const int c = it - 1;
+        if (c >= 0 && c < NC) {
+          const float* vec = vec_of(c);
+          char* sat = sAT + (c & 1) * CF::CC_BYTES;
+          if constexpr (TW) {
+            // Inverse of each 16x16 diagonal block of (I + A): lane (block
+            // q4, column n16) runs forward substitution down the block.
+            if (q4 < NB) {
+              const float* A = sAD + (c & 1) * NB * CF::AD_BLK + q4 * CF::AD_BLK;
+              // Row i holds columns 0..i-1: whole 4-wide pieces, then a 2-
+              // and/or 1-wide piece, so every value read is used.
+              float ar[16][16];
+#pragma unroll
+              for (int i = 1; i < 16; ++i) {
+                const float* row = A + i * CF::AD_ROW;
+#pragma unroll
+                for (int l = 0; l + 4 <= i; l += 4) {
+                  const f32x4 v = *reinterpret_cast<const f32x4*>(row + l);
+                  ar[i][l] = v[0]; ar[i][l + 1] = v[1]; ar[i][l + 2] = v[2]; ar[i][l + 3] = v[3];
+                }
+                const int l0 = i & ~3;
+                if (i & 2) {
+                  const f32x2 v = *reinterpret_cast<const f32x2*>(row + l0);
+                  ar[i][l0] = v[0]; ar[i][l0 + 1] = v[1];
+                }
+                if (i & 1) ar[i][i - 1] = row[i - 1];
+              }
+              // Right-looking order: once entry l is final it is folded
+              // into every later row, so the rows' sums proceed side by side
+              // (each row still accumulates its terms in increasing l).
+              float tc[16];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) tc[i] = (i == n16) ? 1.f : 0.f;
+#pragma unroll
+              for (int l = 0; l < 15; ++l)
+#pragma unroll
+                for (int i = l + 1; i < 16; ++i) tc[i] = __builtin_fmaf(-ar[i][l], tc[l], tc[i]);
+#pragma unroll
+              for (int m = 0; m < 4; ++m)
+                lds_st<bf16x4>(sat, t_dst[m],
+                               bf16x4{(__bf16)tc[4 * m], (__bf16)tc[4 * m + 1], (__bf16)tc[4 * m + 2],
+                                      (__bf16)tc[4 * m + 3]});
+            }
+            flag_release(&sFLAG[1], c + 1);
+          } else {
+            flag_wait_lds(&sFLAG[1], c + 1);
+          }
+
+          F Tf[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) Tf[b] = cat(lds_read_tr(sat, t_base[b >> 1] + 16 * CCR * b + 8 * (b & 1)), z4);
+          // Row blocks of A left of the diagonal as pi-order fragments;
+          // where the slab's upper half is the diagonal block the matching
+          // operand half is zero.
+          F Af[NB][NTS];
+#pragma unroll
+          for (int b = 1; b < NB; ++b)
+#pragma unroll
+            for (int s = 0; 32 * s < 16 * b; ++s) Af[b][s] = lds_at<F>(sat + cc_frag[s] + 16 * CCR * b);
+          const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+          if constexpr (TW) {
+            f32x4 RT[NB][NB];
+            bf16x4 RH[NB][NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+              for (int col = 0; col <= b; ++col) {
+                bf16x4 xh;
+                if (col == b) {
+                  const __bf16 bcol = (__bf16)vec[CF::F_BETA * C + 16 * b + n16];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) xh[e] = 4 * q4 + e == n16 ? bcol : (__bf16)0.f;
+                } else {
+                  f32x4 r = zero4;
+#pragma unroll
+                  for (int s = 0; 32 * s < 16 * b; ++s) {
+                    if (2 * s + 1 < col) continue;  // both blocks of the slab are zero
+                    const bf16x4 lo = 2 * s >= col ? RH[2 * s][col] : z4;
+                    const bf16x4 hi = 2 * s + 1 < b ? RH[2 * s + 1][col] : z4;
+                    r = MM::mma(Af[b][s], cat(lo, hi), r);
+                  }
+                  f32x4 x;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) x[e] = -r[e];
+                  xh = cvt4(x);
+                }
+                RT[b][col] = MM::mma(Tf[b], cat(xh, z4), zero4);
+                RH[b][col] = cvt4(RT[b][col]);
+              }
+            }
+            // Publish T' = -R diag(Gam) as T'^T, once the state wave has
+            // read the previous chunk's.
+            flag_wait_lds(&sFLAG[2], c);
+            char* tp = sTP;
+#pragma unroll
+            for (int col = 0; col < NB; ++col) {
+              const float ng = -vec[CF::F_GAM * C + 16 * col + n16];
+#pragma unroll
+              for (int b = col; b < NB; ++b) {
+                f32x4 t;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = RT[b][col][e] * ng;
+                lds_st<bf16x4>(tp, tp_off(b, col), cvt4(t));
+              }
+            }
+          } else {
+            const char* sv = sV + (c % CF::NVR) * CF::V_BYTES;
+            bf16x4 Vr[NB][NCB];
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb) Vr[tb][cb] = lds_read_tr(sv, v_base[cb] + 16 * CF::V_ROWB * tb);
+            f32x4 RU[NB][NCB];
+            bf16x4 RH[NB][NCB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + CF::F_BETA * C + 16 * b + 4 * q4);
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = bt[e] * (float)Vr[b][cb][e];
+                if (b > 0) {
+                  f32x4 r = zero4;
+#pragma unroll
+                  for (int s = 0; 32 * s < 16 * b; ++s)
+                    r = MM::mma(Af[b][s], cat(RH[2 * s][cb], 2 * s + 1 < b ? RH[2 * s + 1][cb] : z4), r);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) x[e] -= r[e];
+                }
+                RU[b][cb] = MM::mma(Tf[b], cat(cvt4(x), z4), zero4);
+                RH[b][cb] = cvt4(RU[b][cb]);
+              }
+            }
+            flag_wait_lds(&sFLAG[2], c);
+            char* uu = sUU;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb) lds_st<f32x4>(uu, ((b * NCB + cb) * 64 + lane) * 16, RU[b][cb]);
+          }
+        }
+        lds_barrier();
+      }
+    };
+    if (wave == CF::W_X) solve_wave(IC<0>{});
+    else solve_wave(IC<1>{});
+  } else if (wave == CF::W_S) {
     // =========================================================== state wave
     const long sbase = (long)chain * DK * p.dv;
     const int col0 = tile * CF::DVT;
@@ -1181,33 +1393,24 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
 
     // Transposing reads.  K^T: rows 32 s + 16 hi + 4 q4 + (src >> 2), the
     // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 (b&1) .. +3.
-    const int src = lane & 15;
     int kt_base[(NKB + 1) / 2];
 #pragma unroll
     for (int bh = 0; bh < (NKB + 1) / 2; ++bh) {
       const int r = 4 * q4 + (src >> 2);
       kt_base[bh] = r * KQR + 16 * ((4 * bh + (src & 3)) ^ swz_kq<GR>(r));
     }
-    // V in accumulator layout: rows 16 tb + 4 q4 + (src >> 2), columns
-    // 16 cb + 4 (src & 3) .. +3.
-    int v_base[NCB];
+    // T' as a row operand (transposing read of T'^T): rows
+    // 32 s + 16 hi + 4 q4 + (src >> 2), columns 16 tb + 4 (src & 3) .. +3.
+    int tp_base[NB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int tb = 0; tb < NB; ++tb) {
       const int r = 4 * q4 + (src >> 2);
-      v_base[cb] = r * CF::V_ROWB + 16 * ((2 * cb + ((src & 3) >> 1)) ^ swz_v(r)) + 8 * (src & 1);
-    }
-    // Tbb (transposing read of Tbb^T): rows 16 b + 4 q4 + (src >> 2),
-    // columns 16 b + 4 (src & 3) .. +3.
-    int t_base[NTS];
-#pragma unroll
-    for (int bh = 0; bh < NTS; ++bh) {
-      const int r = 4 * q4 + (src >> 2);
-      t_base[bh] = r * CCR + 16 * ((4 * bh + (src & 3)) ^ swz_cc<C>(r));
+      tp_base[tb] = r * CCR + 16 * ((2 * tb + ((src & 3) >> 1)) ^ swz_cc<C>(r)) + 8 * (src & 1);
     }
 
     F Mf[NKS][NCB];
-    auto publish_state = [&](int slot) {
-      char* mf = sMF + slot * CF::MF_BYTES;
+    auto publish_state = [&]() {
+      char* mf = sMF;
 #pragma unroll
       for (int s = 0; s < NKS; ++s)
 #pragma unroll
@@ -1216,84 +1419,94 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
           lds_st<F>(mf, ((cb * NKS + s) * 64 + lane) * 16, Mf[s][cb]);
         }
     };
-    publish_state(0);
+    publish_state();
     lds_barrier();
 
     for (int it = 0; it < NIT; ++it) {
-      const int c = it - 1;
+      const int c = it - 2;
       if (c >= 0 && c < NC) {
-        const char* sk = sK + (c % 3) * CF::KQ_BYTES;
-        const char* sv = sV + (c % 3) * CF::V_BYTES;
-        const char* sat = sAT + (c & 1) * CF::CC_BYTES;
+        const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
         const float* vec = vec_of(c);
 
-        // Operands that do not depend on the state.  K is read one row block
-        // ahead of its use to keep the live register set small.
+        // u and T' into registers first, so that the solve waves may
+        // overwrite them with the next chunk's early.
+        f32x4 U[NB][NCB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) U[tb][cb] = lds_at<f32x4>(sUU + ((tb * NCB + cb) * 64 + lane) * 16);
+        // T' (lower triangular) as row operands: slab s2 of row block tb is
+        // used for 32 s2 <= 16 tb, its upper half only when 16 tb > 32 s2.
+        F TPf[NB][NTS];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int s = 0; 32 * s <= 16 * tb; ++s) {
+            const bf16x4 lo = lds_read_tr(sTP, tp_base[tb] + 32 * s * CCR);
+            F f{};
+            f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+            if (32 * s + 16 <= 16 * tb) {
+              const bf16x4 hi = lds_read_tr(sTP, tp_base[tb] + (32 * s + 16) * CCR);
+              f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+            }
+            TPf[tb][s] = f;
+          }
+
+        // Y = K M, K read one row block ahead of its use.
         F Kf[2][NKS];
         auto read_k = [&](int tb) {
 #pragma unroll
           for (int s = 0; s < NKS; ++s) Kf[tb & 1][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * tb);
         };
         read_k(0);
-        F Tf[NB];
+        f32x4 Y[NB][NCB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const bf16x4 t = lds_read_tr(sat, t_base[b >> 1] + 16 * CCR * b + 8 * (b & 1));
-          F f{};
-          f[0] = t[0]; f[1] = t[1]; f[2] = t[2]; f[3] = t[3];
-          Tf[b] = f;
-        }
-        // Row blocks of A left of the diagonal as pi-order fragments; where
-        // the slab's upper half is the diagonal block the matching operand
-        // half is zero.
-        F Af[NB][NTS];
-#pragma unroll
-        for (int b = 1; b < NB; ++b)
-#pragma unroll
-          for (int s = 0; 32 * s < 16 * b; ++s) Af[b][s] = lds_at<F>(sat + cc_frag[s] + 16 * CCR * b);
-        bf16x4 Vr[NB][NCB];
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) Vr[tb][cb] = lds_read_tr(sv, v_base[cb] + 16 * CF::V_ROWB * tb);
-
-        // Row block b: Y_b = K_b M, X_b = beta V_b - beta Gam Y_b and
-        // U_b = Tbb (X_b - sum_{j<b} A_bj U_j), one block at a time so that
-        // the products of block b+1 can fill the latency of block b's solve.
-        f32x4 U[NB][NCB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (b + 1 < NB) read_k(b + 1);
-          const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + CF::F_BETA * C + 16 * b + 4 * q4);
-          const f32x4 bg = *reinterpret_cast<const f32x4*>(vec + CF::F_BG * C + 16 * b + 4 * q4);
-          f32x4 x[NCB];
+        for (int tb = 0; tb < NB; ++tb) {
+          if (tb + 1 < NB) read_k(tb + 1);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[b & 1][s], Mf[s][cb], y);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[cb][e] = __builtin_fmaf(-bg[e], y[e], bt[e] * (float)Vr[b][cb][e]);
-          }
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            if (b > 0) {
-              f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int s = 0; 32 * s < 16 * b; ++s) {
-                const F ub = 32 * s + 16 < 16 * b ? MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb])
-                                                  : MM::from_acc1(U[2 * s][cb]);
-                r = MM::mma(Af[b][s], ub, r);
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) x[cb][e] -= r[e];
-            }
-            U[b][cb] = MM::mma(Tf[b], MM::from_acc1(x[cb]), f32x4{0.f, 0.f, 0.f, 0.f});
+            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[tb & 1][s], Mf[s][cb], y);
+            Y[tb][cb] = y;
           }
         }
+        flag_release(&sFLAG[2], c + 1);
+        // U = u + T' Y
+        F Yf[NTS][NCB];
+#pragma unroll
+        for (int s = 0; s < NTS; ++s)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) Yf[s][cb] = MM::from_acc(Y[2 * s][cb], Y[2 * s + 1][cb]);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int s = 0; 32 * s <= 16 * tb; ++s)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) U[tb][cb] = MM::mma(TPf[tb][s], Yf[s][cb], U[tb][cb]);
+
+        // Publish U for the output waves; W = diag(w) U for the update.
+        F Wf[NTS][NCB];
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 4 * q4);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 16 + 4 * q4);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            lds_st<F>(sUF, ((cb * NTS + s) * 64 + lane) * 16, MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb]));
+            f32x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] = w0[e] * U[2 * s][cb][e];
+              b[e] = w1[e] * U[2 * s + 1][cb][e];
+            }
+            Wf[s][cb] = MM::from_acc(a, b);
+          }
+        }
+        flag_release(&sFLAG[0], c + 1);
 
         // K^T for the update (transposing reads, tokens in pi order to match
-        // the W fragments); Gam_C M and W are formed while they arrive.
+        // the W fragments); Gam_C M is formed while they arrive.
         F KT[NKB][NTS];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -1312,26 +1525,6 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) Macc[kb][cb][e] *= gC;
 
-        // Publish U for the output wave; W = diag(w) U for the update.
-        char* uf = sUF + (c & 1) * CF::UF_BYTES;
-        F Wf[NTS][NCB];
-#pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 4 * q4);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 16 + 4 * q4);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            lds_st<F>(uf, ((cb * NTS + s) * 64 + lane) * 16, MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb]));
-            f32x4 a, b;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a[e] = w0[e] * U[2 * s][cb][e];
-              b[e] = w1[e] * U[2 * s + 1][cb][e];
-            }
-            Wf[s][cb] = MM::from_acc(a, b);
-          }
-        }
-
         // M <- Gam_C M + K^T diag(w) U
 #pragma unroll
         for (int b = 0; b < NKB; ++b)
@@ -1342,7 +1535,10 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
             for (int s = 0; s < NTS; ++s) m = MM::mma(KT[b][s], Wf[s][cb], m);
             Macc[b][cb] = m;
           }
-        publish_state((c + 1) & 1);
+        // The output waves have read this chunk's state: publish the next.
+        flag_wait_lds(&sFLAG[3], c + 1);
+        flag_wait_lds(&sFLAG[4], c + 1);
+        publish_state();
       }
       lds_barrier();
     }
@@ -1354,115 +1550,146 @@ __global__ __launch_bounds__(256, 1) void gdn_bf16_kernel(const Params p) {
         for (int e = 0; e < 4; ++e)
           p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col0 + 16 * cb + n16] = Macc[b][cb][e];
   } else {
-    // ========================================================== output wave
-    // Output rows: lane (token 16 tb + n16, columns 16 cb + 4 q4 .. +3).
-    int o_off[NB];
+    // ========================================================= output waves
+    auto out_wave = [&](auto oc) {
+      constexpr int OW = decltype(oc)::value;
+      constexpr int NOWN = CF::NOWN;
+      constexpr int KMAX = CF::own_tb(OW, NOWN - 1) > CF::own_tb(OW, 0) ? CF::own_tb(OW, NOWN - 1) : CF::own_tb(OW, 0);
+      // Output rows: lane (token 16 tb + n16, columns 16 cb + 4 q4 .. +3).
+      int o_off[NOWN];
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) o_off[tb] = (int)((16 * tb + n16) * v_stride) + 8 * q4;
-    lds_barrier();
-    // One step: finish chunk it-2 (+ P U, store); then for chunk it-1
-    // diag(Gam) Q M and P = (Q K^T) * D, kept in registers.
-    auto step = [&](int it, F (&Pc)[NB][NTS], F (&Pn)[NB][NTS], f32x4 (&Ofin)[NB][NCB], f32x4 (&Onew)[NB][NCB]) {
-      const int c2 = it - 2, c1 = it - 1;
-      if (c2 >= 0 && c2 < NC) {
-        const char* uf = sUF + (c2 & 1) * CF::UF_BYTES;
-        F Uf[NTS][NCB];
+      for (int i = 0; i < NOWN; ++i) o_off[i] = (int)((16 * CF::own_tb(OW, i) + n16) * v_stride) + 8 * q4;
+      // q fragments straight from HBM into registers, one step ahead of
+      // use: lane (token 16 tb + n16, keys 32 s + 8 q4 .. +7).
+      int q_off[NOWN];
 #pragma unroll
-        for (int s = 0; s < NTS; ++s)
+      for (int i = 0; i < NOWN; ++i) q_off[i] = (int)((16 * CF::own_tb(OW, i) + n16) * kq_stride) + 16 * q4;
+      // Issued unconditionally (a chunk past the end gets an empty
+      // descriptor and reads zeros), so that the waits for the previous
+      // step's loads never cover these.
+      auto load_q = [&](int c, F (&Qn)[NOWN][NKS]) {
+        const long row0 = rowbase + (long)c * C;
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(p.q + row0 * kq_stride + hh * DK * 2, c < NC ? (long)(len - c * C) * kq_stride : 0);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) Uf[s][cb] = lds_at<F>(uf + ((cb * NTS + s) * 64 + lane) * 16);
-        const long row0 = rowbase + (long)c2 * C;
-        const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(p.out + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, (long)(len - c2 * C) * v_stride);
+        for (int i = 0; i < NOWN; ++i)
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
+          for (int s = 0; s < NKS; ++s)
+            Qn[i][s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rq, q_off[i] + 64 * s, 0, 0));
+      };
+      // Step it (2 <= it < NC + 2): load q of chunk it-1; finish chunk it-2
+      // with the q loaded one step earlier.
+      auto step = [&](int it, F (&Qf)[NOWN][NKS], F (&Qn)[NOWN][NKS]) {
+        load_q(it - 1, Qn);
+        const int c = it - 2;
+        {
+          const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
+          const float* vec = vec_of(c);
+          F Mf[NKS][NCB];
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            f32x4 o = Ofin[tb][cb];
+          for (int s = 0; s < NKS; ++s)
 #pragma unroll
-            for (int s = 0; s <= (16 * tb + 15) / 32; ++s) o = MM::mma(Uf[s][cb], Pc[tb][s], o);
-            const bf16x4 ob = cvt4(o);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro, o_off[tb] + 32 * cb, 0, 0);
-          }
-      }
-      if (c1 >= 0 && c1 < NC) {
-        const char* sq = sQ + (c1 % 3) * CF::KQ_BYTES;
-        const char* sk = sK + (c1 % 3) * CF::KQ_BYTES;
-        const char* mf = sMF + (c1 & 1) * CF::MF_BYTES;
-        const float* vec = vec_of(c1);
-        F Qf[NB][NKS];
+            for (int cb = 0; cb < NCB; ++cb) Mf[s][cb] = lds_at<F>(sMF + ((cb * NKS + s) * 64 + lane) * 16);
+          flag_release(&sFLAG[3 + OW], c + 1);
+          // O^T = (M^T Q^T) diag(Gam): lane (token 16 tb + n16, q4) holds
+          // columns 16 cb + 4 q4 + e.
+          f32x4 Oacc[NOWN][NCB];
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
+          for (int i = 0; i < NOWN; ++i) {
+            const int tb = CF::own_tb(OW, i);
+            const float gcol = vec[CF::F_GAM * C + 16 * tb + n16];
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) Qf[tb][s] = lds_at<F>(sq + kq_frag[s] + 16 * KQR * tb);
-        F Mf[NKS][NCB];
+            for (int cb = 0; cb < NCB; ++cb) {
+              f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
+              for (int s = 0; s < NKS; ++s) o = MM::mma(Mf[s][cb], Qf[i][s], o);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) Mf[s][cb] = lds_at<F>(mf + ((cb * NKS + s) * 64 + lane) * 16);
-        // O^T = (M^T Q^T) diag(Gam): lane (token 16 tb + n16, q4) holds
-        // columns 16 cb + 4 q4 + e.
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-          const float gcol = vec[CF::F_GAM * C + 16 * tb + n16];
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) o = MM::mma(Mf[s][cb], Qf[tb][s], o);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] *= gcol;
-            Onew[tb][cb] = o;
-          }
-        }
-        // P: lane (n16, q4) of block (b1, b2) holds row i = 16 b1 + n16 and
-        // columns j = 16 b2 + 4 q4 + e, which is the pi-order B operand of
-        // P U for slab b2 >> 1.
-        F Kf[NB][NKS];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) Kf[b][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * b);
-#pragma unroll
-        for (int b1 = 0; b1 < NB; ++b1) {
-          const float li = vec[CF::F_LAM * C + 16 * b1 + n16];
-          const float eri = vec[CF::F_ER * C + 16 * b1 + n16];
-          f32x4 pb[NB];
-#pragma unroll
-          for (int b2 = 0; b2 <= b1; ++b2) {
-            f32x4 pq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) pq = MM::mma(Kf[b2][s], Qf[b1][s], pq);
-            if (b2 < b1) {
-              const f32x4 ec = *reinterpret_cast<const f32x4*>(vec + (CF::F_ER + b1) * C + 16 * b2 + 4 * q4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pb[b2][e] = pq[e] * (eri * ec[e]);
-            } else {
-              const f32x4 lj = *reinterpret_cast<const f32x4*>(vec + CF::F_LAM * C + 16 * b1 + 4 * q4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pb[b2][e] = 4 * q4 + e <= n16 ? pq[e] * exp2_fast(li - lj[e]) : 0.f;
+              for (int e = 0; e < 4; ++e) o[e] *= gcol;
+              Oacc[i][cb] = o;
             }
           }
+          // P: lane (n16, q4) of block (b1, b2) holds row i = 16 b1 + n16 and
+          // columns j = 16 b2 + 4 q4 + e, which is the pi-order B operand of
+          // P U for slab b2 >> 1.
+          F Kf[KMAX + 1][NKS];
 #pragma unroll
-          for (int s = 0; 32 * s <= 16 * b1; ++s)
-            Pn[b1][s] = 2 * s + 1 <= b1 ? MM::from_acc(pb[2 * s], pb[2 * s + 1]) : MM::from_acc1(pb[2 * s]);
+          for (int b = 0; b <= KMAX; ++b)
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) Kf[b][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * b);
+          F Pf[NOWN][NTS];
+#pragma unroll
+          for (int i = 0; i < NOWN; ++i) {
+            const int b1 = CF::own_tb(OW, i);
+            const float li = vec[CF::F_LAM * C + 16 * b1 + n16];
+            const float eri = vec[CF::F_ER * C + 16 * b1 + n16];
+            f32x4 pb[NB];
+#pragma unroll
+            for (int b2 = 0; b2 <= b1; ++b2) {
+              f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int s = 0; s < NKS; ++s) pq = MM::mma(Kf[b2][s], Qf[i][s], pq);
+              if (b2 < b1) {
+                const f32x4 ec = *reinterpret_cast<const f32x4*>(vec + (CF::F_ER + b1) * C + 16 * b2 + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pb[b2][e] = pq[e] * (eri * ec[e]);
+              } else {
+                const f32x4 lj = *reinterpret_cast<const f32x4*>(vec + CF::F_LAM * C + 16 * b1 + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pb[b2][e] = 4 * q4 + e <= n16 ? pq[e] * exp2_fast(li - lj[e]) : 0.f;
+              }
+            }
+#pragma unroll
+            for (int s = 0; 32 * s <= 16 * b1; ++s)
+              Pf[i][s] = 2 * s + 1 <= b1 ? MM::from_acc(pb[2 * s], pb[2 * s + 1]) : MM::from_acc1(pb[2 * s]);
+          }
+
+          flag_wait_lds(&sFLAG[0], c + 1);
+          constexpr int NUS = (16 * KMAX + 15) / 32 + 1;  // U slabs used
+          F Uf[NUS][NCB];
+#pragma unroll
+          for (int s = 0; s < NUS; ++s)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) Uf[s][cb] = lds_at<F>(sUF + ((cb * NTS + s) * 64 + lane) * 16);
+          const long row0 = rowbase + (long)c * C;
+          const __amdgpu_buffer_rsrc_t ro =
+              make_rsrc(p.out + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, (long)(len - c * C) * v_stride);
+#pragma unroll
+          for (int i = 0; i < NOWN; ++i) {
+            const int tb = CF::own_tb(OW, i);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              f32x4 o = Oacc[i][cb];
+#pragma unroll
+              for (int s = 0; 32 * s <= 16 * tb; ++s) o = MM::mma(Uf[s][cb], Pf[i][s], o);
+              const bf16x4 ob = cvt4(o);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro, o_off[i] + 32 * cb, 0, 0);
+            }
+          }
         }
-      }
+        lds_barrier();
+      };
       lds_barrier();
+      F Q0[NOWN][NKS], Q1[NOWN][NKS];
+      if (NIT > 0) {
+        lds_barrier();  // step 0
+        load_q(0, Q0);
+        lds_barrier();  // step 1
+      }
+      for (int it = 2; it < NIT; it += 2) {
+        step(it, Q0, Q1);
+        if (it + 1 < NIT) step(it + 1, Q1, Q0);
+      }
     };
-    F P0[NB][NTS], P1[NB][NTS];
-    f32x4 O0[NB][NCB], O1[NB][NCB];
-    for (int it = 0; it < NIT; it += 2) {
-      step(it, P1, P0, O1, O0);
-      if (it + 1 < NIT) step(it + 1, P0, P1, O0, O1);
-    }
+    if (wave == CF::W_OA) out_wave(IC<0>{});
+    else out_wave(IC<1>{});
   }
 }
 
 template <int DK, int C>
 int launch16(const Params& p, int nwg, hipStream_t stream) {
-  static_assert(Cfg16<DK, C>::LDS <= 160 * 1024, "LDS budget");
-  hipLaunchKernelGGL((gdn_bf16_kernel<DK, C>), dim3(nwg), dim3(256), 0, stream, p);
+  using CF = Cfg16<DK, C>;
+  static_assert(CF::LDS <= 160 * 1024, "LDS budget");
+  hipLaunchKernelGGL((gdn_bf16_kernel<DK, C>), dim3(nwg), dim3(64 * CF::NW), 0, stream, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
