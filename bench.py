@@ -94,7 +94,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # about 40 ms of warm-up: the first ~10 ms of launches after an idle
+    # period run at a lower GPU clock
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="wide_head", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")

@@ -869,6 +869,10 @@ __device__ static inline int swz_cc(int r) {
   else return (r >> 1) & 3;
 }
 
+#ifndef GDN_ROLEMAP
+#define GDN_ROLEMAP 0x76325410u
+#endif
+
 template <int DK, int C>
 struct Cfg16 {
   static constexpr int DVT = 32, NCB = 2;  // value columns per workgroup, 16-column blocks
@@ -889,9 +893,12 @@ struct Cfg16 {
   static constexpr int AD_ROW = 20, AD_BLK = 16 * AD_ROW + 4;
   static constexpr int KQ_INS = KQ_BYTES / 1024, V_INS = V_BYTES / 1024;  // copies per chunk
   static constexpr int KQ_RPI = 1024 / KQ_ROWB, V_RPI = 1024 / V_ROWB;    // rows per copy
-  // Wave roles.  Waves w and w + 4 share a SIMD: the state wave shares
-  // with the loader, the T solve wave has its SIMD to itself.
-  static constexpr int W_S = 0, W_OA = 1, W_OB = 2, W_X = 3, W_L = 4, W_G = 5, W_XU = 6, NW = 7;
+  // Wave roles.  ROLEMAP holds the role of wave w in bits [4w, 4w + 4);
+  // waves w and w + 4 share a SIMD, so the map also places the roles on
+  // SIMDs (by default: each state half with one output wave, the T solve
+  // wave with the loader, the u solve wave with the Gram wave).
+  static constexpr int R_S0 = 0, R_S1 = 1, R_OA = 2, R_OB = 3, R_X = 4, R_XU = 5, R_L = 6, R_G = 7, NW = 8;
+  static constexpr unsigned ROLEMAP = GDN_ROLEMAP;
   // Output wave o owns row blocks own_tb(o, 0..NOWN-1): {0, 3} and {1, 2}
   // for four blocks (equal MFMA work), {0} and {1} for two.
   static constexpr int NOWN = NB == 4 ? 2 : 1;
@@ -901,7 +908,7 @@ struct Cfg16 {
   // is copied two steps ahead of the u solve.
   static constexpr int NKR = 5, NVR = 3;
   static constexpr int LDS = NKR * KQ_BYTES + NVR * V_BYTES + 3 * CC_BYTES + UU_BYTES + MF_BYTES + UF_BYTES +
-                             4 * NF * C * 4 + 2 * NB * AD_BLK * 4 + 32;
+                             4 * NF * C * 4 + NB * AD_BLK * 4 + 32;
   static_assert(NB >= 2 && NB <= 4 && NKS >= 1 && GR >= 4, "shape");
 };
 
@@ -952,9 +959,9 @@ template <typename V>
 __device__ static inline V lds_at(const char* p) { return *reinterpret_cast<const V*>(p); }
 
 template <int DK, int C>
-__global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
+__global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
   using CF = Cfg16<DK, C>;
-  static_assert(64 * CF::NW == 448, "launch bounds");
+  static_assert(64 * CF::NW == 512, "launch bounds");
   using MM = Mma<__bf16>;
   using F = bf16x8;
   constexpr int NB = CF::NB, NTS = CF::NTS, NKB = CF::NKB, NKS = CF::NKS, NCB = CF::NCB, NF = CF::NF;
@@ -971,17 +978,19 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
   __shared__ __attribute__((aligned(16))) char sMF[CF::MF_BYTES];
   __shared__ __attribute__((aligned(16))) char sUF[CF::UF_BYTES];
   __shared__ __attribute__((aligned(16))) float sVEC[4 * NF * C];
-  __shared__ __attribute__((aligned(16))) float sAD[2 * NB * CF::AD_BLK];
+  __shared__ __attribute__((aligned(16))) float sAD[NB * CF::AD_BLK];
   // Flags, each holding chunk index + 1:
-  //   [0] U published (state -> output waves);
-  //   [1] diagonal-block inverses published (T -> u solve wave);
-  //   [2] T' and u read (state -> solve waves, which then overwrite them);
-  //   [3], [4] state read by output wave 0 / 1 (-> state wave, which then
-  //   publishes the next state over it).
+  //   [0], [1] U published by state wave 0 / 1 (-> output waves);
+  //   [2], [3] T' and u read by state wave 0 / 1 (-> solve waves, which
+  //            then overwrite them);
+  //   [4], [5] state read by output wave 0 / 1 (-> state waves, which then
+  //            publish the next state over it);
+  //   [6] diagonal blocks of A published (Gram -> loader wave).
   __shared__ int sFLAG[8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int role = (CF::ROLEMAP >> (4 * wave)) & 15;
   const int q4 = lane >> 4, n16 = lane & 15;
   const int src = lane & 15;  // source lane of a transposing read
 
@@ -1018,7 +1027,7 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
   for (int s = 0; s < NTS; ++s) cc_frag[s] = n16 * CCR + 16 * ((4 * s + q4) ^ swz_cc<C>(n16));
 
-  if (wave == CF::W_L) {
+  if (role == CF::R_L) {
     // ========================================================== loader wave
     // Copy i of a chunk writes LDS bytes [1024 i, 1024 i + 1024): lane l
     // fills granule l % GR of row i*RPI + l/GR with the logical granule
@@ -1090,6 +1099,57 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
       }
     };
 
+    // Diagonal-block inverse: lane (block q4, column n16) writes row n16 of
+    // Tbb^T (= column n16 of Tbb): four 4-wide pieces.
+    int t_dst[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = 16 * q4 + n16;
+      t_dst[m] = r * CCR + 16 * ((4 * (q4 >> 1) + m) ^ swz_cc<C>(r)) + 8 * (q4 & 1);
+    }
+    // Inverse of each 16x16 diagonal block of (I + A) of chunk c, once the
+    // Gram wave has published them: lane (block q4, column n16) runs forward
+    // substitution down the block.
+    auto diag_inverse = [&](int c) {
+      flag_wait_lds(&sFLAG[6], c + 1);
+      if (q4 < NB) {
+        const float* A = sAD + q4 * CF::AD_BLK;
+        // Row i holds columns 0..i-1: whole 4-wide pieces, then a 2- and/or
+        // 1-wide piece, so every value read is used.
+        float ar[16][16];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+          const float* row = A + i * CF::AD_ROW;
+#pragma unroll
+          for (int l = 0; l + 4 <= i; l += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(row + l);
+            ar[i][l] = v[0]; ar[i][l + 1] = v[1]; ar[i][l + 2] = v[2]; ar[i][l + 3] = v[3];
+          }
+          const int l0 = i & ~3;
+          if (i & 2) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(row + l0);
+            ar[i][l0] = v[0]; ar[i][l0 + 1] = v[1];
+          }
+          if (i & 1) ar[i][i - 1] = row[i - 1];
+        }
+        // Right-looking order: once entry l is final it is folded into every
+        // later row, so the rows' sums proceed side by side (each row still
+        // accumulates its terms in increasing l).
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tc[i] = (i == n16) ? 1.f : 0.f;
+#pragma unroll
+        for (int l = 0; l < 15; ++l)
+#pragma unroll
+          for (int i = l + 1; i < 16; ++i) tc[i] = __builtin_fmaf(-ar[i][l], tc[l], tc[i]);
+        char* sat = sAT + (c & 1) * CF::CC_BYTES;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          lds_st<bf16x4>(sat, t_dst[m],
+                         bf16x4{(__bf16)tc[4 * m], (__bf16)tc[4 * m + 1], (__bf16)tc[4 * m + 2], (__bf16)tc[4 * m + 3]});
+      }
+    };
+
     // Wait until at most the current step's loads and copies are in flight
     // and this wave's LDS stores are done, then join the barrier.  (A plain
     // LDS fence here would also wait for the copies just issued.)
@@ -1116,20 +1176,22 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
     step_barrier();  // k of chunk 0 has landed
 
     // Step it: v of chunk it+1 and k of chunk it+2 (two steps ahead of
-    // their first readers), g and beta of chunk it+2, and the vectors of
-    // chunk it+1 from the g and beta loaded one step earlier.
+    // their first readers), g and beta of chunk it+2, the vectors of chunk
+    // it+1 from the g and beta loaded one step earlier, and the diagonal-
+    // block inverses of chunk it.
     auto step = [&](int it, float& gu, float& bu, float& gl, float& bl) {
       load_gb(it + 2, gl, bl);
       issue_v(it + 1);
       issue_k(it + 2);
       if (it + 1 < NC) make_vec(it + 1, gu, bu);
+      if (it < NC) diag_inverse(it);
       step_barrier();
     };
     for (int it = 0; it < NIT; it += 2) {
       step(it, g1, b1, g0, b0);
       if (it + 1 < NIT) step(it + 1, g0, b0, g1, b1);
     }
-  } else if (wave == CF::W_G) {
+  } else if (role == CF::R_G) {
     // ============================================================ Gram wave
     lds_barrier();
     for (int it = 0; it < NIT; ++it) {
@@ -1137,35 +1199,36 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
       if (c < NC) {
         const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
         const float* vec = vec_of(c);
-        float* ad = sAD + (c & 1) * NB * CF::AD_BLK;
         char* sat = sAT + (c & 1) * CF::CC_BYTES;
+        // A block result: lane (n16, q4) holds row i = 16 b1 + n16 and
+        // columns j = 16 b2 + 4 q4 + e.  Diagonal blocks first (fp32, j < i),
+        // published for the loader's inverses.
         F Kf[NB][NKS];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int s = 0; s < NKS; ++s) Kf[b][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * b);
-        // A block result: lane (n16, q4) holds row i = 16 b1 + n16 and
-        // columns j = 16 b2 + 4 q4 + e.
-        float li[NB], bi[NB], eri[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          li[b] = vec[CF::F_LAM * C + 16 * b + n16];
-          bi[b] = vec[CF::F_BETA * C + 16 * b + n16];
-          eri[b] = vec[CF::F_ER * C + 16 * b + n16];
-        }
-        // Diagonal blocks (j < i), fp32.
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
+          const float li = vec[CF::F_LAM * C + 16 * b + n16];
+          const float bi0 = vec[CF::F_BETA * C + 16 * b + n16];
           const f32x4 lj = *reinterpret_cast<const f32x4*>(vec + CF::F_LAM * C + 16 * b + 4 * q4);
           f32x4 kk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < NKS; ++s) kk = MM::mma(Kf[b][s], Kf[b][s], kk);
           f32x4 r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = 4 * q4 + e < n16 ? bi[b] * kk[e] * exp2_fast(li[b] - lj[e]) : 0.f;
-          *reinterpret_cast<f32x4*>(ad + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
+          for (int e = 0; e < 4; ++e) r[e] = 4 * q4 + e < n16 ? bi0 * kk[e] * exp2_fast(li - lj[e]) : 0.f;
+          *reinterpret_cast<f32x4*>(sAD + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
         }
-        // Off-diagonal blocks.
+        flag_release(&sFLAG[6], c + 1);
+        // Off-diagonal blocks (bf16).
+        float bi[NB], eri[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          bi[b] = vec[CF::F_BETA * C + 16 * b + n16];
+          eri[b] = vec[CF::F_ER * C + 16 * b + n16];
+        }
 #pragma unroll
         for (int b1 = 1; b1 < NB; ++b1)
 #pragma unroll
@@ -1183,16 +1246,8 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
       }
       lds_barrier();
     }
-  } else if (wave == CF::W_X || wave == CF::W_XU) {
+  } else if (role == CF::R_X || role == CF::R_XU) {
     // ========================================================= solve waves
-    // Diagonal-block inverse: lane (block q4, column n16) writes row n16 of
-    // Tbb^T (= column n16 of Tbb): four 4-wide pieces.
-    int t_dst[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int r = 16 * q4 + n16;
-      t_dst[m] = r * CCR + 16 * ((4 * (q4 >> 1) + m) ^ swz_cc<C>(r)) + 8 * (q4 & 1);
-    }
     // Tbb as an MFMA row operand (transposing read of Tbb^T): rows
     // 16 b + 4 q4 + (src >> 2), columns 16 b + 4 (src & 3) .. +3.
     int t_base[NTS];
@@ -1230,50 +1285,6 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
         if (c >= 0 && c < NC) {
           const float* vec = vec_of(c);
           char* sat = sAT + (c & 1) * CF::CC_BYTES;
-          if constexpr (TW) {
-            // Inverse of each 16x16 diagonal block of (I + A): lane (block
-            // q4, column n16) runs forward substitution down the block.
-            if (q4 < NB) {
-              const float* A = sAD + (c & 1) * NB * CF::AD_BLK + q4 * CF::AD_BLK;
-              // Row i holds columns 0..i-1: whole 4-wide pieces, then a 2-
-              // and/or 1-wide piece, so every value read is used.
-              float ar[16][16];
-#pragma unroll
-              for (int i = 1; i < 16; ++i) {
-                const float* row = A + i * CF::AD_ROW;
-#pragma unroll
-                for (int l = 0; l + 4 <= i; l += 4) {
-                  const f32x4 v = *reinterpret_cast<const f32x4*>(row + l);
-                  ar[i][l] = v[0]; ar[i][l + 1] = v[1]; ar[i][l + 2] = v[2]; ar[i][l + 3] = v[3];
-                }
-                const int l0 = i & ~3;
-                if (i & 2) {
-                  const f32x2 v = *reinterpret_cast<const f32x2*>(row + l0);
-                  ar[i][l0] = v[0]; ar[i][l0 + 1] = v[1];
-                }
-                if (i & 1) ar[i][i - 1] = row[i - 1];
-              }
-              // Right-looking order: once entry l is final it is folded
-              // into every later row, so the rows' sums proceed side by side
-              // (each row still accumulates its terms in increasing l).
-              float tc[16];
-#pragma unroll
-              for (int i = 0; i < 16; ++i) tc[i] = (i == n16) ? 1.f : 0.f;
-#pragma unroll
-              for (int l = 0; l < 15; ++l)
-#pragma unroll
-                for (int i = l + 1; i < 16; ++i) tc[i] = __builtin_fmaf(-ar[i][l], tc[l], tc[i]);
-#pragma unroll
-              for (int m = 0; m < 4; ++m)
-                lds_st<bf16x4>(sat, t_dst[m],
-                               bf16x4{(__bf16)tc[4 * m], (__bf16)tc[4 * m + 1], (__bf16)tc[4 * m + 2],
-                                      (__bf16)tc[4 * m + 3]});
-            }
-            flag_release(&sFLAG[1], c + 1);
-          } else {
-            flag_wait_lds(&sFLAG[1], c + 1);
-          }
-
           F Tf[NB];
 #pragma unroll
           for (int b = 0; b < NB; ++b) Tf[b] = cat(lds_read_tr(sat, t_base[b >> 1] + 16 * CCR * b + 8 * (b & 1)), z4);
@@ -1320,6 +1331,7 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
             // Publish T' = -R diag(Gam) as T'^T, once the state wave has
             // read the previous chunk's.
             flag_wait_lds(&sFLAG[2], c);
+            flag_wait_lds(&sFLAG[3], c);
             char* tp = sTP;
 #pragma unroll
             for (int col = 0; col < NB; ++col) {
@@ -1362,6 +1374,7 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
               }
             }
             flag_wait_lds(&sFLAG[2], c);
+            flag_wait_lds(&sFLAG[3], c);
             char* uu = sUU;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -1372,25 +1385,16 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
         lds_barrier();
       }
     };
-    if (wave == CF::W_X) solve_wave(IC<0>{});
+    if (role == CF::R_X) solve_wave(IC<0>{});
     else solve_wave(IC<1>{});
-  } else if (wave == CF::W_S) {
-    // =========================================================== state wave
+  } else if (role == CF::R_S0 || role == CF::R_S1) {
+    // ========================================================== state waves
+    // Two waves, one per 16-column half of the tile; each carries its half
+    // of the state for the whole sequence.
     const long sbase = (long)chain * DK * p.dv;
-    const int col0 = tile * CF::DVT;
-    // Accumulator block b, element e of column block cb holds
-    // M[key(b, 4q + e)][col0 + 16 cb + n16]; two stacked blocks form a
-    // fragment with natural key positions.
+    // Accumulator block b holds M[key(b, 4q + e)][column n16 of the half];
+    // two stacked blocks form a fragment with natural key positions.
     auto key_of = [&](int b, int r) { return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3); };
-    f32x4 Macc[NKB][NCB];
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Macc[b][cb][e] = p.h0 ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col0 + 16 * cb + n16] : 0.f;
-
     // Transposing reads.  K^T: rows 32 s + 16 hi + 4 q4 + (src >> 2), the
     // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 (b&1) .. +3.
     int kt_base[(NKB + 1) / 2];
@@ -1408,147 +1412,138 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
       tp_base[tb] = r * CCR + 16 * ((2 * tb + ((src & 3) >> 1)) ^ swz_cc<C>(r)) + 8 * (src & 1);
     }
 
-    F Mf[NKS][NCB];
-    auto publish_state = [&]() {
-      char* mf = sMF;
+    auto state_wave = [&](auto hc) {
+      constexpr int cb = decltype(hc)::value;  // this wave's column block
+      const long col = (long)tile * CF::DVT + 16 * cb + n16;
+      f32x4 Macc[NKB];
 #pragma unroll
-      for (int s = 0; s < NKS; ++s)
+      for (int b = 0; b < NKB; ++b)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          Mf[s][cb] = MM::from_acc(Macc[2 * s][cb], Macc[2 * s + 1][cb]);
-          lds_st<F>(mf, ((cb * NKS + s) * 64 + lane) * 16, Mf[s][cb]);
+        for (int e = 0; e < 4; ++e) Macc[b][e] = p.h0 ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] : 0.f;
+
+      F Mf[NKS];
+      auto publish_state = [&]() {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          Mf[s] = MM::from_acc(Macc[2 * s], Macc[2 * s + 1]);
+          lds_st<F>(sMF, ((cb * NKS + s) * 64 + lane) * 16, Mf[s]);
         }
-    };
-    publish_state();
-    lds_barrier();
+      };
+      publish_state();
+      lds_barrier();
 
-    for (int it = 0; it < NIT; ++it) {
-      const int c = it - 2;
-      if (c >= 0 && c < NC) {
-        const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
-        const float* vec = vec_of(c);
+      for (int it = 0; it < NIT; ++it) {
+        const int c = it - 2;
+        if (c >= 0 && c < NC) {
+          const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
+          const float* vec = vec_of(c);
 
-        // u and T' into registers first, so that the solve waves may
-        // overwrite them with the next chunk's early.
-        f32x4 U[NB][NCB];
+          // u and T' into registers first, so that the solve waves may
+          // overwrite them with the next chunk's early.
+          f32x4 U[NB];
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
+          for (int tb = 0; tb < NB; ++tb) U[tb] = lds_at<f32x4>(sUU + ((tb * NCB + cb) * 64 + lane) * 16);
+          // T' (lower triangular) as row operands: slab s2 of row block tb
+          // is used for 32 s2 <= 16 tb, its upper half only when
+          // 16 tb > 32 s2.
+          F TPf[NB][NTS];
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) U[tb][cb] = lds_at<f32x4>(sUU + ((tb * NCB + cb) * 64 + lane) * 16);
-        // T' (lower triangular) as row operands: slab s2 of row block tb is
-        // used for 32 s2 <= 16 tb, its upper half only when 16 tb > 32 s2.
-        F TPf[NB][NTS];
+          for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-#pragma unroll
-          for (int s = 0; 32 * s <= 16 * tb; ++s) {
-            const bf16x4 lo = lds_read_tr(sTP, tp_base[tb] + 32 * s * CCR);
-            F f{};
-            f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-            if (32 * s + 16 <= 16 * tb) {
-              const bf16x4 hi = lds_read_tr(sTP, tp_base[tb] + (32 * s + 16) * CCR);
-              f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+            for (int s = 0; 32 * s <= 16 * tb; ++s) {
+              const bf16x4 lo = lds_read_tr(sTP, tp_base[tb] + 32 * s * CCR);
+              F f{};
+              f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+              if (32 * s + 16 <= 16 * tb) {
+                const bf16x4 hi = lds_read_tr(sTP, tp_base[tb] + (32 * s + 16) * CCR);
+                f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+              }
+              TPf[tb][s] = f;
             }
-            TPf[tb][s] = f;
-          }
 
-        // Y = K M, K read one row block ahead of its use.
-        F Kf[2][NKS];
-        auto read_k = [&](int tb) {
+          // Y = K M, K read one row block ahead of its use.
+          F Kf[2][NKS];
+          auto read_k = [&](int tb) {
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) Kf[tb & 1][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * tb);
-        };
-        read_k(0);
-        f32x4 Y[NB][NCB];
+            for (int s = 0; s < NKS; ++s) Kf[tb & 1][s] = lds_at<F>(sk + kq_frag[s] + 16 * KQR * tb);
+          };
+          read_k(0);
+          f32x4 Y[NB];
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-          if (tb + 1 < NB) read_k(tb + 1);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
+          for (int tb = 0; tb < NB; ++tb) {
+            if (tb + 1 < NB) read_k(tb + 1);
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[tb & 1][s], Mf[s][cb], y);
-            Y[tb][cb] = y;
+            for (int s = 0; s < NKS; ++s) y = MM::mma(Kf[tb & 1][s], Mf[s], y);
+            Y[tb] = y;
           }
-        }
-        flag_release(&sFLAG[2], c + 1);
-        // U = u + T' Y
-        F Yf[NTS][NCB];
+          flag_release(&sFLAG[2 + cb], c + 1);
+          // U = u + T' Y
+          F Yf[NTS];
 #pragma unroll
-        for (int s = 0; s < NTS; ++s)
+          for (int s = 0; s < NTS; ++s) Yf[s] = MM::from_acc(Y[2 * s], Y[2 * s + 1]);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) Yf[s][cb] = MM::from_acc(Y[2 * s][cb], Y[2 * s + 1][cb]);
+          for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-#pragma unroll
-          for (int s = 0; 32 * s <= 16 * tb; ++s)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) U[tb][cb] = MM::mma(TPf[tb][s], Yf[s][cb], U[tb][cb]);
+            for (int s = 0; 32 * s <= 16 * tb; ++s) U[tb] = MM::mma(TPf[tb][s], Yf[s], U[tb]);
 
-        // Publish U for the output waves; W = diag(w) U for the update.
-        F Wf[NTS][NCB];
+          // Publish U for the output waves; W = diag(w) U for the update.
+          F Wf[NTS];
 #pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 4 * q4);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 16 + 4 * q4);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            lds_st<F>(sUF, ((cb * NTS + s) * 64 + lane) * 16, MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb]));
+          for (int s = 0; s < NTS; ++s) {
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 4 * q4);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + CF::F_W * C + 32 * s + 16 + 4 * q4);
+            lds_st<F>(sUF, ((cb * NTS + s) * 64 + lane) * 16, MM::from_acc(U[2 * s], U[2 * s + 1]));
             f32x4 a, b;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              a[e] = w0[e] * U[2 * s][cb][e];
-              b[e] = w1[e] * U[2 * s + 1][cb][e];
+              a[e] = w0[e] * U[2 * s][e];
+              b[e] = w1[e] * U[2 * s + 1][e];
             }
-            Wf[s][cb] = MM::from_acc(a, b);
+            Wf[s] = MM::from_acc(a, b);
           }
+          flag_release(&sFLAG[cb], c + 1);
+
+          // K^T for the update (transposing reads, tokens in pi order to
+          // match the W fragments); Gam_C M is formed while they arrive.
+          F KT[NKB][NTS];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int s = 0; s < NTS; ++s) {
+              const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
+              const bf16x4 lo = lds_read_tr(p0, 0);
+              const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
+              KT[kb][s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+          const float gC = vec[CF::F_GAM * C + C - 1];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Macc[kb][e] *= gC;
+
+          // M <- Gam_C M + K^T diag(w) U
+#pragma unroll
+          for (int b = 0; b < NKB; ++b) {
+            f32x4 m = Macc[b];
+#pragma unroll
+            for (int s = 0; s < NTS; ++s) m = MM::mma(KT[b][s], Wf[s], m);
+            Macc[b] = m;
+          }
+          // The output waves have read this chunk's state: publish the next.
+          flag_wait_lds(&sFLAG[4], c + 1);
+          flag_wait_lds(&sFLAG[5], c + 1);
+          publish_state();
         }
-        flag_release(&sFLAG[0], c + 1);
-
-        // K^T for the update (transposing reads, tokens in pi order to match
-        // the W fragments); Gam_C M is formed while they arrive.
-        F KT[NKB][NTS];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int s = 0; s < NTS; ++s) {
-            const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
-            const bf16x4 lo = lds_read_tr(p0, 0);
-            const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
-            KT[kb][s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        const float gC = vec[CF::F_GAM * C + C - 1];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Macc[kb][cb][e] *= gC;
-
-        // M <- Gam_C M + K^T diag(w) U
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            f32x4 m = Macc[b][cb];
-#pragma unroll
-            for (int s = 0; s < NTS; ++s) m = MM::mma(KT[b][s], Wf[s][cb], m);
-            Macc[b][cb] = m;
-          }
-        // The output waves have read this chunk's state: publish the next.
-        flag_wait_lds(&sFLAG[3], c + 1);
-        flag_wait_lds(&sFLAG[4], c + 1);
-        publish_state();
+        lds_barrier();
       }
-      lds_barrier();
-    }
 #pragma unroll
-    for (int b = 0; b < NKB; ++b)
+      for (int b = 0; b < NKB; ++b)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col0 + 16 * cb + n16] = Macc[b][cb][e];
+        for (int e = 0; e < 4; ++e) p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] = Macc[b][e];
+    };
+    if (role == CF::R_S0) state_wave(IC<0>{});
+    else state_wave(IC<1>{});
   } else {
     // ========================================================= output waves
     auto out_wave = [&](auto oc) {
@@ -1590,7 +1585,7 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
           for (int s = 0; s < NKS; ++s)
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) Mf[s][cb] = lds_at<F>(sMF + ((cb * NKS + s) * 64 + lane) * 16);
-          flag_release(&sFLAG[3 + OW], c + 1);
+          flag_release(&sFLAG[4 + OW], c + 1);
           // O^T = (M^T Q^T) diag(Gam): lane (token 16 tb + n16, q4) holds
           // columns 16 cb + 4 q4 + e.
           f32x4 Oacc[NOWN][NCB];
@@ -1644,6 +1639,7 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
           }
 
           flag_wait_lds(&sFLAG[0], c + 1);
+          flag_wait_lds(&sFLAG[1], c + 1);
           constexpr int NUS = (16 * KMAX + 15) / 32 + 1;  // U slabs used
           F Uf[NUS][NCB];
 #pragma unroll
@@ -1680,7 +1676,7 @@ __global__ __launch_bounds__(448, 1) void gdn_bf16_kernel(const Params p) {
         if (it + 1 < NIT) step(it + 1, Q1, Q0);
       }
     };
-    if (wave == CF::W_OA) out_wave(IC<0>{});
+    if (role == CF::R_OA) out_wave(IC<0>{});
     else out_wave(IC<1>{});
   }
 }
