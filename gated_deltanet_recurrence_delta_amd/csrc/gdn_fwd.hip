@@ -869,6 +869,11 @@ __device__ static inline int swz_cc(int r) {
   else return (r >> 1) & 3;
 }
 
+// Issue priority (s_setprio) of the critical chains; 0 leaves all waves at
+// the default.
+#ifndef GDN_PRIO
+#define GDN_PRIO 1
+#endif
 #ifndef GDN_ROLEMAP
 #define GDN_ROLEMAP 0x76325410u
 #endif
@@ -1184,7 +1189,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
       issue_v(it + 1);
       issue_k(it + 2);
       if (it + 1 < NC) make_vec(it + 1, gu, bu);
-      if (it < NC) diag_inverse(it);
+      if (it < NC) {
+        if (GDN_PRIO) __builtin_amdgcn_s_setprio(3);
+        diag_inverse(it);
+        if (GDN_PRIO) __builtin_amdgcn_s_setprio(0);
+      }
       step_barrier();
     };
     for (int it = 0; it < NIT; it += 2) {
@@ -1197,6 +1206,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     for (int it = 0; it < NIT; ++it) {
       const int c = it;
       if (c < NC) {
+        if (GDN_PRIO) __builtin_amdgcn_s_setprio(3);
         const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
         const float* vec = vec_of(c);
         char* sat = sAT + (c & 1) * CF::CC_BYTES;
@@ -1222,6 +1232,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
           *reinterpret_cast<f32x4*>(sAD + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
         }
         flag_release(&sFLAG[6], c + 1);
+        if (GDN_PRIO) __builtin_amdgcn_s_setprio(0);
         // Off-diagonal blocks (bf16).
         float bi[NB], eri[NB];
 #pragma unroll
@@ -1413,6 +1424,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     }
 
     auto state_wave = [&](auto hc) {
+      if (GDN_PRIO) __builtin_amdgcn_s_setprio(2);
       constexpr int cb = decltype(hc)::value;  // this wave's column block
       const long col = (long)tile * CF::DVT + 16 * cb + n16;
       f32x4 Macc[NKB];
@@ -1461,6 +1473,19 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
               TPf[tb][s] = f;
             }
 
+          // K^T for the update (transposing reads, tokens in pi order to
+          // match the W fragments), issued early so that they arrive while
+          // Y and U are formed.
+          F KT[NKB][NTS];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int s = 0; s < NTS; ++s) {
+              const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
+              const bf16x4 lo = lds_read_tr(p0, 0);
+              const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
+              KT[kb][s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
           // Y = K M, K read one row block ahead of its use.
           F Kf[2][NKS];
           auto read_k = [&](int tb) {
@@ -1504,18 +1529,6 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
           }
           flag_release(&sFLAG[cb], c + 1);
 
-          // K^T for the update (transposing reads, tokens in pi order to
-          // match the W fragments); Gam_C M is formed while they arrive.
-          F KT[NKB][NTS];
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int s = 0; s < NTS; ++s) {
-              const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
-              const bf16x4 lo = lds_read_tr(p0, 0);
-              const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
-              KT[kb][s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
           const float gC = vec[CF::F_GAM * C + C - 1];
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
