@@ -813,22 +813,27 @@ __global__ __launch_bounds__(64 * (DVT / 16 + 2), 1) void gdn_fwd_kernel(const P
 //
 // so that only Y, one triangular product and the update remain in the
 // chunk-to-chunk recurrence.  One workgroup per (chain, 32-column value
-// tile), six waves, one LDS barrier per step:
+// tile), eight waves (two per SIMD), one LDS barrier per step; chunk c is
+// Gram-processed at step c, solved at step c+1, finished at step c+2:
 //
-//   loader wave (step c): copies k, v of chunk c+1 and q of chunk c into
-//       the LDS rings; g and beta of chunk c+1 -> per-token vectors.
+//   loader wave (step c): copies v of chunk c+1 and k of chunk c+2 into the
+//       LDS rings (two steps ahead of their first readers); g and beta of
+//       chunk c+2; per-token vectors of chunk c+1; once the Gram wave has
+//       published them (LDS flag), the inverses of the 16x16 diagonal
+//       blocks of (I + A) of chunk c (fp32 forward substitution, one lane
+//       per column).
 //   Gram wave (step c): diagonal blocks of A of chunk c (fp32, published
-//       first, LDS flag), then the off-diagonal blocks (bf16, second flag).
-//   solve wave (step c): inverses of the 16x16 diagonal blocks of (I + A)
-//       (fp32 forward substitution, one lane per column), then block
-//       forward substitution of (I + A) [R_T | R_u] = [diag(beta) |
-//       diag(beta) V] on the MFMA; publishes T' = -R_T diag(Gam) and
-//       u = R_u.
-//   state wave (step c+1): Y = K M, U = u + T' Y, publishes U (LDS flag),
-//       the update M <- Gam_C M + K^T diag(w) U, publishes the bf16 state.
-//   two output waves (step c+1), each owning half of the chunk's 16-row
-//       blocks: diag(Gam) Q M and the masked decayed P = (Q K^T) * D of
-//       chunk c, then (once U is published) P U, and the stores.
+//       first), then the off-diagonal blocks (bf16).
+//   T and u solve waves (step c+1): block forward substitution of (I + A)
+//       R = diag(beta) and of (I + A) R = diag(beta) V on the MFMA;
+//       publish T' = -R diag(Gam) and u = R.
+//   two state waves (step c+2), one per 16-column half: Y = K M,
+//       U = u + T' Y, publish U (LDS flag), the update
+//       M <- Gam_C M + K^T diag(w) U, publish the bf16 state.
+//   two output waves (step c+2), each owning half of the chunk's 16-row
+//       blocks: diag(Gam) Q M and the masked decayed P = (Q K^T) * D, then
+//       (once U is published) P U, and the stores; q comes straight from
+//       HBM into registers one step ahead.
 //
 // The decay exp(gamma_i - gamma_j) of an off-diagonal block (rows in block
 // b1, columns in an earlier block) is the product of two factors through
