@@ -874,13 +874,14 @@ __device__ static inline int swz_cc(int r) {
   else return (r >> 1) & 3;
 }
 
-// Issue priority (s_setprio) of the critical chains; 0 leaves all waves at
-// the default.
+// Issue priority (s_setprio) of the critical chains, a bit mask: 1 raises
+// the Gram wave's diagonal phase and the loader's diagonal-block inverses,
+// 2 the state waves, 4 the output waves; 0 leaves all waves at the default.
 #ifndef GDN_PRIO
-#define GDN_PRIO 1
+#define GDN_PRIO 3
 #endif
 #ifndef GDN_ROLEMAP
-#define GDN_ROLEMAP 0x76325410u
+#define GDN_ROLEMAP 0x54673210u
 #endif
 
 template <int DK, int C>
@@ -905,8 +906,9 @@ struct Cfg16 {
   static constexpr int KQ_RPI = 1024 / KQ_ROWB, V_RPI = 1024 / V_ROWB;    // rows per copy
   // Wave roles.  ROLEMAP holds the role of wave w in bits [4w, 4w + 4);
   // waves w and w + 4 share a SIMD, so the map also places the roles on
-  // SIMDs (by default: each state half with one output wave, the T solve
-  // wave with the loader, the u solve wave with the Gram wave).
+  // SIMDs (by default: state half 0 with the Gram wave, state half 1 with
+  // the loader, each output wave with one of the solve waves, whose work
+  // ends early in the step).
   static constexpr int R_S0 = 0, R_S1 = 1, R_OA = 2, R_OB = 3, R_X = 4, R_XU = 5, R_L = 6, R_G = 7, NW = 8;
   static constexpr unsigned ROLEMAP = GDN_ROLEMAP;
   // Output wave o owns row blocks own_tb(o, 0..NOWN-1): {0, 3} and {1, 2}
@@ -938,6 +940,13 @@ __device__ static inline void flag_wait_lds(const int* f, int v) {
     if (__builtin_amdgcn_readfirstlane(x) >= v) break;
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Make v's value exist at this point of the instruction stream: the work
+// that produces it is then done before, not after, a following wait.
+template <typename T>
+__device__ static inline void settle(T& v) {
+  asm volatile("" : "+v"(v));
 }
 
 __device__ static inline void flag_release(int* f, int v) {
@@ -1195,9 +1204,9 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
       issue_k(it + 2);
       if (it + 1 < NC) make_vec(it + 1, gu, bu);
       if (it < NC) {
-        if (GDN_PRIO) __builtin_amdgcn_s_setprio(3);
+        if (GDN_PRIO & 1) __builtin_amdgcn_s_setprio(3);
         diag_inverse(it);
-        if (GDN_PRIO) __builtin_amdgcn_s_setprio(0);
+        if (GDN_PRIO & 1) __builtin_amdgcn_s_setprio(0);
       }
       step_barrier();
     };
@@ -1211,7 +1220,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     for (int it = 0; it < NIT; ++it) {
       const int c = it;
       if (c < NC) {
-        if (GDN_PRIO) __builtin_amdgcn_s_setprio(3);
+        if (GDN_PRIO & 1) __builtin_amdgcn_s_setprio(3);
         const char* sk = sK + (c % CF::NKR) * CF::KQ_BYTES;
         const float* vec = vec_of(c);
         char* sat = sAT + (c & 1) * CF::CC_BYTES;
@@ -1237,7 +1246,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
           *reinterpret_cast<f32x4*>(sAD + b * CF::AD_BLK + n16 * CF::AD_ROW + 4 * q4) = r;
         }
         flag_release(&sFLAG[6], c + 1);
-        if (GDN_PRIO) __builtin_amdgcn_s_setprio(0);
+        if (GDN_PRIO & 1) __builtin_amdgcn_s_setprio(0);
         // Off-diagonal blocks (bf16).
         float bi[NB], eri[NB];
 #pragma unroll
@@ -1429,7 +1438,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     }
 
     auto state_wave = [&](auto hc) {
-      if (GDN_PRIO) __builtin_amdgcn_s_setprio(2);
+      if (GDN_PRIO & 2) __builtin_amdgcn_s_setprio(2);
       constexpr int cb = decltype(hc)::value;  // this wave's column block
       const long col = (long)tile * CF::DVT + 16 * cb + n16;
       f32x4 Macc[NKB];
@@ -1566,6 +1575,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     // ========================================================= output waves
     auto out_wave = [&](auto oc) {
       constexpr int OW = decltype(oc)::value;
+      if (GDN_PRIO & 4) __builtin_amdgcn_s_setprio(2);
       constexpr int NOWN = CF::NOWN;
       constexpr int KMAX = CF::own_tb(OW, NOWN - 1) > CF::own_tb(OW, 0) ? CF::own_tb(OW, NOWN - 1) : CF::own_tb(OW, 0);
       // Output rows: lane (token 16 tb + n16, columns 16 cb + 4 q4 .. +3).
@@ -1656,6 +1666,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
               Pf[i][s] = 2 * s + 1 <= b1 ? MM::from_acc(pb[2 * s], pb[2 * s + 1]) : MM::from_acc1(pb[2 * s]);
           }
 
+          // Finish P and diag(Gam) Q M before spinning on U.
+#pragma unroll
+          for (int i = 0; i < NOWN; ++i) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) settle(Oacc[i][cb]);
+#pragma unroll
+            for (int s = 0; 32 * s <= 16 * CF::own_tb(OW, i); ++s) settle(Pf[i][s]);
+          }
           flag_wait_lds(&sFLAG[0], c + 1);
           flag_wait_lds(&sFLAG[1], c + 1);
           constexpr int NUS = (16 * KMAX + 15) / 32 + 1;  // U slabs used
