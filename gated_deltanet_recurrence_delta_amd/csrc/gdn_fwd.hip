@@ -859,12 +859,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Granule permutation of a q/k row (GR granules of 16 bytes): distinct low
-// three bits over any 8 consecutive rows, so the 16 lanes of a fragment read
-// (16 consecutive rows, one granule each) hit distinct bank groups.
+// Granule permutation of a q/k row (GR granules of 16 bytes).  LDS has 64
+// banks of 4 bytes (a 256-byte period).  A 16-byte read is served 16 lanes
+// at a time: the lanes that agree in lane bit 5 and in the parity of lane
+// bits 2..4.  An 8-byte (plain or transposing) read is served 32 lanes at a
+// time: the lanes that agree in lane bit 5.  For 256-byte rows the
+// permutation below puts each such group of a fragment read (16 rows, one
+// granule each) and of a state wave's transposing read (8 rows, four
+// 8-byte pieces each, alternating halves) on distinct banks.
 template <int GR>
 __device__ static inline int swz_kq(int r) {
-  if constexpr (GR >= 8) return 2 * (r & 3) + ((r >> 2) & 1);
+  if constexpr (GR >= 16) return 8 * (r & 1) + 4 * ((r >> 1) & 1) + 3 * ((r >> 2) & 1);
+  else if constexpr (GR >= 8) return 2 * (r & 3) + ((r >> 2) & 1);
   else return (r >> 1) & 3;  // two 64-byte rows share a 128-byte bank line
 }
 __device__ static inline int swz_v(int r) { return r & 2; }
@@ -1425,17 +1431,21 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     // Two waves, one per 16-column half of the tile; each carries its half
     // of the state for the whole sequence.
     const long sbase = (long)chain * DK * p.dv;
-    // Accumulator block b holds M[key(b, 4q + e)][column n16 of the half];
-    // two stacked blocks form a fragment with natural key positions.
-    auto key_of = [&](int b, int r) { return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3); };
+    // Accumulator block b holds M[key(b, 4q + e)][column n16 of the half]:
+    // of the 32 keys of slab b >> 1, block b takes from each 8-key group g
+    // the half (b ^ g) & 1, so that the transposing reads of K alternate
+    // halves across lanes.  Two stacked blocks form a fragment with natural
+    // key positions once lanes with odd q4 swap the blocks.
+    auto key_of = [&](int b, int r) { return 32 * (b >> 1) + 8 * (r >> 2) + 4 * ((b ^ (r >> 2)) & 1) + (r & 3); };
     // Transposing reads.  K^T: rows 32 s + 16 hi + 4 q4 + (src >> 2), the
-    // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 (b&1) .. +3.
+    // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 ((b^src)&1) .. +3.
     int kt_base[(NKB + 1) / 2];
 #pragma unroll
     for (int bh = 0; bh < (NKB + 1) / 2; ++bh) {
       const int r = 4 * q4 + (src >> 2);
-      kt_base[bh] = r * KQR + 16 * ((4 * bh + (src & 3)) ^ swz_kq<GR>(r));
+      kt_base[bh] = r * KQR + 16 * ((4 * bh + (src & 3)) ^ swz_kq<GR>(r)) + 8 * (src & 1);
     }
+    const int kt_flip = 8 - 16 * (src & 1);  // to the other half (odd blocks)
     // T' as a row operand (transposing read of T'^T): rows
     // 32 s + 16 hi + 4 q4 + (src >> 2), columns 16 tb + 4 (src & 3) .. +3.
     int tp_base[NB];
@@ -1456,10 +1466,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
         for (int e = 0; e < 4; ++e) Macc[b][e] = p.h0 ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] : 0.f;
 
       F Mf[NKS];
+      const bool odd = q4 & 1;
       auto publish_state = [&]() {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          Mf[s] = MM::from_acc(Macc[2 * s], Macc[2 * s + 1]);
+          const u32x4 u = __builtin_bit_cast(u32x4, MM::from_acc(Macc[2 * s], Macc[2 * s + 1]));
+          Mf[s] = __builtin_bit_cast(F, u32x4{odd ? u[2] : u[0], odd ? u[3] : u[1], odd ? u[0] : u[2], odd ? u[1] : u[3]});
           lds_st<F>(sMF, ((cb * NKS + s) * 64 + lane) * 16, Mf[s]);
         }
       };
@@ -1503,7 +1515,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int s = 0; s < NTS; ++s) {
-              const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
+              const char* p0 = sk + kt_base[kb >> 1] + ((kb & 1) ? kt_flip : 0) + 32 * s * KQR;
               const bf16x4 lo = lds_read_tr(p0, 0);
               const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
               KT[kb][s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
