@@ -873,7 +873,13 @@ __device__ static inline int swz_kq(int r) {
   else if constexpr (GR >= 8) return 2 * (r & 3) + ((r >> 2) & 1);
   else return (r >> 1) & 3;  // two 64-byte rows share a 128-byte bank line
 }
-__device__ static inline int swz_v(int r) { return r & 2; }
+__device__ static inline int swz_v(int r) { return (r >> 2) & 1; }
+// Value columns of a 32-column tile: position r (0..15) of 16-column block
+// cb holds tile column 8 (r >> 2) + 4 ((cb ^ (r >> 2)) & 1) + (r & 3).  The
+// two blocks' positions 4g .. 4g+3 together cover the eight columns 8g ..
+// 8g+7, so an output lane writes 16 contiguous bytes, and the transposing
+// reads of v alternate 8-byte halves across lanes (no bank conflicts).
+__device__ static inline int tile_col(int cb, int r) { return 8 * (r >> 2) + 4 * ((cb ^ (r >> 2)) & 1) + (r & 3); }
 template <int C>
 __device__ static inline int swz_cc(int r) {
   if constexpr (C == 64) return r & 7;
@@ -1295,13 +1301,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
       const int r = 4 * q4 + (src >> 2);
       t_base[bh] = r * CCR + 16 * ((4 * bh + (src & 3)) ^ swz_cc<C>(r));
     }
-    // V in accumulator layout: rows 16 tb + 4 q4 + (src >> 2), columns
-    // 16 cb + 4 (src & 3) .. +3.
+    // V in accumulator layout: rows 16 tb + 4 q4 + (src >> 2), block
+    // positions 4 (src & 3) .. +3 of block cb (tile columns tile_col).
     int v_base[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int r = 4 * q4 + (src >> 2);
-      v_base[cb] = r * CF::V_ROWB + 16 * ((2 * cb + ((src & 3) >> 1)) ^ swz_v(r)) + 8 * (src & 1);
+      const int r = 4 * q4 + (src >> 2), g = src & 3;
+      v_base[cb] = r * CF::V_ROWB + 16 * (g ^ swz_v(r)) + 8 * ((cb ^ g) & 1);
     }
     // T'^T store: row j = 16 col + n16, columns 16 b + 4 q4 .. +3.
     auto tp_off = [&](int b, int col) {
@@ -1458,7 +1464,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     auto state_wave = [&](auto hc) {
       if (GDN_PRIO_S) __builtin_amdgcn_s_setprio(GDN_PRIO_S);
       constexpr int cb = decltype(hc)::value;  // this wave's column block
-      const long col = (long)tile * CF::DVT + 16 * cb + n16;
+      const long col = (long)tile * CF::DVT + tile_col(cb, n16);
       f32x4 Macc[NKB];
 #pragma unroll
       for (int b = 0; b < NKB; ++b)
@@ -1598,10 +1604,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
       if (GDN_PRIO_O) __builtin_amdgcn_s_setprio(GDN_PRIO_O);
       constexpr int NOWN = CF::NOWN;
       constexpr int KMAX = CF::own_tb(OW, NOWN - 1) > CF::own_tb(OW, 0) ? CF::own_tb(OW, NOWN - 1) : CF::own_tb(OW, 0);
-      // Output rows: lane (token 16 tb + n16, columns 16 cb + 4 q4 .. +3).
+      // Output rows: lane (token 16 tb + n16, tile columns 8 q4 .. +7).
       int o_off[NOWN];
 #pragma unroll
-      for (int i = 0; i < NOWN; ++i) o_off[i] = (int)((16 * CF::own_tb(OW, i) + n16) * v_stride) + 8 * q4;
+      for (int i = 0; i < NOWN; ++i) o_off[i] = (int)((16 * CF::own_tb(OW, i) + n16) * v_stride) + 16 * q4;
+      const bool odd = q4 & 1;
       // q fragments straight from HBM into registers, one step ahead of
       // use: lane (token 16 tb + n16, keys 32 s + 8 q4 .. +7).
       int q_off[NOWN];
@@ -1708,14 +1715,17 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
           for (int i = 0; i < NOWN; ++i) {
             const int tb = CF::own_tb(OW, i);
+            u32x2 ob[NCB];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
               f32x4 o = Oacc[i][cb];
 #pragma unroll
               for (int s = 0; 32 * s <= 16 * tb; ++s) o = MM::mma(Uf[s][cb], Pf[i][s], o);
-              const bf16x4 ob = cvt4(o);
-              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro, o_off[i] + 32 * cb, 0, 0);
+              ob[cb] = __builtin_bit_cast(u32x2, cvt4(o));
             }
+            // Block 0 holds columns 8 q4 .. +3 for even q4, 8 q4 + 4 .. +7 for odd.
+            const u32x2 lo = odd ? ob[1] : ob[0], hi = odd ? ob[0] : ob[1];
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, ro, o_off[i], 0, 0);
           }
         }
         lds_barrier();
