@@ -68,6 +68,16 @@ struct Mma<__bf16> {
   __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  // Half-depth product: the same lane pairing as mma() restricted to the
+  // first four positions of each lane group (for operands whose other half
+  // is zero).
+  __device__ static inline f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0,
+                                                     0);
+  }
+  __device__ static inline bf16x4 lo(frag f) { return bf16x4{f[0], f[1], f[2], f[3]}; }
+  __device__ static inline bf16x4 hi(frag f) { return bf16x4{f[4], f[5], f[6], f[7]}; }
   __device__ static inline frag zero() { return frag{}; }
   // Fragment from two stacked accumulators (pi order).
   __device__ static inline frag from_acc(f32x4 lo, f32x4 hi) {
@@ -1314,7 +1324,6 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
       const int j = 16 * col + n16;
       return j * CCR + 16 * ((2 * b + (q4 >> 1)) ^ swz_cc<C>(j)) + 8 * (q4 & 1);
     };
-    const bf16x4 z4 = {};
     auto cat = [](bf16x4 lo, bf16x4 hi) { return F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; };
 
     // Row block b of (I + A) R = X: R_b = Tbb (X_b - sum_{j<b} A_bj R_j).
@@ -1330,9 +1339,9 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
         if (c >= 0 && c < NC) {
           const float* vec = vec_of(c);
           char* sat = sAT + (c & 1) * CF::CC_BYTES;
-          F Tf[NB];
+          bf16x4 Tf[NB];
 #pragma unroll
-          for (int b = 0; b < NB; ++b) Tf[b] = cat(lds_read_tr(sat, t_base[b >> 1] + 16 * CCR * b + 8 * (b & 1)), z4);
+          for (int b = 0; b < NB; ++b) Tf[b] = lds_read_tr(sat, t_base[b >> 1] + 16 * CCR * b + 8 * (b & 1));
           // Row blocks of A left of the diagonal as pi-order fragments;
           // where the slab's upper half is the diagonal block the matching
           // operand half is zero.
@@ -1360,16 +1369,16 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
                   for (int s = 0; 32 * s < 16 * b; ++s) {
                     if (2 * s + 1 < col) continue;  // both blocks of the slab are zero
-                    const bf16x4 lo = 2 * s >= col ? RH[2 * s][col] : z4;
-                    const bf16x4 hi = 2 * s + 1 < b ? RH[2 * s + 1][col] : z4;
-                    r = MM::mma(Af[b][s], cat(lo, hi), r);
+                    if (2 * s + 1 >= b) r = MM::mma16(MM::lo(Af[b][s]), RH[2 * s][col], r);
+                    else if (2 * s < col) r = MM::mma16(MM::hi(Af[b][s]), RH[2 * s + 1][col], r);
+                    else r = MM::mma(Af[b][s], cat(RH[2 * s][col], RH[2 * s + 1][col]), r);
                   }
                   f32x4 x;
 #pragma unroll
                   for (int e = 0; e < 4; ++e) x[e] = -r[e];
                   xh = cvt4(x);
                 }
-                RT[b][col] = MM::mma(Tf[b], cat(xh, z4), zero4);
+                RT[b][col] = MM::mma16(Tf[b], xh, zero4);
                 RH[b][col] = cvt4(RT[b][col]);
               }
             }
@@ -1410,11 +1419,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
                   f32x4 r = zero4;
 #pragma unroll
                   for (int s = 0; 32 * s < 16 * b; ++s)
-                    r = MM::mma(Af[b][s], cat(RH[2 * s][cb], 2 * s + 1 < b ? RH[2 * s + 1][cb] : z4), r);
+                    r = 2 * s + 1 < b ? MM::mma(Af[b][s], cat(RH[2 * s][cb], RH[2 * s + 1][cb]), r)
+                                      : MM::mma16(MM::lo(Af[b][s]), RH[2 * s][cb], r);
 #pragma unroll
                   for (int e = 0; e < 4; ++e) x[e] -= r[e];
                 }
-                RU[b][cb] = MM::mma(Tf[b], cat(cvt4(x), z4), zero4);
+                RU[b][cb] = MM::mma16(Tf[b], cvt4(x), zero4);
                 RH[b][cb] = cvt4(RU[b][cb]);
               }
             }
@@ -1550,7 +1560,9 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
           for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-            for (int s = 0; 32 * s <= 16 * tb; ++s) U[tb] = MM::mma(TPf[tb][s], Yf[s], U[tb]);
+            for (int s = 0; 32 * s <= 16 * tb; ++s)
+              U[tb] = 32 * s + 16 <= 16 * tb ? MM::mma(TPf[tb][s], Yf[s], U[tb])
+                                             : MM::mma16(MM::lo(TPf[tb][s]), MM::lo(Yf[s]), U[tb]);
 
           // Publish U for the output waves; W = diag(w) U for the update.
           F Wf[NTS];
@@ -1720,7 +1732,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
             for (int cb = 0; cb < NCB; ++cb) {
               f32x4 o = Oacc[i][cb];
 #pragma unroll
-              for (int s = 0; 32 * s <= 16 * tb; ++s) o = MM::mma(Uf[s][cb], Pf[i][s], o);
+              for (int s = 0; 32 * s <= 16 * tb; ++s)
+                o = 2 * s + 1 <= tb ? MM::mma(Uf[s][cb], Pf[i][s], o) : MM::mma16(MM::lo(Uf[s][cb]), MM::lo(Pf[i][s]), o);
               ob[cb] = __builtin_bit_cast(u32x2, cvt4(o));
             }
             // Block 0 holds columns 8 q4 .. +3 for even q4, 8 q4 + 4 .. +7 for odd.
