@@ -968,7 +968,6 @@ __device__ static inline void flag_wait_lds(const int* f, int v) {
     int x;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
     if (__builtin_amdgcn_readfirstlane(x) >= v) break;
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
