@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdn_fwd", "fwd", "GdnError", "lib_path", "load", "version"]
+__all__ = ["gdn_fwd", "gdn_fwd_recurrent", "fwd", "fwd_recurrent", "GdnError", "lib_path", "load",
+           "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -45,6 +46,8 @@ def load():
         I = ctypes.c_int
         lib.gdn_fwd.restype = I
         lib.gdn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I]
+        lib.gdn_fwd_recurrent.restype = I
+        lib.gdn_fwd_recurrent.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I]
         lib.gdn_strerror.restype = ctypes.c_char_p
         lib.gdn_strerror.argtypes = [I]
         lib.gdn_version.restype = I
@@ -69,9 +72,17 @@ def gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
                           stream, int(dtype), int(chunk))
 
 
+def gdn_fwd_recurrent(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
+                      stream, dtype) -> int:
+    """Raw C call of the token-by-token form (0 = NULL).  Returns the status."""
+    return load().gdn_fwd_recurrent(q, k, v, g, beta, h0, cu_seqlens, out, hT,
+                                    int(B), int(T), int(H), int(dk), int(dv),
+                                    stream, int(dtype))
+
+
 def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
         out=None, hT=None, stream=None):
-    """Gated-delta-rule forward on torch device tensors.
+    """Gated-delta-rule forward on torch device tensors (chunkwise form).
 
     q, k: (B,T,H,dk); v: (B,T,H,dv); g, beta: (B,T,H) float32 (packed:
     drop B and pass int32 ``cu_seqlens`` of length B+1).  q/k/v share one
@@ -79,6 +90,25 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
     Returns (out, hT); out has q's dtype, hT is float32.  Runs on the
     current stream (or ``stream``), asynchronously.
     """
+    a, out, hT = _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream)
+    rc = gdn_fwd(*a, chunk)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT
+
+
+def fwd_recurrent(q, k, v, g, beta, h0=None, cu_seqlens=None, out=None, hT=None,
+                  stream=None):
+    """Token-by-token form of ``fwd`` (same arguments but no chunk length)."""
+    a, out, hT = _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream)
+    rc = gdn_fwd_recurrent(*a)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT
+
+
+def _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream):
+    """Check the tensors, allocate missing outputs; the C arguments up to dtype."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -127,8 +157,6 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     ptr = lambda t: 0 if t is None else t.data_ptr()
-    rc = gdn_fwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(h0), ptr(cu_seqlens),
-                 ptr(out), ptr(hT), B, T, H, dk, dv, stream.cuda_stream, dtype, chunk)
-    if rc != 0:
-        raise GdnError(rc, strerror(rc))
-    return out, hT
+    args = (ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(h0), ptr(cu_seqlens),
+            ptr(out), ptr(hT), B, T, H, dk, dv, stream.cuda_stream, dtype)
+    return args, out, hT

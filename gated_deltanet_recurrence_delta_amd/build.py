@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "gdn_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("gdn_fwd.hip", "gdn_recurrent.hip")]
 LIB = os.path.join(HERE, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -29,9 +29,9 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/gdn_fwd.hip into libgdn.so (always recompiles)."""
+    """Compile the csrc/*.hip sources into libgdn.so (always recompiles)."""
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

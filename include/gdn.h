@@ -91,6 +91,31 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
             void* out, float* hT, int B, int T, int H, int dk, int dv,
             void* stream, int dtype, int chunk);
 
+/*
+ * gdn_fwd_recurrent -- the same operation in its token-by-token form, for
+ * decoding and other short sequences: per token one rank-1 state update,
+ *
+ *   alpha = exp(g_t),  p = S_{t-1} k_t,
+ *   S_t = alpha S_{t-1} + beta_t (v_t - alpha p) k_t^T,  o_t = S_t q_t,
+ *
+ * with the state kept on chip for the whole sequence ("Model Architecture
+ * Walkthrough", sections 6.2-6.4, the read-after-write order of section
+ * 5.2.1).  Arguments, layouts (dense and packed), state semantics, aliasing,
+ * ownership, error behaviour and determinism are those of gdn_fwd; there is
+ * no chunk argument.  Arithmetic is fp32 throughout (bf16 storage is widened
+ * on load and the output rounded to nearest even), so for bf16 storage the
+ * result differs from gdn_fwd's by the latter's bf16 operand rounding.  The
+ * work per token is sequential, so gdn_fwd is the faster choice once a
+ * sequence spans more than a few dozen tokens; this form's traffic is one
+ * read of h0 and one write of hT per chain plus a single pass over the
+ * tokens.
+ */
+int gdn_fwd_recurrent(const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* h0,
+                      const int32_t* cu_seqlens, void* out, float* hT,
+                      int B, int T, int H, int dk, int dv, void* stream,
+                      int dtype);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* gdn_strerror(int status);
 

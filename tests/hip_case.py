@@ -47,6 +47,18 @@ def run_hip(inp: synth.Inputs, chunk=None, d=None, **kw):
     return out, hT
 
 
+def run_hip_recurrent(inp: synth.Inputs, d=None, **kw):
+    """(out, hT) of the token-by-token entry point as torch device tensors."""
+    import torch
+    import gated_deltanet_recurrence_delta_amd as gdn
+
+    d = d or device_inputs(inp)
+    out, hT = gdn.fwd_recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                d["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return out, hT
+
+
 def run_oracle(inp: synth.Inputs, chains=None):
     a = [inp.as_f64(n) for n in ("q", "k", "v", "g", "beta", "h0")]
     return oracle.fwd_seq(*a, cu_seqlens=inp.cu_seqlens, chains=chains)

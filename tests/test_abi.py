@@ -23,7 +23,7 @@ def _declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["gdn_fwd", "gdn_strerror", "gdn_version"]
+    assert _declared_functions() == ["gdn_fwd", "gdn_fwd_recurrent", "gdn_strerror", "gdn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -85,3 +85,34 @@ def test_python_wrapper_rejects_cpu_tensors():
     g = torch.zeros(1, 4, 1)
     with pytest.raises(ValueError):
         gdn.fwd(q, q, q, g, g)
+
+
+# -------------------------------------------------- token-by-token entry --
+
+def _call_rec(**kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, out=P, hT=P,
+             B=1, T=8, H=1, dk=32, dv=32, stream=None, dtype=1)
+    a.update(kw)
+    return gdn.gdn_fwd_recurrent(**a)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "out", "hT"])
+def test_recurrent_null_required_pointer(name):
+    assert _call_rec(**{name: 0}) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=0), dict(dk=0), dict(dv=-4),
+                                dict(dtype=2), dict(dtype=-1)])
+def test_recurrent_invalid_sizes(kw):
+    assert _call_rec(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(dk=16), dict(dv=256), dict(dk=96), dict(dv=48)])
+def test_recurrent_unsupported(kw):
+    assert _call_rec(**kw) == UNSUPPORTED
+
+
+def test_recurrent_no_chains_is_a_no_op():
+    assert _call_rec(B=0) == OK
+    assert _call_rec(B=0, T=0, q=0, k=0, v=0, g=0, beta=0, out=0, hT=0) == OK
+    assert _call_rec(hT=0, T=0) == INVALID
