@@ -11,6 +11,10 @@ Prints ONE JSON line: tokens/s over the timed steps, the roofline of the
 kernel (algorithmic HBM bytes per launch / mean launch time measured with
 HIP events on the launch stream, against the 8 TB/s HBM3E peak), and the
 FP64 oracle timed on the host cores on the same workload.
+
+``--workload decode`` (one token per sequence, B=128 H=16 d=128, nonzero
+state) times the token-by-token entry point gdn_fwd_recurrent instead;
+``--form`` picks the entry point for any workload.
 """
 from __future__ import annotations
 
@@ -107,6 +111,9 @@ def main():
     # period run at a lower GPU clock
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="wide_head", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--form", choices=("chunked", "recurrent"), default=None,
+                    help="entry point (default: recurrent for the decode workload, "
+                         "chunked otherwise)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-parity", action="store_true", help="skip the sampled parity check")
@@ -129,6 +136,7 @@ def main():
     from hip_case import device_inputs
 
     wl = synth.WORKLOADS[args.workload]
+    form = args.form or ("recurrent" if args.workload == "decode" else "chunked")
     inp = synth.generate(wl)
     sets = []
     for _ in range(max(1, args.sets)):
@@ -143,21 +151,30 @@ def main():
     # Validate once through the checked wrapper, then time the raw C entry
     # point with pre-extracted pointers so host overhead stays off the clock.
     for d in sets:
-        gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
-                chunk=wl.chunk, out=d["out"], hT=d["hT"], stream=stream)
+        if form == "recurrent":
+            gdn.fwd_recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
+                              out=d["out"], hT=d["hT"], stream=stream)
+        else:
+            gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
+                    chunk=wl.chunk, out=d["out"], hT=d["hT"], stream=stream)
     ptr = lambda t: 0 if t is None else t.data_ptr()
     dtype_code = gdn.GDN_BF16 if wl.dtype == "bf16" else gdn.GDN_F32
     B = len(inp.cu_seqlens) - 1 if inp.cu_seqlens is not None else wl.B
     T = int(inp.cu_seqlens[-1]) if inp.cu_seqlens is not None else wl.T
     calls = [tuple(ptr(d[n]) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens", "out", "hT"))
              for d in sets]
-    raw = gdn.load().gdn_fwd
     sh = stream.cuda_stream
+    if form == "recurrent":
+        raw = gdn.load().gdn_fwd_recurrent
+        tail = (B, T, wl.H, wl.dk, wl.dv, sh, dtype_code)
+    else:
+        raw = gdn.load().gdn_fwd
+        tail = (B, T, wl.H, wl.dk, wl.dv, sh, dtype_code, wl.chunk)
 
     def step(i):
-        rc = raw(*calls[i % len(calls)], B, T, wl.H, wl.dk, wl.dv, sh, dtype_code, wl.chunk)
+        rc = raw(*calls[i % len(calls)], *tail)
         if rc != 0:
-            raise SystemExit(f"gdn_fwd failed with status {rc}")
+            raise SystemExit(f"{form} entry point failed with status {rc}")
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
@@ -196,7 +213,7 @@ def main():
     alg = algorithmic_bytes(wl, inp.h0 is not None)
     mean_launch_s = float(launch_ms.mean()) / 1e3
     achieved = alg / mean_launch_s / 1e9
-    traffic = measured_traffic() if args.workload == "wide_head" else None
+    traffic = measured_traffic() if (args.workload == "wide_head" and form == "chunked") else None
 
     rec = {
         "metric": METRIC,
@@ -213,7 +230,10 @@ def main():
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
                 "beta=sigmoid(N(0,1)), g=-softplus(N(%g,1)))" % wl.g_mean,
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} dk={wl.dk} dv={wl.dv} "
-                               f"{wl.dtype} chunk={wl.chunk}" + (" varlen" if wl.varlen else ""),
+                               f"{wl.dtype} " + (f"chunk={wl.chunk}" if form == "chunked"
+                                                 else "token-by-token")
+                               + (" varlen" if wl.varlen else ""),
+                   "entry_point": "gdn_fwd" if form == "chunked" else "gdn_fwd_recurrent",
                    "tokens_per_step": tokens, "rotated_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -74,6 +74,10 @@ WORKLOADS = {
                       dtype=BF16, chunk=64),
     "long_context": Workload("long_context", 4, B=1, T=32768, H=16, dk=128,
                              dv=128, dtype=BF16, chunk=64, g_mean=-2.0),
+    # One decoding step at batch scale (the token-by-token entry point's
+    # workload): the traffic is dominated by the state read and write.
+    "decode": Workload("decode", 5, B=128, T=1, H=16, dk=128, dv=128, dtype=BF16,
+                       chunk=64, h0_std=0.02),
 }
 
 
