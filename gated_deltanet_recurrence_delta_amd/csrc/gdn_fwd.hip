@@ -292,7 +292,11 @@ struct Params {
   char* out;
   float* hT;
   int T, H, dv, ntile, nwg;
+  int lpt;  // packed batch: longest sequences dispatched first (chunkwise bf16 kernel)
 };
+
+// Largest packed batch whose sequences the bf16 kernel orders by length.
+constexpr int GDN_LPT_MAX = 512;
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Give
 // each XCD a contiguous range of work items so that the value tiles of one
@@ -1042,9 +1046,39 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
   const int q4 = lane >> 4, n16 = lane & 15;
   const int src = lane & 15;  // source lane of a transposing read
 
-  const int item = xcd_remap(blockIdx.x, p.nwg);
-  const int chain = __builtin_amdgcn_readfirstlane(item / p.ntile);
-  const int tile = __builtin_amdgcn_readfirstlane(item % p.ntile);
+  // Packed batch: workgroups start in dispatch order, so the longest
+  // sequences are handed out first (longest-processing-time-first); chains
+  // are dealt round-robin over the 8 XCDs, a chain's value tiles together
+  // on one XCD.  Otherwise each XCD takes a contiguous range of items.
+  __shared__ int sLEN[GDN_LPT_MAX];
+  __shared__ int sPICK;
+  int chain_v, tile_v;
+  if (p.lpt) {
+    const int nseq = p.nwg / (p.ntile * p.H);
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int k = (slot / p.ntile) * 8 + xcd;  // k-th chain in length order
+    tile_v = slot % p.ntile;
+    const int t = threadIdx.x;
+    if (t < nseq) sLEN[t] = p.cu[t + 1] - p.cu[t];
+    __syncthreads();
+    if (t < nseq) {
+      const int lt = sLEN[t];
+      int rank = 0;  // sequences ahead of t: longer, or as long with a lower index
+      for (int m = 0; m < nseq; ++m) {
+        const int lm = sLEN[m];
+        rank += (lm > lt || (lm == lt && m < t)) ? 1 : 0;
+      }
+      if (rank == k / p.H) sPICK = t;
+    }
+    __syncthreads();
+    chain_v = sPICK * p.H + k % p.H;
+  } else {
+    const int item = xcd_remap(blockIdx.x, p.nwg);
+    chain_v = item / p.ntile;
+    tile_v = item % p.ntile;
+  }
+  const int chain = __builtin_amdgcn_readfirstlane(chain_v);
+  const int tile = __builtin_amdgcn_readfirstlane(tile_v);
   const int H = p.H;
   const int bseq = chain / H, hh = chain % H;
   long rowbase;
@@ -1243,6 +1277,9 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
       step(it, g1, b1, g0, b0);
       if (it + 1 < NIT) step(it + 1, g0, b0, g1, b1);
     }
+    // The last steps' copies (of chunks past the end) still write LDS: let
+    // them land before this wave ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else if (role == CF::R_G) {
     // ============================================================ Gram wave
     lds_barrier();
@@ -1836,6 +1873,7 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   p.dv = dv;
   p.ntile = ntile;
   p.nwg = nwg;
+  p.lpt = (cu_seqlens && B <= GDN_LPT_MAX && nwg % (8 * ntile) == 0) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == GDN_BF16 ? by_dk<__bf16>(p, nwg, s, dk, chunk) : by_dk<float>(p, nwg, s, dk, chunk);
 }

@@ -133,6 +133,35 @@ def test_packed_equals_per_sequence_bitwise():
         assert torch.equal(_bits(hT[n]), _bits(h1[0])), f"sequence {n} hT"
 
 
+def test_length_ordered_dispatch_bitwise():
+    """A packed batch large enough for the kernel to hand out the longest
+    sequences first (equal lengths and empty sequences included): every
+    sequence is still bitwise its own single-sequence run, and within
+    tolerance of the oracle."""
+    lens = [70, 0, 130, 70, 1, 200, 0, 64]
+    wl = synth.custom(name="lpt", seed=39, H=4, dk=128, dv=128, dtype="bf16", chunk=64,
+                      seq_lens=lens)
+    inp = synth.generate(wl)
+    d = device_inputs(inp)
+    h0 = torch.randn(len(lens), 4, 128, 128, device="cuda") * 0.1
+    d["h0"] = h0
+    out, hT = run_hip(inp, d=d)
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        one = dict(q=d["q"][s:e][None].contiguous(), k=d["k"][s:e][None].contiguous(),
+                   v=d["v"][s:e][None].contiguous(), g=d["g"][s:e][None].contiguous(),
+                   beta=d["beta"][s:e][None].contiguous(), h0=h0[n:n + 1].contiguous(),
+                   cu_seqlens=None)
+        o1, h1 = run_hip(inp, d=one)
+        assert torch.equal(_bits(out[s:e]), _bits(o1[0])), f"sequence {n} out"
+        assert torch.equal(_bits(hT[n]), _bits(h1[0])), f"sequence {n} hT"
+    import dataclasses
+
+    eo, eh = compare(dataclasses.replace(inp, h0=h0.cpu().numpy()), out, hT)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
 def test_causality_bitwise():
     wl = synth.custom(name="causal", seed=32, B=1, T=256, H=2, dk=128, dv=128, dtype="bf16",
                       chunk=64, h0_std=0.2)
