@@ -75,6 +75,31 @@ def measured_traffic():
     return d.get("bytes_per_launch")
 
 
+def copy_reference(nbytes: int, stream) -> float:
+    """Achievable-bandwidth reference: GB/s of a plain device-to-device copy
+    moving ``nbytes`` (half read, half written) per call, over four rotated
+    buffer pairs so that the last-level cache cannot serve it."""
+    import torch
+
+    n = max(1, nbytes // 8)  # float32 elements per buffer
+    src = [torch.empty(n, dtype=torch.float32, device="cuda").uniform_() for _ in range(4)]
+    dst = [torch.empty_like(src[0]) for _ in range(4)]
+    with torch.cuda.stream(stream):
+        for i in range(20):
+            dst[i % 4].copy_(src[i % 4])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(40)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            dst[i % 4].copy_(src[i % 4])
+            b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    med_s = t[len(t) // 2] / 1e3
+    del src, dst
+    return 2 * n * 4 / med_s / 1e9
+
+
 def cpu_baseline(inp: synth.Inputs):
     """The FP64 oracle on the host cores over the whole workload."""
     import oracle
@@ -185,6 +210,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    copy_gbs = copy_reference(algorithmic_bytes(wl, inp.h0 is not None), stream)
+
     # The sampled parity check (CPU oracle) runs before the warm-up, so that
     # the warm-up steps lead straight into the timed ones and the GPU is
     # not left idle (and its clock low) between them.
@@ -237,6 +264,7 @@ def main():
                    "tokens_per_step": tokens, "rotated_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
                      "algorithmic_bytes": alg, "mean_launch_us": mean_launch_s * 1e6,
                      "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
                      "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
