@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdn_fwd", "gdn_fwd_recurrent", "fwd", "fwd_recurrent", "GdnError", "lib_path", "load",
+__all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "fwd",
+           "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent", "GdnError", "lib_path", "load",
            "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,10 @@ def load():
         lib.gdn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I]
         lib.gdn_fwd_recurrent.restype = I
         lib.gdn_fwd_recurrent.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I]
+        lib.gdn_diag_fwd.restype = I
+        lib.gdn_diag_fwd.argtypes = [P] * 11 + [I] * 5 + [P, I, I]
+        lib.gdn_diag_fwd_recurrent.restype = I
+        lib.gdn_diag_fwd_recurrent.argtypes = [P] * 11 + [I] * 5 + [P, I]
         lib.gdn_strerror.restype = ctypes.c_char_p
         lib.gdn_strerror.argtypes = [I]
         lib.gdn_version.restype = I
@@ -159,4 +164,108 @@ def _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream):
     ptr = lambda t: 0 if t is None else t.data_ptr()
     args = (ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(h0), ptr(cu_seqlens),
             ptr(out), ptr(hT), B, T, H, dk, dv, stream.cuda_stream, dtype)
+    return args, out, hT
+
+
+# ------------------------------------------- diagonal-decay additive form ---
+
+def gdn_diag_fwd(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, B, T, H, S, D,
+                 stream, dtype, chunk) -> int:
+    """Raw C call of the diagonal-decay form (0 = NULL).  Returns the status."""
+    return load().gdn_diag_fwd(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT,
+                               int(B), int(T), int(H), int(S), int(D), stream, int(dtype),
+                               int(chunk))
+
+
+def gdn_diag_fwd_recurrent(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, B, T, H,
+                           S, D, stream, dtype) -> int:
+    """Raw C call of the diagonal-decay form, token by token.  Returns the status."""
+    return load().gdn_diag_fwd_recurrent(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out,
+                                         hT, int(B), int(T), int(H), int(S), int(D), stream,
+                                         int(dtype))
+
+
+def diag_fwd(v, b, c, g, A_log, D=None, gate=None, h0=None, cu_seqlens=None, chunk: int = 0,
+             out=None, hT=None, stream=None):
+    """HyMo's diagonal-decay recurrence with its epilogue, chunkwise form.
+
+    v: (B,T,H,D); b, c: (B,T,H,S); g, gate: (B,T,H) float32; A_log: (H,S)
+    float32; D: (H,) float32 or None; h0: (B,H,S,D) float32 or None (packed:
+    drop B, pass int32 cu_seqlens).  v/b/c share one dtype.  Returns
+    (out, hT); out has v's dtype, hT is float32.
+    """
+    a, out, hT = _marshal_diag(v, b, c, g, A_log, D, gate, h0, cu_seqlens, out, hT, stream)
+    rc = gdn_diag_fwd(*a, chunk)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT
+
+
+def diag_fwd_recurrent(v, b, c, g, A_log, D=None, gate=None, h0=None, cu_seqlens=None,
+                       out=None, hT=None, stream=None):
+    """Token-by-token form of ``diag_fwd`` (same arguments but no chunk)."""
+    a, out, hT = _marshal_diag(v, b, c, g, A_log, D, gate, h0, cu_seqlens, out, hT, stream)
+    rc = gdn_diag_fwd_recurrent(*a)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT
+
+
+def _marshal_diag(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, stream):
+    import torch
+
+    if v.dtype == torch.bfloat16:
+        dtype = GDN_BF16
+    elif v.dtype == torch.float32:
+        dtype = GDN_F32
+    else:
+        raise TypeError(f"v/b/c dtype must be float32 or bfloat16, got {v.dtype}")
+    for name, t in (("b", b), ("c", c)):
+        if t.dtype != v.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != v dtype {v.dtype}")
+    for name, t in (("g", g), ("A_log", A_log), ("D", Dskip), ("gate", gate), ("h0", h0)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    tensors = [v, b, c, g, A_log] + [x for x in (Dskip, gate, h0, cu_seqlens, out, hT)
+                                     if x is not None]
+    dev = v.device
+    for t in tensors:
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        if v.dim() != 3:
+            raise ValueError("packed v must be (T, H, D)")
+        T, H, D = v.shape
+        B = cu_seqlens.numel() - 1
+        if B < 0:
+            raise ValueError("cu_seqlens must have at least one entry")
+    else:
+        if v.dim() != 4:
+            raise ValueError("v must be (B, T, H, D)")
+        B, T, H, D = v.shape
+    S = b.shape[-1]
+    lead = tuple(v.shape[:-1])
+    if tuple(b.shape) != lead + (S,) or tuple(c.shape) != lead + (S,):
+        raise ValueError("b and c must be v's shape with S as the last dimension")
+    if tuple(g.shape) != lead or (gate is not None and tuple(gate.shape) != lead):
+        raise ValueError("g/gate must have v's shape without the last dimension")
+    if tuple(A_log.shape) != (H, S):
+        raise ValueError("A_log must be (H, S)")
+    if Dskip is not None and tuple(Dskip.shape) != (H,):
+        raise ValueError("D must be (H,)")
+    if h0 is not None and tuple(h0.shape) != (B, H, S, D):
+        raise ValueError("h0 must be (B, H, S, D)")
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if hT is None:
+        hT = torch.empty((B, H, S, D), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    args = (ptr(v), ptr(b), ptr(c), ptr(g), ptr(A_log), ptr(Dskip), ptr(gate), ptr(h0),
+            ptr(cu_seqlens), ptr(out), ptr(hT), B, T, H, S, D, stream.cuda_stream, dtype)
     return args, out, hT

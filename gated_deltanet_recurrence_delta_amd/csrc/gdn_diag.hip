@@ -1,0 +1,682 @@
+// The diagonal-decay additive recurrence that HyMo writes for its GDN
+// layer, for gfx950.
+//
+// Per head, with the state H of shape (S, D) (key rows x value columns),
+// A = -exp(A_log) (HyMo "Model Architecture Walkthrough", section 5.2.1;
+// A_log of shape (H, S) as in "Optimization Quartet", section 3.2):
+//
+//   H_t = exp(g_t A) (.) H_{t-1} + b_t (x) v_t     each key row decays alone
+//   o_t = c_t^T H_t                                 read after the write
+//
+// followed by the block's epilogue o_t <- (o_t + D_h v_t) * gate_t
+// (Walkthrough, section 5.5 step 6 and section 5.6), each factor optional.
+//
+// Every value column of the state evolves on its own: column d only ever
+// meets v_t[d].  That is what both forms below exploit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DShape {
+  int T, H, S, D, width, nslab, nitems;
+};
+
+// ---------------------------------------------------------------------------
+// Token-by-token form (decoding and short sequences).
+//
+// One wave per (chain, slab of up to 64 value columns); lane j holds column
+// j of the state, all S key rows, in registers, so the read c_t^T H_t is a
+// sum inside the lane.  The token's b and c rows and its g, gate, the same
+// for every lane, are read through the scalar unit; v and out are one
+// element per lane.  The per-row decay rates A_s log2(e) are formed once per
+// wave when they fit in registers next to the state (S <= 64).
+// ---------------------------------------------------------------------------
+constexpr int RWAVES = 4;
+
+template <typename TI>
+__device__ static inline float row_el(const TI* __restrict__ base, long row0, int i) {
+  if constexpr (sizeof(TI) == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(base + row0)[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return base[row0 + i];
+  }
+}
+
+// log2 of the decay factor per unit of g for key row s: A_s log2(e), A_s = -exp(A_log).
+__device__ static inline float decay_rate2(const float* __restrict__ alog, int i) {
+  return -__builtin_amdgcn_exp2f(alog[i] * kLog2e) * kLog2e;
+}
+
+template <typename TI, int S>
+__global__ __launch_bounds__(64 * RWAVES) void diag_recurrent_kernel(
+    const TI* __restrict__ vp, const TI* __restrict__ bp, const TI* __restrict__ cp, const float* __restrict__ gp,
+    const float* __restrict__ alog, const float* __restrict__ dskip, const float* __restrict__ gatep,
+    const float* __restrict__ h0, const int32_t* __restrict__ cu, TI* __restrict__ out, float* __restrict__ hT,
+    const DShape p) {
+  constexpr bool kHoist = S <= 64;
+  const int lane = threadIdx.x & 63;
+  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * RWAVES + (threadIdx.x >> 6));
+  if (item >= p.nitems) return;  // whole waves leave together
+  const int chain = item / p.nslab, slab = item % p.nslab;
+  const int H = p.H, D = p.D;
+  const int bseq = chain / H, hh = chain % H;
+  long rowbase;
+  int len;
+  if (cu) {
+    rowbase = cu[bseq];
+    len = cu[bseq + 1] - cu[bseq];
+  } else {
+    rowbase = (long)bseq * p.T;
+    len = p.T;
+  }
+  const bool active = lane < p.width;
+  const int col = slab * p.width + (active ? lane : 0);
+  const long sbase = (long)chain * S * D + col;
+  const float* __restrict__ arow = alog + (long)hh * S;
+
+  float st[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) st[s] = 0.f;
+  if (h0 && active) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) st[s] = h0[sbase + (long)s * D];
+  }
+  float a2[kHoist ? S : 1];
+  if constexpr (kHoist) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) a2[s] = decay_rate2(arow, s);
+  }
+  const float dh = dskip ? dskip[hh] : 0.f;
+
+  for (int t = 0; t < len; ++t) {
+    const long th = (rowbase + t) * H + hh;  // token-head index
+    const float gt = gp[th];
+    const float vc = active ? (float)vp[th * D + col] : 0.f;
+    const long r0 = th * S;
+    float os[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float rate = kHoist ? a2[s] : decay_rate2(arow, s);
+      const float a = __builtin_amdgcn_exp2f(gt * rate);
+      st[s] = __builtin_fmaf(a, st[s], row_el(bp, r0, s) * vc);
+      os[s & 3] = __builtin_fmaf(row_el(cp, r0, s), st[s], os[s & 3]);
+    }
+    float o = (os[0] + os[1]) + (os[2] + os[3]);
+    if (dskip) o = __builtin_fmaf(dh, vc, o);
+    if (gatep) o = o * gatep[th];
+    if (active) out[th * D + col] = (TI)o;  // rounded to nearest even for bf16
+  }
+  if (active) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) hT[sbase + (long)s * D] = st[s];
+  }
+}
+
+template <typename TI, int S>
+int launch_recurrent(const void* v, const void* b, const void* c, const float* g, const float* alog,
+                     const float* dskip, const float* gate, const float* h0, const int32_t* cu, void* out, float* hT,
+                     const DShape& p, hipStream_t s) {
+  const int nwg = (p.nitems + RWAVES - 1) / RWAVES;
+  hipLaunchKernelGGL((diag_recurrent_kernel<TI, S>), dim3(nwg), dim3(64 * RWAVES), 0, s, static_cast<const TI*>(v),
+                     static_cast<const TI*>(b), static_cast<const TI*>(c), g, alog, dskip, gate, h0, cu,
+                     static_cast<TI*>(out), hT, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+template <typename TI>
+int dispatch_recurrent(const void* v, const void* b, const void* c, const float* g, const float* alog,
+                       const float* dskip, const float* gate, const float* h0, const int32_t* cu, void* out,
+                       float* hT, const DShape& p, hipStream_t s) {
+  switch (p.S) {
+    case 16: return launch_recurrent<TI, 16>(v, b, c, g, alog, dskip, gate, h0, cu, out, hT, p, s);
+    case 32: return launch_recurrent<TI, 32>(v, b, c, g, alog, dskip, gate, h0, cu, out, hT, p, s);
+    case 64: return launch_recurrent<TI, 64>(v, b, c, g, alog, dskip, gate, h0, cu, out, hT, p, s);
+    case 128: return launch_recurrent<TI, 128>(v, b, c, g, alog, dskip, gate, h0, cu, out, hT, p, s);
+    default: return GDN_ERR_UNSUPPORTED;
+  }
+}
+
+bool pow2_dim(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+
+// Host-side checks shared by both entry points; fills the shape on success.
+int diag_validate(const void* v, const void* b, const void* c, const float* g, const float* alog, const void* out,
+                  const float* hT, int B, int T, int H, int S, int D, int dtype, DShape* p) {
+  if (B < 0 || T < 0 || H < 1 || S < 1 || D < 1) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!v || !b || !c || !g || !alog || !out)) return GDN_ERR_INVALID_ARG;
+  if (B > 0 && !hT) return GDN_ERR_INVALID_ARG;
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (!pow2_dim(S) || !pow2_dim(D)) return GDN_ERR_UNSUPPORTED;
+  p->T = T;
+  p->H = H;
+  p->S = S;
+  p->D = D;
+  p->width = D < 64 ? D : 64;
+  p->nslab = D / p->width;
+  const long items = (long)B * H * p->nslab;
+  if (items > 0x7fffffffL - 64) return GDN_ERR_INVALID_ARG;
+  p->nitems = (int)items;
+  return GDN_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Chunkwise form (long sequences), bf16 storage, S = D = 32.
+//
+// The pages run this layer as a chunked kernel with 64-token chunks
+// ("Optimization Quartet", section 3.2): parallel inside a chunk, the state
+// carried across chunks in series.  The algebra below follows from the
+// unrolled sum of Walkthrough section 5.3.1.  Within a chunk let
+// gamma_t = g_1 + ... + g_t (chunk-relative, inclusive) and x_t[s] =
+// A_s gamma_t, which falls with t because A_s < 0 < g.  Then
+//
+//   o_t = c_t^T (e^{x_t} (.) H_c) + sum_{tau <= t} sum_s c_t[s] b_tau[s]
+//                                     e^{x_t[s] - x_tau[s]} v_tau,
+//   H_{c+1} = e^{x_63} (.) H_c + sum_tau (e^{x_63 - x_tau} (.) b_tau) v_tau^T.
+//
+// Every exponent used is <= 0 (a factor in [0, 1]), so nothing overflows;
+// a factor that underflows to zero stands for a contribution below 1e-38 of
+// its neighbours.  A chunk is worked as four 16-token sub-chunks k with a
+// local state that starts at zero: O = Qt_k H0_k + P_k V_k with
+// Qt_k = c (.) e^{x_t - x_ref(k)} (ref(k) = the token before the sub-chunk),
+// P_k[t][tau] = sum_s c_t[s] b_tau[s] prod_{j = tau+1..t} e^{A_s g_j} for
+// tau <= t inside the sub-chunk (the decay product formed by multiplication,
+// so each factor stays in [0, 1] even for rows that decay by e^-40 per
+// token), and H0_{k+1} = E_k (.) H0_k + Bt_k^T V_k.  The chunk's entry
+// state then adds Qh_k H_c with Qh = c (.) e^{x_t}.
+//
+// Mapping: one workgroup per chain (sequence, head), 8 waves; wave w takes
+// chunks w, w+8, ...  All work that does not need the entry state is done
+// before the wave waits for it; the state itself (32 x 32 fp32) is handed
+// from the wave of chunk c to the wave of chunk c+1 through LDS, guarded by
+// a counter, as H_{c+1} = e^{x_63} (.) H_c + H0_4 -- one multiply-add per
+// element on the serial path.  Products with a contraction go to the bf16
+// MFMA (fp32 accumulation): Bt^T V and P V with the 16-deep form, Qt H and
+// Qh H with the 32-deep form; the state is rounded to bf16 only as an MFMA
+// operand and carried in fp32.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int CW = 8;                // waves per workgroup
+constexpr int CC = 64;               // tokens per chunk
+constexpr int CS = 32;               // key rows
+constexpr int CD = 32;               // value columns
+constexpr int ROWB = 64;             // bytes per token row of b, c or v (32 bf16)
+constexpr int SPIN_LIMIT = 1 << 26;  // bound on a wait for the previous chunk's state
+
+struct ChunkParams {
+  const __bf16* v;
+  const __bf16* b;
+  const __bf16* c;
+  const float* g;
+  const float* alog;
+  const float* dskip;
+  const float* gate;
+  const float* h0;
+  const int32_t* cu;
+  __bf16* out;
+  float* hT;
+  int T, H;
+};
+
+// Per-wave LDS region.
+struct WaveLds {
+  char b[CC * ROWB];       // chunk rows of b (bf16, token-major)
+  char c[CC * ROWB];
+  char v[CC * ROWB];
+  float at[16 * CS];       // e^{A_s g_t} for the current sub-chunk
+  float ct[16 * CS];       // c rows of the current sub-chunk in fp32
+  float p[16 * 16];        // P of the current sub-chunk, [t][tau]
+  float gam[CC];           // chunk-relative inclusive cumsum of g
+  float graw[CC];
+  float gate[CC];
+  __bf16 o[16 * CD];       // output staging for 16-byte stores
+};
+
+struct ChunkLds {
+  WaveLds w[CW];
+  float state[2][CS * CD];  // entry states, lane-major (16 floats per lane)
+  float a2[CS];             // A_s log2(e)
+  int ready;                // index of the latest entry state in `state`
+};
+
+__device__ static inline f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ static inline f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                   0, 0);
+}
+
+// Transposing LDS read (gfx950): within each 16-lane group, destination
+// lane i, element k receives element (i & 3) of the 8 bytes addressed by
+// source lane (i >> 2) + 4k.
+__device__ static inline bf16x4 lds_read_tr(const char* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ static inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ static inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ static inline float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ static inline float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
+// LDS-only ordering among the lanes of one wave.
+__device__ static inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+__device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at
+// lds + 16 * lane; bytes at or past the buffer's end read as zero.
+__device__ static inline void copy_to_lds(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ static inline bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+}
+__device__ static inline bf16x4 pack4(f32x4 x) {
+  return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+
+// Wait until the LDS counter holds at least v (bounded: a wait that runs
+// out leaves the loop so that the wave still ends).
+__device__ static inline void wait_ready(const int* f, int v) {
+  const unsigned addr = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) int*)f;
+  for (int i = 0; i < SPIN_LIMIT; ++i) {
+    int x;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+    if (__builtin_amdgcn_readfirstlane(x) >= v) break;
+  }
+}
+
+__global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParams p) {
+  __shared__ ChunkLds L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, q = lane >> 4;
+  const int chain = blockIdx.x;
+  const int H = p.H;
+  const int seq = chain / H, hh = chain % H;
+  long row0;
+  int len;
+  if (p.cu) {
+    row0 = p.cu[seq];
+    len = p.cu[seq + 1] - p.cu[seq];
+  } else {
+    row0 = (long)seq * p.T;
+    len = p.T;
+  }
+  const int nch = (len + CC - 1) / CC;
+  WaveLds& W = L.w[wave];
+  const long sbase = (long)chain * CS * CD;
+
+  // ---- prologue: decay rates, entry state of chunk 0 ------------------------
+  if (wave == 0) {
+    if (lane < CS) L.a2[lane] = p.alog ? -__builtin_amdgcn_exp2f(p.alog[hh * CS + lane] * kLog2e) * kLog2e : 0.f;
+    // lane holds rows 16*mt + 4q + i, column 16*nt + n  (accumulator layout)
+    float* slot = L.state[0] + 16 * lane;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * mt + 4 * q + i, d = 16 * nt + n;
+          const float x = p.h0 ? p.h0[sbase + s * CD + d] : 0.f;
+          slot[8 * mt + 4 * nt + i] = x;
+          if (nch == 0) p.hT[sbase + s * CD + d] = x;
+        }
+    if (lane == 0) L.ready = 0;
+  }
+  __syncthreads();
+  if (wave >= nch) return;
+
+  // Decay rates in the lane's layouts: rows sigma(q, j) (= accumulator rows
+  // 16*mt + 4q + i), rows n and n + 16, and the group 8*(lane & 3) + j.
+  float a2s[8], a2g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a2s[j] = L.a2[(j < 4 ? 0 : 16) + 4 * q + (j & 3)];
+    a2g[j] = L.a2[8 * (lane & 3) + j];
+  }
+  const float a2n0 = L.a2[n], a2n1 = L.a2[n + 16];
+  const float dh = p.dskip ? p.dskip[hh] : 0.f;
+
+  const long tok_stride = (long)H * ROWB;  // bytes between token rows of one head
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<const char*>(p.b) + (row0 * H + hh) * ROWB,
+                                              (long)len * tok_stride);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(p.c) + (row0 * H + hh) * ROWB,
+                                              (long)len * tok_stride);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const char*>(p.v) + (row0 * H + hh) * ROWB,
+                                              (long)len * tok_stride);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<char*>(p.out) + (row0 * H + hh) * ROWB,
+                                              (long)len * tok_stride);
+  auto issue_copies = [&](int c) {
+    // lane -> row 16*i + (lane >> 2) of the chunk, 16-byte granule lane & 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int voff = (int)(((long)(c * CC + 16 * i + (lane >> 2))) * tok_stride) + 16 * (lane & 3);
+      copy_to_lds(rb, W.b + 1024 * i, voff);
+      copy_to_lds(rc, W.c + 1024 * i, voff);
+      copy_to_lds(rv, W.v + 1024 * i, voff);
+    }
+  };
+  issue_copies(wave);
+
+  for (int c = wave; c < nch; c += CW) {
+    // Lane-dependent offsets are re-derived in each iteration instead of
+    // being held in registers across the whole loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int nn = ln & 15, qq = ln >> 4, m4 = ln & 3, hi4 = ln >> 2;
+
+    // ---- gates of the chunk: lane = token ----------------------------------
+    const int tok = c * CC + ln;
+    const bool live = tok < len;
+    const long th = (row0 + (live ? tok : 0)) * H + hh;
+    const float gt = live ? p.g[th] : 0.f;
+    const float gate_t = (live && p.gate) ? p.gate[th] : 1.f;
+    float gam = gt;  // inclusive scan over the 64 lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(gam, d);
+      if (ln >= d) gam += y;
+    }
+    W.gam[ln] = gam;
+    W.graw[ln] = gt;
+    W.gate[ln] = gate_t;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // chunk rows are in LDS
+    wave_lds_sync();
+    const float gend = W.gam[CC - 1];
+
+    // ---- phase A: the chunk's own contribution to the next state ----------
+    // dH = sum_tau (e^{x_63 - x_tau} (.) b_tau) v_tau^T over the chunk.
+    f32x4 dH[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) dH[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int trow0 = 4 * qq + (nn >> 2);  // source row of the transposing reads
+    const int tcol = 4 * (ln & 3);         // source column of the transposing reads
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t0 = 16 * k;
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&W.gam[t0 + 4 * qq]);
+      bf16x4 vf[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + 2 * (16 * nt + tcol));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x4 braw = lds_read_tr(W.b + (t0 + trow0) * ROWB + 2 * (16 * mt + tcol));
+        const float a2r = mt ? a2n1 : a2n0;
+        f32x4 bt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bt[j] = (float)braw[j] * __builtin_amdgcn_exp2f(a2r * (gend - g4[j]));
+        const bf16x4 bb = pack4(bt);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) dH[mt][nt] = mma16(bb, vf[nt], dH[mt][nt]);
+      }
+    }
+    float ec[8];  // e^{x_63} on the lane's accumulator rows
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ec[j] = __builtin_amdgcn_exp2f(a2s[j] * gend);
+
+    // ---- entry state: wait for it, pass the next one on -------------------
+    wait_ready(&L.ready, c);
+    f32x4 hs[2][2];  // state at the start of the current sub-chunk
+    {
+      const f32x4* src = reinterpret_cast<const f32x4*>(L.state[c & 1] + 16 * ln);
+      hs[0][0] = src[0];
+      hs[0][1] = src[1];
+      hs[1][0] = src[2];
+      hs[1][1] = src[3];
+    }
+    {
+      f32x4 hn[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hn[mt][nt][i] = __builtin_fmaf(ec[4 * mt + i], hs[mt][nt][i], dH[mt][nt][i]);
+      if (c + 1 < nch) {
+        f32x4* dst = reinterpret_cast<f32x4*>(L.state[(c + 1) & 1] + 16 * ln);
+        dst[0] = hn[0][0];
+        dst[1] = hn[0][1];
+        dst[2] = hn[1][0];
+        dst[3] = hn[1][1];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (ln == 0) __hip_atomic_store(&L.ready, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.hT[sbase + (16 * mt + 4 * qq + i) * CD + 16 * nt + nn] = hn[mt][nt][i];
+      }
+    }
+
+    // ---- phase B: outputs, sub-chunk by sub-chunk with the running state ---
+#pragma unroll 1
+    for (int k = 0; k < 4; ++k) {
+      const int t0 = 16 * k;
+      const float gref = k ? W.gam[t0 - 1] : 0.f;
+      const float gsub = W.gam[t0 + 15];
+      // tables for P: e^{A_s g_t} and c in fp32; lane -> (token hi4, rows 8*m4 + j)
+      {
+        const float gu = W.graw[t0 + hi4];
+        f32x4 x0, x1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x0[j] = __builtin_amdgcn_exp2f(a2g[j] * gu);
+          x1[j] = __builtin_amdgcn_exp2f(a2g[j + 4] * gu);
+        }
+        *reinterpret_cast<f32x4*>(&W.at[hi4 * CS + 8 * m4]) = x0;
+        *reinterpret_cast<f32x4*>(&W.at[hi4 * CS + 8 * m4 + 4]) = x1;
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + 16 * m4);
+        *reinterpret_cast<f32x4*>(&W.ct[hi4 * CS + 8 * m4]) = f32x4{bf_lo(cw[0]), bf_hi(cw[0]), bf_lo(cw[1]), bf_hi(cw[1])};
+        *reinterpret_cast<f32x4*>(&W.ct[hi4 * CS + 8 * m4 + 4]) =
+            f32x4{bf_lo(cw[2]), bf_hi(cw[2]), bf_lo(cw[3]), bf_hi(cw[3])};
+      }
+      // Qt = c (.) e^{x_t - x_ref}: row t0 + nn, key rows sigma(qq, j)
+      bf16x8 Qt;
+      {
+        const float gt_n = W.gam[t0 + nn];
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(W.c + (t0 + nn) * ROWB + 8 * qq);
+        const u32x2 c1 = *reinterpret_cast<const u32x2*>(W.c + (t0 + nn) * ROWB + 32 + 8 * qq);
+        const float cv[8] = {bf_lo(c0[0]), bf_hi(c0[0]), bf_lo(c0[1]), bf_hi(c0[1]),
+                             bf_lo(c1[0]), bf_hi(c1[0]), bf_lo(c1[1]), bf_hi(c1[1])};
+        f32x4 lo, hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo[j] = cv[j] * __builtin_amdgcn_exp2f(a2s[j] * (gt_n - gref));
+          hi[j] = cv[j + 4] * __builtin_amdgcn_exp2f(a2s[j + 4] * (gt_n - gref));
+        }
+        Qt = pack8(lo, hi);
+      }
+      // v fragments and the sub-chunk's own write, decayed to its end
+      bf16x4 vf[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + 2 * (16 * nt + tcol));
+      f32x4 dk[2][2];
+      {
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&W.gam[t0 + 4 * qq]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x4 braw = lds_read_tr(W.b + (t0 + trow0) * ROWB + 2 * (16 * mt + tcol));
+          const float a2r = mt ? a2n1 : a2n0;
+          f32x4 bt;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bt[j] = (float)braw[j] * __builtin_amdgcn_exp2f(a2r * (gsub - g4[j]));
+          const bf16x4 bb = pack4(bt);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bb, vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+      }
+      wave_lds_sync();  // tables written above are visible to every lane
+      // P[t][tau]; lane -> (tau = hi4, key rows 8*m4 + j)
+      {
+        const u32x4 bw = *reinterpret_cast<const u32x4*>(W.b + (t0 + hi4) * ROWB + 16 * m4);
+        const float bv[8] = {bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1]),
+                             bf_lo(bw[2]), bf_hi(bw[2]), bf_lo(bw[3]), bf_hi(bw[3])};
+        float r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = 0.f;
+        float pt[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(&W.at[t * CS + 8 * m4]);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(&W.at[t * CS + 8 * m4 + 4]);
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(&W.ct[t * CS + 8 * m4]);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(&W.ct[t * CS + 8 * m4 + 4]);
+          const bool start = t == hi4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            r[j] = start ? bv[j] : r[j] * a0[j];
+            r[j + 4] = start ? bv[j + 4] : r[j + 4] * a1[j];
+          }
+          float s0 = c0[0] * r[0], s1 = c0[1] * r[1];
+          s0 = __builtin_fmaf(c0[2], r[2], s0);
+          s1 = __builtin_fmaf(c0[3], r[3], s1);
+          s0 = __builtin_fmaf(c1[0], r[4], s0);
+          s1 = __builtin_fmaf(c1[1], r[5], s1);
+          s0 = __builtin_fmaf(c1[2], r[6], s0);
+          s1 = __builtin_fmaf(c1[3], r[7], s1);
+          pt[t] = s0 + s1;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          pt[t] += dpp_xor1(pt[t]);
+          pt[t] += dpp_xor2(pt[t]);
+        }
+        // the four lanes of a quad hold the same sums; one of them stores
+        if (m4 == 0) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) W.p[t * 16 + hi4] = pt[t];
+        }
+      }
+      wave_lds_sync();
+      // O = Qt H_start + P V, then the epilogue and 16-byte stores
+      {
+        const f32x4 pr = *reinterpret_cast<const f32x4*>(&W.p[nn * 16 + 4 * qq]);
+        const bf16x4 pa = pack4(pr);
+        const f32x4 gt4 = *reinterpret_cast<const f32x4*>(&W.gate[t0 + 4 * qq]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          // Two accumulators, added on the VALU: a 16-deep MFMA that takes a
+          // 32-deep MFMA's result as its accumulator a few instructions
+          // later can read the register before that result lands.
+          const f32x4 qh = mma32(Qt, pack8(hs[0][nt], hs[1][nt]), f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 pv = mma16(pa, vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float y = qh[i] + pv[i];
+            if (p.dskip) y = __builtin_fmaf(dh, (float)vf[nt][i], y);
+            W.o[(4 * qq + i) * CD + 16 * nt + nn] = (__bf16)(y * gt4[i]);
+          }
+        }
+      }
+      // the state at the next sub-chunk's start
+      if (k < 3) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = __builtin_amdgcn_exp2f(a2s[j] * (gsub - gref));
+          const int mt = j >> 2, i = j & 3;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) hs[mt][nt][i] = __builtin_fmaf(e, hs[mt][nt][i], dk[mt][nt][i]);
+        }
+      }
+      wave_lds_sync();
+      {
+        const u32x4 ow = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(W.o) + 16 * ln);
+        const int orow = c * CC + t0 + hi4;
+        __builtin_amdgcn_raw_buffer_store_b128(ow, ro, (int)((long)orow * tok_stride) + 16 * m4, 0, 0);
+      }
+      wave_lds_sync();  // the tables and staging are rewritten next
+    }
+
+    // The chunk rows are no longer read: fetch this wave's next chunk.
+    if (c + CW < nch) issue_copies(c + CW);
+  }
+}
+
+int launch_chunk(const void* v, const void* b, const void* c, const float* g, const float* alog, const float* dskip,
+                 const float* gate, const float* h0, const int32_t* cu, void* out, float* hT, int nchain, int T,
+                 int H, hipStream_t s) {
+  ChunkParams p;
+  p.v = static_cast<const __bf16*>(v);
+  p.b = static_cast<const __bf16*>(b);
+  p.c = static_cast<const __bf16*>(c);
+  p.g = g;
+  p.alog = alog;
+  p.dskip = dskip;
+  p.gate = gate;
+  p.h0 = h0;
+  p.cu = cu;
+  p.out = static_cast<__bf16*>(out);
+  p.hT = hT;
+  p.T = T;
+  p.H = H;
+  hipLaunchKernelGGL(diag_chunk_kernel, dim3(nchain), dim3(64 * CW), 0, s, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c, const float* g,
+                                      const float* A_log, const float* Dskip, const float* gate, const float* h0,
+                                      const int32_t* cu_seqlens, void* out, float* hT, int B, int T, int H, int S,
+                                      int D, void* stream, int dtype) {
+  DShape p;
+  const int rc = diag_validate(v, b, c, g, A_log, out, hT, B, T, H, S, D, dtype, &p);
+  if (rc != GDN_OK) return rc;
+  if (p.nitems == 0) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == GDN_BF16
+             ? dispatch_recurrent<__bf16>(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, p, s)
+             : dispatch_recurrent<float>(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, p, s);
+}
+
+extern "C" int gdn_diag_fwd(const void* v, const void* b, const void* c, const float* g, const float* A_log,
+                            const float* Dskip, const float* gate, const float* h0, const int32_t* cu_seqlens,
+                            void* out, float* hT, int B, int T, int H, int S, int D, void* stream, int dtype,
+                            int chunk) {
+  DShape p;
+  const int rc = diag_validate(v, b, c, g, A_log, out, hT, B, T, H, S, D, dtype, &p);
+  if (rc != GDN_OK) return rc;
+  if (chunk != 0 && chunk != CC) return GDN_ERR_UNSUPPORTED;
+  if (dtype != GDN_BF16 || S != CS || D != CD) return GDN_ERR_UNSUPPORTED;
+  if ((long)(T + CC) * H * ROWB > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;  // 32-bit buffer offsets
+  const long nchain = (long)B * H;
+  if (nchain > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
+  if (nchain == 0) return GDN_OK;
+  return launch_chunk(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, (int)nchain, T, H,
+                      static_cast<hipStream_t>(stream));
+}

@@ -116,6 +116,71 @@ int gdn_fwd_recurrent(const void* q, const void* k, const void* v,
                       int B, int T, int H, int dk, int dv, void* stream,
                       int dtype);
 
+/*
+ * gdn_diag_fwd -- the diagonal-decay additive recurrence that HyMo writes
+ * for its GDN layer, chunkwise form, with the block's epilogue fused:
+ *
+ *   H_t = exp(g_t A) (.) H_{t-1} + b_t (x) v_t,   A = -exp(A_log[h, :]),
+ *   o_t = (c_t^T H_t + D_h v_t) * gate_t,
+ *
+ * per head, with the state H of shape (S, D): every key row s decays by its
+ * own factor exp(g_t A_s), the write key b_t and value v_t add an outer
+ * product (nothing is erased), and the read key c_t reads the state after
+ * the write ("Model Architecture Walkthrough", section 5.2.1; the epilogue
+ * of section 5.5 step 6 and section 5.6; the tensor layout of
+ * "Optimization Quartet", section 3.2).
+ *
+ * Dense mode (cu_seqlens == NULL): B sequences of T tokens each.
+ *   v    : (B, T, H, D)  dtype      values
+ *   b, c : (B, T, H, S)  dtype      write and read keys
+ *   g    : (B, T, H)     float32    per-head gate, g >= 0 (the pages' g is
+ *                                   a sigmoid output); the chunkwise form
+ *                                   relies on it (every decay factor <= 1)
+ *   A_log: (H, S)        float32    A = -exp(A_log), one rate per key row
+ *   Dskip: (H,)          float32    skip weight D_h, or NULL (no skip term)
+ *   gate : (B, T, H)     float32    output gate, or NULL (no gate)
+ *   out  : (B, T, H, D)  dtype      written (bf16: round to nearest even)
+ * Packed mode (cu_seqlens != NULL): as for gdn_fwd -- the same tensors
+ *   without the leading B, cu_seqlens a DEVICE int32 array of B+1 offsets
+ *   (not checked on the device); each sequence is its own recurrence.
+ * State: h0 (B, H, S, D) float32 or NULL (zero); hT (B, H, S, D) float32,
+ *   hT[b,h,s,d] = H[s,d] after the sequence's last token; hT may alias h0
+ *   exactly; a sequence of length 0 gets hT = h0 (or zeros).
+ *
+ * This form supports dtype GDN_BF16 with S = D = 32 (the pages' layer) and
+ * chunk 0 or 64; other valid requests return GDN_ERR_UNSUPPORTED (the
+ * token-by-token entry point below takes every size and both dtypes).
+ * Sizes: B >= 0, T >= 0, H >= 1, (T + 64) * H * 64 < 2^31 bytes.
+ * Pointers: v, b, c, g, A_log, out are required when T > 0; hT when B > 0.
+ * Behaviour, ownership, stream semantics and determinism are those of
+ * gdn_fwd.  Arithmetic: bf16 MFMA operands (keys scaled by their decays, the
+ * state rounded to bf16 only as an operand) with fp32 accumulation; the
+ * state is carried in fp32 and decays are formed in fp32.
+ */
+int gdn_diag_fwd(const void* v, const void* b, const void* c, const float* g,
+                 const float* A_log, const float* Dskip, const float* gate,
+                 const float* h0, const int32_t* cu_seqlens, void* out, float* hT,
+                 int B, int T, int H, int S, int D, void* stream, int dtype,
+                 int chunk);
+
+/*
+ * gdn_diag_fwd_recurrent -- the same operation token by token, for decoding
+ * and short sequences: per token alpha_s = exp(g_t A_s), H <- alpha (.) H +
+ * b_t v_t^T, o_t = (c_t^T H + D_h v_t) * gate_t, with the state kept on chip
+ * for the whole sequence (the loop the pages describe, "Model Architecture
+ * Walkthrough", sections 5.5 step 5 and 6.2-6.4).  Arguments, layouts,
+ * state semantics, aliasing and error behaviour are those of gdn_diag_fwd
+ * without the chunk; any g is accepted.  S and D in {16, 32, 64, 128};
+ * dtype GDN_F32 or GDN_BF16; arithmetic fp32 throughout (bf16 storage
+ * widened on load, output rounded to nearest even).
+ */
+int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c,
+                           const float* g, const float* A_log,
+                           const float* Dskip, const float* gate,
+                           const float* h0, const int32_t* cu_seqlens,
+                           void* out, float* hT, int B, int T, int H, int S,
+                           int D, void* stream, int dtype);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* gdn_strerror(int status);
 

@@ -23,7 +23,8 @@ def _declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["gdn_fwd", "gdn_fwd_recurrent", "gdn_strerror", "gdn_version"]
+    assert _declared_functions() == ["gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_fwd",
+                                     "gdn_fwd_recurrent", "gdn_strerror", "gdn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -116,3 +117,51 @@ def test_recurrent_no_chains_is_a_no_op():
     assert _call_rec(B=0) == OK
     assert _call_rec(B=0, T=0, q=0, k=0, v=0, g=0, beta=0, out=0, hT=0) == OK
     assert _call_rec(hT=0, T=0) == INVALID
+
+
+# ------------------------------------------- diagonal-decay additive form ---
+
+def _diag_args(**kw):
+    a = dict(v=P, b=P, c=P, g=P, A_log=P, Dskip=0, gate=0, h0=0, cu_seqlens=0, out=P, hT=P,
+             B=2, T=64, H=3, S=32, D=32, stream=0, dtype=1)
+    a.update(kw)
+    return a
+
+
+def _call_diag(chunk=0, **kw):
+    return gdn.gdn_diag_fwd(**_diag_args(**kw), chunk=chunk)
+
+
+def _call_diag_rec(**kw):
+    return gdn.gdn_diag_fwd_recurrent(**_diag_args(**kw))
+
+
+@pytest.mark.parametrize("call", [_call_diag, _call_diag_rec])
+@pytest.mark.parametrize("name", ["v", "b", "c", "g", "A_log", "out", "hT"])
+def test_diag_null_required_pointer(call, name):
+    assert call(**{name: 0}) == INVALID
+
+
+@pytest.mark.parametrize("call", [_call_diag, _call_diag_rec])
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=0), dict(S=0), dict(D=-4),
+                                dict(dtype=2), dict(dtype=-1)])
+def test_diag_invalid_sizes(call, kw):
+    assert call(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(S=8), dict(D=256), dict(S=48), dict(D=96)])
+def test_diag_recurrent_unsupported(kw):
+    assert _call_diag_rec(**kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(S=64), dict(D=16), dict(chunk=32),
+                                dict(chunk=16), dict(T=1 << 20, H=64)])
+def test_diag_chunked_unsupported(kw):
+    assert _call_diag(**kw) == UNSUPPORTED
+
+
+def test_diag_no_chains_is_a_no_op():
+    for call in (_call_diag, _call_diag_rec):
+        assert call(B=0) == OK
+        assert call(B=0, T=0, v=0, b=0, c=0, g=0, A_log=0, out=0, hT=0) == OK
+        assert call(hT=0, T=0) == INVALID
