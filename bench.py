@@ -15,6 +15,11 @@ FP64 oracle timed on the host cores on the same workload.
 ``--workload decode`` (one token per sequence, B=128 H=16 d=128, nonzero
 state) times the token-by-token entry point gdn_fwd_recurrent instead;
 ``--form`` picks the entry point for any workload.
+
+``--workload hymo`` / ``hymo_decode`` time the diagonal-decay additive
+recurrence with its epilogue (gdn_diag_fwd / gdn_diag_fwd_recurrent) on the
+HyMo layer's shape (B=4, T=4096, H=40, S=D=32, bf16) and on one decoding
+step of it at batch 256; their lines carry their own metric name.
 """
 from __future__ import annotations
 
@@ -37,6 +42,8 @@ METRIC = "gated-delta-rule fwd tokens/s + achieved HBM GB/s (% roofline), 1 MI35
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc", "gdn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wide_head.json")
 COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
+METRIC_DIAG = ("diagonal-decay recurrence (HyMo GDN layer) fwd tokens/s + achieved HBM GB/s "
+               "(% roofline), 1 MI355X")
 
 
 def algorithmic_bytes(wl: synth.Workload, has_h0: bool) -> int:
@@ -128,6 +135,145 @@ def parity_sample(inp, out, hT):
     return eo, eh
 
 
+def diag_algorithmic_bytes(wl, has_h0: bool, has_gate: bool) -> int:
+    """Minimum HBM traffic of one diagonal-decay call: read v, b, c, g (and
+    gate) once, write out once, read h0 (if given), write hT, read A_log/D."""
+    s = 2 if wl.dtype == "bf16" else 4
+    per_token_head = (2 * wl.D + 2 * wl.S) * s + 4 + (4 if has_gate else 0)
+    state = wl.B * wl.H * wl.S * wl.D * 4
+    params = wl.H * wl.S * 4 + wl.H * 4
+    return wl.tokens * wl.H * per_token_head + state * (2 if has_h0 else 1) + params
+
+
+def diag_main(args):
+    """The diagonal-decay form: same protocol as ``main`` (rotated sets, HIP
+    events on the launch stream, sampled oracle check, CPU oracle leg)."""
+    import torch
+
+    import gated_deltanet_recurrence_delta_amd as gdn
+    import synth.diag as sd
+    from oracle import diag as odiag
+    from oracle import rel_err
+
+    wl = sd.WORKLOADS[args.workload]
+    form = args.form or ("recurrent" if wl.T == 1 else "chunked")
+    inp = sd.generate(wl)
+
+    def dev(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    names = ("v", "b", "c", "g", "A_log", "Dskip", "gate", "h0", "cu_seqlens")
+    sets = []
+    for _ in range(max(1, args.sets)):
+        d = {n: dev(getattr(inp, n)) for n in names}
+        d["out"] = torch.empty(d["v"].shape, dtype=d["v"].dtype, device="cuda")
+        d["hT"] = torch.empty((wl.B, wl.H, wl.S, wl.D), dtype=torch.float32, device="cuda")
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+    f = gdn.diag_fwd if form == "chunked" else gdn.diag_fwd_recurrent
+    for d in sets:
+        f(d["v"], d["b"], d["c"], d["g"], d["A_log"], D=d["Dskip"], gate=d["gate"], h0=d["h0"],
+          cu_seqlens=d["cu_seqlens"], out=d["out"], hT=d["hT"], stream=stream)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    calls = [tuple(ptr(d[n]) for n in names + ("out", "hT")) for d in sets]
+    dtype_code = gdn.GDN_BF16 if wl.dtype == "bf16" else gdn.GDN_F32
+    sh = stream.cuda_stream
+    if form == "chunked":
+        raw = gdn.load().gdn_diag_fwd
+        tail = (wl.B, wl.T, wl.H, wl.S, wl.D, sh, dtype_code, 0)
+    else:
+        raw = gdn.load().gdn_diag_fwd_recurrent
+        tail = (wl.B, wl.T, wl.H, wl.S, wl.D, sh, dtype_code)
+
+    def step(i):
+        rc = raw(*calls[i % len(calls)], *tail)
+        if rc != 0:
+            raise SystemExit(f"diagonal-decay {form} entry point failed with status {rc}")
+
+    alg = diag_algorithmic_bytes(wl, inp.h0 is not None, inp.gate is not None)
+    copy_gbs = copy_reference(alg, stream)
+    torch.cuda.synchronize()
+    errs = None
+    if not args.no_parity:
+        # oracle on the first and last batch rows (every head of each)
+        out = sets[0]["out"].float().cpu().numpy()
+        hT = sets[0]["hT"].cpu().numpy()
+        eo = eh = 0.0
+        for b in sorted({0, wl.B - 1}):
+            sub = lambda n: None if getattr(inp, n) is None else inp.as_f64(n)
+            cut = lambda x: None if x is None else x[b:b + 1]
+            o_ref, h_ref = odiag.diag_fwd_seq(cut(sub("v")), cut(sub("b")), cut(sub("c")),
+                                              cut(sub("g")), sub("A_log"), cut(sub("h0")), None,
+                                              sub("Dskip"), cut(sub("gate")))
+            eo = max(eo, rel_err(out[b:b + 1], o_ref))
+            eh = max(eh, rel_err(hT[b:b + 1], h_ref))
+        if not (eo <= 2e-2 and eh <= 2e-2):
+            raise SystemExit(f"parity check failed: rel err out {eo:.3e} hT {eh:.3e}")
+        errs = (eo, eh)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(e) for a, e in zip(starts, ends)])
+    ms_per_step = wall * 1e3 / args.steps
+    mean_launch_s = float(launch_ms.mean()) / 1e3
+    achieved = alg / mean_launch_s / 1e9
+    rec = {
+        "metric": METRIC_DIAG,
+        "value": wl.tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; v N(0,1), b,c N(0,1/S), g=sigmoid(N(0,1)), "
+                "A_log=log(h+1)+N(0,0.25^2), D=1+N(0,0.1^2), gate=sigmoid(N(0,0.25^2)))",
+        "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} S={wl.S} D={wl.D} "
+                               f"{wl.dtype} " + ("chunk=64" if form == "chunked" else "token-by-token")
+                               + " epilogue D*v, gate",
+                   "entry_point": "gdn_diag_fwd" if form == "chunked" else "gdn_diag_fwd_recurrent",
+                   "tokens_per_step": wl.tokens, "rotated_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
+                     "algorithmic_bytes": alg, "mean_launch_us": mean_launch_s * 1e6,
+                     "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
+                     "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
+                     "p90_us": float(np.percentile(launch_ms, 90)) * 1e3},
+    }
+    if errs is not None:
+        rec["parity"] = {"rel_err_out": errs[0], "rel_err_hT": errs[1],
+                         "chains": "first and last batch rows, every head"}
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        a = {n: None if getattr(inp, n) is None else inp.as_f64(n) for n in names[:-1]}
+        odiag.diag_fwd_seq(a["v"], a["b"], a["c"], a["g"], a["A_log"], a["h0"], None,
+                           a["Dskip"], a["gate"])
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": wl.tokens / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"whole workload ({wl.B * wl.H} chains x {wl.T} tokens), "
+                                         f"NumPy token loop, {dt:.2f} s wall"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +281,10 @@ def main():
     # about 40 ms of warm-up: the first ~10 ms of launches after an idle
     # period run at a lower GPU clock
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="wide_head", choices=sorted(synth.WORKLOADS))
+    import synth.diag as sd
+
+    ap.add_argument("--workload", default="wide_head",
+                    choices=sorted(synth.WORKLOADS) + sorted(sd.WORKLOADS))
     ap.add_argument("--form", choices=("chunked", "recurrent"), default=None,
                     help="entry point (default: recurrent for the decode workload, "
                          "chunked otherwise)")
@@ -153,6 +302,9 @@ def main():
               f"WORLD_SIZE {world}); chains shard across GPUs with no communication, "
               "so there is no multi-GPU step to time.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in sd.WORKLOADS:
+        return diag_main(args)
 
     import torch
 

@@ -206,7 +206,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int CW = 8;                // waves per workgroup
 constexpr int CC = 64;               // tokens per chunk
@@ -230,25 +231,26 @@ struct ChunkParams {
   int T, H;
 };
 
-// Per-wave LDS region.
+// Per-wave LDS region.  The P tables carry 16 spare rows so that the lane
+// working on column tau can address rows tau + delta (delta < 16) with a
+// constant offset; what lands in or comes from rows 16..31 is never used.
 struct WaveLds {
-  char b[CC * ROWB];       // chunk rows of b (bf16, token-major)
-  char c[CC * ROWB];
-  char v[CC * ROWB];
-  float at[16 * CS];       // e^{A_s g_t} for the current sub-chunk
-  float ct[16 * CS];       // c rows of the current sub-chunk in fp32
-  float p[16 * 16];        // P of the current sub-chunk, [t][tau]
-  float gam[CC];           // chunk-relative inclusive cumsum of g
-  float graw[CC];
-  float gate[CC];
-  __bf16 o[16 * CD];       // output staging for 16-byte stores
+  alignas(16) char b[CC * ROWB];     // chunk rows of b (bf16, token-major)
+  alignas(16) char c[CC * ROWB];
+  alignas(16) char v[CC * ROWB];
+  alignas(16) _Float16 at[32 * CS];  // e^{A_s g_t} of the current sub-chunk (fp16); output staging after P
+  alignas(16) _Float16 ct[32 * CS];  // c rows of the current sub-chunk (fp16)
+  alignas(16) float p[32 * 16];      // P of the current sub-chunk, [t][tau]; zero above the diagonal
+  alignas(16) float gam[CC];         // chunk-relative inclusive cumsum of g
+  alignas(16) float graw[CC];
+  alignas(16) float gate[CC];
 };
 
 struct ChunkLds {
   WaveLds w[CW];
-  float state[2][CS * CD];  // entry states, lane-major (16 floats per lane)
-  float a2[CS];             // A_s log2(e)
-  int ready;                // index of the latest entry state in `state`
+  alignas(16) float state[2][CS * CD];  // entry states, lane-major (16 floats per lane)
+  alignas(16) float a2[CS];             // A_s log2(e)
+  int ready;                            // index of the latest entry state in `state`
 };
 
 __device__ static inline f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -290,12 +292,6 @@ __device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-// 16 bytes per lane from the buffer at byte offset voff into LDS at
-// lds + 16 * lane; bytes at or past the buffer's end read as zero.
-__device__ static inline void copy_to_lds(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
-
 __device__ static inline bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
                 (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
@@ -316,7 +312,7 @@ __device__ static inline void wait_ready(const int* f, int v) {
 }
 
 __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParams p) {
-  __shared__ ChunkLds L;
+  __shared__ __attribute__((aligned(16))) ChunkLds L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
@@ -377,17 +373,35 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
                                               (long)len * tok_stride);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<char*>(p.out) + (row0 * H + hh) * ROWB,
                                               (long)len * tok_stride);
-  auto issue_copies = [&](int c) {
-    // lane -> row 16*i + (lane >> 2) of the chunk, 16-byte granule lane & 3
+  // The next chunk of this wave is fetched into registers while the current
+  // one is worked on (12 x 16 bytes per lane of b, c and v rows, plus the
+  // lane's token gate values), and written to LDS when its turn comes.
+  // Lane -> row 16*i + (lane >> 2) of the chunk, 16-byte granule lane & 3.
+  u32x4 pf[12];
+  float pg = 0.f, pgate = 1.f;
+  auto prefetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int voff = (int)(((long)(c * CC + 16 * i + (lane >> 2))) * tok_stride) + 16 * (lane & 3);
-      copy_to_lds(rb, W.b + 1024 * i, voff);
-      copy_to_lds(rc, W.c + 1024 * i, voff);
-      copy_to_lds(rv, W.v + 1024 * i, voff);
+      pf[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0);
+      pf[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0);
+      pf[8 + i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
     }
+    const int tok = c * CC + lane;
+    const long th = (row0 + tok) * H + hh;
+    pg = tok < len ? p.g[th] : 0.f;
+    pgate = (tok < len && p.gate) ? p.gate[th] : 1.f;
   };
-  issue_copies(wave);
+  prefetch(wave);
+  {
+    // P's entries above the diagonal are never written: zero them once, and
+    // the spare table rows too (their products are computed and dropped)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<f32x4*>(W.p + 4 * (lane + 64 * i)) = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.at) + 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.ct) + 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+  }
 
   for (int c = wave; c < nch; c += CW) {
     // Lane-dependent offsets are re-derived in each iteration instead of
@@ -396,13 +410,16 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
     asm volatile("" : "+v"(ln));
     const int nn = ln & 15, qq = ln >> 4, m4 = ln & 3, hi4 = ln >> 2;
 
-    // ---- gates of the chunk: lane = token ----------------------------------
-    const int tok = c * CC + ln;
-    const bool live = tok < len;
-    const long th = (row0 + (live ? tok : 0)) * H + hh;
-    const float gt = live ? p.g[th] : 0.f;
-    const float gate_t = (live && p.gate) ? p.gate[th] : 1.f;
-    float gam = gt;  // inclusive scan over the 64 lanes
+    // ---- this chunk's rows into LDS; fetch the wave's next chunk ----------
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(W.b + 1024 * i + 16 * ln) = pf[i];
+      *reinterpret_cast<u32x4*>(W.c + 1024 * i + 16 * ln) = pf[4 + i];
+      *reinterpret_cast<u32x4*>(W.v + 1024 * i + 16 * ln) = pf[8 + i];
+    }
+    const float gt = pg, gate_t = pgate;
+    if (c + CW < nch) prefetch(c + CW);
+    float gam = gt;  // inclusive scan of g over the chunk (lane = token)
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const float y = __shfl_up(gam, d);
@@ -411,7 +428,6 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
     W.gam[ln] = gam;
     W.graw[ln] = gt;
     W.gate[ln] = gate_t;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // chunk rows are in LDS
     wave_lds_sync();
     const float gend = W.gam[CC - 1];
 
@@ -489,21 +505,21 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       const int t0 = 16 * k;
       const float gref = k ? W.gam[t0 - 1] : 0.f;
       const float gsub = W.gam[t0 + 15];
-      // tables for P: e^{A_s g_t} and c in fp32; lane -> (token hi4, rows 8*m4 + j)
+      // tables for P in fp16: e^{A_s g_t} and c; lane -> (token hi4, rows 8*m4 + j)
       {
         const float gu = W.graw[t0 + hi4];
-        f32x4 x0, x1;
+        h16x8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (_Float16)__builtin_amdgcn_exp2f(a2g[j] * gu);
+        *reinterpret_cast<h16x8*>(&W.at[hi4 * CS + 8 * m4]) = x;
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + 16 * m4);
+        h16x8 y;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          x0[j] = __builtin_amdgcn_exp2f(a2g[j] * gu);
-          x1[j] = __builtin_amdgcn_exp2f(a2g[j + 4] * gu);
+          y[2 * j] = (_Float16)bf_lo(cw[j]);
+          y[2 * j + 1] = (_Float16)bf_hi(cw[j]);
         }
-        *reinterpret_cast<f32x4*>(&W.at[hi4 * CS + 8 * m4]) = x0;
-        *reinterpret_cast<f32x4*>(&W.at[hi4 * CS + 8 * m4 + 4]) = x1;
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + 16 * m4);
-        *reinterpret_cast<f32x4*>(&W.ct[hi4 * CS + 8 * m4]) = f32x4{bf_lo(cw[0]), bf_hi(cw[0]), bf_lo(cw[1]), bf_hi(cw[1])};
-        *reinterpret_cast<f32x4*>(&W.ct[hi4 * CS + 8 * m4 + 4]) =
-            f32x4{bf_lo(cw[2]), bf_hi(cw[2]), bf_lo(cw[3]), bf_hi(cw[3])};
+        *reinterpret_cast<h16x8*>(&W.ct[hi4 * CS + 8 * m4]) = y;
       }
       // Qt = c (.) e^{x_t - x_ref}: row t0 + nn, key rows sigma(qq, j)
       bf16x8 Qt;
@@ -541,45 +557,42 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
         }
       }
       wave_lds_sync();  // tables written above are visible to every lane
-      // P[t][tau]; lane -> (tau = hi4, key rows 8*m4 + j)
+      // P[t][tau] for t = tau + delta; lane -> (tau = hi4, key rows 8*m4 + j).
+      // The running product r = b_tau (.) prod_{j = tau+1..t} e^{A g_j} and the
+      // sum over the lane's eight rows use packed fp16 operands with fp32
+      // accumulation (two rows per dot-product instruction).
       {
-        const u32x4 bw = *reinterpret_cast<const u32x4*>(W.b + (t0 + hi4) * ROWB + 16 * m4);
-        const float bv[8] = {bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1]),
-                             bf_lo(bw[2]), bf_hi(bw[2]), bf_lo(bw[3]), bf_hi(bw[3])};
-        float r[8];
+        const int tau = hi4;
+        const u32x4 bw = *reinterpret_cast<const u32x4*>(W.b + (t0 + tau) * ROWB + 16 * m4);
+        h16x2 r[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = 0.f;
+        for (int j = 0; j < 4; ++j) r[j] = h16x2{(_Float16)bf_lo(bw[j]), (_Float16)bf_hi(bw[j])};
         float pt[16];
+        const _Float16* arow = &W.at[tau * CS + 8 * m4];
+        const _Float16* crow = &W.ct[tau * CS + 8 * m4];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(&W.at[t * CS + 8 * m4]);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(&W.at[t * CS + 8 * m4 + 4]);
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(&W.ct[t * CS + 8 * m4]);
-          const f32x4 c1 = *reinterpret_cast<const f32x4*>(&W.ct[t * CS + 8 * m4 + 4]);
-          const bool start = t == hi4;
+        for (int dl = 0; dl < 16; ++dl) {
+          if (dl) {
+            const h16x8 a = *reinterpret_cast<const h16x8*>(arow + dl * CS);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            r[j] = start ? bv[j] : r[j] * a0[j];
-            r[j + 4] = start ? bv[j + 4] : r[j + 4] * a1[j];
+            for (int j = 0; j < 4; ++j) r[j] = r[j] * h16x2{a[2 * j], a[2 * j + 1]};
           }
-          float s0 = c0[0] * r[0], s1 = c0[1] * r[1];
-          s0 = __builtin_fmaf(c0[2], r[2], s0);
-          s1 = __builtin_fmaf(c0[3], r[3], s1);
-          s0 = __builtin_fmaf(c1[0], r[4], s0);
-          s1 = __builtin_fmaf(c1[1], r[5], s1);
-          s0 = __builtin_fmaf(c1[2], r[6], s0);
-          s1 = __builtin_fmaf(c1[3], r[7], s1);
-          pt[t] = s0 + s1;
+          const h16x8 cc = *reinterpret_cast<const h16x8*>(crow + dl * CS);
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{cc[2 * j], cc[2 * j + 1]}, r[j], acc, false);
+          pt[dl] = acc;
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          pt[t] += dpp_xor1(pt[t]);
-          pt[t] += dpp_xor2(pt[t]);
+        for (int dl = 0; dl < 16; ++dl) {
+          pt[dl] += dpp_xor1(pt[dl]);
+          pt[dl] += dpp_xor2(pt[dl]);
         }
         // the four lanes of a quad hold the same sums; one of them stores
         if (m4 == 0) {
+          float* pcol = &W.p[tau * 16 + tau];
 #pragma unroll
-          for (int t = 0; t < 16; ++t) W.p[t * 16 + hi4] = pt[t];
+          for (int dl = 0; dl < 16; ++dl) pcol[dl * 16] = pt[dl];  // rows past 15 are spare
         }
       }
       wave_lds_sync();
@@ -599,7 +612,7 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
           for (int i = 0; i < 4; ++i) {
             float y = qh[i] + pv[i];
             if (p.dskip) y = __builtin_fmaf(dh, (float)vf[nt][i], y);
-            W.o[(4 * qq + i) * CD + 16 * nt + nn] = (__bf16)(y * gt4[i]);
+            reinterpret_cast<__bf16*>(W.at)[(4 * qq + i) * CD + 16 * nt + nn] = (__bf16)(y * gt4[i]);
           }
         }
       }
@@ -615,15 +628,13 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       }
       wave_lds_sync();
       {
-        const u32x4 ow = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(W.o) + 16 * ln);
+        const u32x4 ow = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(W.at) + 16 * ln);
         const int orow = c * CC + t0 + hi4;
         __builtin_amdgcn_raw_buffer_store_b128(ow, ro, (int)((long)orow * tok_stride) + 16 * m4, 0, 0);
       }
       wave_lds_sync();  // the tables and staging are rewritten next
     }
 
-    // The chunk rows are no longer read: fetch this wave's next chunk.
-    if (c + CW < nch) issue_copies(c + CW);
   }
 }
 
