@@ -155,7 +155,10 @@ int gdn_fwd_recurrent(const void* q, const void* k, const void* v,
  * Behaviour, ownership, stream semantics and determinism are those of
  * gdn_fwd.  Arithmetic: bf16 MFMA operands (keys scaled by their decays, the
  * state rounded to bf16 only as an operand) with fp32 accumulation; the
- * state is carried in fp32 and decays are formed in fp32.
+ * state is carried in fp32 and decays are formed in fp32.  The products of
+ * per-token decays inside 16-token blocks use fp16 operands with fp32
+ * accumulation, so |b| and |c| must stay below 65504 (the fp16 range);
+ * a decay product below 2^-24 counts as zero there.
  */
 int gdn_diag_fwd(const void* v, const void* b, const void* c, const float* g,
                  const float* A_log, const float* Dskip, const float* gate,
