@@ -70,7 +70,11 @@ struct Mma<__bf16> {
   }
   // Half-depth product: the same lane pairing as mma() restricted to the
   // first four positions of each lane group (for operands whose other half
-  // is zero).
+  // is zero).  Its accumulator never comes from a full-depth product: the
+  // compiler inserts no wait states between the two shapes, and a
+  // half-depth MFMA issued two instructions after a full-depth one read its
+  // accumulator register before the result had landed.  Mixed sums keep one
+  // accumulator per depth and add them on the VALU.
   __device__ static inline f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0,
@@ -1401,17 +1405,18 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
                   for (int e = 0; e < 4; ++e) xh[e] = 4 * q4 + e == n16 ? bcol : (__bf16)0.f;
                 } else {
-                  f32x4 r = zero4;
+                  // full- and half-depth products accumulate apart (see mma16)
+                  f32x4 r = zero4, r16 = zero4;
 #pragma unroll
                   for (int s = 0; 32 * s < 16 * b; ++s) {
                     if (2 * s + 1 < col) continue;  // both blocks of the slab are zero
-                    if (2 * s + 1 >= b) r = MM::mma16(MM::lo(Af[b][s]), RH[2 * s][col], r);
-                    else if (2 * s < col) r = MM::mma16(MM::hi(Af[b][s]), RH[2 * s + 1][col], r);
+                    if (2 * s + 1 >= b) r16 = MM::mma16(MM::lo(Af[b][s]), RH[2 * s][col], r16);
+                    else if (2 * s < col) r16 = MM::mma16(MM::hi(Af[b][s]), RH[2 * s + 1][col], r16);
                     else r = MM::mma(Af[b][s], cat(RH[2 * s][col], RH[2 * s + 1][col]), r);
                   }
                   f32x4 x;
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) x[e] = -r[e];
+                  for (int e = 0; e < 4; ++e) x[e] = -(r[e] + r16[e]);
                   xh = cvt4(x);
                 }
                 RT[b][col] = MM::mma16(Tf[b], xh, zero4);
@@ -1452,13 +1457,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = bt[e] * (float)Vr[b][cb][e];
                 if (b > 0) {
-                  f32x4 r = zero4;
+                  f32x4 r = zero4, r16 = zero4;  // full- and half-depth apart (see mma16)
 #pragma unroll
-                  for (int s = 0; 32 * s < 16 * b; ++s)
-                    r = 2 * s + 1 < b ? MM::mma(Af[b][s], cat(RH[2 * s][cb], RH[2 * s + 1][cb]), r)
-                                      : MM::mma16(MM::lo(Af[b][s]), RH[2 * s][cb], r);
+                  for (int s = 0; 32 * s < 16 * b; ++s) {
+                    if (2 * s + 1 < b) r = MM::mma(Af[b][s], cat(RH[2 * s][cb], RH[2 * s + 1][cb]), r);
+                    else r16 = MM::mma16(MM::lo(Af[b][s]), RH[2 * s][cb], r16);
+                  }
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) x[e] -= r[e];
+                  for (int e = 0; e < 4; ++e) x[e] -= r[e] + r16[e];
                 }
                 RU[b][cb] = MM::mma16(Tf[b], cvt4(x), zero4);
                 RH[b][cb] = cvt4(RU[b][cb]);
@@ -1596,9 +1602,15 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
           for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-            for (int s = 0; 32 * s <= 16 * tb; ++s)
-              U[tb] = 32 * s + 16 <= 16 * tb ? MM::mma(TPf[tb][s], Yf[s], U[tb])
-                                             : MM::mma16(MM::lo(TPf[tb][s]), MM::lo(Yf[s]), U[tb]);
+            for (int s = 0; 32 * s <= 16 * tb; ++s) {
+              if (32 * s + 16 <= 16 * tb) {
+                U[tb] = MM::mma(TPf[tb][s], Yf[s], U[tb]);
+              } else {
+                const f32x4 h = MM::mma16(MM::lo(TPf[tb][s]), MM::lo(Yf[s]), f32x4{0.f, 0.f, 0.f, 0.f});  // see mma16
+#pragma unroll
+                for (int e = 0; e < 4; ++e) U[tb][e] += h[e];
+              }
+            }
 
           // Publish U for the output waves; W = diag(w) U for the update.
           F Wf[NTS];
@@ -1768,8 +1780,15 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
             for (int cb = 0; cb < NCB; ++cb) {
               f32x4 o = Oacc[i][cb];
 #pragma unroll
-              for (int s = 0; 32 * s <= 16 * tb; ++s)
-                o = 2 * s + 1 <= tb ? MM::mma(Uf[s][cb], Pf[i][s], o) : MM::mma16(MM::lo(Uf[s][cb]), MM::lo(Pf[i][s]), o);
+              for (int s = 0; 32 * s <= 16 * tb; ++s) {
+                if (2 * s + 1 <= tb) {
+                  o = MM::mma(Uf[s][cb], Pf[i][s], o);
+                } else {
+                  const f32x4 h = MM::mma16(MM::lo(Uf[s][cb]), MM::lo(Pf[i][s]), f32x4{0.f, 0.f, 0.f, 0.f});  // see mma16
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) o[e] += h[e];
+                }
+              }
               ob[cb] = __builtin_bit_cast(u32x2, cvt4(o));
             }
             // Block 0 holds columns 8 q4 .. +3 for even q4, 8 q4 + 4 .. +7 for odd.
