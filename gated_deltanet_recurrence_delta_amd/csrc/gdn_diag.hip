@@ -228,7 +228,7 @@ struct ChunkParams {
   const int32_t* cu;
   __bf16* out;
   float* hT;
-  int T, H;
+  int T, H, nchain;
 };
 
 // Per-wave LDS region.  The P tables carry 16 spare rows so that the lane
@@ -316,7 +316,13 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
-  const int chain = blockIdx.x;
+  // Consecutive chains (neighbouring heads, whose 64-byte token slices share
+  // 128-byte cache lines) go to the same XCD: each XCD takes a contiguous
+  // range of chains (the dispatcher deals workgroups round-robin over the 8).
+  const int chain = [](int bid, int n) {
+    const int xcd = bid & 7, slot = bid >> 3, q8 = n >> 3, r8 = n & 7;
+    return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+  }(blockIdx.x, p.nchain);
   const int H = p.H;
   const int seq = chain / H, hh = chain % H;
   long row0;
@@ -432,7 +438,9 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
     const float gend = W.gam[CC - 1];
 
     // ---- phase A: the chunk's own contribution to the next state ----------
-    // dH = sum_tau (e^{x_63 - x_tau} (.) b_tau) v_tau^T over the chunk.
+    // dH = sum_tau (e^{x_63 - x_tau} (.) b_tau) v_tau^T over the chunk.  The
+    // keys are first decayed to the end of their own sub-chunk (kept for the
+    // output phase), then by the row's decay from there to the chunk's end.
     f32x4 dH[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -440,9 +448,11 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       for (int nt = 0; nt < 2; ++nt) dH[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int trow0 = 4 * qq + (nn >> 2);  // source row of the transposing reads
     const int tcol = 4 * (ln & 3);         // source column of the transposing reads
+    bf16x4 bsub[4][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t0 = 16 * k;
+      const float gsub = W.gam[t0 + 15];
       const f32x4 g4 = *reinterpret_cast<const f32x4*>(&W.gam[t0 + 4 * qq]);
       bf16x4 vf[2];
 #pragma unroll
@@ -451,17 +461,45 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       for (int mt = 0; mt < 2; ++mt) {
         const bf16x4 braw = lds_read_tr(W.b + (t0 + trow0) * ROWB + 2 * (16 * mt + tcol));
         const float a2r = mt ? a2n1 : a2n0;
-        f32x4 bt;
+        const float f = __builtin_amdgcn_exp2f(a2r * (gend - gsub));
+        f32x4 bt, btc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bt[j] = (float)braw[j] * __builtin_amdgcn_exp2f(a2r * (gend - g4[j]));
-        const bf16x4 bb = pack4(bt);
+        for (int j = 0; j < 4; ++j) {
+          bt[j] = (float)braw[j] * __builtin_amdgcn_exp2f(a2r * (gsub - g4[j]));
+          btc[j] = bt[j] * f;
+        }
+        bsub[k][mt] = pack4(bt);
+        const bf16x4 bb = pack4(btc);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dH[mt][nt] = mma16(bb, vf[nt], dH[mt][nt]);
       }
     }
-    float ec[8];  // e^{x_63} on the lane's accumulator rows
+    // Per-row decays over each sub-chunk (E_k) and over the chunk (e^{x_63}),
+    // one exponential per lane and value, kept in the spare rows of the P
+    // table (whatever the P products read from there is dropped).
+    float* const ex = reinterpret_cast<float*>(W.at + 16 * CS);  // [k * 32 + s], chunk at [128 + s]
+    {
+      const int srow = ln & 31, k0 = 2 * (ln >> 5);
+      const float a2l = L.a2[srow];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ec[j] = __builtin_amdgcn_exp2f(a2s[j] * gend);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = k0 + kk;
+        const float gr = k ? W.gam[16 * k - 1] : 0.f;
+        ex[k * 32 + srow] = __builtin_amdgcn_exp2f(a2l * (W.gam[16 * k + 15] - gr));
+      }
+      if (ln < 32) ex[128 + srow] = __builtin_amdgcn_exp2f(a2l * gend);
+    }
+    wave_lds_sync();
+    float ec[8];  // e^{x_63} on the lane's accumulator rows
+    {
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(&ex[128 + 4 * qq]);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(&ex[128 + 16 + 4 * qq]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ec[j] = e0[j];
+        ec[j + 4] = e1[j];
+      }
+    }
 
     // ---- entry state: wait for it, pass the next one on -------------------
     wait_ready(&L.ready, c);
@@ -500,11 +538,10 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
     }
 
     // ---- phase B: outputs, sub-chunk by sub-chunk with the running state ---
-#pragma unroll 1
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t0 = 16 * k;
       const float gref = k ? W.gam[t0 - 1] : 0.f;
-      const float gsub = W.gam[t0 + 15];
       // tables for P in fp16: e^{A_s g_t} and c; lane -> (token hi4, rows 8*m4 + j)
       {
         const float gu = W.graw[t0 + hi4];
@@ -542,20 +579,10 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + 2 * (16 * nt + tcol));
       f32x4 dk[2][2];
-      {
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&W.gam[t0 + 4 * qq]);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x4 braw = lds_read_tr(W.b + (t0 + trow0) * ROWB + 2 * (16 * mt + tcol));
-          const float a2r = mt ? a2n1 : a2n0;
-          f32x4 bt;
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bt[j] = (float)braw[j] * __builtin_amdgcn_exp2f(a2r * (gsub - g4[j]));
-          const bf16x4 bb = pack4(bt);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bb, vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
-        }
-      }
+        for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bsub[k][mt], vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
       wave_lds_sync();  // tables written above are visible to every lane
       // P[t][tau] for t = tau + delta; lane -> (tau = hi4, key rows 8*m4 + j).
       // The running product r = b_tau (.) prod_{j = tau+1..t} e^{A g_j} and the
@@ -618,9 +645,11 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       }
       // the state at the next sub-chunk's start
       if (k < 3) {
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&ex[k * 32 + 4 * qq]);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&ex[k * 32 + 16 + 4 * qq]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float e = __builtin_amdgcn_exp2f(a2s[j] * (gsub - gref));
+          const float e = j < 4 ? e0[j] : e1[j - 4];
           const int mt = j >> 2, i = j & 3;
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) hs[mt][nt][i] = __builtin_fmaf(e, hs[mt][nt][i], dk[mt][nt][i]);
@@ -655,6 +684,7 @@ int launch_chunk(const void* v, const void* b, const void* c, const float* g, co
   p.hT = hT;
   p.T = T;
   p.H = H;
+  p.nchain = nchain;
   hipLaunchKernelGGL(diag_chunk_kernel, dim3(nchain), dim3(64 * CW), 0, s, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
