@@ -210,3 +210,45 @@ def test_chunked_hymo_workload_sampled():
     eh = rel_err(_host(hT)[b:b + 1], h_ref)
     print(f"hymo batch row {b}: rel err out {eo:.2e} hT {eh:.2e}", flush=True)
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("which", ["skip_only", "gate_only"])
+@pytest.mark.parametrize("form", ["chunked", "recurrent"])
+def test_epilogue_factors_separately(which, form):
+    inp = sd.generate(sd.custom(f"epi_{which}_{form}", seed=21, B=2, T=90, H=3, dtype="bf16",
+                                h0_std=0.2))
+    inp = dataclasses.replace(inp, gate=None) if which == "skip_only" else dataclasses.replace(inp, Dskip=None)
+    check(inp, form)
+
+
+def test_chunked_many_heads_one_sequence():
+    """One sequence, 96 heads: more chains than one XCD's share, B = 1."""
+    inp = sd.generate(sd.custom("chunk_h96", seed=22, B=1, T=150, H=96, dtype="bf16", h0_std=0.2))
+    check(inp, "chunked")
+
+
+def test_chunked_packed_ragged_lengths():
+    """Packed lengths off the 16- and 64-token grids, one of them spanning
+    more chunks than the workgroup has waves (9 x 64 + 5 tokens)."""
+    lens = [3, 17, 31, 47, 64 * 9 + 5, 80, 2, 0, 129]
+    inp = sd.generate(sd.custom("chunk_ragged", seed=23, H=2, dtype="bf16", h0_std=0.2,
+                                seq_lens=lens))
+    check(inp, "chunked")
+
+
+def test_recurrent_packed_equals_per_sequence_bitwise():
+    import torch
+
+    lens = [9, 0, 21, 4]
+    inp = sd.generate(sd.custom("rec_bitwise", seed=24, H=3, dtype="f32", h0_std=0.3,
+                                seq_lens=lens))
+    out, hT = run(inp, "recurrent")
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        sub = dataclasses.replace(
+            inp, wl=sd.custom("one", seed=0, B=1, T=e - s, H=3, dtype="f32"),
+            v=inp.v[None, s:e], b=inp.b[None, s:e], c=inp.c[None, s:e], g=inp.g[None, s:e],
+            gate=inp.gate[None, s:e], h0=inp.h0[n:n + 1], cu_seqlens=None)
+        o1, h1 = run(sub, "recurrent")
+        assert torch.equal(o1[0], out[s:e]) and torch.equal(h1[0], hT[n])
