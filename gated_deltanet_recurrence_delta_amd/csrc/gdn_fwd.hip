@@ -297,7 +297,21 @@ struct Params {
   float* hT;
   int T, H, dv, ntile, nwg;
   int lpt;  // packed batch: longest sequences dispatched first (chunkwise bf16 kernel)
+  // Dense batch with fewer chains than CUs (chunkwise bf16 kernel): each
+  // chain's sequence is cut into nseg segments of seg_chunks chunks, one
+  // workgroup per (chain, segment, value tile).
+  int nseg, seg_chunks;
 };
+
+// A segment's workgroup starts its recurrence from a zero state at the
+// latest chunk boundary behind the segment from which the product of the
+// per-token transition norms, alpha_t max(1, |1 - beta_t |k_t|^2|), is at
+// most e^-HALO_NATS (or at the sequence start, from h0).  Each token's
+// transition M -> alpha (I - beta k k^T) M has spectral norm alpha
+// max(1, |1 - beta |k|^2|), so the state the segment starts from differs
+// from the exact one by at most e^-HALO_NATS times the exact state's norm
+// at the halo's start.  Outputs of the halo's chunks are not stored.
+constexpr float HALO_NATS = 40.f;
 
 // Largest packed batch whose sequences the bf16 kernel orders by length.
 constexpr int GDN_LPT_MAX = 512;
@@ -1056,7 +1070,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
   // on one XCD.  Otherwise each XCD takes a contiguous range of items.
   __shared__ int sLEN[GDN_LPT_MAX];
   __shared__ int sPICK;
-  int chain_v, tile_v;
+  int chain_v, tile_v, seg_v = 0;
   if (p.lpt) {
     const int nseq = p.nwg / (p.ntile * p.H);
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -1078,11 +1092,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
     chain_v = sPICK * p.H + k % p.H;
   } else {
     const int item = xcd_remap(blockIdx.x, p.nwg);
-    chain_v = item / p.ntile;
+    chain_v = item / (p.ntile * p.nseg);
+    seg_v = (item / p.ntile) % p.nseg;
     tile_v = item % p.ntile;
   }
   const int chain = __builtin_amdgcn_readfirstlane(chain_v);
   const int tile = __builtin_amdgcn_readfirstlane(tile_v);
+  const int seg = __builtin_amdgcn_readfirstlane(seg_v);
   const int H = p.H;
   const int bseq = chain / H, hh = chain % H;
   long rowbase;
@@ -1096,6 +1112,51 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
   }
   rowbase = __builtin_amdgcn_readfirstlane((int)rowbase);
   len = __builtin_amdgcn_readfirstlane(len);
+  // Sequence segments: find where this segment's recurrence starts (see
+  // HALO_NATS), then narrow the token range to [halo start, segment end).
+  int use_h0 = 1, write_hT = 1, store_from = 0;
+  if (p.nseg > 1) {
+    __shared__ int sSTART;
+    const int c0 = seg * p.seg_chunks;                        // first chunk whose outputs are stored
+    const int c1 = min(c0 + p.seg_chunks, (len + C - 1) / C);  // one past the segment's last chunk
+    if (wave == 0) {
+      int cs = c0;
+      float acc = 0.f;  // log of the transition-norm product over chunks [cs, c0)
+      while (cs > 0 && acc > -HALO_NATS) {
+        --cs;  // chunks before c0 are whole: every lane < C holds a token
+        float e = 0.f;
+        if (lane < C) {
+          const long th = (rowbase + (long)cs * C + lane) * H + hh;
+          const uint4* kr = reinterpret_cast<const uint4*>(p.k + th * DK * 2);
+          float n2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < DK / 8; ++i) {
+            const uint4 w = kr[i];
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float lo = __uint_as_float(u[j] << 16), hi = __uint_as_float(u[j] & 0xffff0000u);
+              n2 = __builtin_fmaf(lo, lo, n2);
+              n2 = __builtin_fmaf(hi, hi, n2);
+            }
+          }
+          const float f = fabsf(1.f - p.beta[th] * n2);
+          e = p.g[th] + (f > 1.f ? __logf(f) : 0.f);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) e += __shfl_xor(e, d);
+        acc += e;
+      }
+      if (lane == 0) sSTART = cs;
+    }
+    __syncthreads();
+    const int cs = sSTART;
+    use_h0 = cs == 0;
+    write_hT = seg == p.nseg - 1;
+    store_from = c0 - cs;
+    rowbase = __builtin_amdgcn_readfirstlane((int)(rowbase + (long)cs * C));
+    len = __builtin_amdgcn_readfirstlane(min(len, c1 * C) - cs * C);
+  }
   const int NC = (len + C - 1) / C;
   const int NIT = NC > 0 ? NC + 2 : 0;
   const long kq_stride = (long)H * DK * 2;  // bytes between tokens in q/k
@@ -1521,7 +1582,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
       for (int b = 0; b < NKB; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Macc[b][e] = p.h0 ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] : 0.f;
+        for (int e = 0; e < 4; ++e)
+          Macc[b][e] = (p.h0 && use_h0) ? p.h0[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] : 0.f;
 
       F Mf[NKS];
       const bool odd = q4 & 1;
@@ -1650,10 +1712,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
         }
         lds_barrier();
       }
+      if (write_hT) {
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
+        for (int b = 0; b < NKB; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] = Macc[b][e];
+          for (int e = 0; e < 4; ++e) p.hT[sbase + (long)key_of(b, 4 * q4 + e) * p.dv + col] = Macc[b][e];
+      }
     };
     if (role == CF::R_S0) state_wave(IC<0>{});
     else state_wave(IC<1>{});
@@ -1770,8 +1834,9 @@ __global__ __launch_bounds__(512, 1) void gdn_bf16_kernel(const Params p) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) Uf[s][cb] = lds_at<F>(sUF + ((cb * NTS + s) * 64 + lane) * 16);
           const long row0 = rowbase + (long)c * C;
-          const __amdgpu_buffer_rsrc_t ro =
-              make_rsrc(p.out + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2, (long)(len - c * C) * v_stride);
+          // a segment's halo chunks are computed but not stored (zero-size descriptor)
+          const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + row0 * v_stride + (hh * p.dv + tile * CF::DVT) * 2,
+                                                      c >= store_from ? (long)(len - c * C) * v_stride : 0);
 #pragma unroll
           for (int i = 0; i < NOWN; ++i) {
             const int tb = CF::own_tb(OW, i);
@@ -1893,8 +1958,28 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   p.ntile = ntile;
   p.nwg = nwg;
   p.lpt = (cu_seqlens && B <= GDN_LPT_MAX && nwg % (8 * ntile) == 0) ? 1 : 0;
+  // Dense bf16 batches with fewer workgroups than CUs: cut each sequence
+  // into segments of at least 8 chunks, about one workgroup per CU.  Not
+  // when hT aliases h0: a segment that starts at the sequence start could
+  // read h0 after the last segment has written hT over it.
+  p.nseg = 1;
+  p.seg_chunks = 0;
+  if (dtype == GDN_BF16 && !cu_seqlens && !(h0 && static_cast<const void*>(h0) == static_cast<const void*>(hT))) {
+    const int nchunks = (T + chunk - 1) / chunk;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && nwg < ncu) {
+      int nseg = ncu / nwg < nchunks / 8 ? ncu / nwg : nchunks / 8;
+      if (nseg >= 2) {
+        p.seg_chunks = (nchunks + nseg - 1) / nseg;
+        p.nseg = (nchunks + p.seg_chunks - 1) / p.seg_chunks;  // every segment holds a chunk
+      }
+    }
+  }
+  const int nwg_all = nwg * p.nseg;
+  p.nwg = nwg_all;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == GDN_BF16 ? by_dk<__bf16>(p, nwg, s, dk, chunk) : by_dk<float>(p, nwg, s, dk, chunk);
+  return dtype == GDN_BF16 ? by_dk<__bf16>(p, nwg_all, s, dk, chunk) : by_dk<float>(p, nwg, s, dk, chunk);
 }
 
 const char* gdn_strerror(int status) {

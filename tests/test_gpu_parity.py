@@ -5,6 +5,8 @@ separately): 1e-4 for float32 storage, 2e-2 for bfloat16 storage with fp32
 accumulation.  Index handling (packing, chunk boundaries, causality,
 aliasing, determinism) is checked bit for bit against other GPU runs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -240,3 +242,48 @@ def test_rejects_bad_args_without_launch():
     d = device_inputs(inp)
     with pytest.raises(gdn.GdnError):
         gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=16)
+
+
+# ---------------------------------------------------------- sequence segments
+# Dense bf16 batches with fewer workgroups than CUs run each sequence as
+# several segments; a segment starts from a zero state far enough back that
+# the transitions in between shrink any state by e^-40 (or at the sequence
+# start).  These shapes have 8 or 16 workgroups and 16-32 chunks per
+# sequence, so they are cut into 2-4 segments.
+
+@pytest.mark.parametrize("kind", ["default_decay", "slow_decay", "no_decay", "long_keys"])
+def test_segmented_sequences(kind):
+    g_mean = {"default_decay": 0.0, "slow_decay": -4.0, "no_decay": 0.0, "long_keys": 0.0}[kind]
+    wl = synth.custom(name=f"seg_{kind}", seed=40, B=1, T=2048, H=2, dk=128, dv=128, dtype="bf16",
+                      chunk=64, h0_std=0.3, g_mean=g_mean)
+    inp = synth.generate(wl)
+    if kind == "no_decay":
+        inp = dataclasses.replace(inp, g=np.zeros_like(inp.g))
+    if kind == "long_keys":
+        # |k| = 1.5 and beta near 1: the transitions can stretch the state
+        # (|1 - beta |k|^2| > 1), which the segment start must account for
+        k = synth.bf16_bits_to_f32(inp.k) * 1.5
+        inp = dataclasses.replace(inp, k=synth.f32_to_bf16_bits(k),
+                                  beta=np.clip(inp.beta + 0.4, 0, 1).astype(np.float32))
+    _check(inp)
+
+
+def test_segmented_small_state():
+    inp = synth.generate(synth.custom(name="seg_small", seed=41, B=2, T=1024, H=4, dk=32, dv=32,
+                                      dtype="bf16", chunk=64, h0_std=0.2))
+    _check(inp)
+
+
+def test_segmented_deterministic_and_alias_fallback():
+    inp = synth.generate(synth.custom(name="seg_det", seed=42, B=1, T=1536, H=2, dk=128, dv=128,
+                                      dtype="bf16", chunk=64, h0_std=0.3, g_mean=-3.0))
+    o1, h1 = run_hip(inp)
+    o2, h2 = run_hip(inp)
+    assert torch.equal(_bits(o1), _bits(o2)) and torch.equal(_bits(h1), _bits(h2))
+    # hT aliasing h0 runs unsegmented; it still matches the oracle
+    d = device_inputs(inp)
+    state = d["h0"].clone()
+    d["h0"] = state
+    o3, h3 = run_hip(inp, d=d, hT=state)
+    eo, eh = compare(inp, o3, state)
+    assert eo <= 2e-2 and eh <= 2e-2, (eo, eh)
