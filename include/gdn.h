@@ -82,7 +82,14 @@ extern "C" {
  * The caller owns all buffers; the library allocates no device memory,
  * keeps no pointer after returning and holds no global mutable state
  * (re-entrant, thread-safe).  Identical inputs give bitwise-identical
- * outputs (no atomics, fixed reduction order).  Arithmetic: bf16 operands
+ * outputs on one device (no atomics, fixed reduction order).  A dense
+ * GDN_BF16 batch with fewer chains x 32-column tiles than the device has
+ * CUs runs each sequence as segments: a segment starts from a zero state at
+ * the latest chunk boundary behind it where the product of the per-token
+ * transition norms exp(g) max(1, |1 - beta |k|^2|) is below e^-40 (or at
+ * the sequence start, from h0), so it differs from the exact sequential
+ * result by less than that factor of the state, beyond rounding; hT == h0
+ * turns this off.  Arithmetic: bf16 operands
  * with fp32 accumulation for GDN_BF16, fp32 throughout for GDN_F32; the
  * state is carried in fp32.  Non-finite inputs propagate.
  */
