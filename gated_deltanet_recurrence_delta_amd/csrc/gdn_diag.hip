@@ -181,24 +181,28 @@ int diag_validate(const void* v, const void* b, const void* c, const float* g, c
 //
 // Every exponent used is <= 0 (a factor in [0, 1]), so nothing overflows;
 // a factor that underflows to zero stands for a contribution below 1e-38 of
-// its neighbours.  A chunk is worked as four 16-token sub-chunks k with a
-// local state that starts at zero: O = Qt_k H0_k + P_k V_k with
-// Qt_k = c (.) e^{x_t - x_ref(k)} (ref(k) = the token before the sub-chunk),
-// P_k[t][tau] = sum_s c_t[s] b_tau[s] prod_{j = tau+1..t} e^{A_s g_j} for
-// tau <= t inside the sub-chunk (the decay product formed by multiplication,
-// so each factor stays in [0, 1] even for rows that decay by e^-40 per
-// token), and H0_{k+1} = E_k (.) H0_k + Bt_k^T V_k.  The chunk's entry
-// state then adds Qh_k H_c with Qh = c (.) e^{x_t}.
+// its neighbours.
 //
 // Mapping: one workgroup per chain (sequence, head), 8 waves; wave w takes
-// chunks w, w+8, ...  All work that does not need the entry state is done
-// before the wave waits for it; the state itself (32 x 32 fp32) is handed
-// from the wave of chunk c to the wave of chunk c+1 through LDS, guarded by
-// a counter, as H_{c+1} = e^{x_63} (.) H_c + H0_4 -- one multiply-add per
-// element on the serial path.  Products with a contraction go to the bf16
-// MFMA (fp32 accumulation): Bt^T V and P V with the 16-deep form, Qt H and
-// Qh H with the 32-deep form; the state is rounded to bf16 only as an MFMA
-// operand and carried in fp32.
+// chunks w, w+8, ...; neighbouring chains run on one XCD.  Per chunk:
+//   phase A (needs no state): the chunk's own write to the next state,
+//     dH = sum_tau (e^{x_63 - x_tau} (.) b_tau) v_tau^T, with each key first
+//     decayed to the end of its 16-token sub-chunk (kept for phase B); the
+//     per-row decays e^{x} over each sub-chunk and over the chunk.
+//   hand-off: wait for H_c (a counter in LDS guards two state slots), pass
+//     H_{c+1} = e^{x_63} (.) H_c + dH on -- one multiply-add per element is
+//     the whole serial path between waves.
+//   phase B: the outputs, sub-chunk by sub-chunk with the running state Hs
+//     (Hs = H_c at the first): O = Qt Hs + P V with Qt = c (.) e^{x_t -
+//     x_ref} (ref = the token before the sub-chunk) and the 16x16 matrix
+//     P[t][tau] = sum_s c_t[s] b_tau[s] prod_{j = tau+1..t} e^{A_s g_j},
+//     tau <= t, whose decay is formed by multiplication so that every factor
+//     stays in [0, 1] even for rows that decay by e^-40 per token; then the
+//     epilogue and Hs <- E_k (.) Hs + Bt_k^T V_k.
+// Products with a contraction go to the bf16 MFMA (fp32 accumulation):
+// Bt^T V and P V with the 16-deep form, Qt Hs with the 32-deep form; the
+// state is rounded to bf16 only as an MFMA operand and carried in fp32.  P
+// is formed in packed fp16 with fp32-accumulating dot products.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
