@@ -213,7 +213,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int CW = 8;                // waves per workgroup
+constexpr int CW = 4;                // waves per workgroup (two workgroups per CU)
 constexpr int CC = 64;               // tokens per chunk
 constexpr int CS = 32;               // key rows
 constexpr int CD = 32;               // value columns
@@ -232,19 +232,19 @@ struct ChunkParams {
   const int32_t* cu;
   __bf16* out;
   float* hT;
-  int T, H, nchain;
+  int T, H, nchain, nseg, seg_chunks;
 };
 
-// Per-wave LDS region.  The P tables carry 16 spare rows so that the lane
-// working on column tau can address rows tau + delta (delta < 16) with a
-// constant offset; what lands in or comes from rows 16..31 is never used.
+// Per-wave LDS region (≈16.8 KB; four waves and the shared part fit twice
+// in a CU's 160 KB).
 struct WaveLds {
   alignas(16) char b[CC * ROWB];     // chunk rows of b (bf16, token-major)
   alignas(16) char c[CC * ROWB];
   alignas(16) char v[CC * ROWB];
-  alignas(16) _Float16 at[32 * CS];  // e^{A_s g_t} of the current sub-chunk (fp16); output staging after P
-  alignas(16) _Float16 ct[32 * CS];  // c rows of the current sub-chunk (fp16)
-  alignas(16) float p[32 * 16];      // P of the current sub-chunk, [t][tau]; zero above the diagonal
+  alignas(16) _Float16 at[16 * CS];  // e^{A_s g_t} of the current sub-chunk (fp16); output staging after P
+  alignas(16) _Float16 ct[16 * CS];  // c rows of the current sub-chunk (fp16)
+  alignas(16) float p[16 * 16];      // P of the current sub-chunk, [t][tau]
+  alignas(16) float ex[5 * CS];      // per-row decays: sub-chunk k at [32 k + s], chunk at [128 + s]
   alignas(16) float gam[CC];         // chunk-relative inclusive cumsum of g
   alignas(16) float graw[CC];
   alignas(16) float gate[CC];
@@ -255,6 +255,7 @@ struct ChunkLds {
   alignas(16) float state[2][CS * CD];  // entry states, lane-major (16 floats per lane)
   alignas(16) float a2[CS];             // A_s log2(e)
   int ready;                            // index of the latest entry state in `state`
+  int cstart;                           // first chunk this workgroup runs
 };
 
 __device__ static inline f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -315,7 +316,7 @@ __device__ static inline void wait_ready(const int* f, int v) {
   }
 }
 
-__global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParams p) {
+__global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParams p) {
   __shared__ __attribute__((aligned(16))) ChunkLds L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -323,10 +324,12 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
   // Consecutive chains (neighbouring heads, whose 64-byte token slices share
   // 128-byte cache lines) go to the same XCD: each XCD takes a contiguous
   // range of chains (the dispatcher deals workgroups round-robin over the 8).
-  const int chain = [](int bid, int n) {
+  // A chain's segments (see below) are consecutive items.
+  const int item = [](int bid, int n) {
     const int xcd = bid & 7, slot = bid >> 3, q8 = n >> 3, r8 = n & 7;
     return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
-  }(blockIdx.x, p.nchain);
+  }(blockIdx.x, p.nchain * p.nseg);
+  const int chain = item / p.nseg, seg = item % p.nseg;
   const int H = p.H;
   const int seq = chain / H, hh = chain % H;
   long row0;
@@ -342,11 +345,38 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
   WaveLds& W = L.w[wave];
   const long sbase = (long)chain * CS * CD;
 
-  // ---- prologue: decay rates, entry state of chunk 0 ------------------------
+  // ---- prologue: decay rates, where this workgroup starts, entry state -----
+  // A dense batch with fewer chains than two per CU cuts each sequence into
+  // segments of seg_chunks chunks, one workgroup each.  A segment's
+  // recurrence starts from a zero state at the latest chunk boundary behind
+  // it where the state's decay since then, prod_t max_s e^{g_t A_s} (the
+  // transition's norm: it is diagonal with entries in [0, 1]), is below
+  // e^-40, or at the sequence start from h0.  The state it then reaches at
+  // the segment's start differs from the exact one by less than e^-40 of
+  // the exact state at that boundary.  The chunks in between (the halo)
+  // are computed and their outputs dropped; only the last segment writes hT.
+  const int c0 = p.nseg > 1 ? seg * p.seg_chunks : 0;                  // first stored chunk
+  const int c1 = p.nseg > 1 ? min(c0 + p.seg_chunks, nch) : nch;        // one past the last
+  const bool write_hT = seg == p.nseg - 1;
   if (wave == 0) {
     if (lane < CS) L.a2[lane] = p.alog ? -__builtin_amdgcn_exp2f(p.alog[hh * CS + lane] * kLog2e) * kLog2e : 0.f;
+    int cs = c0;
+    if (cs > 0) {
+      wave_lds_sync();
+      float a2max = L.a2[lane & 31];  // the slowest row: its rate is the transition's norm
+#pragma unroll
+      for (int d = 16; d >= 1; d >>= 1) a2max = fmaxf(a2max, __shfl_xor(a2max, d));
+      float acc = 0.f;  // log2 of the decay over chunks [cs, c0)
+      while (cs > 0 && acc > -40.f * kLog2e) {
+        --cs;  // chunks before c0 are whole: every lane holds a token
+        float e = p.g[(row0 + (long)cs * CC + lane) * H + hh] * a2max;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) e += __shfl_xor(e, d);
+        acc += e;
+      }
+    }
     // lane holds rows 16*mt + 4q + i, column 16*nt + n  (accumulator layout)
-    float* slot = L.state[0] + 16 * lane;
+    float* slot = L.state[cs & 1] + 16 * lane;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -354,14 +384,18 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * mt + 4 * q + i, d = 16 * nt + n;
-          const float x = p.h0 ? p.h0[sbase + s * CD + d] : 0.f;
+          const float x = (p.h0 && cs == 0) ? p.h0[sbase + s * CD + d] : 0.f;
           slot[8 * mt + 4 * nt + i] = x;
           if (nch == 0) p.hT[sbase + s * CD + d] = x;
         }
-    if (lane == 0) L.ready = 0;
+    if (lane == 0) {
+      L.ready = cs;
+      L.cstart = cs;
+    }
   }
   __syncthreads();
-  if (wave >= nch) return;
+  const int cs = L.cstart;
+  if (cs + wave >= c1) return;
 
   // Decay rates in the lane's layouts: rows sigma(q, j) (= accumulator rows
   // 16*mt + 4q + i), rows n and n + 16, and the group 8*(lane & 3) + j.
@@ -402,18 +436,8 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
     pg = tok < len ? p.g[th] : 0.f;
     pgate = (tok < len && p.gate) ? p.gate[th] : 1.f;
   };
-  prefetch(wave);
-  {
-    // P's entries above the diagonal are never written: zero them once, and
-    // the spare table rows too (their products are computed and dropped)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<f32x4*>(W.p + 4 * (lane + 64 * i)) = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.at) + 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.ct) + 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  for (int c = wave; c < nch; c += CW) {
+  prefetch(cs + wave);
+  for (int c = cs + wave; c < c1; c += CW) {
     // Lane-dependent offsets are re-derived in each iteration instead of
     // being held in registers across the whole loop.
     int ln = lane;
@@ -428,7 +452,7 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       *reinterpret_cast<u32x4*>(W.v + 1024 * i + 16 * ln) = pf[8 + i];
     }
     const float gt = pg, gate_t = pgate;
-    if (c + CW < nch) prefetch(c + CW);
+    if (c + CW < c1) prefetch(c + CW);
     float gam = gt;  // inclusive scan of g over the chunk (lane = token)
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -479,9 +503,8 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
       }
     }
     // Per-row decays over each sub-chunk (E_k) and over the chunk (e^{x_63}),
-    // one exponential per lane and value, kept in the spare rows of the P
-    // table (whatever the P products read from there is dropped).
-    float* const ex = reinterpret_cast<float*>(W.at + 16 * CS);  // [k * 32 + s], chunk at [128 + s]
+    // one exponential per lane and value.
+    float* const ex = W.ex;
     {
       const int srow = ln & 31, k0 = 2 * (ln >> 5);
       const float a2l = L.a2[srow];
@@ -523,7 +546,7 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) hn[mt][nt][i] = __builtin_fmaf(ec[4 * mt + i], hs[mt][nt][i], dH[mt][nt][i]);
-      if (c + 1 < nch) {
+      if (c + 1 < c1) {
         f32x4* dst = reinterpret_cast<f32x4*>(L.state[(c + 1) & 1] + 16 * ln);
         dst[0] = hn[0][0];
         dst[1] = hn[0][1];
@@ -531,7 +554,7 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
         dst[3] = hn[1][1];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         if (ln == 0) __hip_atomic_store(&L.ready, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else {
+      } else if (write_hT) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -542,6 +565,8 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
     }
 
     // ---- phase B: outputs, sub-chunk by sub-chunk with the running state ---
+    // (a halo chunk only carries the state)
+    if (c < c0) continue;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t0 = 16 * k;
@@ -588,42 +613,45 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bsub[k][mt], vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
       wave_lds_sync();  // tables written above are visible to every lane
-      // P[t][tau] for t = tau + delta; lane -> (tau = hi4, key rows 8*m4 + j).
-      // The running product r = b_tau (.) prod_{j = tau+1..t} e^{A g_j} and the
-      // sum over the lane's eight rows use packed fp16 operands with fp32
-      // accumulation (two rows per dot-product instruction).
+      // P[t][tau]; lane -> (tau = hi4, key rows 8*m4 + j).  The running
+      // product r = b_tau (.) prod_{j = tau+1..t} e^{A g_j} (zero before
+      // t = tau) and the sum over the lane's eight rows use packed fp16
+      // operands with fp32 accumulation (two rows per dot-product
+      // instruction); every lane walks the same token t, so the table
+      // reads are broadcasts at constant offsets.
       {
         const int tau = hi4;
         const u32x4 bw = *reinterpret_cast<const u32x4*>(W.b + (t0 + tau) * ROWB + 16 * m4);
-        h16x2 r[4];
+        h16x2 bb2[4], r[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = h16x2{(_Float16)bf_lo(bw[j]), (_Float16)bf_hi(bw[j])};
+        for (int j = 0; j < 4; ++j) {
+          bb2[j] = h16x2{(_Float16)bf_lo(bw[j]), (_Float16)bf_hi(bw[j])};
+          r[j] = h16x2{(_Float16)0.f, (_Float16)0.f};
+        }
+        const _Float16* arow = &W.at[8 * m4];
+        const _Float16* crow = &W.ct[8 * m4];
         float pt[16];
-        const _Float16* arow = &W.at[tau * CS + 8 * m4];
-        const _Float16* crow = &W.ct[tau * CS + 8 * m4];
 #pragma unroll
-        for (int dl = 0; dl < 16; ++dl) {
-          if (dl) {
-            const h16x8 a = *reinterpret_cast<const h16x8*>(arow + dl * CS);
+        for (int t = 0; t < 16; ++t) {
+          const h16x8 a = *reinterpret_cast<const h16x8*>(arow + t * CS);
+          const bool start = t == tau;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) r[j] = r[j] * h16x2{a[2 * j], a[2 * j + 1]};
-          }
-          const h16x8 cc = *reinterpret_cast<const h16x8*>(crow + dl * CS);
+          for (int j = 0; j < 4; ++j) r[j] = start ? bb2[j] : r[j] * h16x2{a[2 * j], a[2 * j + 1]};
+          const h16x8 cc = *reinterpret_cast<const h16x8*>(crow + t * CS);
           float acc = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{cc[2 * j], cc[2 * j + 1]}, r[j], acc, false);
-          pt[dl] = acc;
+          pt[t] = acc;
         }
 #pragma unroll
-        for (int dl = 0; dl < 16; ++dl) {
-          pt[dl] += dpp_xor1(pt[dl]);
-          pt[dl] += dpp_xor2(pt[dl]);
+        for (int t = 0; t < 16; ++t) {
+          pt[t] += dpp_xor1(pt[t]);
+          pt[t] += dpp_xor2(pt[t]);
         }
         // the four lanes of a quad hold the same sums; one of them stores
         if (m4 == 0) {
-          float* pcol = &W.p[tau * 16 + tau];
 #pragma unroll
-          for (int dl = 0; dl < 16; ++dl) pcol[dl * 16] = pt[dl];  // rows past 15 are spare
+          for (int t = 0; t < 16; ++t) W.p[t * 16 + tau] = pt[t];
         }
       }
       wave_lds_sync();
@@ -673,7 +701,7 @@ __global__ __launch_bounds__(64 * CW, 1) void diag_chunk_kernel(const ChunkParam
 
 int launch_chunk(const void* v, const void* b, const void* c, const float* g, const float* alog, const float* dskip,
                  const float* gate, const float* h0, const int32_t* cu, void* out, float* hT, int nchain, int T,
-                 int H, hipStream_t s) {
+                 int H, int nseg, int seg_chunks, hipStream_t s) {
   ChunkParams p;
   p.v = static_cast<const __bf16*>(v);
   p.b = static_cast<const __bf16*>(b);
@@ -689,7 +717,9 @@ int launch_chunk(const void* v, const void* b, const void* c, const float* g, co
   p.T = T;
   p.H = H;
   p.nchain = nchain;
-  hipLaunchKernelGGL(diag_chunk_kernel, dim3(nchain), dim3(64 * CW), 0, s, p);
+  p.nseg = nseg;
+  p.seg_chunks = seg_chunks;
+  hipLaunchKernelGGL(diag_chunk_kernel, dim3(nchain * nseg), dim3(64 * CW), 0, s, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -722,6 +752,26 @@ extern "C" int gdn_diag_fwd(const void* v, const void* b, const void* c, const f
   const long nchain = (long)B * H;
   if (nchain > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
   if (nchain == 0) return GDN_OK;
-  return launch_chunk(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, (int)nchain, T, H,
-                      static_cast<hipStream_t>(stream));
+  // Dense batches with fewer chains than two workgroups per CU: segments of
+  // at least 4 chunks, about two workgroups per CU (not when hT aliases h0:
+  // a segment starting at the sequence start could read h0 after the last
+  // segment has overwritten it).
+  int nseg = 1, seg_chunks = 0;
+  if (!cu_seqlens && !(h0 && static_cast<const void*>(h0) == static_cast<const void*>(hT))) {
+    const int nchunks = (T + CC - 1) / CC;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        nchain < 2L * ncu) {
+      const int want = (int)(2L * ncu / nchain);
+      const int n = want < nchunks / 4 ? want : nchunks / 4;
+      if (n >= 2) {
+        seg_chunks = (nchunks + n - 1) / n;
+        nseg = (nchunks + seg_chunks - 1) / seg_chunks;  // every segment holds a chunk
+      }
+    }
+  }
+  if ((long)nchain * nseg > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
+  return launch_chunk(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, (int)nchain, T, H, nseg,
+                      seg_chunks, static_cast<hipStream_t>(stream));
 }
