@@ -89,7 +89,10 @@ extern "C" {
  * transition norms exp(g) max(1, |1 - beta |k|^2|) is below e^-40 (or at
  * the sequence start, from h0), so it differs from the exact sequential
  * result by less than that factor of the state, beyond rounding; hT == h0
- * turns this off.  Arithmetic: bf16 operands
+ * turns this off, and packed batches are never cut.  So a packed sequence's
+ * slice equals the same sequence run alone bit for bit when that run is not
+ * cut (fewer than 16 chunks, or at least as many chains x tiles as CUs), and
+ * within rounding otherwise.  Arithmetic: bf16 operands
  * with fp32 accumulation for GDN_BF16, fp32 throughout for GDN_F32; the
  * state is carried in fp32.  Non-finite inputs propagate.
  */
