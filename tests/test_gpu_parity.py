@@ -309,3 +309,11 @@ def test_segmented_single_sequence_matches_packed():
     eo = np.max(np.abs(host_f64(o1[0]) - ref)) / np.max(np.abs(ref))
     eh = np.max(np.abs(host_f64(h1[0]) - host_f64(hT[0]))) / np.max(np.abs(host_f64(hT[0])))
     assert eo <= 2e-2 and eh <= 2e-2, (eo, eh)
+
+
+@pytest.mark.parametrize("dk,dv,chunk", [(64, 64, 64), (128, 128, 32), (32, 128, 64)])
+def test_segmented_other_shapes(dk, dv, chunk):
+    inp = synth.generate(synth.custom(name=f"seg_{dk}_{dv}_{chunk}", seed=44, B=1, T=1600, H=3,
+                                      dk=dk, dv=dv, dtype="bf16", chunk=chunk, h0_std=0.2,
+                                      g_mean=-2.0))
+    _check(inp)
