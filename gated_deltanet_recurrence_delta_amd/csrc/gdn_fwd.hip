@@ -1937,6 +1937,7 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
     return GDN_ERR_UNSUPPORTED;
   if (dtype == GDN_BF16 && chunk == 16) return GDN_ERR_UNSUPPORTED;
   if (dtype == GDN_F32 && chunk == 64) return GDN_ERR_UNSUPPORTED;
+  if (!cu_seqlens && (long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;  // token rows are 32-bit
   const int ntile = dv / 32;
   const long nwg_l = (long)B * H * ntile;
   if (nwg_l > 0x7fffffffL) return GDN_ERR_INVALID_ARG;

@@ -64,7 +64,7 @@ extern "C" {
  *   hT may alias h0 exactly (in-place state update); out must not alias
  *   any input.  A sequence of length 0 gets hT = h0 (or zeros).
  *
- * Sizes: B >= 0, T >= 0, H >= 1.  dk, dv in {32, 64, 128}.
+ * Sizes: B >= 0, T >= 0, H >= 1, B*T < 2^31 tokens.  dk, dv in {32, 64, 128}.
  * dtype: GDN_F32 or GDN_BF16.
  * chunk: tokens per chunk; 0 selects 64 for GDN_BF16 and 16 for GDN_F32.
  *        GDN_BF16 accepts 32 and 64; GDN_F32 accepts 16 and 32 (64-token

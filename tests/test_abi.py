@@ -108,6 +108,10 @@ def test_recurrent_invalid_sizes(kw):
     assert _call_rec(**kw) == INVALID
 
 
+def test_token_rows_fit_32_bits():
+    assert _call(B=1 << 16, T=1 << 15) == UNSUPPORTED
+
+
 @pytest.mark.parametrize("kw", [dict(dk=16), dict(dv=256), dict(dk=96), dict(dv=48)])
 def test_recurrent_unsupported(kw):
     assert _call_rec(**kw) == UNSUPPORTED
