@@ -13,9 +13,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "fwd",
-           "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent", "GdnError", "lib_path", "load",
-           "version"]
+__all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
+           "gdn_bwd_workspace_size", "fwd", "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent",
+           "bwd", "GdnError", "lib_path", "load", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -53,6 +53,10 @@ def load():
         lib.gdn_diag_fwd.argtypes = [P] * 11 + [I] * 5 + [P, I, I]
         lib.gdn_diag_fwd_recurrent.restype = I
         lib.gdn_diag_fwd_recurrent.argtypes = [P] * 11 + [I] * 5 + [P, I]
+        lib.gdn_bwd.restype = I
+        lib.gdn_bwd.argtypes = [P] * 16 + [ctypes.c_longlong] + [I] * 5 + [P, I]
+        lib.gdn_bwd_workspace_size.restype = ctypes.c_longlong
+        lib.gdn_bwd_workspace_size.argtypes = [I] * 6
         lib.gdn_strerror.restype = ctypes.c_char_p
         lib.gdn_strerror.argtypes = [I]
         lib.gdn_version.restype = I
@@ -269,3 +273,63 @@ def _marshal_diag(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, strea
     args = (ptr(v), ptr(b), ptr(c), ptr(g), ptr(A_log), ptr(Dskip), ptr(gate), ptr(h0),
             ptr(cu_seqlens), ptr(out), ptr(hT), B, T, H, S, D, stream.cuda_stream, dtype)
     return args, out, hT
+
+
+# ------------------------------------------------------------- backward ---
+
+def gdn_bwd_workspace_size(B, T, H, dk, dv, packed) -> int:
+    """Workspace bytes ``gdn_bwd`` needs (negative: a status code)."""
+    return load().gdn_bwd_workspace_size(int(B), int(T), int(H), int(dk), int(dv), int(packed))
+
+
+def gdn_bwd(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, dh0,
+            workspace, workspace_bytes, B, T, H, dk_, dv_, stream, dtype) -> int:
+    """Raw C call of the backward pass (0 = NULL).  Returns the status."""
+    return load().gdn_bwd(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta,
+                          dh0, workspace, int(workspace_bytes), int(B), int(T), int(H),
+                          int(dk_), int(dv_), stream, int(dtype))
+
+
+def bwd(q, k, v, g, beta, dout, h0=None, cu_seqlens=None, dhT=None, want_dh0=True,
+        workspace=None, stream=None):
+    """Gradients of <dout, out> + <dhT, hT> for ``fwd``'s outputs (out, hT).
+
+    Arguments as for ``fwd``; dout has out's shape and dtype, dhT is
+    (B,H,dk,dv) float32 or None (zero).  Returns a dict with dq, dk, dv (the
+    inputs' dtype), dg, dbeta (float32) and dh0 (float32, or None when
+    ``want_dh0`` is false).  ``workspace``: a uint8 device tensor of at least
+    ``gdn_bwd_workspace_size`` bytes, allocated here when None.
+    """
+    import torch
+
+    # out/hT slots carry dout/dhT so that nothing extra is allocated; unused
+    a, _, _ = _marshal(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, stream)
+    B, T, H, dk_, dv_ = a[9:14]
+    strm, dtype = a[14], a[15]
+    dev = q.device
+    if dout.dtype != v.dtype or tuple(dout.shape) != tuple(v.shape) or dout.device != dev:
+        raise ValueError("dout must have v's shape, dtype and device")
+    if not dout.is_contiguous():
+        raise ValueError("dout must be contiguous")
+    if dhT is not None and (dhT.dtype != torch.float32 or tuple(dhT.shape) != (B, H, dk_, dv_)
+                            or dhT.device != dev or not dhT.is_contiguous()):
+        raise ValueError("dhT must be contiguous float32 (B, H, dk, dv) on q's device")
+    need = gdn_bwd_workspace_size(B, T, H, dk_, dv_, cu_seqlens is not None)
+    if need < 0:
+        raise GdnError(need, strerror(need))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be on q's device and hold {need} bytes")
+    grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+             "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+             "dh0": torch.empty((B, H, dk_, dv_), dtype=torch.float32, device=dev)
+             if want_dh0 else None}
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    rc = gdn_bwd(a[0], a[1], a[2], a[3], a[4], a[5], a[6], ptr(dout), ptr(dhT),
+                 ptr(grads["dq"]), ptr(grads["dk"]), ptr(grads["dv"]), ptr(grads["dg"]),
+                 ptr(grads["dbeta"]), ptr(grads["dh0"]), ptr(workspace),
+                 workspace.numel() * workspace.element_size(), B, T, H, dk_, dv_, strm, dtype)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return grads

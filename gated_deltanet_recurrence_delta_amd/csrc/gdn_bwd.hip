@@ -1,0 +1,722 @@
+// Backward pass of the gated delta rule, chunkwise, for gfx950.
+//
+// The forward rule, per chain, with the state kept as M = S^T (dk x dv) and
+// alpha_t = exp(g_t) (HyMo "Model Architecture Walkthrough", sections 5.2.1
+// and 5.2.2):
+//
+//   u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t),
+//   M_t = alpha_t M_{t-1} + k_t u_t^T,      o_t = M_t^T q_t.
+//
+// The pages train through this layer with a backward pass that recomputes
+// what it needs from the saved inputs ("Optimization Quartet", sections
+// 3.3-3.4; the walkthrough's section 6.5).  Here the gradients of
+// <do, out> + <dhT, hT> are formed chunk by chunk.  For a chunk of C tokens
+// with entry state M, exit state M', in-chunk cumulative log-decay gamma,
+// Gam = exp(gamma), w_i = exp(gamma_C - gamma_i), E_ij = exp(gamma_i - gamma_j):
+//
+//   A   = strict_lower(diag(beta) (K K^T) . E),   T = (I + A)^-1
+//   X   = diag(beta) (V - diag(Gam) K M),         U = T X
+//   P   = lower(Q K^T . E)
+//   O   = diag(Gam) Q M + P U,                    M' = Gam_C M + K^T diag(w) U
+//
+// Reverse mode through these, given dO and dM' (the gradient reaching the
+// chunk's exit state):
+//
+//   dU = P^T dO + diag(w) K dM',   dX = T^T dU,
+//   dM = Gam_C dM' + Q^T diag(Gam) dO - K^T diag(beta Gam) dX
+//
+// which runs backwards over the chunks (the state's adjoint), and per chunk
+//
+//   dV = diag(beta) dX,  dA = -strict_lower(dX U^T),  dP = lower(dO U^T),
+//   dQ = diag(Gam) dO M^T + (dP . E) K,
+//   dK = -diag(beta Gam) dX M^T + G K + G^T K + (dP . E)^T Q + diag(w) U dM'^T,
+//        with G = dA . E . beta_i,
+//   dbeta_i = sum_j dX_ij (V - Gam K M)_ij + sum_j dA_ij (K K^T . E)_ij,
+//   dgamma  = rowsum(Z) - colsum(Z) + dGam . Gam - dw . w  (+ sum(dw . w) at
+//             the chunk's last token), Z = strict_lower(dA . A + dP . P),
+//   dGam_i  = -beta_i sum_j dX_ij (K M)_ij + sum_j dO_ij (Q M)_ij
+//             (+ <M, dM'> at the last token),  dw_i = sum_j U_ij (K dM')_ij,
+//   dg      = reverse cumulative sum of dgamma within the chunk, the w terms
+//             summed as sum_{u < t} dw_u w_u (what they add up to).
+//
+// Four kernels, all in fp32 (bf16 storage is widened on load, the token
+// gradients rounded to nearest even on store):
+//   prep     (chunk, head), parallel:  T and P of every chunk;
+//   states   (chain, 16-column tile), serial over chunks: the state at every
+//            chunk's entry, from h0;
+//   adjoint  (chain, 16-column tile), serial over chunks in reverse: the
+//            gradient reaching every chunk's exit state, from dhT; dh0;
+//   grad     (chunk, head), parallel: dq, dk, dv, dg, dbeta of the chunk from
+//            its entry state and exit gradient, all value columns.
+// T, P, the entry states and the exit gradients live in a caller-supplied
+// workspace, one slot per (head, chunk).  Chunks restart at every sequence
+// start; chunk c of sequence n (its tokens start at offset s_n) takes slot
+// floor(s_n / C) + n + c, which is distinct for distinct (n, c) and below
+// floor(total tokens / C) + B + 1.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace {
+
+constexpr int BC = 32;  // tokens per chunk
+constexpr int TW = 16;  // value columns per tile
+constexpr int NT = 256; // threads per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BShape {
+  int B, T, H, dv;  // T: tokens per sequence (dense) or in total (packed)
+  int nslots;       // chunk slots per head
+  int ntile;        // dv / TW
+};
+
+__device__ inline float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+template <typename TI>
+__device__ inline float ldf(const TI* __restrict__ p, long i) {
+  return (float)p[i];
+}
+
+__device__ inline void seq_info(const int32_t* __restrict__ cu, const BShape& p, int n, long& row0, int& len) {
+  if (cu) {
+    row0 = cu[n];
+    len = cu[n + 1] - cu[n];
+  } else {
+    row0 = (long)n * p.T;
+    len = p.T;
+  }
+}
+
+__device__ inline int slot_key(const int32_t* __restrict__ cu, const BShape& p, int n) {
+  const long start = cu ? (long)cu[n] : (long)n * p.T;
+  return (int)(start / BC) + n;
+}
+
+// The sequence that owns slot s: the largest n with slot_key(n) <= s.
+__device__ inline int find_seq(const int32_t* __restrict__ cu, const BShape& p, int s) {
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_key(cu, p, mid) <= s)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// In-chunk cumulative log-decay, summed in token order (every kernel forms
+// it the same way); rows past the chunk's length add nothing.
+__device__ inline void chunk_gamma(const float* __restrict__ g, long row0, int t0, int Lc, int H, int h, int tid,
+                                   float* gam) {
+  if (tid < BC) {
+    float acc = 0.f;
+    for (int u = 0; u <= tid; ++u) acc += (u < Lc) ? g[(row0 + t0 + u) * H + h] : 0.f;
+    gam[tid] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- prep ----
+template <typename TI, int DK>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                                                      const float* __restrict__ g, const float* __restrict__ beta,
+                                                      const int32_t* __restrict__ cu, float* __restrict__ wsT,
+                                                      float* __restrict__ wsP, const BShape p) {
+  __shared__ float qs[BC][DK + 1], ks[BC][DK + 1], As[BC][BC + 1], Ts[BC][BC + 1];
+  __shared__ float gam[BC], bet[BC];
+  const int tid = threadIdx.x, s = blockIdx.x, h = blockIdx.y, H = p.H;
+  const int n = find_seq(cu, p, s);
+  long row0;
+  int len;
+  seq_info(cu, p, n, row0, len);
+  const int c = s - slot_key(cu, p, n);
+  if (c < 0 || (long)c * BC >= len) return;  // slot not used
+  const int t0 = c * BC, Lc = min(BC, len - t0);
+  for (int e = tid; e < BC * DK; e += NT) {
+    const int t = e / DK, i = e % DK;
+    const long off = ((row0 + t0 + t) * H + h) * DK + i;
+    qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
+    ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
+  }
+  if (tid < BC) bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
+  chunk_gamma(g, row0, t0, Lc, H, h, tid, gam);
+  __syncthreads();
+  const size_t base = ((size_t)h * p.nslots + s) * (BC * BC);
+  for (int e = tid; e < BC * BC; e += NT) {
+    const int t = e / BC, u = e % BC;
+    float kk = 0.f, qk = 0.f;
+    for (int i = 0; i < DK; ++i) {
+      kk = __builtin_fmaf(ks[t][i], ks[u][i], kk);
+      qk = __builtin_fmaf(qs[t][i], ks[u][i], qk);
+    }
+    const float E = u <= t ? ex(gam[t] - gam[u]) : 0.f;
+    As[t][u] = u < t ? bet[t] * kk * E : 0.f;
+    wsP[base + e] = qk * E;
+  }
+  __syncthreads();
+  // (I + A)^-1 by forward substitution, one column per thread
+  if (tid < BC) {
+    const int u = tid;
+    for (int t = 0; t < BC; ++t) {
+      float x = t == u ? 1.f : 0.f;
+      for (int r = u; r < t; ++r) x = __builtin_fmaf(-As[t][r], Ts[r][u], x);
+      Ts[t][u] = x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < BC * BC; e += NT) wsT[base + e] = Ts[e / BC][e % BC];
+}
+
+// -------------------------------------------------------------- states ----
+// State owner mapping for a DK x TW tile: thread -> row si, columns
+// sj0 .. sj0 + JP - 1.
+template <int DK>
+struct Owner {
+  static constexpr int JP = DK * TW / NT;
+  int si, sj0;
+  __device__ Owner(int tid) : si(tid % DK), sj0((tid / DK) * JP) {}
+};
+
+template <typename TI, int DK>
+__global__ __launch_bounds__(NT) void bwd_states_kernel(const TI* __restrict__ k, const TI* __restrict__ v,
+                                                        const float* __restrict__ g,
+                                                        const float* __restrict__ beta,
+                                                        const float* __restrict__ h0,
+                                                        const int32_t* __restrict__ cu,
+                                                        const float* __restrict__ wsT, float* __restrict__ wsM,
+                                                        const BShape p) {
+  constexpr int JP = Owner<DK>::JP;
+  __shared__ float ks[BC][DK + 1], vs[BC][TW + 1], Ts[BC][BC + 1], Xs[BC][TW + 1], Ms[DK][TW + 1];
+  __shared__ float gam[BC], bet[BC];
+  const int tid = threadIdx.x, H = p.H, dv = p.dv;
+  const int chain = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
+  const int n = chain / H, h = chain % H, col0 = tile * TW;
+  long row0;
+  int len;
+  seq_info(cu, p, n, row0, len);
+  const int key = slot_key(cu, p, n), nch = (len + BC - 1) / BC;
+  const Owner<DK> o(tid);
+  float M[JP];
+#pragma unroll
+  for (int r = 0; r < JP; ++r) M[r] = h0 ? h0[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] : 0.f;
+  const int yt = tid >> 3, yj = (tid & 7) * 2;  // (token, column pair) mapping
+
+  for (int c = 0; c < nch; ++c) {
+    const size_t sb = (size_t)h * p.nslots + key + c;
+    float* mo = wsM + sb * DK * dv;
+#pragma unroll
+    for (int r = 0; r < JP; ++r) {
+      mo[(long)o.si * dv + col0 + o.sj0 + r] = M[r];
+      Ms[o.si][o.sj0 + r] = M[r];
+    }
+    const int t0 = c * BC, Lc = min(BC, len - t0);
+    for (int e = tid; e < BC * DK; e += NT) {
+      const int t = e / DK, i = e % DK;
+      ks[t][i] = t < Lc ? ldf(k, ((row0 + t0 + t) * H + h) * DK + i) : 0.f;
+    }
+    for (int e = tid; e < BC * TW; e += NT) {
+      const int t = e / TW, j = e % TW;
+      vs[t][j] = t < Lc ? ldf(v, ((row0 + t0 + t) * H + h) * (long)dv + col0 + j) : 0.f;
+    }
+    for (int e = tid; e < BC * BC; e += NT) Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
+    if (tid < BC) bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
+    chunk_gamma(g, row0, t0, Lc, H, h, tid, gam);
+    __syncthreads();
+    {  // X = beta (V - Gam K M)
+      float y0 = 0.f, y1 = 0.f;
+      for (int i = 0; i < DK; ++i) {
+        const float kv = ks[yt][i];
+        y0 = __builtin_fmaf(kv, Ms[i][yj], y0);
+        y1 = __builtin_fmaf(kv, Ms[i][yj + 1], y1);
+      }
+      const float G = ex(gam[yt]);
+      Xs[yt][yj] = bet[yt] * (vs[yt][yj] - G * y0);
+      Xs[yt][yj + 1] = bet[yt] * (vs[yt][yj + 1] - G * y1);
+    }
+    __syncthreads();
+    {  // W = diag(w) T X, into vs
+      float u0 = 0.f, u1 = 0.f;
+      for (int r = 0; r <= yt; ++r) {
+        const float tv = Ts[yt][r];
+        u0 = __builtin_fmaf(tv, Xs[r][yj], u0);
+        u1 = __builtin_fmaf(tv, Xs[r][yj + 1], u1);
+      }
+      const float w = ex(gam[BC - 1] - gam[yt]);
+      vs[yt][yj] = w * u0;
+      vs[yt][yj + 1] = w * u1;
+    }
+    __syncthreads();
+    const float GC = ex(gam[BC - 1]);
+#pragma unroll
+    for (int r = 0; r < JP; ++r) {
+      float acc = 0.f;
+      for (int t = 0; t < BC; ++t) acc = __builtin_fmaf(ks[t][o.si], vs[t][o.sj0 + r], acc);
+      M[r] = __builtin_fmaf(GC, M[r], acc);
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- adjoint ----
+template <typename TI, int DK>
+__global__ __launch_bounds__(NT) void bwd_adjoint_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                                                         const TI* __restrict__ dO, const float* __restrict__ g,
+                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ dhT,
+                                                         const int32_t* __restrict__ cu,
+                                                         const float* __restrict__ wsT,
+                                                         const float* __restrict__ wsP, float* __restrict__ wsD,
+                                                         float* __restrict__ dh0, const BShape p) {
+  constexpr int JP = Owner<DK>::JP;
+  __shared__ float qs[BC][DK + 1], ks[BC][DK + 1], ds[BC][TW + 1], Ts[BC][BC + 1], Ps[BC][BC + 1];
+  __shared__ float Us[BC][TW + 1], Zs[BC][TW + 1], Ds[DK][TW + 1];
+  __shared__ float gam[BC], bet[BC];
+  const int tid = threadIdx.x, H = p.H, dv = p.dv;
+  const int chain = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
+  const int n = chain / H, h = chain % H, col0 = tile * TW;
+  long row0;
+  int len;
+  seq_info(cu, p, n, row0, len);
+  const int key = slot_key(cu, p, n), nch = (len + BC - 1) / BC;
+  const Owner<DK> o(tid);
+  float D[JP];
+#pragma unroll
+  for (int r = 0; r < JP; ++r) D[r] = dhT ? dhT[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] : 0.f;
+  const int yt = tid >> 3, yj = (tid & 7) * 2;
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const size_t sb = (size_t)h * p.nslots + key + c;
+    float* dout = wsD + sb * DK * dv;
+#pragma unroll
+    for (int r = 0; r < JP; ++r) {
+      dout[(long)o.si * dv + col0 + o.sj0 + r] = D[r];
+      Ds[o.si][o.sj0 + r] = D[r];
+    }
+    const int t0 = c * BC, Lc = min(BC, len - t0);
+    for (int e = tid; e < BC * DK; e += NT) {
+      const int t = e / DK, i = e % DK;
+      const long off = ((row0 + t0 + t) * H + h) * DK + i;
+      qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
+      ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
+    }
+    for (int e = tid; e < BC * TW; e += NT) {
+      const int t = e / TW, j = e % TW;
+      ds[t][j] = t < Lc ? ldf(dO, ((row0 + t0 + t) * H + h) * (long)dv + col0 + j) : 0.f;
+    }
+    for (int e = tid; e < BC * BC; e += NT) {
+      Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
+      Ps[e / BC][e % BC] = wsP[sb * (BC * BC) + e];
+    }
+    if (tid < BC) bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
+    chunk_gamma(g, row0, t0, Lc, H, h, tid, gam);
+    __syncthreads();
+    {  // dU = P^T dO + diag(w) K dM'
+      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+      for (int i = 0; i < DK; ++i) {
+        const float kv = ks[yt][i];
+        a0 = __builtin_fmaf(kv, Ds[i][yj], a0);
+        a1 = __builtin_fmaf(kv, Ds[i][yj + 1], a1);
+      }
+      for (int r = yt; r < BC; ++r) {
+        const float pv = Ps[r][yt];
+        b0 = __builtin_fmaf(pv, ds[r][yj], b0);
+        b1 = __builtin_fmaf(pv, ds[r][yj + 1], b1);
+      }
+      const float w = ex(gam[BC - 1] - gam[yt]);
+      Us[yt][yj] = __builtin_fmaf(w, a0, b0);
+      Us[yt][yj + 1] = __builtin_fmaf(w, a1, b1);
+    }
+    __syncthreads();
+    {  // dX = T^T dU; Z = diag(beta Gam) dX; dO <- diag(Gam) dO
+      float x0 = 0.f, x1 = 0.f;
+      for (int r = yt; r < BC; ++r) {
+        const float tv = Ts[r][yt];
+        x0 = __builtin_fmaf(tv, Us[r][yj], x0);
+        x1 = __builtin_fmaf(tv, Us[r][yj + 1], x1);
+      }
+      const float G = ex(gam[yt]), bg = bet[yt] * G;
+      Zs[yt][yj] = bg * x0;
+      Zs[yt][yj + 1] = bg * x1;
+      ds[yt][yj] *= G;
+      ds[yt][yj + 1] *= G;
+    }
+    __syncthreads();
+    const float GC = ex(gam[BC - 1]);
+#pragma unroll
+    for (int r = 0; r < JP; ++r) {
+      float acc = 0.f;
+      for (int t = 0; t < BC; ++t) {
+        acc = __builtin_fmaf(qs[t][o.si], ds[t][o.sj0 + r], acc);
+        acc = __builtin_fmaf(-ks[t][o.si], Zs[t][o.sj0 + r], acc);
+      }
+      D[r] = __builtin_fmaf(GC, D[r], acc);
+    }
+    __syncthreads();
+  }
+  if (dh0) {
+#pragma unroll
+    for (int r = 0; r < JP; ++r) dh0[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] = D[r];
+  }
+}
+
+// ---------------------------------------------------------------- grad ----
+template <int DK>
+struct GradLds {
+  float qs[BC][DK + 1], ks[BC][DK + 1];
+  float Ts[BC][BC + 1], Ps[BC][BC + 1];
+  union {
+    struct {
+      float Mt[DK][TW + 1], Dt[DK][TW + 1];
+    } tile;
+    struct {
+      float Gs[BC][BC + 1], dPs[BC][BC + 1], Zs[BC][BC + 1];
+    } fin;
+  } u;
+  float vt[BC][TW + 1], dot[BC][TW + 1], Yt[BC][TW + 1], QMt[BC][TW + 1], KDt[BC][TW + 1];
+  float Xt[BC][TW + 1], Ut[BC][TW + 1], dUt[BC][TW + 1], dXt[BC][TW + 1];
+  float gam[BC], bet[BC], sb1[BC], sg1[BC], sw[BC], sb2[BC], red[NT / 64];
+};
+
+template <typename TI, int DK>
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(
+    const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const TI* __restrict__ dO,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    const float* __restrict__ wsT, const float* __restrict__ wsP, const float* __restrict__ wsM,
+    const float* __restrict__ wsD, TI* __restrict__ dq, TI* __restrict__ dk, TI* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta, const BShape p) {
+  constexpr int JQ = DK / 8;  // dq / dk entries per thread: token yt, key columns (tid & 7) + 8 r
+  constexpr int JP = Owner<DK>::JP;
+  __shared__ GradLds<DK> L;
+  const int tid = threadIdx.x, s = blockIdx.x, h = blockIdx.y, H = p.H, dvn = p.dv;
+  const int n = find_seq(cu, p, s);
+  long row0;
+  int len;
+  seq_info(cu, p, n, row0, len);
+  const int c = s - slot_key(cu, p, n);
+  if (c < 0 || (long)c * BC >= len) return;  // slot not used
+  const int t0 = c * BC, Lc = min(BC, len - t0);
+  const size_t sb = (size_t)h * p.nslots + s;
+  for (int e = tid; e < BC * DK; e += NT) {
+    const int t = e / DK, i = e % DK;
+    const long off = ((row0 + t0 + t) * H + h) * DK + i;
+    L.qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
+    L.ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
+  }
+  for (int e = tid; e < BC * BC; e += NT) {
+    L.Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
+    L.Ps[e / BC][e % BC] = wsP[sb * (BC * BC) + e];
+  }
+  if (tid < BC) L.bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
+  chunk_gamma(g, row0, t0, Lc, H, h, tid, L.gam);
+
+  const int yt = tid >> 3, yl = tid & 7, yj = yl * 2;
+  const Owner<DK> o(tid);
+  float dQa[JQ], dKa[JQ], dXU[4], dOU[4];
+#pragma unroll
+  for (int r = 0; r < JQ; ++r) dQa[r] = dKa[r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dXU[r] = dOU[r] = 0.f;
+  float sb1 = 0.f, sg1 = 0.f, sw = 0.f, sGC = 0.f;
+  const float* mbase = wsM + sb * DK * dvn;
+  const float* dbase = wsD + sb * DK * dvn;
+
+  for (int tile = 0; tile < p.ntile; ++tile) {
+    const int col0 = tile * TW;
+    __syncthreads();  // the previous tile's readers are done
+    for (int e = tid; e < DK * TW; e += NT) {
+      const int i = e / TW, j = e % TW;
+      L.u.tile.Mt[i][j] = mbase[(long)i * dvn + col0 + j];
+      L.u.tile.Dt[i][j] = dbase[(long)i * dvn + col0 + j];
+    }
+    for (int e = tid; e < BC * TW; e += NT) {
+      const int t = e / TW, j = e % TW;
+      const long off = ((row0 + t0 + t) * H + h) * (long)dvn + col0 + j;
+      L.vt[t][j] = t < Lc ? ldf(v, off) : 0.f;
+      L.dot[t][j] = t < Lc ? ldf(dO, off) : 0.f;
+    }
+    __syncthreads();
+    const float G = ex(L.gam[yt]), bt = L.bet[yt], w = ex(L.gam[BC - 1] - L.gam[yt]);
+    {  // Y = K M, QM = Q M, KD = K dM', X = beta (V - Gam Y)
+      float y[2] = {0.f, 0.f}, qm[2] = {0.f, 0.f}, kd[2] = {0.f, 0.f};
+#pragma unroll 4
+      for (int i = 0; i < DK; ++i) {
+        const float kv = L.ks[yt][i], qv = L.qs[yt][i];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const float m = L.u.tile.Mt[i][yj + x], d = L.u.tile.Dt[i][yj + x];
+          y[x] = __builtin_fmaf(kv, m, y[x]);
+          qm[x] = __builtin_fmaf(qv, m, qm[x]);
+          kd[x] = __builtin_fmaf(kv, d, kd[x]);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        L.Yt[yt][yj + x] = y[x];
+        L.QMt[yt][yj + x] = qm[x];
+        L.KDt[yt][yj + x] = kd[x];
+        L.Xt[yt][yj + x] = bt * (L.vt[yt][yj + x] - G * y[x]);
+      }
+    }
+    __syncthreads();
+    {  // U = T X, dU = P^T dO + diag(w) KD
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        float uu = 0.f, du = 0.f;
+        for (int r = 0; r <= yt; ++r) uu = __builtin_fmaf(L.Ts[yt][r], L.Xt[r][yj + x], uu);
+        for (int r = yt; r < BC; ++r) du = __builtin_fmaf(L.Ps[r][yt], L.dot[r][yj + x], du);
+        L.Ut[yt][yj + x] = uu;
+        L.dUt[yt][yj + x] = __builtin_fmaf(w, L.KDt[yt][yj + x], du);
+      }
+    }
+    __syncthreads();
+    {  // dX = T^T dU, dV, and the per-token sums
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        float dx = 0.f;
+        for (int r = yt; r < BC; ++r) dx = __builtin_fmaf(L.Ts[r][yt], L.dUt[r][yj + x], dx);
+        L.dXt[yt][yj + x] = dx;
+        const float yv = L.Yt[yt][yj + x];
+        sb1 = __builtin_fmaf(dx, L.vt[yt][yj + x] - G * yv, sb1);
+        sg1 = __builtin_fmaf(-bt * dx, yv, sg1);
+        sg1 = __builtin_fmaf(L.dot[yt][yj + x], L.QMt[yt][yj + x], sg1);
+        sw = __builtin_fmaf(L.Ut[yt][yj + x], L.KDt[yt][yj + x], sw);
+        if (yt < Lc) dv[((row0 + t0 + yt) * H + h) * (long)dvn + col0 + yj + x] = (TI)(bt * dx);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < JP; ++r)
+      sGC = __builtin_fmaf(L.u.tile.Mt[o.si][o.sj0 + r], L.u.tile.Dt[o.si][o.sj0 + r], sGC);
+    __syncthreads();
+    // C x C accumulations over the tile's columns
+    {
+      float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int j = 0; j < TW; ++j) {
+        const float xv = L.dXt[yt][j], ov = L.dot[yt][j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float uv = L.Ut[yl + 8 * r][j];
+          a[r] = __builtin_fmaf(xv, uv, a[r]);
+          b[r] = __builtin_fmaf(ov, uv, b[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dXU[r] += a[r];
+        dOU[r] += b[r];
+      }
+    }
+    {  // dQ += Gam dO M^T;  dK += -beta Gam dX M^T + w U dM'^T
+      float a[JQ], b[JQ], d[JQ];
+#pragma unroll
+      for (int r = 0; r < JQ; ++r) a[r] = b[r] = d[r] = 0.f;
+#pragma unroll 2
+      for (int j = 0; j < TW; ++j) {
+        const float ov = L.dot[yt][j], xv = L.dXt[yt][j], uv = L.Ut[yt][j];
+#pragma unroll
+        for (int r = 0; r < JQ; ++r) {
+          const float m = L.u.tile.Mt[yl + 8 * r][j];
+          a[r] = __builtin_fmaf(ov, m, a[r]);
+          b[r] = __builtin_fmaf(xv, m, b[r]);
+          d[r] = __builtin_fmaf(uv, L.u.tile.Dt[yl + 8 * r][j], d[r]);
+        }
+      }
+      const float bg = -bt * G;
+#pragma unroll
+      for (int r = 0; r < JQ; ++r) {
+        dQa[r] = __builtin_fmaf(G, a[r], dQa[r]);
+        dKa[r] = __builtin_fmaf(bg, b[r], dKa[r]);
+        dKa[r] = __builtin_fmaf(w, d[r], dKa[r]);
+      }
+    }
+  }
+  // lane sums over the 8 threads of a token (lanes yt*8 .. yt*8+7 of one wave)
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    sb1 += __shfl_xor(sb1, m);
+    sg1 += __shfl_xor(sg1, m);
+    sw += __shfl_xor(sw, m);
+  }
+  // <M, dM'> over the whole state: wave sums, then the workgroup's
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) sGC += __shfl_xor(sGC, m);
+  __syncthreads();  // the last tile's readers of Mt / Dt are done (fin reuses them)
+  if (yl == 0) {
+    L.sb1[yt] = sb1;
+    L.sg1[yt] = sg1;
+    L.sw[yt] = sw;
+  }
+  if ((tid & 63) == 0) L.red[tid >> 6] = sGC;
+  {  // dA, G, dP . E, Z and the second dbeta term
+    const float gt = L.gam[yt], bt = L.bet[yt];
+    float sb2 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int uu = yl + 8 * r;
+      float kk = 0.f;
+      if (uu < yt)
+#pragma unroll 4
+        for (int i = 0; i < DK; ++i) kk = __builtin_fmaf(L.ks[yt][i], L.ks[uu][i], kk);
+      const float E = uu <= yt ? ex(gt - L.gam[uu]) : 0.f;
+      const float dA = uu < yt ? -dXU[r] : 0.f;
+      const float kke = kk * E;
+      const float dP = uu <= yt ? dOU[r] : 0.f;
+      L.u.fin.Gs[yt][uu] = dA * E * bt;
+      L.u.fin.dPs[yt][uu] = dP * E;
+      // the diagonal adds to a token's row and column alike: left out
+      L.u.fin.Zs[yt][uu] = uu < yt ? __builtin_fmaf(dA, bt * kke, dP * L.Ps[yt][uu]) : 0.f;
+      sb2 = __builtin_fmaf(dA, kke, sb2);
+    }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) sb2 += __shfl_xor(sb2, m);
+    if (yl == 0) L.sb2[yt] = sb2;
+  }
+  __syncthreads();
+  {  // dQ += (dP . E) K;  dK += G K + G^T K + (dP . E)^T Q
+    float a[JQ], b[JQ];
+#pragma unroll
+    for (int r = 0; r < JQ; ++r) a[r] = b[r] = 0.f;
+#pragma unroll 2
+    for (int uu = 0; uu < BC; ++uu) {
+      const float pe = L.u.fin.dPs[yt][uu], gg = L.u.fin.Gs[yt][uu] + L.u.fin.Gs[uu][yt];
+      const float pt = L.u.fin.dPs[uu][yt];
+#pragma unroll
+      for (int r = 0; r < JQ; ++r) {
+        const float kv = L.ks[uu][yl + 8 * r];
+        a[r] = __builtin_fmaf(pe, kv, a[r]);
+        b[r] = __builtin_fmaf(gg, kv, b[r]);
+        b[r] = __builtin_fmaf(pt, L.qs[uu][yl + 8 * r], b[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < JQ; ++r) {
+      dQa[r] += a[r];
+      dKa[r] += b[r];
+      if (yt < Lc) {
+        const long off = ((row0 + t0 + yt) * H + h) * DK + yl + 8 * r;
+        dq[off] = (TI)dQa[r];
+        dk[off] = (TI)dKa[r];
+      }
+    }
+  }
+  if (tid < BC) {  // per-token terms
+    const int t = tid, last = Lc - 1;
+    float rz = 0.f, cz = 0.f;
+    for (int uu = 0; uu < BC; ++uu) {
+      rz += L.u.fin.Zs[t][uu];
+      cz += L.u.fin.Zs[uu][t];
+    }
+    float gc = 0.f;
+    for (int wv = 0; wv < NT / 64; ++wv) gc += L.red[wv];
+    const float Gt = ex(L.gam[t]), wt = ex(L.gam[BC - 1] - L.gam[t]);
+    const float dGam = L.sg1[t] + (t == last ? gc : 0.f);
+    L.sb1[t] += L.sb2[t];                      // dbeta, kept in place
+    L.sg1[t] = __builtin_fmaf(dGam, Gt, rz - cz);  // dgamma without the w terms, in place
+    L.sw[t] *= wt;                             // dw . w, in place
+  }
+  __syncthreads();
+  // dg_t = sum_{u >= t} dgamma_u.  The w terms (-dw_u w_u at every token,
+  // +sum_u dw_u w_u at the last) are summed in the form they take after the
+  // reverse sum, sum_{u < t} dw_u w_u, which does not cancel large terms
+  // when the decay is strong.
+  if (tid < Lc) {
+    const int t = tid;
+    float acc = 0.f;
+    for (int uu = Lc - 1; uu >= t; --uu) acc += L.sg1[uu];
+    for (int uu = 0; uu < t; ++uu) acc += L.sw[uu];
+    const long th = (row0 + t0 + t) * H + h;
+    dg[th] = acc;
+    dbeta[th] = L.sb1[t];
+  }
+}
+
+// ---------------------------------------------------------------- host ----
+size_t slots_per_head(long ttot, int B) { return (size_t)(ttot / BC) + (size_t)B + 1; }
+
+size_t ws_floats(size_t nslots, int H, int dk, int dv) {
+  return (size_t)H * nslots * (2 * (size_t)BC * BC + 2 * (size_t)dk * dv);
+}
+
+template <typename TI, int DK>
+int launch_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta, const float* h0,
+               const int32_t* cu, const void* dO, const float* dhT, void* dq, void* dk, void* dv, float* dg,
+               float* dbeta, float* dh0, float* ws, const BShape& p, hipStream_t st) {
+  const size_t cc = (size_t)p.H * p.nslots * BC * BC;
+  const size_t sm = (size_t)p.H * p.nslots * DK * p.dv;
+  float* wsT = ws;
+  float* wsP = wsT + cc;
+  float* wsM = wsP + cc;
+  float* wsD = wsM + sm;
+  const TI *qq = static_cast<const TI*>(q), *kk = static_cast<const TI*>(k), *vv = static_cast<const TI*>(v);
+  const TI* oo = static_cast<const TI*>(dO);
+  const dim3 chunks(p.nslots, p.H), chains(p.B * p.H * p.ntile);
+  if (p.B * p.H * p.ntile == 0) return GDN_OK;
+  hipLaunchKernelGGL((bwd_prep_kernel<TI, DK>), chunks, dim3(NT), 0, st, qq, kk, g, beta, cu, wsT, wsP, p);
+  hipLaunchKernelGGL((bwd_states_kernel<TI, DK>), chains, dim3(NT), 0, st, kk, vv, g, beta, h0, cu, wsT, wsM, p);
+  hipLaunchKernelGGL((bwd_adjoint_kernel<TI, DK>), chains, dim3(NT), 0, st, qq, kk, oo, g, beta, dhT, cu, wsT,
+                     wsP, wsD, dh0, p);
+  hipLaunchKernelGGL((bwd_grad_kernel<TI, DK>), chunks, dim3(NT), 0, st, qq, kk, vv, oo, g, beta, cu, wsT, wsP,
+                     wsM, wsD, static_cast<TI*>(dq), static_cast<TI*>(dk), static_cast<TI*>(dv), dg, dbeta, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+template <typename TI>
+int launch_dtype(int dkn, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                 const float* h0, const int32_t* cu, const void* dO, const float* dhT, void* dq, void* dk, void* dv,
+                 float* dg, float* dbeta, float* dh0, float* ws, const BShape& p, hipStream_t st) {
+  switch (dkn) {
+    case 32: return launch_bwd<TI, 32>(q, k, v, g, beta, h0, cu, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws, p, st);
+    case 64: return launch_bwd<TI, 64>(q, k, v, g, beta, h0, cu, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws, p, st);
+    case 128: return launch_bwd<TI, 128>(q, k, v, g, beta, h0, cu, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws, p, st);
+    default: return GDN_ERR_UNSUPPORTED;
+  }
+}
+
+bool bwd_sizes_ok(int B, int T, int H, int dk, int dv, int packed) {
+  if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return false;
+  if (!packed && (long)B * T > 0x7fffffffL) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" long long gdn_bwd_workspace_size(int B, int T, int H, int dk, int dv, int packed) {
+  if (!bwd_sizes_ok(B, T, H, dk, dv, packed)) return GDN_ERR_INVALID_ARG;
+  if (H > 65535) return GDN_ERR_UNSUPPORTED;
+  if ((dk != 32 && dk != 64 && dk != 128) || (dv != 32 && dv != 64 && dv != 128)) return GDN_ERR_UNSUPPORTED;
+  const long ttot = packed ? (long)T : (long)B * T;
+  return (long long)(ws_floats(slots_per_head(ttot, B), H, dk, dv) * sizeof(float));
+}
+
+extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT, void* dq,
+                       void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
+                       long long workspace_bytes, int B, int T, int H, int dkn, int dvn, void* stream, int dtype) {
+  if (!bwd_sizes_ok(B, T, H, dkn, dvn, cu_seqlens != nullptr)) return GDN_ERR_INVALID_ARG;
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+    return GDN_ERR_INVALID_ARG;
+  if ((dkn != 32 && dkn != 64 && dkn != 128) || (dvn != 32 && dvn != 64 && dvn != 128)) return GDN_ERR_UNSUPPORTED;
+  if (H > 65535) return GDN_ERR_UNSUPPORTED;
+  const long ttot = cu_seqlens ? (long)T : (long)B * T;
+  const size_t nslots = slots_per_head(ttot, B);
+  if ((long long)(nslots * (size_t)H) > 0x7fffffffLL || nslots > 0x7fffffffULL) return GDN_ERR_UNSUPPORTED;
+  const size_t need = ws_floats(nslots, H, dkn, dvn) * sizeof(float);
+  if (B > 0 && (!workspace || workspace_bytes < 0 || (size_t)workspace_bytes < need)) return GDN_ERR_INVALID_ARG;
+  if ((long)B * H * (dvn / TW) > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  BShape p;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.dv = dvn;
+  p.nslots = (int)nslots;
+  p.ntile = dvn / TW;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  return dtype == GDN_BF16 ? launch_dtype<__bf16>(dkn, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
+                                                  dbeta, dh0, ws, p, st)
+                           : launch_dtype<float>(dkn, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
+                                                 dbeta, dh0, ws, p, st);
+}

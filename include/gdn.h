@@ -194,6 +194,60 @@ int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c,
                            void* out, float* hT, int B, int T, int H, int S,
                            int D, void* stream, int dtype);
 
+/*
+ * gdn_bwd -- gradients of the gated delta rule's forward pass (gdn_fwd's
+ * operation) for training: given the output gradient dout and the final-state
+ * gradient dhT, it returns the gradients of <dout, out> + <dhT, hT> with
+ * respect to q, k, v, g, beta and h0.  The pages train through this layer
+ * with a backward pass that recomputes what it needs from the saved inputs
+ * ("Optimization Quartet", sections 3.3-3.4; "Model Architecture
+ * Walkthrough", section 6.5); so does this one: it takes only the forward's
+ * inputs, not its outputs.
+ *
+ * Arguments and layouts are gdn_fwd's (dense or packed, the same dtype for
+ * q, k, v, dout, dq, dk and dv), plus:
+ *   dout : like out           dtype     gradient of the output
+ *   dhT  : (B, H, dk, dv)     float32   gradient of hT, or NULL (zero)
+ *   dq, dk : like q           dtype     written (bf16: round to nearest even)
+ *   dv   : like v             dtype     written
+ *   dg, dbeta : like g        float32   written
+ *   dh0  : (B, H, dk, dv)     float32   written, or NULL (not wanted); it is
+ *                                       the gradient of h0 whether or not h0
+ *                                       was given
+ *   workspace : DEVICE buffer of at least gdn_bwd_workspace_size(...) bytes,
+ *        owned by the caller; overwritten (no contents needed on entry or kept
+ *        on return).  It holds, per head and 32-token chunk, two 32x32 fp32
+ *        matrices, the state at the chunk's entry and the gradient reaching
+ *        its exit state (dk x dv fp32 each): about
+ *        (total tokens / 32 + B + 1) * H * (8 KB + 8 dk dv) bytes.
+ *
+ * Sizes: as for gdn_fwd (dk, dv in {32, 64, 128}; H <= 65535).  Pointers:
+ * the inputs and the five token gradients are required when T > 0; the
+ * workspace when B > 0.  No output may alias an input or another output.
+ *
+ * Behaviour: host-side arguments are validated first; on any error a
+ * negative status is returned and nothing is launched.  Four kernels are
+ * queued on `stream` (chunk matrices, chunk-entry states, the state
+ * gradient swept backwards over the chunks, the per-chunk token gradients);
+ * results are valid once the stream has been synchronised.  Arithmetic is
+ * fp32 throughout; results are bitwise reproducible on one device (no
+ * atomics).  The library allocates nothing and keeps no pointer.
+ */
+int gdn_bwd(const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* h0, const int32_t* cu_seqlens,
+            const void* dout, const float* dhT, void* dq, void* dk, void* dv,
+            float* dg, float* dbeta, float* dh0, void* workspace,
+            long long workspace_bytes, int B, int T, int H, int dk_, int dv_,
+            void* stream, int dtype);
+
+/*
+ * gdn_bwd_workspace_size -- bytes of workspace gdn_bwd needs for these sizes
+ * (packed != 0: T is the total token count of a packed batch of B
+ * sequences).  Returns a negative status for sizes gdn_bwd rejects.
+ */
+long long gdn_bwd_workspace_size(int B, int T, int H, int dk, int dv,
+                                 int packed);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* gdn_strerror(int status);
 

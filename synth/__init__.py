@@ -205,3 +205,35 @@ def generate(wl: Workload) -> Inputs:
 def chain_bounds(inp: Inputs, n: int):
     """(token start, token end) of sequence ``n`` in the packed layout."""
     return int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+
+
+@dataclasses.dataclass
+class OutputGrads:
+    """Seeded gradients of the forward's outputs, for the backward pass.
+
+    dout has out's layout and storage dtype (float32, or uint16 bfloat16 bit
+    patterns); dhT is float32 (B, H, dk, dv) or None.
+    """
+
+    dout: np.ndarray
+    dhT: Optional[np.ndarray]
+
+    def as_f64(self, name: str) -> Optional[np.ndarray]:
+        x = getattr(self, name)
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return bf16_bits_to_f64(x)
+        return x.astype(np.float64)
+
+
+def output_grads(inp: Inputs, seed: int, dhT_std: float = 1.0) -> OutputGrads:
+    """dout ~ N(0, 1) in v's shape and dtype, dhT ~ N(0, dhT_std^2) (None
+    when ``dhT_std`` is 0), drawn from ``default_rng(seed)`` in that order."""
+    rng = np.random.default_rng(seed)
+    wl = inp.wl
+    dout = _store(rng.standard_normal(inp.v.shape), wl.dtype)
+    dhT = None
+    if dhT_std > 0:
+        dhT = (rng.standard_normal((wl.B, wl.H, wl.dk, wl.dv)) * dhT_std).astype(np.float32)
+    return OutputGrads(dout=dout, dhT=dhT)

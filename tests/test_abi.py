@@ -23,8 +23,9 @@ def _declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_fwd",
-                                     "gdn_fwd_recurrent", "gdn_strerror", "gdn_version"]
+    assert _declared_functions() == ["gdn_bwd", "gdn_bwd_workspace_size", "gdn_diag_fwd",
+                                     "gdn_diag_fwd_recurrent", "gdn_fwd", "gdn_fwd_recurrent",
+                                     "gdn_strerror", "gdn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -169,3 +170,58 @@ def test_diag_no_chains_is_a_no_op():
         assert call(B=0) == OK
         assert call(B=0, T=0, v=0, b=0, c=0, g=0, A_log=0, out=0, hT=0) == OK
         assert call(hT=0, T=0) == INVALID
+
+
+# ------------------------------------------------------------- backward ---
+
+def _ws_floats(ttot, B, H, dk, dv):
+    nslots = ttot // 32 + B + 1
+    return H * nslots * (2 * 32 * 32 + 2 * dk * dv)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,packed", [(4, 4096, 16, 128, 128, 0), (1, 1, 1, 32, 32, 0),
+                                                (3, 100, 2, 64, 32, 1), (2, 0, 3, 32, 64, 0)])
+def test_bwd_workspace_size(B, T, H, dk, dv, packed):
+    ttot = T if packed else B * T
+    assert gdn.gdn_bwd_workspace_size(B, T, H, dk, dv, packed) == 4 * _ws_floats(ttot, B, H, dk, dv)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(B=-1), INVALID), (dict(H=0), INVALID),
+                                     (dict(dk=48), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
+                                     (dict(H=70000), UNSUPPORTED),
+                                     (dict(B=70000, T=70000), INVALID)])
+def test_bwd_workspace_size_rejects(kw, code):
+    a = dict(B=1, T=8, H=1, dk=32, dv=32, packed=0)
+    a.update(kw)
+    assert gdn.gdn_bwd_workspace_size(**a) == code
+
+
+def _bcall(**kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, dout=P, dhT=0, dq=P, dk=P, dv=P,
+             dg=P, dbeta=P, dh0=0, workspace=P, workspace_bytes=1 << 40, B=1, T=8, H=1, dk_=32,
+             dv_=32, stream=None, dtype=1)
+    a.update(kw)
+    return gdn.gdn_bwd(**a)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "dout", "dq", "dk", "dv", "dg",
+                                  "dbeta", "workspace"])
+def test_bwd_null_required_pointer(name):
+    assert _bcall(**{name: 0}) == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [(dict(B=-1), INVALID), (dict(T=-1), INVALID),
+                                     (dict(H=0), INVALID), (dict(dtype=2), INVALID),
+                                     (dict(dk_=16), UNSUPPORTED), (dict(dv_=96), UNSUPPORTED),
+                                     (dict(H=70000), UNSUPPORTED),
+                                     (dict(workspace_bytes=-1), INVALID),
+                                     (dict(workspace_bytes=4 * _ws_floats(8, 1, 1, 32, 32) - 1),
+                                      INVALID)])
+def test_bwd_invalid(kw, code):
+    assert _bcall(**kw) == code
+
+
+def test_bwd_exact_workspace_accepted_without_launch():
+    """The exact workspace size passes validation; B = 0 launches nothing."""
+    need = gdn.gdn_bwd_workspace_size(0, 8, 1, 32, 32, 0)
+    assert _bcall(B=0, workspace_bytes=need) == OK

@@ -1,0 +1,190 @@
+"""Backward entry point (gdn_bwd) vs the FP64 reverse-sweep oracle
+(``oracle.bwd``), element by element, through the C ABI.
+
+Every gradient (dq, dk, dv, dg, dbeta, dh0) is compared in the infinity
+norm relative to the oracle's largest entry of the same tensor.  The kernels
+compute in fp32 from the stored inputs, so float32 storage is held to 1e-4
+and bfloat16 storage to 2e-2 (the token gradients are rounded to bfloat16 on
+store).  Sizes span several 32-token chunks with ragged tails, both storage
+dtypes, every supported head size, packed batches with empty and one-token
+sequences, and the degenerate decays (none, and strong).
+"""
+import numpy as np
+import pytest
+
+import synth
+from hip_case import TOL, dev, host_f64
+from oracle.bwd import bwd_seq
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _run(inp, og, want_dh0=True, workspace=None):
+    import gated_deltanet_recurrence_delta_amd as gdn
+
+    grads = gdn.bwd(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                    dev(og.dout), h0=dev(inp.h0), cu_seqlens=dev(inp.cu_seqlens),
+                    dhT=dev(og.dhT), want_dh0=want_dh0, workspace=workspace)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _oracle(inp, og):
+    return bwd_seq(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), inp.as_f64("g"),
+                   inp.as_f64("beta"), inp.as_f64("h0"), inp.cu_seqlens,
+                   og.as_f64("dout"), og.as_f64("dhT"))
+
+
+def _rel(a, b):
+    if b.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(b)))
+    num = float(np.max(np.abs(a - b)))
+    return 0.0 if num == 0.0 else num / max(den, 1e-30)
+
+
+def _check(inp, og, tol=None, label=""):
+    grads = _run(inp, og)
+    ref = _oracle(inp, og)
+    tol = tol if tol is not None else TOL[inp.wl.dtype]
+    errs = {n: _rel(host_f64(grads[n]), ref[n]) for n in NAMES}
+    print(f"{label or inp.wl.name}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items())
+          + f" (tol {tol:g})", flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+    return grads
+
+
+CASES = [
+    # (dtype, B, T, H, dk, dv, h0_std, dhT_std, g_mean)
+    ("f32", 2, 75, 2, 32, 32, 0.3, 1.0, 0.0),
+    ("f32", 1, 100, 2, 64, 128, 0.0, 0.0, 0.0),
+    ("f32", 1, 64, 1, 128, 64, 0.3, 0.5, 0.0),
+    ("f32", 2, 33, 3, 128, 128, 0.2, 1.0, -2.0),
+    ("f32", 1, 1, 2, 64, 64, 0.5, 1.0, 0.0),
+    ("f32", 1, 31, 2, 32, 128, 0.0, 1.0, 0.0),
+    ("bf16", 2, 97, 2, 128, 128, 0.3, 1.0, 0.0),
+    ("bf16", 1, 130, 2, 32, 64, 0.0, 1.0, 0.0),
+    ("bf16", 1, 64, 3, 64, 32, 0.2, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_shapes(case):
+    dtype, B, T, H, dk, dv, h0, dh, gm = case
+    wl = synth.custom(name="bwd", seed=700 + CASES.index(case), B=B, T=T, H=H, dk=dk, dv=dv,
+                      dtype=dtype, h0_std=h0, g_mean=gm)
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 800 + CASES.index(case), dh))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed(dtype):
+    """Packed sequences with an empty one, a one-token one, exact and ragged
+    multiples of the chunk."""
+    wl = synth.custom(name="bwd_packed", seed=710, H=2, dk=64, dv=32, dtype=dtype,
+                      h0_std=0.3, seq_lens=(33, 0, 1, 70, 32, 5))
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 810))
+
+
+def test_packed_wide():
+    wl = synth.custom(name="bwd_packed_wide", seed=711, H=2, dk=128, dv=128, dtype="bf16",
+                      h0_std=0.2, seq_lens=(40, 95, 0, 64))
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 811))
+
+
+def test_no_decay():
+    """g = 0: nothing decays, every exponential factor is 1."""
+    wl = synth.custom(name="bwd_g0", seed=712, B=1, T=70, H=2, dk=32, dv=32, dtype="f32",
+                      h0_std=0.3)
+    inp = synth.generate(wl)
+    inp.g[...] = 0.0
+    _check(inp, synth.output_grads(inp, 812))
+
+
+def test_strong_decay():
+    """g = -30 on every token: each token forgets all earlier ones (the
+    exponential factors underflow to zero)."""
+    wl = synth.custom(name="bwd_gneg", seed=713, B=1, T=50, H=2, dk=32, dv=64, dtype="f32",
+                      h0_std=0.3)
+    inp = synth.generate(wl)
+    inp.g[...] = -30.0
+    _check(inp, synth.output_grads(inp, 813))
+
+
+def test_empty_sequences():
+    """T = 0: no token gradients; dh0 = dhT."""
+    wl = synth.custom(name="bwd_empty", seed=714, B=2, T=0, H=2, dk=32, dv=32, dtype="f32",
+                      h0_std=0.3)
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 814)
+    grads = _run(inp, og)
+    assert grads["dq"].numel() == 0
+    assert torch.equal(grads["dh0"].cpu(), torch.from_numpy(og.dhT))
+
+
+def test_packed_equals_per_sequence_bitwise():
+    """Each sequence of a packed call gets exactly the gradients of a call
+    with that sequence alone (same chunking, same arithmetic)."""
+    lens = (45, 7, 64)
+    wl = synth.custom(name="bwd_pps", seed=715, H=2, dk=64, dv=64, dtype="bf16", h0_std=0.3,
+                      seq_lens=lens)
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 815)
+    grads = _run(inp, og)
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        one = synth.Inputs(wl=wl, q=inp.q[s:e][None], k=inp.k[s:e][None], v=inp.v[s:e][None],
+                           g=inp.g[s:e][None], beta=inp.beta[s:e][None],
+                           h0=inp.h0[n:n + 1], cu_seqlens=None)
+        one_og = synth.OutputGrads(dout=og.dout[s:e][None], dhT=og.dhT[n:n + 1])
+        g1 = _run(one, one_og)
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert torch.equal(grads[name][s:e], g1[name][0]), (n, name)
+        assert torch.equal(grads["dh0"][n], g1["dh0"][0]), n
+
+
+def test_deterministic_and_optional_dh0():
+    wl = synth.custom(name="bwd_det", seed=716, B=2, T=90, H=2, dk=128, dv=64, dtype="bf16",
+                      h0_std=0.2)
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 816)
+    a = _run(inp, og)
+    b = _run(inp, og, want_dh0=False)
+    assert b["dh0"] is None
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_workspace_reuse():
+    """A caller-held workspace, used for a larger and then a smaller call,
+    gives the same results as a fresh one (nothing is carried over)."""
+    import gated_deltanet_recurrence_delta_amd as gdn
+
+    big = synth.generate(synth.custom(name="bwd_ws1", seed=717, B=2, T=80, H=2, dk=64, dv=64,
+                                      dtype="f32", h0_std=0.3))
+    small = synth.generate(synth.custom(name="bwd_ws2", seed=718, B=1, T=37, H=2, dk=64, dv=64,
+                                        dtype="f32", h0_std=0.3))
+    need = gdn.gdn_bwd_workspace_size(2, 80, 2, 64, 64, 0)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+    og_b, og_s = synth.output_grads(big, 817), synth.output_grads(small, 818)
+    ref = _run(small, og_s)
+    _run(big, og_b, workspace=ws)
+    again = _run(small, og_s, workspace=ws)
+    for name in NAMES:
+        assert torch.equal(ref[name], again[name]), name
+
+
+def test_wide_head_shape_two_chains():
+    """The wide_head shape (dk = dv = 128, bf16, nonzero h0) at 2,048 tokens,
+    two chains, every gradient against the oracle."""
+    wl = synth.custom(name="bwd_wide", seed=719, B=1, T=2048, H=2, dk=128, dv=128,
+                      dtype="bf16", h0_std=0.02)
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 819))
