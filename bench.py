@@ -16,6 +16,11 @@ FP64 oracle timed on the host cores on the same workload.
 state) times the token-by-token entry point gdn_fwd_recurrent instead;
 ``--form`` picks the entry point for any workload.
 
+``--pass bwd`` times the backward entry point gdn_bwd on the same workload
+(dq, dk, dv, dg, dbeta, dh0 from seeded output gradients dout ~ N(0,1),
+dhT ~ N(0,1)); its roofline is fp32 vector arithmetic (the backward's four
+kernels compute in fp32 on the VALU).
+
 ``--workload hymo`` / ``hymo_decode`` time the diagonal-decay additive
 recurrence with its epilogue (gdn_diag_fwd / gdn_diag_fwd_recurrent) on the
 HyMo layer's shape (B=4, T=4096, H=40, S=D=32, bf16) and on one decoding
@@ -42,6 +47,8 @@ METRIC = "gated-delta-rule fwd tokens/s + achieved HBM GB/s (% roofline), 1 MI35
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc", "gdn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wide_head.json")
 COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
+METRIC_BWD = "gated-delta-rule bwd tokens/s + achieved fp32 TFLOP/s (% roofline), 1 MI355X"
+FP32_PEAK_TFLOPS = 157.3
 METRIC_DIAG = ("diagonal-decay recurrence (HyMo GDN layer) fwd tokens/s + achieved HBM GB/s "
                "(% roofline), 1 MI355X")
 
@@ -274,6 +281,154 @@ def diag_main(args):
     print(json.dumps(rec), flush=True)
 
 
+def bwd_flops(wl: synth.Workload, lens) -> int:
+    """Floating-point operations of one gdn_bwd call as its four kernels
+    compute it (32-token chunks; 2 per multiply-add).  Per chunk of L <= 32
+    tokens (C = 32, the padded chunk), per head:
+      prep     K K^T and Q K^T (2 C^2 dk), the triangular inverse (C^3 / 6)
+      states   K M, K^T diag(w) U (2 C dk dv), T X (C^2 dv / 2)
+      adjoint  K dM', Q^T dO, K^T dX (3 C dk dv), P^T dO, T^T dU (C^2 dv)
+      grad     K M, Q M, K dM', dO M^T, dX M^T, U dM'^T (6 C dk dv),
+               T X, P^T dO, T^T dU (3 C^2 dv / 2), dX U^T, dO U^T (2 C^2 dv),
+               K K^T (C^2 dk / 2), (dP.E) K, G K, G^T K, (dP.E)^T Q (4 C^2 dk)."""
+    C, dk, dv = 32, wl.dk, wl.dv
+    per_chunk = (2 * C * C * dk + C ** 3 // 6
+                 + 2 * C * dk * dv + C * C * dv // 2
+                 + 3 * C * dk * dv + C * C * dv
+                 + 6 * C * dk * dv + 3 * C * C * dv // 2 + 2 * C * C * dv
+                 + C * C * dk // 2 + 4 * C * C * dk)
+    chunks = sum((int(n) + C - 1) // C for n in lens)
+    return 2 * per_chunk * chunks * wl.H
+
+
+def bwd_main(args):
+    """The backward pass: same protocol as ``main`` (rotated sets, HIP events
+    on the launch stream around each gdn_bwd call, sampled oracle check,
+    CPU oracle leg)."""
+    import torch
+
+    import gated_deltanet_recurrence_delta_amd as gdn
+    from oracle.bwd import bwd_seq
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from hip_case import dev, device_inputs, host_f64
+
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 1000 + wl.seed)
+    B = len(inp.cu_seqlens) - 1 if inp.cu_seqlens is not None else wl.B
+    T = int(inp.cu_seqlens[-1]) if inp.cu_seqlens is not None else wl.T
+    lens = (np.diff(inp.cu_seqlens) if inp.cu_seqlens is not None else [wl.T] * wl.B)
+    need = gdn.gdn_bwd_workspace_size(B, T, wl.H, wl.dk, wl.dv, inp.cu_seqlens is not None)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    sets = []
+    for _ in range(max(1, args.sets)):
+        d = device_inputs(inp)
+        d["dout"], d["dhT"] = dev(og.dout), dev(og.dhT)
+        for n, like in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta")):
+            d[n] = torch.empty_like(d[like])
+        d["dh0"] = torch.empty((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+    first = gdn.bwd(sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["g"], sets[0]["beta"],
+                    sets[0]["dout"], h0=sets[0]["h0"], cu_seqlens=sets[0]["cu_seqlens"],
+                    dhT=sets[0]["dhT"], workspace=ws, stream=stream)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    names = ("q", "k", "v", "g", "beta", "h0", "cu_seqlens", "dout", "dhT", "dq", "dk", "dv",
+             "dg", "dbeta", "dh0")
+    calls = [tuple(ptr(d[n]) for n in names) for d in sets]
+    dtype_code = gdn.GDN_BF16 if wl.dtype == "bf16" else gdn.GDN_F32
+    raw = gdn.load().gdn_bwd
+    tail = (ws.data_ptr(), need, B, T, wl.H, wl.dk, wl.dv, stream.cuda_stream, dtype_code)
+
+    def step(i):
+        rc = raw(*calls[i % len(calls)], *tail)
+        if rc != 0:
+            raise SystemExit(f"gdn_bwd failed with status {rc}")
+
+    torch.cuda.synchronize()
+    errs = None
+    if not args.no_parity and inp.cu_seqlens is None:
+        # oracle on two chains: (first sequence, first head), (last, last)
+        worst = {}
+        for b, h in sorted({(0, 0), (wl.B - 1, wl.H - 1)}):
+            cut = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]
+            ref = bwd_seq(*(cut(inp.as_f64(n)) for n in ("q", "k", "v", "g", "beta")),
+                          None if inp.h0 is None else inp.as_f64("h0")[b:b + 1, h:h + 1], None,
+                          cut(og.as_f64("dout")),
+                          None if og.dhT is None else og.as_f64("dhT")[b:b + 1, h:h + 1])
+            for n in ("dq", "dk", "dv", "dg", "dbeta"):
+                got = host_f64(first[n][b:b + 1, :, h:h + 1])
+                e = float(np.max(np.abs(got - ref[n])) / max(np.max(np.abs(ref[n])), 1e-30))
+                worst[n] = max(worst.get(n, 0.0), e)
+            got = host_f64(first["dh0"][b:b + 1, h:h + 1])
+            e = float(np.max(np.abs(got - ref["dh0"])) / max(np.max(np.abs(ref["dh0"])), 1e-30))
+            worst["dh0"] = max(worst.get("dh0", 0.0), e)
+        tol = 2e-2 if wl.dtype == "bf16" else 1e-4
+        if not all(e <= tol for e in worst.values()):
+            raise SystemExit(f"parity check failed: {worst}")
+        errs = worst
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(e) for a, e in zip(starts, ends)])
+    ms_per_step = wall * 1e3 / args.steps
+    mean_s = float(launch_ms.mean()) / 1e3
+    flops = bwd_flops(wl, lens)
+    achieved = flops / mean_s / 1e12
+    rec = {
+        "metric": METRIC_BWD,
+        "value": wl.tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
+                "g=-softplus(N(%g,1)), dout N(0,1), dhT N(0,1))" % wl.g_mean,
+        "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} dk={wl.dk} dv={wl.dv} "
+                               f"{wl.dtype} backward, 32-token chunks"
+                               + (" varlen" if wl.varlen else ""),
+                   "entry_point": "gdn_bwd", "tokens_per_step": wl.tokens,
+                   "rotated_sets": len(sets), "workspace_bytes": need},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "gdn_bwd, all four kernels of one call",
+                     "algorithmic_flops": flops, "mean_launch_us": mean_s * 1e6,
+                     "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
+                     "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
+                     "p90_us": float(np.percentile(launch_ms, 90)) * 1e3},
+    }
+    if errs is not None:
+        rec["parity"] = dict(errs, chains="(first sequence, first head), (last, last)")
+    if not args.no_cpu and inp.cu_seqlens is None:
+        t0 = time.perf_counter()
+        cut = lambda x: None if x is None else x[0:1, :, 0:1]
+        bwd_seq(*(cut(inp.as_f64(n)) for n in ("q", "k", "v", "g", "beta")),
+                None if inp.h0 is None else inp.as_f64("h0")[0:1, 0:1], None,
+                cut(og.as_f64("dout")), None if og.dhT is None else og.as_f64("dhT")[0:1, 0:1])
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": (wl.T / wl.H) / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one chain (first sequence, first head) of {wl.T} "
+                                         f"tokens, NumPy reverse sweep, {dt:.2f} s wall; one "
+                                         f"chain is 1/{wl.H} of a token's heads"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +443,8 @@ def main():
     ap.add_argument("--form", choices=("chunked", "recurrent"), default=None,
                     help="entry point (default: recurrent for the decode workload, "
                          "chunked otherwise)")
+    ap.add_argument("--pass", dest="direction", choices=("fwd", "bwd"), default="fwd",
+                    help="forward (default) or backward entry point")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-parity", action="store_true", help="skip the sampled parity check")
@@ -304,7 +461,11 @@ def main():
         sys.exit(2)
 
     if args.workload in sd.WORKLOADS:
+        if args.direction == "bwd":
+            raise SystemExit("the diagonal-decay form has no backward entry point")
         return diag_main(args)
+    if args.direction == "bwd":
+        return bwd_main(args)
 
     import torch
 

@@ -106,16 +106,65 @@ __device__ inline int find_seq(const int32_t* __restrict__ cu, const BShape& p, 
   return lo;
 }
 
-// In-chunk cumulative log-decay, summed in token order (every kernel forms
-// it the same way); rows past the chunk's length add nothing.
-__device__ inline void chunk_gamma(const float* __restrict__ g, long row0, int t0, int Lc, int H, int h, int tid,
-                                   float* gam) {
-  if (tid < BC) {
-    float acc = 0.f;
-    for (int u = 0; u <= tid; ++u) acc += (u < Lc) ? g[(row0 + t0 + u) * H + h] : 0.f;
-    gam[tid] = acc;
+// In-chunk cumulative log-decay: gv is token tid's g (0 past the chunk's
+// length and for tid >= C); wave 0 forms the inclusive prefix sum with a
+// fixed shuffle tree (every kernel forms it the same way) and writes gam.
+__device__ inline void chunk_gamma(float gv, int tid, float* gam) {
+  if (tid < 64) {
+    float x = gv;
+#pragma unroll
+    for (int off = 1; off < BC; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      if (tid >= off) x += y;
+    }
+    if (tid < BC) gam[tid] = x;
   }
 }
+
+__device__ inline float token_f(const float* __restrict__ x, long row0, int t0, int Lc, int H, int h, int tid) {
+  return tid < Lc ? x[(row0 + t0 + tid) * H + h] : 0.f;
+}
+
+// A chunk's C rows of a (token, head, W) tensor (columns col0 .. col0+W-1 of
+// rows of length ld), held in registers between a fetch and an LDS store;
+// rows past the chunk's length are zero.
+template <typename TI, int W>
+struct RowsReg {
+  static constexpr int N = BC * W / NT;
+  TI r[N];
+  __device__ void fetch(const TI* __restrict__ p, long row0, int t0, int Lc, int H, int h, long ld, int col0,
+                        int tid) {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      const int e = tid + NT * x, t = e / W, i = e % W;
+      r[x] = t < Lc ? p[((row0 + t0 + t) * H + h) * ld + col0 + i] : (TI)0.f;
+    }
+  }
+  __device__ void store(float (*dst)[W + 1], int tid) const {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      const int e = tid + NT * x;
+      dst[e / W][e % W] = (float)r[x];
+    }
+  }
+};
+
+// One chunk's C x C matrix from the workspace, in registers.
+struct CCReg {
+  static constexpr int N = BC * BC / NT;
+  float r[N];
+  __device__ void fetch(const float* __restrict__ p, int tid) {
+#pragma unroll
+    for (int x = 0; x < N; ++x) r[x] = p[tid + NT * x];
+  }
+  __device__ void store(float (*dst)[BC + 1], int tid) const {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      const int e = tid + NT * x;
+      dst[e / BC][e % BC] = r[x];
+    }
+  }
+};
 
 // ---------------------------------------------------------------- prep ----
 template <typename TI, int DK>
@@ -139,8 +188,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, 
     qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
     ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
   }
-  if (tid < BC) bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
-  chunk_gamma(g, row0, t0, Lc, H, h, tid, gam);
+  if (tid < BC) bet[tid] = token_f(beta, row0, t0, Lc, H, h, tid);
+  chunk_gamma(tid < BC ? token_f(g, row0, t0, Lc, H, h, tid) : 0.f, tid, gam);
   __syncthreads();
   const size_t base = ((size_t)h * p.nslots + s) * (BC * BC);
   for (int e = tid; e < BC * BC; e += NT) {
@@ -179,7 +228,7 @@ struct Owner {
 };
 
 template <typename TI, int DK>
-__global__ __launch_bounds__(NT) void bwd_states_kernel(const TI* __restrict__ k, const TI* __restrict__ v,
+__global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict__ k, const TI* __restrict__ v,
                                                         const float* __restrict__ g,
                                                         const float* __restrict__ beta,
                                                         const float* __restrict__ h0,
@@ -202,6 +251,23 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const TI* __restrict__ k
   for (int r = 0; r < JP; ++r) M[r] = h0 ? h0[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] : 0.f;
   const int yt = tid >> 3, yj = (tid & 7) * 2;  // (token, column pair) mapping
 
+  // the next chunk's inputs, fetched into registers while this one computes
+  RowsReg<TI, DK> kr;
+  RowsReg<TI, TW> vr;
+  CCReg tr;
+  float gr = 0.f, br = 0.f;
+  auto fetch = [&](int c) {
+    const int t0 = c * BC, Lc = min(BC, len - t0);
+    kr.fetch(k, row0, t0, Lc, H, h, DK, 0, tid);
+    vr.fetch(v, row0, t0, Lc, H, h, dv, col0, tid);
+    tr.fetch(wsT + ((size_t)h * p.nslots + key + c) * (BC * BC), tid);
+    if (tid < BC) {
+      gr = token_f(g, row0, t0, Lc, H, h, tid);
+      br = token_f(beta, row0, t0, Lc, H, h, tid);
+    }
+  };
+  if (nch > 0) fetch(0);
+
   for (int c = 0; c < nch; ++c) {
     const size_t sb = (size_t)h * p.nslots + key + c;
     float* mo = wsM + sb * DK * dv;
@@ -210,21 +276,16 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const TI* __restrict__ k
       mo[(long)o.si * dv + col0 + o.sj0 + r] = M[r];
       Ms[o.si][o.sj0 + r] = M[r];
     }
-    const int t0 = c * BC, Lc = min(BC, len - t0);
-    for (int e = tid; e < BC * DK; e += NT) {
-      const int t = e / DK, i = e % DK;
-      ks[t][i] = t < Lc ? ldf(k, ((row0 + t0 + t) * H + h) * DK + i) : 0.f;
-    }
-    for (int e = tid; e < BC * TW; e += NT) {
-      const int t = e / TW, j = e % TW;
-      vs[t][j] = t < Lc ? ldf(v, ((row0 + t0 + t) * H + h) * (long)dv + col0 + j) : 0.f;
-    }
-    for (int e = tid; e < BC * BC; e += NT) Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
-    if (tid < BC) bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
-    chunk_gamma(g, row0, t0, Lc, H, h, tid, gam);
+    kr.store(ks, tid);
+    vr.store(vs, tid);
+    tr.store(Ts, tid);
+    if (tid < BC) bet[tid] = br;
+    chunk_gamma(gr, tid, gam);
+    if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
     {  // X = beta (V - Gam K M)
       float y0 = 0.f, y1 = 0.f;
+#pragma unroll 8
       for (int i = 0; i < DK; ++i) {
         const float kv = ks[yt][i];
         y0 = __builtin_fmaf(kv, Ms[i][yj], y0);
@@ -251,6 +312,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const TI* __restrict__ k
 #pragma unroll
     for (int r = 0; r < JP; ++r) {
       float acc = 0.f;
+#pragma unroll 8
       for (int t = 0; t < BC; ++t) acc = __builtin_fmaf(ks[t][o.si], vs[t][o.sj0 + r], acc);
       M[r] = __builtin_fmaf(GC, M[r], acc);
     }
@@ -260,7 +322,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const TI* __restrict__ k
 
 // ------------------------------------------------------------- adjoint ----
 template <typename TI, int DK>
-__global__ __launch_bounds__(NT) void bwd_adjoint_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+__global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                                                          const TI* __restrict__ dO, const float* __restrict__ g,
                                                          const float* __restrict__ beta,
                                                          const float* __restrict__ dhT,
@@ -285,6 +347,26 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(const TI* __restrict__ 
   for (int r = 0; r < JP; ++r) D[r] = dhT ? dhT[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] : 0.f;
   const int yt = tid >> 3, yj = (tid & 7) * 2;
 
+  // the previous chunk's inputs, fetched into registers while this one computes
+  RowsReg<TI, DK> qr, kr;
+  RowsReg<TI, TW> dr;
+  CCReg tr, pr;
+  float gr = 0.f, br = 0.f;
+  auto fetch = [&](int c) {
+    const int t0 = c * BC, Lc = min(BC, len - t0);
+    qr.fetch(q, row0, t0, Lc, H, h, DK, 0, tid);
+    kr.fetch(k, row0, t0, Lc, H, h, DK, 0, tid);
+    dr.fetch(dO, row0, t0, Lc, H, h, dv, col0, tid);
+    const size_t sb = (size_t)h * p.nslots + key + c;
+    tr.fetch(wsT + sb * (BC * BC), tid);
+    pr.fetch(wsP + sb * (BC * BC), tid);
+    if (tid < BC) {
+      gr = token_f(g, row0, t0, Lc, H, h, tid);
+      br = token_f(beta, row0, t0, Lc, H, h, tid);
+    }
+  };
+  if (nch > 0) fetch(nch - 1);
+
   for (int c = nch - 1; c >= 0; --c) {
     const size_t sb = (size_t)h * p.nslots + key + c;
     float* dout = wsD + sb * DK * dv;
@@ -293,26 +375,18 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(const TI* __restrict__ 
       dout[(long)o.si * dv + col0 + o.sj0 + r] = D[r];
       Ds[o.si][o.sj0 + r] = D[r];
     }
-    const int t0 = c * BC, Lc = min(BC, len - t0);
-    for (int e = tid; e < BC * DK; e += NT) {
-      const int t = e / DK, i = e % DK;
-      const long off = ((row0 + t0 + t) * H + h) * DK + i;
-      qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
-      ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
-    }
-    for (int e = tid; e < BC * TW; e += NT) {
-      const int t = e / TW, j = e % TW;
-      ds[t][j] = t < Lc ? ldf(dO, ((row0 + t0 + t) * H + h) * (long)dv + col0 + j) : 0.f;
-    }
-    for (int e = tid; e < BC * BC; e += NT) {
-      Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
-      Ps[e / BC][e % BC] = wsP[sb * (BC * BC) + e];
-    }
-    if (tid < BC) bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
-    chunk_gamma(g, row0, t0, Lc, H, h, tid, gam);
+    qr.store(qs, tid);
+    kr.store(ks, tid);
+    dr.store(ds, tid);
+    tr.store(Ts, tid);
+    pr.store(Ps, tid);
+    if (tid < BC) bet[tid] = br;
+    chunk_gamma(gr, tid, gam);
+    if (c > 0) fetch(c - 1);
     __syncthreads();
     {  // dU = P^T dO + diag(w) K dM'
       float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll 8
       for (int i = 0; i < DK; ++i) {
         const float kv = ks[yt][i];
         a0 = __builtin_fmaf(kv, Ds[i][yj], a0);
@@ -346,6 +420,7 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(const TI* __restrict__ 
 #pragma unroll
     for (int r = 0; r < JP; ++r) {
       float acc = 0.f;
+#pragma unroll 8
       for (int t = 0; t < BC; ++t) {
         acc = __builtin_fmaf(qs[t][o.si], ds[t][o.sj0 + r], acc);
         acc = __builtin_fmaf(-ks[t][o.si], Zs[t][o.sj0 + r], acc);
@@ -379,7 +454,7 @@ struct GradLds {
 };
 
 template <typename TI, int DK>
-__global__ __launch_bounds__(NT) void bwd_grad_kernel(
+__global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const TI* __restrict__ dO,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const float* __restrict__ wsT, const float* __restrict__ wsP, const float* __restrict__ wsM,
@@ -407,8 +482,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     L.Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
     L.Ps[e / BC][e % BC] = wsP[sb * (BC * BC) + e];
   }
-  if (tid < BC) L.bet[tid] = tid < Lc ? beta[(row0 + t0 + tid) * H + h] : 0.f;
-  chunk_gamma(g, row0, t0, Lc, H, h, tid, L.gam);
+  if (tid < BC) L.bet[tid] = token_f(beta, row0, t0, Lc, H, h, tid);
+  chunk_gamma(tid < BC ? token_f(g, row0, t0, Lc, H, h, tid) : 0.f, tid, L.gam);
 
   const int yt = tid >> 3, yl = tid & 7, yj = yl * 2;
   const Owner<DK> o(tid);
