@@ -147,6 +147,14 @@ struct RowsReg {
       dst[e / W][e % W] = (float)r[x];
     }
   }
+  template <int S>
+  __device__ void store_s(float (*dst)[S], int tid) const {
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+      const int e = tid + NT * x;
+      dst[e / W][e % W] = (float)r[x];
+    }
+  }
 };
 
 // One chunk's C x C matrix from the workspace, in registers.
@@ -436,21 +444,36 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
 }
 
 // ---------------------------------------------------------------- grad ----
-template <int DK>
+// The products run on the fp32 matrix cores: v_mfma_f32_16x16x4f32 takes
+// A (16 x 4) and B (4 x 16) one element per lane -- lane l holds A[l % 16][l / 16]
+// and B[l / 16][l % 16] -- and accumulates D (16 x 16), of which lane l holds
+// rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.  LDS rows are padded to
+// a stride of 8 mod 64 words, which keeps both operand read patterns (down a
+// column, along a row) within two-way bank conflicts.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int SC = BC + 8;  // row stride of the C x C arrays
+constexpr int ST = TW + 8;  // row stride of the tile arrays
+
+template <typename TI, int DK>
 struct GradLds {
-  float qs[BC][DK + 1], ks[BC][DK + 1];
-  float Ts[BC][BC + 1], Ps[BC][BC + 1];
+  static constexpr int SK = DK + 8;
+  TI qs[BC][SK], ks[BC][SK];  // stored as given (bf16 is widened on read)
+  float Ts[BC][SC], Ps[BC][SC];
   union {
     struct {
-      float Mt[DK][TW + 1], Dt[DK][TW + 1];
+      float Mt[DK][ST], Dt[DK][ST];
     } tile;
     struct {
-      float Gs[BC][BC + 1], dPs[BC][BC + 1], Zs[BC][BC + 1];
+      float Gs[BC][SC], dPs[BC][SC], Zs[BC][SC], Bs[BC][SC];
     } fin;
   } u;
-  float vt[BC][TW + 1], dot[BC][TW + 1], Yt[BC][TW + 1], QMt[BC][TW + 1], KDt[BC][TW + 1];
-  float Xt[BC][TW + 1], Ut[BC][TW + 1], dUt[BC][TW + 1], dXt[BC][TW + 1];
-  float gam[BC], bet[BC], sb1[BC], sg1[BC], sw[BC], sb2[BC], red[NT / 64];
+  float vt[BC][ST], dot[BC][ST], Yt[BC][ST], KDt[BC][ST], Xt[BC][ST], Ut[BC][ST], dUt[BC][ST], dXt[BC][ST];
+  float gam[BC], bet[BC], sgA[BC], sgB[BC], sb1[BC], sw[BC], red[NT / 64];
 };
 
 template <typename TI, int DK>
@@ -460,9 +483,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
     const float* __restrict__ wsT, const float* __restrict__ wsP, const float* __restrict__ wsM,
     const float* __restrict__ wsD, TI* __restrict__ dq, TI* __restrict__ dk, TI* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta, const BShape p) {
-  constexpr int JQ = DK / 8;  // dq / dk entries per thread: token yt, key columns (tid & 7) + 8 r
+  constexpr int NB = DK / 8 / 4;  // 16x16 blocks of the C x DK gradients per wave
   constexpr int JP = Owner<DK>::JP;
-  __shared__ GradLds<DK> L;
+  __shared__ GradLds<TI, DK> L;
   const int tid = threadIdx.x, s = blockIdx.x, h = blockIdx.y, H = p.H, dvn = p.dv;
   const int n = find_seq(cu, p, s);
   long row0;
@@ -475,8 +498,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
   for (int e = tid; e < BC * DK; e += NT) {
     const int t = e / DK, i = e % DK;
     const long off = ((row0 + t0 + t) * H + h) * DK + i;
-    L.qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
-    L.ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
+    L.qs[t][i] = t < Lc ? q[off] : (TI)0.f;
+    L.ks[t][i] = t < Lc ? k[off] : (TI)0.f;
   }
   for (int e = tid; e < BC * BC; e += NT) {
     L.Ts[e / BC][e % BC] = wsT[sb * (BC * BC) + e];
@@ -484,211 +507,221 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
   }
   if (tid < BC) L.bet[tid] = token_f(beta, row0, t0, Lc, H, h, tid);
   chunk_gamma(tid < BC ? token_f(g, row0, t0, Lc, H, h, tid) : 0.f, tid, L.gam);
+  auto kf = [&](int r, int i) { return (float)L.ks[r][i]; };
+  auto qf = [&](int r, int i) { return (float)L.qs[r][i]; };
 
-  const int yt = tid >> 3, yl = tid & 7, yj = yl * 2;
+  const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
+  const int rb = wave & 1;          // row block of the tile phases
+  const int r16 = 16 * rb + ln;     // the lane's A-operand row in those phases
   const Owner<DK> o(tid);
-  float dQa[JQ], dKa[JQ], dXU[4], dOU[4];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accQ[NB], accK[NB], accXU = zero, accOU = zero;
 #pragma unroll
-  for (int r = 0; r < JQ; ++r) dQa[r] = dKa[r] = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) dXU[r] = dOU[r] = 0.f;
-  float sb1 = 0.f, sg1 = 0.f, sw = 0.f, sGC = 0.f;
+  for (int m = 0; m < NB; ++m) accQ[m] = accK[m] = zero;
+  float pA[4] = {0.f, 0.f, 0.f, 0.f}, pB[4] = {0.f, 0.f, 0.f, 0.f};  // per-row partial sums
+  float sGC = 0.f;
   const float* mbase = wsM + sb * DK * dvn;
   const float* dbase = wsD + sb * DK * dvn;
+  // the next tile's entry state, exit gradient, v and dO, fetched into
+  // registers while this one computes
+  constexpr int NS = DK * TW / NT;
+  float mr[NS], dr[NS];
+  RowsReg<TI, TW> vr, orr;
+  auto fetch = [&](int tile) {
+    const int col0 = tile * TW;
+#pragma unroll
+    for (int x = 0; x < NS; ++x) {
+      const int e = tid + NT * x, i = e / TW, j = e % TW;
+      mr[x] = mbase[(long)i * dvn + col0 + j];
+      dr[x] = dbase[(long)i * dvn + col0 + j];
+    }
+    vr.fetch(v, row0, t0, Lc, H, h, dvn, col0, tid);
+    orr.fetch(dO, row0, t0, Lc, H, h, dvn, col0, tid);
+  };
+  fetch(0);
 
   for (int tile = 0; tile < p.ntile; ++tile) {
     const int col0 = tile * TW;
     __syncthreads();  // the previous tile's readers are done
-    for (int e = tid; e < DK * TW; e += NT) {
-      const int i = e / TW, j = e % TW;
-      L.u.tile.Mt[i][j] = mbase[(long)i * dvn + col0 + j];
-      L.u.tile.Dt[i][j] = dbase[(long)i * dvn + col0 + j];
-    }
-    for (int e = tid; e < BC * TW; e += NT) {
-      const int t = e / TW, j = e % TW;
-      const long off = ((row0 + t0 + t) * H + h) * (long)dvn + col0 + j;
-      L.vt[t][j] = t < Lc ? ldf(v, off) : 0.f;
-      L.dot[t][j] = t < Lc ? ldf(dO, off) : 0.f;
-    }
-    __syncthreads();
-    const float G = ex(L.gam[yt]), bt = L.bet[yt], w = ex(L.gam[BC - 1] - L.gam[yt]);
-    {  // Y = K M, QM = Q M, KD = K dM', X = beta (V - Gam Y)
-      float y[2] = {0.f, 0.f}, qm[2] = {0.f, 0.f}, kd[2] = {0.f, 0.f};
-#pragma unroll 4
-      for (int i = 0; i < DK; ++i) {
-        const float kv = L.ks[yt][i], qv = L.qs[yt][i];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const float m = L.u.tile.Mt[i][yj + x], d = L.u.tile.Dt[i][yj + x];
-          y[x] = __builtin_fmaf(kv, m, y[x]);
-          qm[x] = __builtin_fmaf(qv, m, qm[x]);
-          kd[x] = __builtin_fmaf(kv, d, kd[x]);
-        }
+    for (int x = 0; x < NS; ++x) {
+      const int e = tid + NT * x, i = e / TW, j = e % TW;
+      L.u.tile.Mt[i][j] = mr[x];
+      L.u.tile.Dt[i][j] = dr[x];
+    }
+    vr.template store_s<ST>(L.vt, tid);
+    orr.template store_s<ST>(L.dot, tid);
+    if (tile + 1 < p.ntile) fetch(tile + 1);
+    __syncthreads();
+    // phase A.  waves 0, 1: Y = K M and QM = Q M on row block rb, then X;
+    //           waves 2, 3: KD = K dM' and P^T dO on row block rb, then dU.
+    if (wave < 2) {
+      f32x4 y = zero, qm = zero;
+#pragma unroll 8
+      for (int kk = 0; kk < DK; kk += 4) {
+        const float b = L.u.tile.Mt[kk + lq][ln];
+        y = mfma4(kf(r16, kk + lq), b, y);
+        qm = mfma4(qf(r16, kk + lq), b, qm);
       }
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        L.Yt[yt][yj + x] = y[x];
-        L.QMt[yt][yj + x] = qm[x];
-        L.KDt[yt][yj + x] = kd[x];
-        L.Xt[yt][yj + x] = bt * (L.vt[yt][yj + x] - G * y[x]);
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * rb + 4 * lq + x;
+        L.Yt[t][ln] = y[x];
+        L.Xt[t][ln] = L.bet[t] * (L.vt[t][ln] - ex(L.gam[t]) * y[x]);
+        pA[x] = __builtin_fmaf(L.dot[t][ln], qm[x], pA[x]);  // dO . QM
       }
-    }
-    __syncthreads();
-    {  // U = T X, dU = P^T dO + diag(w) KD
+    } else {
+      f32x4 kd = zero, pd = zero;
+#pragma unroll 8
+      for (int kk = 0; kk < DK; kk += 4) kd = mfma4(kf(r16, kk + lq), L.u.tile.Dt[kk + lq][ln], kd);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        float uu = 0.f, du = 0.f;
-        for (int r = 0; r <= yt; ++r) uu = __builtin_fmaf(L.Ts[yt][r], L.Xt[r][yj + x], uu);
-        for (int r = yt; r < BC; ++r) du = __builtin_fmaf(L.Ps[r][yt], L.dot[r][yj + x], du);
-        L.Ut[yt][yj + x] = uu;
-        L.dUt[yt][yj + x] = __builtin_fmaf(w, L.KDt[yt][yj + x], du);
+      for (int kk = 0; kk < BC; kk += 4) pd = mfma4(L.Ps[kk + lq][r16], L.dot[kk + lq][ln], pd);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * rb + 4 * lq + x;
+        L.KDt[t][ln] = kd[x];
+        L.dUt[t][ln] = __builtin_fmaf(ex(L.gam[BC - 1] - L.gam[t]), kd[x], pd[x]);
       }
     }
     __syncthreads();
-    {  // dX = T^T dU, dV, and the per-token sums
+    // phase B.  waves 0, 1: U = T X;  waves 2, 3: dX = T^T dU, dV.
+    if (wave < 2) {
+      f32x4 uu = zero;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        float dx = 0.f;
-        for (int r = yt; r < BC; ++r) dx = __builtin_fmaf(L.Ts[r][yt], L.dUt[r][yj + x], dx);
-        L.dXt[yt][yj + x] = dx;
-        const float yv = L.Yt[yt][yj + x];
-        sb1 = __builtin_fmaf(dx, L.vt[yt][yj + x] - G * yv, sb1);
-        sg1 = __builtin_fmaf(-bt * dx, yv, sg1);
-        sg1 = __builtin_fmaf(L.dot[yt][yj + x], L.QMt[yt][yj + x], sg1);
-        sw = __builtin_fmaf(L.Ut[yt][yj + x], L.KDt[yt][yj + x], sw);
-        if (yt < Lc) dv[((row0 + t0 + yt) * H + h) * (long)dvn + col0 + yj + x] = (TI)(bt * dx);
+      for (int kk = 0; kk < BC; kk += 4) uu = mfma4(L.Ts[r16][kk + lq], L.Xt[kk + lq][ln], uu);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * rb + 4 * lq + x;
+        L.Ut[t][ln] = uu[x];
+        pB[x] = __builtin_fmaf(uu[x], L.KDt[t][ln], pB[x]);  // U . KD
+      }
+    } else {
+      f32x4 dx = zero;
+#pragma unroll
+      for (int kk = 0; kk < BC; kk += 4) dx = mfma4(L.Ts[kk + lq][r16], L.dUt[kk + lq][ln], dx);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * rb + 4 * lq + x;
+        const float bt = L.bet[t], yv = L.Yt[t][ln];
+        L.dXt[t][ln] = dx[x];
+        pA[x] = __builtin_fmaf(dx[x], L.vt[t][ln] - ex(L.gam[t]) * yv, pA[x]);  // dX . R
+        pB[x] = __builtin_fmaf(-bt * dx[x], yv, pB[x]);                        // -beta dX . Y
+        if (t < Lc) dv[((row0 + t0 + t) * H + h) * (long)dvn + col0 + ln] = (TI)(bt * dx[x]);
       }
     }
 #pragma unroll
     for (int r = 0; r < JP; ++r)
       sGC = __builtin_fmaf(L.u.tile.Mt[o.si][o.sj0 + r], L.u.tile.Dt[o.si][o.sj0 + r], sGC);
     __syncthreads();
-    // C x C accumulations over the tile's columns
+    // phase C, all waves.  dX U^T and dO U^T (C x C, block `wave`), and
+    // dQ += diag(Gam) dO M^T, dK += -diag(beta Gam) dX M^T + diag(w) U dM'^T
+    // (C x DK, blocks wave + 4 m).
     {
-      float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int j = 0; j < TW; ++j) {
-        const float xv = L.dXt[yt][j], ov = L.dot[yt][j];
+      const int cr = 16 * (wave >> 1) + ln, cc = 16 * (wave & 1) + ln;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float uv = L.Ut[yl + 8 * r][j];
-          a[r] = __builtin_fmaf(xv, uv, a[r]);
-          b[r] = __builtin_fmaf(ov, uv, b[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        dXU[r] += a[r];
-        dOU[r] += b[r];
+      for (int kk = 0; kk < TW; kk += 4) {
+        const float b = L.Ut[cc][kk + lq];
+        accXU = mfma4(L.dXt[cr][kk + lq], b, accXU);
+        accOU = mfma4(L.dot[cr][kk + lq], b, accOU);
       }
     }
-    {  // dQ += Gam dO M^T;  dK += -beta Gam dX M^T + w U dM'^T
-      float a[JQ], b[JQ], d[JQ];
 #pragma unroll
-      for (int r = 0; r < JQ; ++r) a[r] = b[r] = d[r] = 0.f;
-#pragma unroll 2
-      for (int j = 0; j < TW; ++j) {
-        const float ov = L.dot[yt][j], xv = L.dXt[yt][j], uv = L.Ut[yt][j];
+    for (int m = 0; m < NB; ++m) {
+      const int blk = wave + 4 * m, br = 16 * (blk & 1) + ln, bc = 16 * (blk >> 1) + ln;
+      const float G = ex(L.gam[br]), bg = -L.bet[br] * G, w = ex(L.gam[BC - 1] - L.gam[br]);
 #pragma unroll
-        for (int r = 0; r < JQ; ++r) {
-          const float m = L.u.tile.Mt[yl + 8 * r][j];
-          a[r] = __builtin_fmaf(ov, m, a[r]);
-          b[r] = __builtin_fmaf(xv, m, b[r]);
-          d[r] = __builtin_fmaf(uv, L.u.tile.Dt[yl + 8 * r][j], d[r]);
-        }
-      }
-      const float bg = -bt * G;
-#pragma unroll
-      for (int r = 0; r < JQ; ++r) {
-        dQa[r] = __builtin_fmaf(G, a[r], dQa[r]);
-        dKa[r] = __builtin_fmaf(bg, b[r], dKa[r]);
-        dKa[r] = __builtin_fmaf(w, d[r], dKa[r]);
+      for (int kk = 0; kk < TW; kk += 4) {
+        const float mv = L.u.tile.Mt[bc][kk + lq], dd = L.u.tile.Dt[bc][kk + lq];
+        accQ[m] = mfma4(G * L.dot[br][kk + lq], mv, accQ[m]);
+        accK[m] = mfma4(bg * L.dXt[br][kk + lq], mv, accK[m]);
+        accK[m] = mfma4(w * L.Ut[br][kk + lq], dd, accK[m]);
       }
     }
   }
-  // lane sums over the 8 threads of a token (lanes yt*8 .. yt*8+7 of one wave)
+  // per-row partial sums: reduce over the 16 lanes of a row group
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    sb1 += __shfl_xor(sb1, m);
-    sg1 += __shfl_xor(sg1, m);
-    sw += __shfl_xor(sw, m);
+  for (int x = 0; x < 4; ++x) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      pA[x] += __shfl_xor(pA[x], m);
+      pB[x] += __shfl_xor(pB[x], m);
+    }
   }
-  // <M, dM'> over the whole state: wave sums, then the workgroup's
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) sGC += __shfl_xor(sGC, m);
   __syncthreads();  // the last tile's readers of Mt / Dt are done (fin reuses them)
-  if (yl == 0) {
-    L.sb1[yt] = sb1;
-    L.sg1[yt] = sg1;
-    L.sw[yt] = sw;
-  }
-  if ((tid & 63) == 0) L.red[tid >> 6] = sGC;
-  {  // dA, G, dP . E, Z and the second dbeta term
-    const float gt = L.gam[yt], bt = L.bet[yt];
-    float sb2 = 0.f;
+  if (ln == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int uu = yl + 8 * r;
-      float kk = 0.f;
-      if (uu < yt)
-#pragma unroll 4
-        for (int i = 0; i < DK; ++i) kk = __builtin_fmaf(L.ks[yt][i], L.ks[uu][i], kk);
-      const float E = uu <= yt ? ex(gt - L.gam[uu]) : 0.f;
-      const float dA = uu < yt ? -dXU[r] : 0.f;
-      const float kke = kk * E;
-      const float dP = uu <= yt ? dOU[r] : 0.f;
-      L.u.fin.Gs[yt][uu] = dA * E * bt;
-      L.u.fin.dPs[yt][uu] = dP * E;
-      // the diagonal adds to a token's row and column alike: left out
-      L.u.fin.Zs[yt][uu] = uu < yt ? __builtin_fmaf(dA, bt * kke, dP * L.Ps[yt][uu]) : 0.f;
-      sb2 = __builtin_fmaf(dA, kke, sb2);
-    }
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) sb2 += __shfl_xor(sb2, m);
-    if (yl == 0) L.sb2[yt] = sb2;
-  }
-  __syncthreads();
-  {  // dQ += (dP . E) K;  dK += G K + G^T K + (dP . E)^T Q
-    float a[JQ], b[JQ];
-#pragma unroll
-    for (int r = 0; r < JQ; ++r) a[r] = b[r] = 0.f;
-#pragma unroll 2
-    for (int uu = 0; uu < BC; ++uu) {
-      const float pe = L.u.fin.dPs[yt][uu], gg = L.u.fin.Gs[yt][uu] + L.u.fin.Gs[uu][yt];
-      const float pt = L.u.fin.dPs[uu][yt];
-#pragma unroll
-      for (int r = 0; r < JQ; ++r) {
-        const float kv = L.ks[uu][yl + 8 * r];
-        a[r] = __builtin_fmaf(pe, kv, a[r]);
-        b[r] = __builtin_fmaf(gg, kv, b[r]);
-        b[r] = __builtin_fmaf(pt, L.qs[uu][yl + 8 * r], b[r]);
+    for (int x = 0; x < 4; ++x) {
+      const int t = 16 * rb + 4 * lq + x;
+      if (wave < 2) {
+        L.sgA[t] = pA[x];  // dO . QM
+        L.sw[t] = pB[x];   // U . KD
+      } else {
+        L.sb1[t] = pA[x];  // dX . R
+        L.sgB[t] = pB[x];  // -beta dX . Y
       }
     }
+  }
+  if ((tid & 63) == 0) L.red[wave] = sGC;
+  {  // K K^T on block `wave`, then dA, G, dP . E, Z and the second dbeta term
+    const int tr0 = 16 * (wave >> 1), uc = 16 * (wave & 1) + ln;
+    f32x4 kk4 = zero;
+#pragma unroll 8
+    for (int kk = 0; kk < DK; kk += 4) kk4 = mfma4(kf(tr0 + ln, kk + lq), kf(uc, kk + lq), kk4);
 #pragma unroll
-    for (int r = 0; r < JQ; ++r) {
-      dQa[r] += a[r];
-      dKa[r] += b[r];
-      if (yt < Lc) {
-        const long off = ((row0 + t0 + yt) * H + h) * DK + yl + 8 * r;
-        dq[off] = (TI)dQa[r];
-        dk[off] = (TI)dKa[r];
+    for (int x = 0; x < 4; ++x) {
+      const int t = tr0 + 4 * lq + x;
+      const float bt = L.bet[t];
+      const float E = uc <= t ? ex(L.gam[t] - L.gam[uc]) : 0.f;
+      const float dA = uc < t ? -accXU[x] : 0.f;
+      const float kke = kk4[x] * E;
+      const float dP = uc <= t ? accOU[x] : 0.f;
+      L.u.fin.Gs[t][uc] = dA * E * bt;
+      L.u.fin.dPs[t][uc] = dP * E;
+      // the diagonal adds to a token's row and column alike: left out
+      L.u.fin.Zs[t][uc] = uc < t ? __builtin_fmaf(dA, bt * kke, dP * L.Ps[t][uc]) : 0.f;
+      L.u.fin.Bs[t][uc] = dA * kke;
+    }
+  }
+  __syncthreads();
+  // dQ += (dP . E) K;  dK += (G + G^T) K + (dP . E)^T Q
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int blk = wave + 4 * m, br = 16 * (blk & 1), bc = 16 * (blk >> 1) + ln;
+#pragma unroll
+    for (int kk = 0; kk < BC; kk += 4) {
+      const int r = kk + lq;
+      const float kv = kf(r, bc), qv = qf(r, bc);
+      accQ[m] = mfma4(L.u.fin.dPs[br + ln][r], kv, accQ[m]);
+      accK[m] = mfma4(L.u.fin.Gs[br + ln][r] + L.u.fin.Gs[r][br + ln], kv, accK[m]);
+      accK[m] = mfma4(L.u.fin.dPs[r][br + ln], qv, accK[m]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int t = br + 4 * lq + x;
+      if (t < Lc) {
+        const long off = ((row0 + t0 + t) * H + h) * DK + bc;
+        dq[off] = (TI)accQ[m][x];
+        dk[off] = (TI)accK[m][x];
       }
     }
   }
   if (tid < BC) {  // per-token terms
     const int t = tid, last = Lc - 1;
-    float rz = 0.f, cz = 0.f;
+    float rz = 0.f, cz = 0.f, b2 = 0.f;
     for (int uu = 0; uu < BC; ++uu) {
       rz += L.u.fin.Zs[t][uu];
       cz += L.u.fin.Zs[uu][t];
+      b2 += L.u.fin.Bs[t][uu];
     }
     float gc = 0.f;
     for (int wv = 0; wv < NT / 64; ++wv) gc += L.red[wv];
     const float Gt = ex(L.gam[t]), wt = ex(L.gam[BC - 1] - L.gam[t]);
-    const float dGam = L.sg1[t] + (t == last ? gc : 0.f);
-    L.sb1[t] += L.sb2[t];                      // dbeta, kept in place
-    L.sg1[t] = __builtin_fmaf(dGam, Gt, rz - cz);  // dgamma without the w terms, in place
-    L.sw[t] *= wt;                             // dw . w, in place
+    const float dGam = L.sgA[t] + L.sgB[t] + (t == last ? gc : 0.f);
+    L.sb1[t] += b2;                                // dbeta, in place
+    L.sgA[t] = __builtin_fmaf(dGam, Gt, rz - cz);  // dgamma without the w terms, in place
+    L.sw[t] *= wt;                                 // dw . w, in place
   }
   __syncthreads();
   // dg_t = sum_{u >= t} dgamma_u.  The w terms (-dw_u w_u at every token,
@@ -698,7 +731,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
   if (tid < Lc) {
     const int t = tid;
     float acc = 0.f;
-    for (int uu = Lc - 1; uu >= t; --uu) acc += L.sg1[uu];
+    for (int uu = Lc - 1; uu >= t; --uu) acc += L.sgA[uu];
     for (int uu = 0; uu < t; ++uu) acc += L.sw[uu];
     const long th = (row0 + t0 + t) * H + h;
     dg[th] = acc;
