@@ -165,7 +165,8 @@ struct CCReg {
 #pragma unroll
     for (int x = 0; x < N; ++x) r[x] = p[tid + NT * x];
   }
-  __device__ void store(float (*dst)[BC + 1], int tid) const {
+  template <int S>
+  __device__ void store_s(float (*dst)[S], int tid) const {
 #pragma unroll
     for (int x = 0; x < N; ++x) {
       const int e = tid + NT * x;
@@ -225,8 +226,23 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, 
   for (int e = tid; e < BC * BC; e += NT) wsT[base + e] = Ts[e / BC][e % BC];
 }
 
-// -------------------------------------------------------------- states ----
-// State owner mapping for a DK x TW tile: thread -> row si, columns
+// ------------------------------------------------------- matrix cores ----
+// The products run on the fp32 matrix cores: v_mfma_f32_16x16x4f32 takes
+// A (16 x 4) and B (4 x 16) one element per lane -- lane l holds A[l % 16][l / 16]
+// and B[l / 16][l % 16] -- and accumulates D (16 x 16), of which lane l holds
+// rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.  LDS rows are padded to
+// a stride of 8 mod 64 words, which keeps both operand read patterns (down a
+// column, along a row) within two-way bank conflicts.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int SC = BC + 8;  // row stride of the C x C arrays
+constexpr int ST = TW + 8;  // row stride of the tile arrays
+
+// A plain owner mapping of a DK x TW tile: thread -> row si, columns
 // sj0 .. sj0 + JP - 1.
 template <int DK>
 struct Owner {
@@ -235,17 +251,47 @@ struct Owner {
   __device__ Owner(int tid) : si(tid % DK), sj0((tid / DK) * JP) {}
 };
 
+// -------------------------------------------------------------- states ----
+// The state tile M (DK x 16) is held in matrix-core accumulator layout:
+// 16-row block b of it belongs to wave b mod 4, lane l holding rows
+// 16 b + 4 (l / 16) .. + 3 of column l % 16.
+template <int DK>
+struct StateBlocks {
+  static constexpr int NBM = DK / 16;            // 16-row blocks of the tile
+  static constexpr int PER = (NBM + 3) / 4;      // blocks per wave (some waves may own fewer)
+};
+
+// Wave 0 forms the chunk's cumulative log-decay gam (see chunk_gamma), and
+// from it Gam_t = exp(gam_t) and w_t = exp(gam_{C-1} - gam_t).
+__device__ inline void chunk_decay(float gv, int tid, float* gam, float* Gam, float* wv) {
+  if (tid < 64) {
+    float x = gv;
+#pragma unroll
+    for (int off = 1; off < BC; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      if (tid >= off) x += y;
+    }
+    const float last = __shfl(x, BC - 1, 64);
+    if (tid < BC) {
+      gam[tid] = x;
+      Gam[tid] = ex(x);
+      wv[tid] = ex(last - x);
+    }
+  }
+}
+
 template <typename TI, int DK>
 __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict__ k, const TI* __restrict__ v,
-                                                        const float* __restrict__ g,
-                                                        const float* __restrict__ beta,
-                                                        const float* __restrict__ h0,
-                                                        const int32_t* __restrict__ cu,
-                                                        const float* __restrict__ wsT, float* __restrict__ wsM,
-                                                        const BShape p) {
-  constexpr int JP = Owner<DK>::JP;
-  __shared__ float ks[BC][DK + 1], vs[BC][TW + 1], Ts[BC][BC + 1], Xs[BC][TW + 1], Ms[DK][TW + 1];
-  __shared__ float gam[BC], bet[BC];
+                                                           const float* __restrict__ g,
+                                                           const float* __restrict__ beta,
+                                                           const float* __restrict__ h0,
+                                                           const int32_t* __restrict__ cu,
+                                                           const float* __restrict__ wsT,
+                                                           float* __restrict__ wsM, const BShape p) {
+  using SBk = StateBlocks<DK>;
+  constexpr int SK = DK + 8;
+  __shared__ float ks[BC][SK], vs[BC][ST], Ts[BC][SC], Xs[BC][ST], Ws[BC][ST], Ms[DK][ST];
+  __shared__ float gam[BC], Gam[BC], wv[BC], bet[BC];
   const int tid = threadIdx.x, H = p.H, dv = p.dv;
   const int chain = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
   const int n = chain / H, h = chain % H, col0 = tile * TW;
@@ -253,11 +299,16 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
   int len;
   seq_info(cu, p, n, row0, len);
   const int key = slot_key(cu, p, n), nch = (len + BC - 1) / BC;
-  const Owner<DK> o(tid);
-  float M[JP];
+  const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 M[SBk::PER];
 #pragma unroll
-  for (int r = 0; r < JP; ++r) M[r] = h0 ? h0[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] : 0.f;
-  const int yt = tid >> 3, yj = (tid & 7) * 2;  // (token, column pair) mapping
+  for (int m = 0; m < SBk::PER; ++m) {
+    const int blk = wave + 4 * m;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      M[m][x] = (h0 && blk < SBk::NBM) ? h0[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln] : 0.f;
+  }
 
   // the next chunk's inputs, fetched into registers while this one computes
   RowsReg<TI, DK> kr;
@@ -280,49 +331,60 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
     const size_t sb = (size_t)h * p.nslots + key + c;
     float* mo = wsM + sb * DK * dv;
 #pragma unroll
-    for (int r = 0; r < JP; ++r) {
-      mo[(long)o.si * dv + col0 + o.sj0 + r] = M[r];
-      Ms[o.si][o.sj0 + r] = M[r];
+    for (int m = 0; m < SBk::PER; ++m) {
+      const int blk = wave + 4 * m;
+      if (blk < SBk::NBM) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 16 * blk + 4 * lq + x;
+          mo[(long)i * dv + col0 + ln] = M[m][x];
+          Ms[i][ln] = M[m][x];
+        }
+      }
     }
-    kr.store(ks, tid);
-    vr.store(vs, tid);
-    tr.store(Ts, tid);
+    kr.template store_s<SK>(ks, tid);
+    vr.template store_s<ST>(vs, tid);
+    tr.store_s<SC>(Ts, tid);
     if (tid < BC) bet[tid] = br;
-    chunk_gamma(gr, tid, gam);
+    chunk_decay(gr, tid, gam, Gam, wv);
     if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
-    {  // X = beta (V - Gam K M)
-      float y0 = 0.f, y1 = 0.f;
+    if (wave < 2) {  // X = beta (V - Gam K M), row block `wave`
+      const int r16 = 16 * wave + ln;
+      f32x4 y = zero;
 #pragma unroll 8
-      for (int i = 0; i < DK; ++i) {
-        const float kv = ks[yt][i];
-        y0 = __builtin_fmaf(kv, Ms[i][yj], y0);
-        y1 = __builtin_fmaf(kv, Ms[i][yj + 1], y1);
-      }
-      const float G = ex(gam[yt]);
-      Xs[yt][yj] = bet[yt] * (vs[yt][yj] - G * y0);
-      Xs[yt][yj + 1] = bet[yt] * (vs[yt][yj + 1] - G * y1);
-    }
-    __syncthreads();
-    {  // W = diag(w) T X, into vs
-      float u0 = 0.f, u1 = 0.f;
-      for (int r = 0; r <= yt; ++r) {
-        const float tv = Ts[yt][r];
-        u0 = __builtin_fmaf(tv, Xs[r][yj], u0);
-        u1 = __builtin_fmaf(tv, Xs[r][yj + 1], u1);
-      }
-      const float w = ex(gam[BC - 1] - gam[yt]);
-      vs[yt][yj] = w * u0;
-      vs[yt][yj + 1] = w * u1;
-    }
-    __syncthreads();
-    const float GC = ex(gam[BC - 1]);
+      for (int kk = 0; kk < DK; kk += 4) y = mfma4(ks[r16][kk + lq], Ms[kk + lq][ln], y);
 #pragma unroll
-    for (int r = 0; r < JP; ++r) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < BC; ++t) acc = __builtin_fmaf(ks[t][o.si], vs[t][o.sj0 + r], acc);
-      M[r] = __builtin_fmaf(GC, M[r], acc);
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * wave + 4 * lq + x;
+        Xs[t][ln] = bet[t] * (vs[t][ln] - Gam[t] * y[x]);
+      }
+    }
+    __syncthreads();
+    if (wave < 2) {  // W = diag(w) T X
+      const int r16 = 16 * wave + ln;
+      f32x4 u = zero;
+#pragma unroll
+      for (int kk = 0; kk < BC; kk += 4) u = mfma4(Ts[r16][kk + lq], Xs[kk + lq][ln], u);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * wave + 4 * lq + x;
+        Ws[t][ln] = wv[t] * u[x];
+      }
+    }
+    __syncthreads();
+    {  // M <- Gam_C M + K^T W
+      const float GC = Gam[BC - 1];
+#pragma unroll
+      for (int m = 0; m < SBk::PER; ++m) {
+        const int blk = wave + 4 * m;
+        if (blk < SBk::NBM) {
+          f32x4 acc = GC * M[m];
+#pragma unroll
+          for (int kk = 0; kk < BC; kk += 4) acc = mfma4(ks[kk + lq][16 * blk + ln], Ws[kk + lq][ln], acc);
+          M[m] = acc;
+        }
+      }
     }
     __syncthreads();
   }
@@ -331,17 +393,20 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
 // ------------------------------------------------------------- adjoint ----
 template <typename TI, int DK>
 __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
-                                                         const TI* __restrict__ dO, const float* __restrict__ g,
-                                                         const float* __restrict__ beta,
-                                                         const float* __restrict__ dhT,
-                                                         const int32_t* __restrict__ cu,
-                                                         const float* __restrict__ wsT,
-                                                         const float* __restrict__ wsP, float* __restrict__ wsD,
-                                                         float* __restrict__ dh0, const BShape p) {
-  constexpr int JP = Owner<DK>::JP;
-  __shared__ float qs[BC][DK + 1], ks[BC][DK + 1], ds[BC][TW + 1], Ts[BC][BC + 1], Ps[BC][BC + 1];
-  __shared__ float Us[BC][TW + 1], Zs[BC][TW + 1], Ds[DK][TW + 1];
-  __shared__ float gam[BC], bet[BC];
+                                                            const TI* __restrict__ dO,
+                                                            const float* __restrict__ g,
+                                                            const float* __restrict__ beta,
+                                                            const float* __restrict__ dhT,
+                                                            const int32_t* __restrict__ cu,
+                                                            const float* __restrict__ wsT,
+                                                            const float* __restrict__ wsP,
+                                                            float* __restrict__ wsD, float* __restrict__ dh0,
+                                                            const BShape p) {
+  using SBk = StateBlocks<DK>;
+  constexpr int SK = DK + 8;
+  __shared__ float qs[BC][SK], ks[BC][SK], ds[BC][ST], Ts[BC][SC], Ps[BC][SC];
+  __shared__ float KDs[BC][ST], PDs[BC][ST], Zs[BC][ST], Ds[DK][ST];
+  __shared__ float gam[BC], Gam[BC], wv[BC], bet[BC];
   const int tid = threadIdx.x, H = p.H, dv = p.dv;
   const int chain = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
   const int n = chain / H, h = chain % H, col0 = tile * TW;
@@ -349,11 +414,16 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
   int len;
   seq_info(cu, p, n, row0, len);
   const int key = slot_key(cu, p, n), nch = (len + BC - 1) / BC;
-  const Owner<DK> o(tid);
-  float D[JP];
+  const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 D[SBk::PER];
 #pragma unroll
-  for (int r = 0; r < JP; ++r) D[r] = dhT ? dhT[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] : 0.f;
-  const int yt = tid >> 3, yj = (tid & 7) * 2;
+  for (int m = 0; m < SBk::PER; ++m) {
+    const int blk = wave + 4 * m;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      D[m][x] = (dhT && blk < SBk::NBM) ? dhT[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln] : 0.f;
+  }
 
   // the previous chunk's inputs, fetched into registers while this one computes
   RowsReg<TI, DK> qr, kr;
@@ -379,86 +449,90 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
     const size_t sb = (size_t)h * p.nslots + key + c;
     float* dout = wsD + sb * DK * dv;
 #pragma unroll
-    for (int r = 0; r < JP; ++r) {
-      dout[(long)o.si * dv + col0 + o.sj0 + r] = D[r];
-      Ds[o.si][o.sj0 + r] = D[r];
+    for (int m = 0; m < SBk::PER; ++m) {
+      const int blk = wave + 4 * m;
+      if (blk < SBk::NBM) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 16 * blk + 4 * lq + x;
+          dout[(long)i * dv + col0 + ln] = D[m][x];
+          Ds[i][ln] = D[m][x];
+        }
+      }
     }
-    qr.store(qs, tid);
-    kr.store(ks, tid);
-    dr.store(ds, tid);
-    tr.store(Ts, tid);
-    pr.store(Ps, tid);
+    qr.template store_s<SK>(qs, tid);
+    kr.template store_s<SK>(ks, tid);
+    dr.template store_s<ST>(ds, tid);
+    tr.store_s<SC>(Ts, tid);
+    pr.store_s<SC>(Ps, tid);
     if (tid < BC) bet[tid] = br;
-    chunk_gamma(gr, tid, gam);
+    chunk_decay(gr, tid, gam, Gam, wv);
     if (c > 0) fetch(c - 1);
     __syncthreads();
-    {  // dU = P^T dO + diag(w) K dM'
-      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    if (wave < 2) {  // KD = K dM' on row block `wave`
+      const int r16 = 16 * wave + ln;
+      f32x4 a = zero;
 #pragma unroll 8
-      for (int i = 0; i < DK; ++i) {
-        const float kv = ks[yt][i];
-        a0 = __builtin_fmaf(kv, Ds[i][yj], a0);
-        a1 = __builtin_fmaf(kv, Ds[i][yj + 1], a1);
-      }
-      for (int r = yt; r < BC; ++r) {
-        const float pv = Ps[r][yt];
-        b0 = __builtin_fmaf(pv, ds[r][yj], b0);
-        b1 = __builtin_fmaf(pv, ds[r][yj + 1], b1);
-      }
-      const float w = ex(gam[BC - 1] - gam[yt]);
-      Us[yt][yj] = __builtin_fmaf(w, a0, b0);
-      Us[yt][yj + 1] = __builtin_fmaf(w, a1, b1);
-    }
-    __syncthreads();
-    {  // dX = T^T dU; Z = diag(beta Gam) dX; dO <- diag(Gam) dO
-      float x0 = 0.f, x1 = 0.f;
-      for (int r = yt; r < BC; ++r) {
-        const float tv = Ts[r][yt];
-        x0 = __builtin_fmaf(tv, Us[r][yj], x0);
-        x1 = __builtin_fmaf(tv, Us[r][yj + 1], x1);
-      }
-      const float G = ex(gam[yt]), bg = bet[yt] * G;
-      Zs[yt][yj] = bg * x0;
-      Zs[yt][yj + 1] = bg * x1;
-      ds[yt][yj] *= G;
-      ds[yt][yj + 1] *= G;
-    }
-    __syncthreads();
-    const float GC = ex(gam[BC - 1]);
+      for (int kk = 0; kk < DK; kk += 4) a = mfma4(ks[r16][kk + lq], Ds[kk + lq][ln], a);
 #pragma unroll
-    for (int r = 0; r < JP; ++r) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < BC; ++t) {
-        acc = __builtin_fmaf(qs[t][o.si], ds[t][o.sj0 + r], acc);
-        acc = __builtin_fmaf(-ks[t][o.si], Zs[t][o.sj0 + r], acc);
+      for (int x = 0; x < 4; ++x) KDs[16 * wave + 4 * lq + x][ln] = a[x];
+    } else {  // P^T dO on row block `wave - 2`
+      const int rb = wave - 2, r16 = 16 * rb + ln;
+      f32x4 a = zero;
+#pragma unroll
+      for (int kk = 0; kk < BC; kk += 4) a = mfma4(Ps[kk + lq][r16], ds[kk + lq][ln], a);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) PDs[16 * rb + 4 * lq + x][ln] = a[x];
+    }
+    __syncthreads();
+    if (wave < 2) {  // dX = T^T dU with dU = P^T dO + diag(w) KD;  Z = diag(beta Gam) dX
+      const int r16 = 16 * wave + ln;
+      f32x4 a = zero;
+#pragma unroll
+      for (int kk = 0; kk < BC; kk += 4) {
+        const int r = kk + lq;
+        a = mfma4(Ts[r][r16], __builtin_fmaf(wv[r], KDs[r][ln], PDs[r][ln]), a);
       }
-      D[r] = __builtin_fmaf(GC, D[r], acc);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int t = 16 * wave + 4 * lq + x;
+        Zs[t][ln] = bet[t] * Gam[t] * a[x];
+      }
+    }
+    __syncthreads();
+    {  // dM <- Gam_C dM' + Q^T diag(Gam) dO - K^T Z
+      const float GC = Gam[BC - 1];
+#pragma unroll
+      for (int m = 0; m < SBk::PER; ++m) {
+        const int blk = wave + 4 * m;
+        if (blk < SBk::NBM) {
+          f32x4 acc = GC * D[m];
+#pragma unroll
+          for (int kk = 0; kk < BC; kk += 4) {
+            const int r = kk + lq;
+            acc = mfma4(qs[r][16 * blk + ln], Gam[r] * ds[r][ln], acc);
+            acc = mfma4(-ks[r][16 * blk + ln], Zs[r][ln], acc);
+          }
+          D[m] = acc;
+        }
+      }
     }
     __syncthreads();
   }
   if (dh0) {
 #pragma unroll
-    for (int r = 0; r < JP; ++r) dh0[((long)chain * DK + o.si) * dv + col0 + o.sj0 + r] = D[r];
+    for (int m = 0; m < SBk::PER; ++m) {
+      const int blk = wave + 4 * m;
+      if (blk < SBk::NBM) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          dh0[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln] = D[m][x];
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------- grad ----
-// The products run on the fp32 matrix cores: v_mfma_f32_16x16x4f32 takes
-// A (16 x 4) and B (4 x 16) one element per lane -- lane l holds A[l % 16][l / 16]
-// and B[l / 16][l % 16] -- and accumulates D (16 x 16), of which lane l holds
-// rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.  LDS rows are padded to
-// a stride of 8 mod 64 words, which keeps both operand read patterns (down a
-// column, along a row) within two-way bank conflicts.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-constexpr int SC = BC + 8;  // row stride of the C x C arrays
-constexpr int ST = TW + 8;  // row stride of the tile arrays
-
 template <typename TI, int DK>
 struct GradLds {
   static constexpr int SK = DK + 8;
