@@ -175,57 +175,6 @@ struct CCReg {
   }
 };
 
-// ---------------------------------------------------------------- prep ----
-template <typename TI, int DK>
-__global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
-                                                      const float* __restrict__ g, const float* __restrict__ beta,
-                                                      const int32_t* __restrict__ cu, float* __restrict__ wsT,
-                                                      float* __restrict__ wsP, const BShape p) {
-  __shared__ float qs[BC][DK + 1], ks[BC][DK + 1], As[BC][BC + 1], Ts[BC][BC + 1];
-  __shared__ float gam[BC], bet[BC];
-  const int tid = threadIdx.x, s = blockIdx.x, h = blockIdx.y, H = p.H;
-  const int n = find_seq(cu, p, s);
-  long row0;
-  int len;
-  seq_info(cu, p, n, row0, len);
-  const int c = s - slot_key(cu, p, n);
-  if (c < 0 || (long)c * BC >= len) return;  // slot not used
-  const int t0 = c * BC, Lc = min(BC, len - t0);
-  for (int e = tid; e < BC * DK; e += NT) {
-    const int t = e / DK, i = e % DK;
-    const long off = ((row0 + t0 + t) * H + h) * DK + i;
-    qs[t][i] = t < Lc ? ldf(q, off) : 0.f;
-    ks[t][i] = t < Lc ? ldf(k, off) : 0.f;
-  }
-  if (tid < BC) bet[tid] = token_f(beta, row0, t0, Lc, H, h, tid);
-  chunk_gamma(tid < BC ? token_f(g, row0, t0, Lc, H, h, tid) : 0.f, tid, gam);
-  __syncthreads();
-  const size_t base = ((size_t)h * p.nslots + s) * (BC * BC);
-  for (int e = tid; e < BC * BC; e += NT) {
-    const int t = e / BC, u = e % BC;
-    float kk = 0.f, qk = 0.f;
-    for (int i = 0; i < DK; ++i) {
-      kk = __builtin_fmaf(ks[t][i], ks[u][i], kk);
-      qk = __builtin_fmaf(qs[t][i], ks[u][i], qk);
-    }
-    const float E = u <= t ? ex(gam[t] - gam[u]) : 0.f;
-    As[t][u] = u < t ? bet[t] * kk * E : 0.f;
-    wsP[base + e] = qk * E;
-  }
-  __syncthreads();
-  // (I + A)^-1 by forward substitution, one column per thread
-  if (tid < BC) {
-    const int u = tid;
-    for (int t = 0; t < BC; ++t) {
-      float x = t == u ? 1.f : 0.f;
-      for (int r = u; r < t; ++r) x = __builtin_fmaf(-As[t][r], Ts[r][u], x);
-      Ts[t][u] = x;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < BC * BC; e += NT) wsT[base + e] = Ts[e / BC][e % BC];
-}
-
 // ------------------------------------------------------- matrix cores ----
 // The products run on the fp32 matrix cores: v_mfma_f32_16x16x4f32 takes
 // A (16 x 4) and B (4 x 16) one element per lane -- lane l holds A[l % 16][l / 16]
@@ -250,6 +199,66 @@ struct Owner {
   int si, sj0;
   __device__ Owner(int tid) : si(tid % DK), sj0((tid / DK) * JP) {}
 };
+
+// ---------------------------------------------------------------- prep ----
+template <typename TI, int DK>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                                                      const float* __restrict__ g, const float* __restrict__ beta,
+                                                      const int32_t* __restrict__ cu, float* __restrict__ wsT,
+                                                      float* __restrict__ wsP, const BShape p) {
+  constexpr int SK = DK + 8;
+  __shared__ TI qs[BC][SK], ks[BC][SK];  // stored as given (bf16 is widened on read)
+  __shared__ float As[BC][SC], Ts[BC][SC];
+  __shared__ float gam[BC], bet[BC];
+  const int tid = threadIdx.x, s = blockIdx.x, h = blockIdx.y, H = p.H;
+  const int n = find_seq(cu, p, s);
+  long row0;
+  int len;
+  seq_info(cu, p, n, row0, len);
+  const int c = s - slot_key(cu, p, n);
+  if (c < 0 || (long)c * BC >= len) return;  // slot not used
+  const int t0 = c * BC, Lc = min(BC, len - t0);
+  for (int e = tid; e < BC * DK; e += NT) {
+    const int t = e / DK, i = e % DK;
+    const long off = ((row0 + t0 + t) * H + h) * DK + i;
+    qs[t][i] = t < Lc ? q[off] : (TI)0.f;
+    ks[t][i] = t < Lc ? k[off] : (TI)0.f;
+  }
+  if (tid < BC) bet[tid] = token_f(beta, row0, t0, Lc, H, h, tid);
+  chunk_gamma(tid < BC ? token_f(g, row0, t0, Lc, H, h, tid) : 0.f, tid, gam);
+  __syncthreads();
+  const size_t base = ((size_t)h * p.nslots + s) * (BC * BC);
+  {  // K K^T and Q K^T on block `wave` of the C x C outputs
+    const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
+    const int tr0 = 16 * (wave >> 1), uc = 16 * (wave & 1) + ln;
+    f32x4 kk4 = {0.f, 0.f, 0.f, 0.f}, qk4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int kk = 0; kk < DK; kk += 4) {
+      const float b = (float)ks[uc][kk + lq];
+      kk4 = mfma4((float)ks[tr0 + ln][kk + lq], b, kk4);
+      qk4 = mfma4((float)qs[tr0 + ln][kk + lq], b, qk4);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int t = tr0 + 4 * lq + x;
+      const float E = uc <= t ? ex(gam[t] - gam[uc]) : 0.f;
+      As[t][uc] = uc < t ? bet[t] * kk4[x] * E : 0.f;
+      wsP[base + t * BC + uc] = qk4[x] * E;
+    }
+  }
+  __syncthreads();
+  // (I + A)^-1 by forward substitution, one column per thread
+  if (tid < BC) {
+    const int u = tid;
+    for (int t = 0; t < BC; ++t) {
+      float x = t == u ? 1.f : 0.f;
+      for (int r = u; r < t; ++r) x = __builtin_fmaf(-As[t][r], Ts[r][u], x);
+      Ts[t][u] = x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < BC * BC; e += NT) wsT[base + e] = Ts[e / BC][e % BC];
+}
 
 // -------------------------------------------------------------- states ----
 // The state tile M (DK x 16) is held in matrix-core accumulator layout:
@@ -547,7 +556,7 @@ struct GradLds {
     } fin;
   } u;
   float vt[BC][ST], dot[BC][ST], Yt[BC][ST], KDt[BC][ST], Xt[BC][ST], Ut[BC][ST], dUt[BC][ST], dXt[BC][ST];
-  float gam[BC], bet[BC], sgA[BC], sgB[BC], sb1[BC], sw[BC], red[NT / 64];
+  float gam[BC], bet[BC], sgQ[2][BC], sgB[BC], sb1[BC], sw[BC], red[NT / 64];
 };
 
 template <typename TI, int DK>
@@ -627,22 +636,17 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
     orr.template store_s<ST>(L.dot, tid);
     if (tile + 1 < p.ntile) fetch(tile + 1);
     __syncthreads();
-    // phase A.  waves 0, 1: Y = K M and QM = Q M on row block rb, then X;
+    // phase A.  waves 0, 1: Y = K M on row block rb, then X;
     //           waves 2, 3: KD = K dM' and P^T dO on row block rb, then dU.
     if (wave < 2) {
-      f32x4 y = zero, qm = zero;
+      f32x4 y = zero;
 #pragma unroll 8
-      for (int kk = 0; kk < DK; kk += 4) {
-        const float b = L.u.tile.Mt[kk + lq][ln];
-        y = mfma4(kf(r16, kk + lq), b, y);
-        qm = mfma4(qf(r16, kk + lq), b, qm);
-      }
+      for (int kk = 0; kk < DK; kk += 4) y = mfma4(kf(r16, kk + lq), L.u.tile.Mt[kk + lq][ln], y);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int t = 16 * rb + 4 * lq + x;
         L.Yt[t][ln] = y[x];
         L.Xt[t][ln] = L.bet[t] * (L.vt[t][ln] - ex(L.gam[t]) * y[x]);
-        pA[x] = __builtin_fmaf(L.dot[t][ln], qm[x], pA[x]);  // dO . QM
       }
     } else {
       f32x4 kd = zero, pd = zero;
@@ -688,8 +692,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
       sGC = __builtin_fmaf(L.u.tile.Mt[o.si][o.sj0 + r], L.u.tile.Dt[o.si][o.sj0 + r], sGC);
     __syncthreads();
     // phase C, all waves.  dX U^T and dO U^T (C x C, block `wave`), and
-    // dQ += diag(Gam) dO M^T, dK += -diag(beta Gam) dX M^T + diag(w) U dM'^T
-    // (C x DK, blocks wave + 4 m).
+    // dQ0 += dO M^T (diag(Gam) is applied after the last tile), dK +=
+    // -diag(beta Gam) dX M^T + diag(w) U dM'^T (C x DK, blocks wave + 4 m).
     {
       const int cr = 16 * (wave >> 1) + ln, cc = 16 * (wave & 1) + ln;
 #pragma unroll
@@ -702,14 +706,27 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
       const int blk = wave + 4 * m, br = 16 * (blk & 1) + ln, bc = 16 * (blk >> 1) + ln;
-      const float G = ex(L.gam[br]), bg = -L.bet[br] * G, w = ex(L.gam[BC - 1] - L.gam[br]);
+      const float bg = -L.bet[br] * ex(L.gam[br]), w = ex(L.gam[BC - 1] - L.gam[br]);
 #pragma unroll
       for (int kk = 0; kk < TW; kk += 4) {
         const float mv = L.u.tile.Mt[bc][kk + lq], dd = L.u.tile.Dt[bc][kk + lq];
-        accQ[m] = mfma4(G * L.dot[br][kk + lq], mv, accQ[m]);
+        accQ[m] = mfma4(L.dot[br][kk + lq], mv, accQ[m]);
         accK[m] = mfma4(bg * L.dXt[br][kk + lq], mv, accK[m]);
         accK[m] = mfma4(w * L.Ut[br][kk + lq], dd, accK[m]);
       }
+    }
+  }
+  // dO_t . (Q M)_t summed over all value columns is q_t . (M dO_t) = q_t . dQ0_t
+  // (this wave's key columns of it); then dQ0 gets its diag(Gam)
+  float pQ[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int bc = 16 * ((wave + 4 * m) >> 1) + ln;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int t = 16 * rb + 4 * lq + x;
+      pQ[x] = __builtin_fmaf(qf(t, bc), accQ[m][x], pQ[x]);
+      accQ[m][x] *= ex(L.gam[t]);
     }
   }
   // per-row partial sums: reduce over the 16 lanes of a row group
@@ -719,6 +736,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
     for (int m = 1; m < 16; m <<= 1) {
       pA[x] += __shfl_xor(pA[x], m);
       pB[x] += __shfl_xor(pB[x], m);
+      pQ[x] += __shfl_xor(pQ[x], m);
     }
   }
 #pragma unroll
@@ -728,9 +746,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int t = 16 * rb + 4 * lq + x;
+      L.sgQ[wave >> 1][t] = pQ[x];  // dO . QM, this wave's key columns
       if (wave < 2) {
-        L.sgA[t] = pA[x];  // dO . QM
-        L.sw[t] = pB[x];   // U . KD
+        L.sw[t] = pB[x];  // U . KD
       } else {
         L.sb1[t] = pA[x];  // dX . R
         L.sgB[t] = pB[x];  // -beta dX . Y
@@ -792,9 +810,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
     float gc = 0.f;
     for (int wv = 0; wv < NT / 64; ++wv) gc += L.red[wv];
     const float Gt = ex(L.gam[t]), wt = ex(L.gam[BC - 1] - L.gam[t]);
-    const float dGam = L.sgA[t] + L.sgB[t] + (t == last ? gc : 0.f);
-    L.sb1[t] += b2;                                // dbeta, in place
-    L.sgA[t] = __builtin_fmaf(dGam, Gt, rz - cz);  // dgamma without the w terms, in place
+    const float dGam = (L.sgQ[0][t] + L.sgQ[1][t]) + L.sgB[t] + (t == last ? gc : 0.f);
+    L.sb1[t] += b2;                                   // dbeta, in place
+    L.sgQ[0][t] = __builtin_fmaf(dGam, Gt, rz - cz);  // dgamma without the w terms, in place
     L.sw[t] *= wt;                                 // dw . w, in place
   }
   __syncthreads();
@@ -805,7 +823,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
   if (tid < Lc) {
     const int t = tid;
     float acc = 0.f;
-    for (int uu = Lc - 1; uu >= t; --uu) acc += L.sgA[uu];
+    for (int uu = Lc - 1; uu >= t; --uu) acc += L.sgQ[0][uu];
     for (int uu = 0; uu < t; ++uu) acc += L.sw[uu];
     const long th = (row0 + t0 + t) * H + h;
     dg[th] = acc;
