@@ -127,32 +127,39 @@ __device__ inline float token_f(const float* __restrict__ x, long row0, int t0, 
 
 // A chunk's C rows of a (token, head, W) tensor (columns col0 .. col0+W-1 of
 // rows of length ld), held in registers between a fetch and an LDS store;
-// rows past the chunk's length are zero.
+// rows past the chunk's length are zero.  bf16 elements travel in pairs
+// (one 32-bit load each).  Every load address is clamped into the chunk
+// (Lc >= 1), so the fetch has no branches.
 template <typename TI, int W>
 struct RowsReg {
-  static constexpr int N = BC * W / NT;
-  TI r[N];
+  static constexpr int PK = sizeof(TI) == 2 ? 2 : 1;  // elements per register
+  static constexpr int N = BC * W / (NT * PK);
+  uint32_t r[N];
   __device__ void fetch(const TI* __restrict__ p, long row0, int t0, int Lc, int H, int h, long ld, int col0,
                         int tid) {
 #pragma unroll
     for (int x = 0; x < N; ++x) {
-      const int e = tid + NT * x, t = e / W, i = e % W;
-      r[x] = t < Lc ? p[((row0 + t0 + t) * H + h) * ld + col0 + i] : (TI)0.f;
-    }
-  }
-  __device__ void store(float (*dst)[W + 1], int tid) const {
-#pragma unroll
-    for (int x = 0; x < N; ++x) {
-      const int e = tid + NT * x;
-      dst[e / W][e % W] = (float)r[x];
+      const int e = PK * (tid + NT * x), t = e / W, i = e % W;
+      const long off = ((row0 + t0 + min(t, Lc - 1)) * H + h) * ld + col0 + i;
+      uint32_t w;
+      if constexpr (PK == 2)
+        w = *reinterpret_cast<const uint32_t*>(p + off);
+      else
+        w = __float_as_uint(p[off]);
+      r[x] = t < Lc ? w : 0u;
     }
   }
   template <int S>
   __device__ void store_s(float (*dst)[S], int tid) const {
 #pragma unroll
     for (int x = 0; x < N; ++x) {
-      const int e = tid + NT * x;
-      dst[e / W][e % W] = (float)r[x];
+      const int e = PK * (tid + NT * x), t = e / W, i = e % W;
+      if constexpr (PK == 2) {
+        dst[t][i] = __uint_as_float(r[x] << 16);
+        dst[t][i + 1] = __uint_as_float(r[x] & 0xffff0000u);
+      } else {
+        dst[t][i] = __uint_as_float(r[x]);
+      }
     }
   }
 };
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, 
     const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
     const int tr0 = 16 * (wave >> 1), uc = 16 * (wave & 1) + ln;
     f32x4 kk4 = {0.f, 0.f, 0.f, 0.f}, qk4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
+#pragma unroll
     for (int kk = 0; kk < DK; kk += 4) {
       const float b = (float)ks[uc][kk + lq];
       kk4 = mfma4((float)ks[tr0 + ln][kk + lq], b, kk4);
@@ -361,7 +368,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
     if (wave < 2) {  // X = beta (V - Gam K M), row block `wave`
       const int r16 = 16 * wave + ln;
       f32x4 y = zero;
-#pragma unroll 8
+#pragma unroll
       for (int kk = 0; kk < DK; kk += 4) y = mfma4(ks[r16][kk + lq], Ms[kk + lq][ln], y);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -481,7 +488,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
     if (wave < 2) {  // KD = K dM' on row block `wave`
       const int r16 = 16 * wave + ln;
       f32x4 a = zero;
-#pragma unroll 8
+#pragma unroll
       for (int kk = 0; kk < DK; kk += 4) a = mfma4(ks[r16][kk + lq], Ds[kk + lq][ln], a);
 #pragma unroll
       for (int x = 0; x < 4; ++x) KDs[16 * wave + 4 * lq + x][ln] = a[x];
@@ -640,7 +647,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
     //           waves 2, 3: KD = K dM' and P^T dO on row block rb, then dU.
     if (wave < 2) {
       f32x4 y = zero;
-#pragma unroll 8
+#pragma unroll
       for (int kk = 0; kk < DK; kk += 4) y = mfma4(kf(r16, kk + lq), L.u.tile.Mt[kk + lq][ln], y);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
       }
     } else {
       f32x4 kd = zero, pd = zero;
-#pragma unroll 8
+#pragma unroll
       for (int kk = 0; kk < DK; kk += 4) kd = mfma4(kf(r16, kk + lq), L.u.tile.Dt[kk + lq][ln], kd);
 #pragma unroll
       for (int kk = 0; kk < BC; kk += 4) pd = mfma4(L.Ps[kk + lq][r16], L.dot[kk + lq][ln], pd);
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
   {  // K K^T on block `wave`, then dA, G, dP . E, Z and the second dbeta term
     const int tr0 = 16 * (wave >> 1), uc = 16 * (wave & 1) + ln;
     f32x4 kk4 = zero;
-#pragma unroll 8
+#pragma unroll
     for (int kk = 0; kk < DK; kk += 4) kk4 = mfma4(kf(tr0 + ln, kk + lq), kf(uc, kk + lq), kk4);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
