@@ -1,4 +1,5 @@
-"""Seeded sweep of random configurations against the FP64 oracles: shapes,
+"""Seeded sweep of random configurations against the FP64 oracles (forward,
+diagonal-decay and backward entry points): shapes,
 dtypes, chunk lengths, dense or packed batches (with empty and ragged
 sequences), with or without an initial state, lengths that do and do not
 trigger sequence segments.  Every case is fixed by its seed."""
@@ -69,3 +70,29 @@ def test_diag_random_configuration(seed):
     check(inp, "chunked")
     if wl.tokens <= 600:
         check(inp, "recurrent")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_bwd_random_configuration(seed):
+    """The backward entry point on random shapes, dtypes, packings, initial
+    states, decays and output gradients (with and without dhT)."""
+    from test_gpu_bwd import _check
+
+    rng = np.random.default_rng(3000 + seed)
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    dk, dv = int(rng.choice([32, 64, 128])), int(rng.choice([32, 64, 128]))
+    H = int(rng.integers(1, 4))
+    h0 = float(rng.choice([0.0, 0.2]))
+    g_mean = float(rng.choice([0.0, -2.0]))
+    dh = float(rng.choice([0.0, 1.0]))
+    if rng.random() < 0.4:
+        lens = [int(x) for x in rng.integers(0, 300, size=int(rng.integers(1, 5)))]
+        wl = synth.custom(name=f"bwd_sweep{seed}", seed=seed, H=H, dk=dk, dv=dv, dtype=dtype,
+                          h0_std=h0, g_mean=g_mean, seq_lens=lens)
+    else:
+        wl = synth.custom(name=f"bwd_sweep{seed}", seed=seed, B=int(rng.integers(1, 3)),
+                          T=int(rng.integers(1, 400)), H=H, dk=dk, dv=dv, dtype=dtype,
+                          h0_std=h0, g_mean=g_mean)
+    inp = synth.generate(wl)
+    print(wl, flush=True)
+    _check(inp, synth.output_grads(inp, 4000 + seed, dh))
