@@ -53,6 +53,27 @@ METRIC_DIAG = ("diagonal-decay recurrence (HyMo GDN layer) fwd tokens/s + achiev
                "(% roofline), 1 MI355X")
 
 
+def _dev(x):
+    """A stored synthetic array (float32, or uint16 bfloat16 bits) as a device tensor."""
+    import torch
+
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _device_inputs(inp: synth.Inputs):
+    return {n: _dev(getattr(inp, n)) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+
+
+def _host_f64(t):
+    import torch
+
+    return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy().astype(np.float64)
+
+
 def algorithmic_bytes(wl: synth.Workload, has_h0: bool) -> int:
     """Minimum HBM traffic of one call: read q, k, v, g, beta once, write out
     once, read h0 (if given) and write hT once."""
@@ -114,32 +135,32 @@ def copy_reference(nbytes: int, stream) -> float:
     return 2 * n * 4 / med_s / 1e9
 
 
-def cpu_baseline(inp: synth.Inputs):
-    """The FP64 oracle on the host cores over the whole workload."""
+def cpu_baseline(inp: synth.Inputs, out=None, hT=None, check=True):
+    """The FP64 oracle on the host cores over the whole workload (timed).
+    When the GPU's (out, hT) are given, the same oracle results also check
+    them (infinity-norm relative error per tensor, within the dtype's
+    tolerance) before any number is reported.  Returns (record, errs)."""
     import oracle
 
     a = [inp.as_f64(n) for n in ("q", "k", "v", "g", "beta", "h0")]
     cores = os.cpu_count() or 1
     oracle.build(force=False)
     t0 = time.perf_counter()
-    oracle.fwd_seq(*a, cu_seqlens=inp.cu_seqlens, nthreads=cores)
+    o_ref, h_ref = oracle.fwd_seq(*a, cu_seqlens=inp.cu_seqlens, nthreads=cores)
     dt = time.perf_counter() - t0
     wl = inp.wl
-    return {"value": wl.tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"whole workload ({wl.B * wl.H} chains x {wl.T} tokens), "
-                      f"{dt:.2f} s wall on {cores} threads"}
-
-
-def parity_sample(inp, out, hT):
-    """Sampled-chain check against the oracle before any number is reported."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from hip_case import TOL, compare
-
-    eo, eh = compare(inp, out, hT, chains=[0, inp.wl.B * inp.wl.H - 1])
-    tol = TOL[inp.wl.dtype]
-    if not (eo <= tol and eh <= tol):
-        raise SystemExit(f"parity check failed: rel err out {eo:.3e} hT {eh:.3e} > {tol}")
-    return eo, eh
+    rec = {"value": wl.tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"whole workload ({wl.B * wl.H} chains x {wl.T} tokens), "
+                     f"{dt:.2f} s wall on {cores} threads"}
+    errs = None
+    if check and out is not None:
+        eo = oracle.rel_err(_host_f64(out), o_ref)
+        eh = oracle.rel_err(_host_f64(hT), h_ref)
+        tol = 2e-2 if wl.dtype == "bf16" else 1e-4
+        if not (eo <= tol and eh <= tol):
+            raise SystemExit(f"parity check failed: rel err out {eo:.3e} hT {eh:.3e} > {tol}")
+        errs = (eo, eh)
+    return rec, errs
 
 
 def diag_algorithmic_bytes(wl, has_h0: bool, has_gate: bool) -> int:
@@ -154,29 +175,20 @@ def diag_algorithmic_bytes(wl, has_h0: bool, has_gate: bool) -> int:
 
 def diag_main(args):
     """The diagonal-decay form: same protocol as ``main`` (rotated sets, HIP
-    events on the launch stream, sampled oracle check, CPU oracle leg)."""
+    events on the launch stream, CPU oracle leg that also checks parity)."""
     import torch
 
     import gated_deltanet_recurrence_delta_amd as gdn
     import synth.diag as sd
-    from oracle import diag as odiag
-    from oracle import rel_err
 
     wl = sd.WORKLOADS[args.workload]
     form = args.form or ("recurrent" if wl.T == 1 else "chunked")
     inp = sd.generate(wl)
 
-    def dev(x):
-        if x is None:
-            return None
-        if x.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-
     names = ("v", "b", "c", "g", "A_log", "Dskip", "gate", "h0", "cu_seqlens")
     sets = []
     for _ in range(max(1, args.sets)):
-        d = {n: dev(getattr(inp, n)) for n in names}
+        d = {n: _dev(getattr(inp, n)) for n in names}
         d["out"] = torch.empty(d["v"].shape, dtype=d["v"].dtype, device="cuda")
         d["hT"] = torch.empty((wl.B, wl.H, wl.S, wl.D), dtype=torch.float32, device="cuda")
         sets.append(d)
@@ -204,23 +216,6 @@ def diag_main(args):
     alg = diag_algorithmic_bytes(wl, inp.h0 is not None, inp.gate is not None)
     copy_gbs = copy_reference(alg, stream)
     torch.cuda.synchronize()
-    errs = None
-    if not args.no_parity:
-        # oracle on the first and last batch rows (every head of each)
-        out = sets[0]["out"].float().cpu().numpy()
-        hT = sets[0]["hT"].cpu().numpy()
-        eo = eh = 0.0
-        for b in sorted({0, wl.B - 1}):
-            sub = lambda n: None if getattr(inp, n) is None else inp.as_f64(n)
-            cut = lambda x: None if x is None else x[b:b + 1]
-            o_ref, h_ref = odiag.diag_fwd_seq(cut(sub("v")), cut(sub("b")), cut(sub("c")),
-                                              cut(sub("g")), sub("A_log"), cut(sub("h0")), None,
-                                              sub("Dskip"), cut(sub("gate")))
-            eo = max(eo, rel_err(out[b:b + 1], o_ref))
-            eh = max(eh, rel_err(hT[b:b + 1], h_ref))
-        if not (eo <= 2e-2 and eh <= 2e-2):
-            raise SystemExit(f"parity check failed: rel err out {eo:.3e} hT {eh:.3e}")
-        errs = (eo, eh)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -265,19 +260,28 @@ def diag_main(args):
                      "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
                      "p90_us": float(np.percentile(launch_ms, 90)) * 1e3},
     }
-    if errs is not None:
-        rec["parity"] = {"rel_err_out": errs[0], "rel_err_hT": errs[1],
-                         "chains": "first and last batch rows, every head"}
     if not args.no_cpu:
+        from oracle import diag as odiag
+        from oracle import rel_err
+
         t0 = time.perf_counter()
         a = {n: None if getattr(inp, n) is None else inp.as_f64(n) for n in names[:-1]}
-        odiag.diag_fwd_seq(a["v"], a["b"], a["c"], a["g"], a["A_log"], a["h0"], None,
-                           a["Dskip"], a["gate"])
+        o_ref, h_ref = odiag.diag_fwd_seq(a["v"], a["b"], a["c"], a["g"], a["A_log"], a["h0"],
+                                          None, a["Dskip"], a["gate"])
         dt = time.perf_counter() - t0
         rec["cpu_baseline"] = {"value": wl.tokens / dt, "unit": "tokens/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"whole workload ({wl.B * wl.H} chains x {wl.T} tokens), "
                                          f"NumPy token loop, {dt:.2f} s wall"}
+        if not args.no_parity:
+            # the same oracle results check sets[0]'s outputs (from its last
+            # timed step: identical inputs, deterministic kernel)
+            eo = rel_err(sets[0]["out"].float().cpu().numpy(), o_ref)
+            eh = rel_err(sets[0]["hT"].cpu().numpy(), h_ref)
+            if not (eo <= 2e-2 and eh <= 2e-2):
+                raise SystemExit(f"parity check failed: rel err out {eo:.3e} hT {eh:.3e}")
+            rec["parity"] = {"rel_err_out": eo, "rel_err_hT": eh,
+                             "chains": "all (the oracle leg's whole-workload run)"}
     print(json.dumps(rec), flush=True)
 
 
@@ -303,14 +307,11 @@ def bwd_flops(wl: synth.Workload, lens) -> int:
 
 def bwd_main(args):
     """The backward pass: same protocol as ``main`` (rotated sets, HIP events
-    on the launch stream around each gdn_bwd call, sampled oracle check,
-    CPU oracle leg)."""
+    on the launch stream around each gdn_bwd call, a CPU oracle leg on two
+    chains whose results also check those chains)."""
     import torch
 
     import gated_deltanet_recurrence_delta_amd as gdn
-    from oracle.bwd import bwd_seq
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from hip_case import dev, device_inputs, host_f64
 
     wl = synth.WORKLOADS[args.workload]
     inp = synth.generate(wl)
@@ -322,8 +323,8 @@ def bwd_main(args):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     sets = []
     for _ in range(max(1, args.sets)):
-        d = device_inputs(inp)
-        d["dout"], d["dhT"] = dev(og.dout), dev(og.dhT)
+        d = _device_inputs(inp)
+        d["dout"], d["dhT"] = _dev(og.dout), _dev(og.dhT)
         for n, like in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta")):
             d[n] = torch.empty_like(d[like])
         d["dh0"] = torch.empty((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
@@ -346,27 +347,6 @@ def bwd_main(args):
             raise SystemExit(f"gdn_bwd failed with status {rc}")
 
     torch.cuda.synchronize()
-    errs = None
-    if not args.no_parity and inp.cu_seqlens is None:
-        # oracle on two chains: (first sequence, first head), (last, last)
-        worst = {}
-        for b, h in sorted({(0, 0), (wl.B - 1, wl.H - 1)}):
-            cut = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]
-            ref = bwd_seq(*(cut(inp.as_f64(n)) for n in ("q", "k", "v", "g", "beta")),
-                          None if inp.h0 is None else inp.as_f64("h0")[b:b + 1, h:h + 1], None,
-                          cut(og.as_f64("dout")),
-                          None if og.dhT is None else og.as_f64("dhT")[b:b + 1, h:h + 1])
-            for n in ("dq", "dk", "dv", "dg", "dbeta"):
-                got = host_f64(first[n][b:b + 1, :, h:h + 1])
-                e = float(np.max(np.abs(got - ref[n])) / max(np.max(np.abs(ref[n])), 1e-30))
-                worst[n] = max(worst.get(n, 0.0), e)
-            got = host_f64(first["dh0"][b:b + 1, h:h + 1])
-            e = float(np.max(np.abs(got - ref["dh0"])) / max(np.max(np.abs(ref["dh0"])), 1e-30))
-            worst["dh0"] = max(worst.get("dh0", 0.0), e)
-        tol = 2e-2 if wl.dtype == "bf16" else 1e-4
-        if not all(e <= tol for e in worst.values()):
-            raise SystemExit(f"parity check failed: {worst}")
-        errs = worst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -412,20 +392,42 @@ def bwd_main(args):
                      "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
                      "p90_us": float(np.percentile(launch_ms, 90)) * 1e3},
     }
-    if errs is not None:
-        rec["parity"] = dict(errs, chains="(first sequence, first head), (last, last)")
     if not args.no_cpu and inp.cu_seqlens is None:
+        from oracle.bwd import bwd_seq
+
+        # the oracle on two chains, (first sequence, first head) and (last,
+        # last); its results also check those chains of the first call
+        chains = sorted({(0, 0), (wl.B - 1, wl.H - 1)})
+        refs = {}
         t0 = time.perf_counter()
-        cut = lambda x: None if x is None else x[0:1, :, 0:1]
-        bwd_seq(*(cut(inp.as_f64(n)) for n in ("q", "k", "v", "g", "beta")),
-                None if inp.h0 is None else inp.as_f64("h0")[0:1, 0:1], None,
-                cut(og.as_f64("dout")), None if og.dhT is None else og.as_f64("dhT")[0:1, 0:1])
+        for b, h in chains:
+            cut = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]
+            refs[(b, h)] = bwd_seq(
+                *(cut(inp.as_f64(n)) for n in ("q", "k", "v", "g", "beta")),
+                None if inp.h0 is None else inp.as_f64("h0")[b:b + 1, h:h + 1], None,
+                cut(og.as_f64("dout")),
+                None if og.dhT is None else og.as_f64("dhT")[b:b + 1, h:h + 1])
         dt = time.perf_counter() - t0
-        rec["cpu_baseline"] = {"value": (wl.T / wl.H) / dt, "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"one chain (first sequence, first head) of {wl.T} "
-                                         f"tokens, NumPy reverse sweep, {dt:.2f} s wall; one "
-                                         f"chain is 1/{wl.H} of a token's heads"}
+        rec["cpu_baseline"] = {"value": (len(chains) * wl.T / wl.H) / dt, "unit": "tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{len(chains)} chains of {wl.T} tokens (first sequence "
+                                         f"first head, last sequence last head), NumPy reverse "
+                                         f"sweep, {dt:.2f} s wall; one chain is 1/{wl.H} of a "
+                                         "token's heads"}
+        if not args.no_parity:
+            worst = {}
+            for (b, h), ref in refs.items():
+                for n in ("dq", "dk", "dv", "dg", "dbeta"):
+                    got = _host_f64(first[n][b:b + 1, :, h:h + 1])
+                    e = float(np.max(np.abs(got - ref[n])) / max(np.max(np.abs(ref[n])), 1e-30))
+                    worst[n] = max(worst.get(n, 0.0), e)
+                got = _host_f64(first["dh0"][b:b + 1, h:h + 1])
+                e = float(np.max(np.abs(got - ref["dh0"])) / max(np.max(np.abs(ref["dh0"])), 1e-30))
+                worst["dh0"] = max(worst.get("dh0", 0.0), e)
+            tol = 2e-2 if wl.dtype == "bf16" else 1e-4
+            if not all(e <= tol for e in worst.values()):
+                raise SystemExit(f"parity check failed: {worst}")
+            rec["parity"] = dict(worst, chains="(first sequence, first head), (last, last)")
     print(json.dumps(rec), flush=True)
 
 
@@ -447,7 +449,8 @@ def main():
                     help="forward (default) or backward entry point")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-parity", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the parity check made with the oracle leg's results")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device-to-device copies, whose HBM "
                          "counter readings calibrate the kernel's FETCH_SIZE/WRITE_SIZE")
@@ -470,15 +473,13 @@ def main():
     import torch
 
     import gated_deltanet_recurrence_delta_amd as gdn
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from hip_case import device_inputs
 
     wl = synth.WORKLOADS[args.workload]
     form = args.form or ("recurrent" if args.workload == "decode" else "chunked")
     inp = synth.generate(wl)
     sets = []
     for _ in range(max(1, args.sets)):
-        d = device_inputs(inp)
+        d = _device_inputs(inp)
         d["out"] = torch.empty(d["v"].shape, dtype=d["v"].dtype, device="cuda")
         d["hT"] = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
         sets.append(d)
@@ -525,13 +526,10 @@ def main():
 
     copy_gbs = copy_reference(algorithmic_bytes(wl, inp.h0 is not None), stream)
 
-    # The sampled parity check (CPU oracle) runs before the warm-up, so that
-    # the warm-up steps lead straight into the timed ones and the GPU is
-    # not left idle (and its clock low) between them.
+    # The warm-up steps lead straight into the timed ones, so that the GPU
+    # is not left idle (and its clock low) between them; the oracle leg
+    # (timing and parity) runs after the timed steps.
     torch.cuda.synchronize()
-    errs = None
-    if not args.no_parity:
-        errs = parity_sample(inp, sets[0]["out"], sets[0]["hT"])
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -583,10 +581,14 @@ def main():
                      "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
                      "p90_us": float(np.percentile(launch_ms, 90)) * 1e3},
     }
-    if errs is not None:
-        rec["parity"] = {"rel_err_out": errs[0], "rel_err_hT": errs[1], "chains": "first and last"}
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(inp)
+        # sets[0]'s outputs come from its last timed step (identical inputs,
+        # bitwise-deterministic kernel)
+        rec["cpu_baseline"], errs = cpu_baseline(inp, sets[0]["out"], sets[0]["hT"],
+                                                 check=not args.no_parity)
+        if errs is not None:
+            rec["parity"] = {"rel_err_out": errs[0], "rel_err_hT": errs[1],
+                             "chains": "all (the oracle leg's whole-workload run)"}
     print(json.dumps(rec), flush=True)
 
 
