@@ -188,3 +188,13 @@ def test_wide_head_shape_two_chains():
                       dtype="bf16", h0_std=0.02)
     inp = synth.generate(wl)
     _check(inp, synth.output_grads(inp, 819))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_sequence(dtype):
+    """4,096 tokens (128 chunks through both serial sweeps) with slow decay and
+    a nonzero initial state: rounding must not build up along the chain."""
+    wl = synth.custom(name="bwd_long", seed=720, B=1, T=4096, H=2, dk=32, dv=32, dtype=dtype,
+                      h0_std=0.3, g_mean=-4.0)
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 820))
