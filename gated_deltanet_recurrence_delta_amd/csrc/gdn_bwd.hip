@@ -39,8 +39,9 @@
 //   dg      = reverse cumulative sum of dgamma within the chunk, the w terms
 //             summed as sum_{u < t} dw_u w_u (what they add up to).
 //
-// Four kernels, all in fp32 (bf16 storage is widened on load, the token
-// gradients rounded to nearest even on store):
+// Four kernels, all in fp32, their products on the fp32 matrix cores (bf16
+// storage is widened on load, the token gradients rounded to nearest even on
+// store):
 //   prep     (chunk, head), parallel:  T and P of every chunk;
 //   states   (chain, 16-column tile), serial over chunks: the state at every
 //            chunk's entry, from h0;
@@ -73,11 +74,6 @@ struct BShape {
 
 __device__ inline float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-template <typename TI>
-__device__ inline float ldf(const TI* __restrict__ p, long i) {
-  return (float)p[i];
-}
-
 __device__ inline void seq_info(const int32_t* __restrict__ cu, const BShape& p, int n, long& row0, int& len) {
   if (cu) {
     row0 = cu[n];
@@ -108,15 +104,20 @@ __device__ inline int find_seq(const int32_t* __restrict__ cu, const BShape& p, 
 
 // In-chunk cumulative log-decay: gv is token tid's g (0 past the chunk's
 // length and for tid >= C); wave 0 forms the inclusive prefix sum with a
-// fixed shuffle tree (every kernel forms it the same way) and writes gam.
+// fixed shuffle tree and writes gam.  Every kernel forms gam with this scan.
+__device__ inline float chunk_scan(float gv, int tid) {
+  float x = gv;
+#pragma unroll
+  for (int off = 1; off < BC; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (tid >= off) x += y;
+  }
+  return x;
+}
+
 __device__ inline void chunk_gamma(float gv, int tid, float* gam) {
   if (tid < 64) {
-    float x = gv;
-#pragma unroll
-    for (int off = 1; off < BC; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (tid >= off) x += y;
-    }
+    const float x = chunk_scan(gv, tid);
     if (tid < BC) gam[tid] = x;
   }
 }
@@ -277,16 +278,11 @@ struct StateBlocks {
   static constexpr int PER = (NBM + 3) / 4;      // blocks per wave (some waves may own fewer)
 };
 
-// Wave 0 forms the chunk's cumulative log-decay gam (see chunk_gamma), and
+// Wave 0 forms the chunk's cumulative log-decay gam (as chunk_gamma), and
 // from it Gam_t = exp(gam_t) and w_t = exp(gam_{C-1} - gam_t).
 __device__ inline void chunk_decay(float gv, int tid, float* gam, float* Gam, float* wv) {
   if (tid < 64) {
-    float x = gv;
-#pragma unroll
-    for (int off = 1; off < BC; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (tid >= off) x += y;
-    }
+    const float x = chunk_scan(gv, tid);
     const float last = __shfl(x, BC - 1, 64);
     if (tid < BC) {
       gam[tid] = x;
