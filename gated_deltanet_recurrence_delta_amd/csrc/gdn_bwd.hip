@@ -67,10 +67,26 @@ constexpr int NT = 256; // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BShape {
-  int B, T, H, dv;  // T: tokens per sequence (dense) or in total (packed)
-  int nslots;       // chunk slots per head
-  int ntile;        // dv / TW
+  int B, T, H, dv;      // T: tokens per sequence (dense) or in total (packed)
+  int nslots;           // chunk slots per head
+  int ntile;            // dv / TW
+  int nseg, seg_chunks; // the two serial sweeps: segments per sequence, chunks per segment
 };
+
+// Sequence segments of the two serial sweeps.  A dense batch with fewer
+// (chain, tile) workgroups than two per CU runs each sequence as nseg
+// segments, one workgroup per (chain, segment, tile).  A token's transition
+// M -> alpha (I - beta k k^T) M has spectral norm alpha max(1, |1 - beta |k|^2|),
+// and the state gradient goes back through the same (symmetric) map.  So the
+// states sweep of a segment starts from a zero state at the latest chunk
+// boundary behind the segment where the product of those norms is below
+// e^-HALO_NATS (or from h0 at the sequence start).  The adjoint sweep starts
+// from a zero gradient at the earliest chunk boundary after the segment where
+// the product over the chunks in between is below that bound (or from dhT at
+// the sequence end).  Either way the result differs from the unsegmented one
+// by less than that factor beyond rounding.  The halo chunks are computed but
+// not stored.
+constexpr float HALO_NATS = 40.f;
 
 __device__ inline float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -124,6 +140,32 @@ __device__ inline void chunk_gamma(float gv, int tid, float* gam) {
 
 __device__ inline float token_f(const float* __restrict__ x, long row0, int t0, int Lc, int H, int h, int tid) {
   return tid < Lc ? x[(row0 + t0 + tid) * H + h] : 0.f;
+}
+
+// Log of the product of the per-token transition-norm bounds over chunk c
+// (log alpha + log max(1, |1 - beta |k|^2|) summed over its tokens), formed by
+// one wave (every lane returns it).
+template <typename TI, int DK>
+__device__ inline float chunk_log_norm(const TI* __restrict__ k, const float* __restrict__ g,
+                                       const float* __restrict__ beta, long row0, int len, int H, int h, int c,
+                                       int lane) {
+  const int t0 = c * BC, Lc = min(BC, len - t0);
+  float e = 0.f;
+  if (lane < Lc) {
+    const long th = (row0 + t0 + lane) * H + h;
+    const TI* kr = k + th * DK;
+    float n2 = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < DK; ++i) {
+      const float x = (float)kr[i];
+      n2 = __builtin_fmaf(x, x, n2);
+    }
+    const float f = fabsf(1.f - beta[th] * n2);
+    e = g[th] + (f > 1.f ? __logf(f) : 0.f);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) e += __shfl_xor(e, d, 64);
+  return e;
 }
 
 // A chunk's C rows of a (token, head, W) tensor (columns col0 .. col0+W-1 of
@@ -305,13 +347,32 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
   __shared__ float ks[BC][SK], vs[BC][ST], Ts[BC][SC], Xs[BC][ST], Ws[BC][ST], Ms[DK][ST];
   __shared__ float gam[BC], Gam[BC], wv[BC], bet[BC];
   const int tid = threadIdx.x, H = p.H, dv = p.dv;
-  const int chain = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
+  const int chain = blockIdx.x / (p.ntile * p.nseg), seg = (blockIdx.x / p.ntile) % p.nseg;
+  const int tile = blockIdx.x % p.ntile;
   const int n = chain / H, h = chain % H, col0 = tile * TW;
   long row0;
   int len;
   seq_info(cu, p, n, row0, len);
   const int key = slot_key(cu, p, n), nch = (len + BC - 1) / BC;
   const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
+  // chunks [c0, c1) are stored; the sweep starts at cs <= c0 (see HALO_NATS)
+  int c0 = 0, c1 = nch, cs = 0;
+  if (p.nseg > 1) {
+    __shared__ int sStart;
+    c0 = min(seg * p.seg_chunks, nch);
+    c1 = min(c0 + p.seg_chunks, nch);
+    if (wave == 0) {
+      int cc = c0;
+      float acc = 0.f;  // log of the norm product over chunks [cc, c0)
+      while (cc > 0 && acc > -HALO_NATS) {
+        --cc;
+        acc += chunk_log_norm<TI, DK>(k, g, beta, row0, len, H, h, cc, tid);
+      }
+      if (tid == 0) sStart = cc;
+    }
+    __syncthreads();
+    cs = sStart;
+  }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 M[SBk::PER];
 #pragma unroll
@@ -319,7 +380,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
     const int blk = wave + 4 * m;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
-      M[m][x] = (h0 && blk < SBk::NBM) ? h0[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln] : 0.f;
+      M[m][x] = (h0 && cs == 0 && blk < SBk::NBM)
+                    ? h0[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln]
+                    : 0.f;
   }
 
   // the next chunk's inputs, fetched into registers while this one computes
@@ -337,11 +400,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
       br = token_f(beta, row0, t0, Lc, H, h, tid);
     }
   };
-  if (nch > 0) fetch(0);
+  if (cs < c1) fetch(cs);
 
-  for (int c = 0; c < nch; ++c) {
+  for (int c = cs; c < c1; ++c) {
     const size_t sb = (size_t)h * p.nslots + key + c;
     float* mo = wsM + sb * DK * dv;
+    const bool store = c >= c0;  // halo chunks are not stored
 #pragma unroll
     for (int m = 0; m < SBk::PER; ++m) {
       const int blk = wave + 4 * m;
@@ -349,7 +413,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = 16 * blk + 4 * lq + x;
-          mo[(long)i * dv + col0 + ln] = M[m][x];
+          if (store) mo[(long)i * dv + col0 + ln] = M[m][x];
           Ms[i][ln] = M[m][x];
         }
       }
@@ -359,7 +423,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_states_kernel(const TI* __restrict_
     tr.store_s<SC>(Ts, tid);
     if (tid < BC) bet[tid] = br;
     chunk_decay(gr, tid, gam, Gam, wv);
-    if (c + 1 < nch) fetch(c + 1);
+    if (c + 1 < c1) fetch(c + 1);
     __syncthreads();
     if (wave < 2) {  // X = beta (V - Gam K M), row block `wave`
       const int r16 = 16 * wave + ln;
@@ -420,13 +484,32 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
   __shared__ float KDs[BC][ST], PDs[BC][ST], Zs[BC][ST], Ds[DK][ST];
   __shared__ float gam[BC], Gam[BC], wv[BC], bet[BC];
   const int tid = threadIdx.x, H = p.H, dv = p.dv;
-  const int chain = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
+  const int chain = blockIdx.x / (p.ntile * p.nseg), seg = (blockIdx.x / p.ntile) % p.nseg;
+  const int tile = blockIdx.x % p.ntile;
   const int n = chain / H, h = chain % H, col0 = tile * TW;
   long row0;
   int len;
   seq_info(cu, p, n, row0, len);
   const int key = slot_key(cu, p, n), nch = (len + BC - 1) / BC;
   const int wave = tid >> 6, ln = tid & 15, lq = (tid >> 4) & 3;
+  // chunks [c0, c1) are stored; the reverse sweep starts at ce >= c1 (see HALO_NATS)
+  int c0 = 0, c1 = nch, ce = nch;
+  if (p.nseg > 1) {
+    __shared__ int sEnd;
+    c0 = min(seg * p.seg_chunks, nch);
+    c1 = min(c0 + p.seg_chunks, nch);
+    if (wave == 0) {
+      int cc = c1;
+      float acc = 0.f;  // log of the norm product over chunks [c1, cc)
+      while (cc < nch && acc > -HALO_NATS) {
+        acc += chunk_log_norm<TI, DK>(k, g, beta, row0, len, H, h, cc, tid);
+        ++cc;
+      }
+      if (tid == 0) sEnd = cc;
+    }
+    __syncthreads();
+    ce = sEnd;
+  }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 D[SBk::PER];
 #pragma unroll
@@ -434,7 +517,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
     const int blk = wave + 4 * m;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
-      D[m][x] = (dhT && blk < SBk::NBM) ? dhT[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln] : 0.f;
+      D[m][x] = (dhT && ce == nch && blk < SBk::NBM)
+                    ? dhT[((long)chain * DK + 16 * blk + 4 * lq + x) * dv + col0 + ln]
+                    : 0.f;
   }
 
   // the previous chunk's inputs, fetched into registers while this one computes
@@ -455,11 +540,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
       br = token_f(beta, row0, t0, Lc, H, h, tid);
     }
   };
-  if (nch > 0) fetch(nch - 1);
+  if (ce > c0) fetch(ce - 1);
 
-  for (int c = nch - 1; c >= 0; --c) {
+  for (int c = ce - 1; c >= c0; --c) {
     const size_t sb = (size_t)h * p.nslots + key + c;
     float* dout = wsD + sb * DK * dv;
+    const bool store = c < c1;  // halo chunks are not stored
 #pragma unroll
     for (int m = 0; m < SBk::PER; ++m) {
       const int blk = wave + 4 * m;
@@ -467,7 +553,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = 16 * blk + 4 * lq + x;
-          dout[(long)i * dv + col0 + ln] = D[m][x];
+          if (store) dout[(long)i * dv + col0 + ln] = D[m][x];
           Ds[i][ln] = D[m][x];
         }
       }
@@ -479,7 +565,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
     pr.store_s<SC>(Ps, tid);
     if (tid < BC) bet[tid] = br;
     chunk_decay(gr, tid, gam, Gam, wv);
-    if (c > 0) fetch(c - 1);
+    if (c > c0) fetch(c - 1);
     __syncthreads();
     if (wave < 2) {  // KD = K dM' on row block `wave`
       const int r16 = 16 * wave + ln;
@@ -531,7 +617,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_adjoint_kernel(const TI* __restrict
     }
     __syncthreads();
   }
-  if (dh0) {
+  if (dh0 && c0 == 0) {  // the segment holding the sequence start
 #pragma unroll
     for (int m = 0; m < SBk::PER; ++m) {
       const int blk = wave + 4 * m;
@@ -853,7 +939,7 @@ int launch_bwd(const void* q, const void* k, const void* v, const float* g, cons
   float* wsD = wsM + sm;
   const TI *qq = static_cast<const TI*>(q), *kk = static_cast<const TI*>(k), *vv = static_cast<const TI*>(v);
   const TI* oo = static_cast<const TI*>(dO);
-  const dim3 chunks(p.nslots, p.H), chains(p.B * p.H * p.ntile);
+  const dim3 chunks(p.nslots, p.H), chains(p.B * p.H * p.ntile * p.nseg);
   if (p.B * p.H * p.ntile == 0) return GDN_OK;
   hipLaunchKernelGGL((bwd_prep_kernel<TI, DK>), chunks, dim3(NT), 0, st, qq, kk, g, beta, cu, wsT, wsP, p);
   hipLaunchKernelGGL((bwd_states_kernel<TI, DK>), chains, dim3(NT), 0, st, kk, vv, g, beta, h0, cu, wsT, wsM, p);
@@ -916,6 +1002,25 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
   p.dv = dvn;
   p.nslots = (int)nslots;
   p.ntile = dvn / TW;
+  // Sequence segments (see HALO_NATS) for dense batches with fewer (chain,
+  // tile) workgroups than two per CU and at least 16 chunks per sequence.
+  p.nseg = 1;
+  p.seg_chunks = 0;
+  if (!cu_seqlens) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      ncu = 0;
+    const long nwg = (long)B * H * p.ntile, slots = 2L * ncu;
+    const int nch = (T + BC - 1) / BC;
+    if (nwg > 0 && nwg < slots && nch >= 16) {
+      const int nseg = (int)(slots / nwg < nch / 8 ? slots / nwg : nch / 8);
+      if (nseg >= 2) {
+        p.seg_chunks = (nch + nseg - 1) / nseg;
+        p.nseg = (nch + p.seg_chunks - 1) / p.seg_chunks;  // every segment holds a chunk
+      }
+    }
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
   return dtype == GDN_BF16 ? launch_dtype<__bf16>(dkn, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,

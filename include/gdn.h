@@ -231,7 +231,16 @@ int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c,
  * gradient swept backwards over the chunks, the per-chunk token gradients);
  * results are valid once the stream has been synchronised.  Arithmetic is
  * fp32 throughout; results are bitwise reproducible on one device (no
- * atomics).  The library allocates nothing and keeps no pointer.
+ * atomics).  A dense batch with fewer chains x 16-column tiles than twice
+ * the device's CUs, and at least 16 chunks per sequence, runs the two
+ * sweeps as sequence segments: a segment's state sweep starts from zero at
+ * the latest chunk boundary behind it where the product of the per-token
+ * transition norms exp(g) max(1, |1 - beta |k|^2|) is below e^-40 (or from
+ * h0 at the sequence start), and its gradient sweep from zero at the
+ * earliest boundary after it where the product is below that bound (or
+ * from dhT at the sequence end); so the result differs from an uncut run
+ * by less than that factor beyond rounding.  Packed batches are never cut.
+ * The library allocates nothing and keeps no pointer.
  */
 int gdn_bwd(const void* q, const void* k, const void* v, const float* g,
             const float* beta, const float* h0, const int32_t* cu_seqlens,

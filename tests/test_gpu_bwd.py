@@ -198,3 +198,32 @@ def test_long_sequence(dtype):
                       h0_std=0.3, g_mean=-4.0)
     inp = synth.generate(wl)
     _check(inp, synth.output_grads(inp, 820))
+
+
+@pytest.mark.parametrize("kind", ["fast_decay", "slow_decay", "no_decay"])
+def test_segmented_sweeps(kind):
+    """One long chain with few (chain, tile) workgroups: both serial sweeps
+    run as segments with halos (2,048 tokens = 64 chunks in 8 segments).
+    With no decay every halo reaches the sequence end, so the result is exact
+    up to rounding; with decay the halos stop where the transition-norm
+    product is below e^-40."""
+    g_mean = {"fast_decay": 0.0, "slow_decay": -4.0, "no_decay": 0.0}[kind]
+    wl = synth.custom(name=f"bwd_seg_{kind}", seed=721, B=1, T=2048, H=1, dk=32, dv=32,
+                      dtype="f32", h0_std=0.3, g_mean=g_mean)
+    inp = synth.generate(wl)
+    if kind == "no_decay":
+        inp.g[...] = 0.0
+    og = synth.output_grads(inp, 821)
+    a = _check(inp, og, label=wl.name)
+    b = _run(inp, og)
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), name  # deterministic
+
+
+def test_segmented_bf16_wide():
+    """Segments at d = 128, bf16: one chain, 1,024 tokens (32 chunks, 8 tiles
+    of 16 columns -> 4 segments)."""
+    wl = synth.custom(name="bwd_seg_wide", seed=722, B=1, T=1024, H=1, dk=128, dv=128,
+                      dtype="bf16", h0_std=0.02, g_mean=-2.0)
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 822))
