@@ -215,8 +215,9 @@ int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c,
  *                                       the gradient of h0 whether or not h0
  *                                       was given
  *   workspace : DEVICE buffer of at least gdn_bwd_workspace_size(...) bytes,
- *        owned by the caller; overwritten (no contents needed on entry or kept
- *        on return).  It holds, per head and 32-token chunk, two 32x32 fp32
+ *        4-byte aligned, owned by the caller; overwritten (no contents needed
+ *        on entry or kept on return).  Calls that share a workspace must be
+ *        ordered (one stream, or synchronised); overlapping calls race.  It holds, per head and 32-token chunk, two 32x32 fp32
  *        matrices, the state at the chunk's entry and the gradient reaching
  *        its exit state (dk x dv fp32 each): about
  *        (total tokens / 32 + B + 1) * H * (8 KB + 8 dk dv) bytes.
