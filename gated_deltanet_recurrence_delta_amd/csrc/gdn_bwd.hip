@@ -992,7 +992,9 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
   const size_t nslots = slots_per_head(ttot, B);
   if ((long long)(nslots * (size_t)H) > 0x7fffffffLL || nslots > 0x7fffffffULL) return GDN_ERR_UNSUPPORTED;
   const size_t need = ws_floats(nslots, H, dkn, dvn) * sizeof(float);
-  if (B > 0 && (!workspace || workspace_bytes < 0 || (size_t)workspace_bytes < need)) return GDN_ERR_INVALID_ARG;
+  if (B > 0 && (!workspace || workspace_bytes < 0 || (size_t)workspace_bytes < need ||
+                (reinterpret_cast<uintptr_t>(workspace) & 3u)))
+    return GDN_ERR_INVALID_ARG;
   if ((long)B * H * (dvn / TW) > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   BShape p;

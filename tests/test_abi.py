@@ -215,6 +215,7 @@ def test_bwd_null_required_pointer(name):
                                      (dict(dk_=16), UNSUPPORTED), (dict(dv_=96), UNSUPPORTED),
                                      (dict(H=70000), UNSUPPORTED),
                                      (dict(workspace_bytes=-1), INVALID),
+                                     (dict(workspace=P + 2), INVALID),
                                      (dict(workspace_bytes=4 * _ws_floats(8, 1, 1, 32, 32) - 1),
                                       INVALID)])
 def test_bwd_invalid(kw, code):
