@@ -27,6 +27,10 @@ time, with every forward state stored (small inputs only):
 
 and dh0 is Lam after the first token.  Layouts are those of the forward
 oracle (``oracle.fwd_seq``): dense (B,T,H,.) or packed with ``cu_seqlens``.
+
+:func:`bwd_chunked` evaluates the same gradients by the chunkwise reverse
+pass (a derived block algebra, not on the pages), as the brute-force check of
+that algebra.
 """
 from __future__ import annotations
 
@@ -104,4 +108,110 @@ def bwd_seq(q, k, v, g, beta, h0=None, cu_seqlens=None, do=None, dhT=None):
             grads["dq"][sel], grads["dk"][sel], grads["dv"][sel] = gq, gk, gv
             grads["dg"][sel], grads["dbeta"][sel] = gg, gb
             grads["dh0"][n, h] = Lam
+    return grads
+
+
+def bwd_chunked(q, k, v, g, beta, h0=None, cu_seqlens=None, do=None, dhT=None, chunk=32):
+    """The same gradients by the chunkwise reverse pass, in FP64, as a check
+    of that block algebra (the GPU kernels follow it; this function shares no
+    code with them).  Per chunk of C tokens with entry state M, exit
+    gradient dM', gamma the in-chunk cumulative g, Gam = exp(gamma),
+    w = exp(gamma_C - gamma), E_ij = exp(gamma_i - gamma_j):
+
+        A = strict_lower(diag(beta) K K^T . E),  T = (I + A)^-1,
+        X = diag(beta)(V - diag(Gam) K M),  U = T X,  P = lower(Q K^T . E),
+        dU = P^T dO + diag(w) K dM',  dX = T^T dU,
+        dM = Gam_C dM' + Q^T diag(Gam) dO - K^T diag(beta Gam) dX,
+
+    and the token gradients of each chunk from its M, dM', X, U, dU, dX by
+    the chain rule through A, E, Gam and w (written out below).  The entry
+    states come from a forward pass over the chunks; the exit gradients from
+    a backward pass over them starting at dhT.
+    """
+    q, k, v, g, beta, h0, do, dhT = map(_f64, (q, k, v, g, beta, h0, do, dhT))
+    if cu_seqlens is not None:
+        T, H, dk_ = q.shape
+        B = len(cu_seqlens) - 1
+    else:
+        B, T, H, dk_ = q.shape
+    dv_ = v.shape[-1]
+    if do is None:
+        do = np.zeros(v.shape)
+    grads = {name: np.zeros(x.shape) for name, x in
+             (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
+    grads["dh0"] = np.zeros((B, H, dk_, dv_))
+
+    def chunk_terms(Q, K, G, Bt):
+        L = K.shape[0]
+        gam = np.cumsum(G)
+        Gam = np.exp(gam)
+        E = np.exp(gam[:, None] - gam[None, :])
+        low = np.tril(np.ones((L, L)), -1)
+        lowi = np.tril(np.ones((L, L)))
+        KK = K @ K.T
+        A = Bt[:, None] * KK * E * low
+        Tm = np.linalg.inv(np.eye(L) + A)
+        P = (Q @ K.T) * E * lowi
+        w = np.exp(gam[-1] - gam)
+        return Gam, E, low, lowi, KK, A, Tm, P, w
+
+    for n, sel in _chains(q, cu_seqlens):
+        Qa, Ka, Va, Ga, Ba, DOa = q[sel], k[sel], v[sel], g[sel], beta[sel], do[sel]
+        L = Qa.shape[0]
+        starts = list(range(0, L, chunk))
+        for h in range(H):
+            cut = [slice(s, min(s + chunk, L)) for s in starts]
+            terms = [chunk_terms(Qa[c, h], Ka[c, h], Ga[c, h], Ba[c, h]) for c in cut]
+            # forward over chunks: entry states
+            M = np.zeros((dk_, dv_)) if h0 is None else h0[n, h].copy()
+            Ms = []
+            for c, (Gam, E, low, lowi, KK, A, Tm, P, w) in zip(cut, terms):
+                Ms.append(M)
+                X = Ba[c, h][:, None] * (Va[c, h] - Gam[:, None] * (Ka[c, h] @ M))
+                M = Gam[-1] * M + Ka[c, h].T @ (w[:, None] * (Tm @ X))
+            # backward over chunks: exit gradients
+            D = np.zeros((dk_, dv_)) if dhT is None else dhT[n, h].copy()
+            Ds = [None] * len(cut)
+            for i in range(len(cut) - 1, -1, -1):
+                c = cut[i]
+                Gam, E, low, lowi, KK, A, Tm, P, w = terms[i]
+                Ds[i] = D
+                dU = P.T @ DOa[c, h] + w[:, None] * (Ka[c, h] @ D)
+                dX = Tm.T @ dU
+                D = (Gam[-1] * D + Qa[c, h].T @ (Gam[:, None] * DOa[c, h])
+                     - Ka[c, h].T @ ((Ba[c, h] * Gam)[:, None] * dX))
+            grads["dh0"][n, h] = D
+            # per-chunk token gradients
+            out = {"dq": np.zeros((L, dk_)), "dk": np.zeros((L, dk_)), "dv": np.zeros((L, dv_)),
+                   "dg": np.zeros(L), "dbeta": np.zeros(L)}
+            for i, c in enumerate(cut):
+                Gam, E, low, lowi, KK, A, Tm, P, w = terms[i]
+                Qc, Kc, Vc, Bc, DOc = Qa[c, h], Ka[c, h], Va[c, h], Ba[c, h], DOa[c, h]
+                M, Dx = Ms[i], Ds[i]
+                Y = Kc @ M
+                R = Vc - Gam[:, None] * Y
+                U = Tm @ (Bc[:, None] * R)
+                KD = Kc @ Dx
+                dU = P.T @ DOc + w[:, None] * KD
+                dX = Tm.T @ dU
+                dA = -(dX @ U.T) * low
+                dP = (DOc @ U.T) * lowi
+                Gm = dA * E * Bc[:, None]
+                dPE = dP * E
+                Z = dA * A + dP * P * low
+                dw = np.sum(U * KD, axis=1)
+                dGam = -Bc * np.sum(dX * Y, axis=1) + np.sum(DOc * (Qc @ M), axis=1)
+                dGam[-1] += np.sum(M * Dx)
+                dgam = Z.sum(1) - Z.sum(0) + dGam * Gam - dw * w
+                dgam[-1] += np.sum(dw * w)
+                out["dv"][c] = Bc[:, None] * dX
+                out["dbeta"][c] = np.sum(dX * R, axis=1) + np.sum(dA * KK * E, axis=1)
+                out["dq"][c] = Gam[:, None] * (DOc @ M.T) + dPE @ Kc
+                out["dk"][c] = (-((Bc * Gam)[:, None] * dX) @ M.T + Gm @ Kc + Gm.T @ Kc
+                                + dPE.T @ Qc + w[:, None] * (U @ Dx.T))
+                out["dg"][c] = np.cumsum(dgam[::-1])[::-1]
+            for name in ("dq", "dk", "dv", "dg", "dbeta"):
+                tgt = grads[name][sel]
+                tgt[:, h] = out[name]
+                grads[name][sel] = tgt
     return grads
