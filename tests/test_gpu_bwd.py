@@ -227,3 +227,29 @@ def test_segmented_bf16_wide():
                       dtype="bf16", h0_std=0.02, g_mean=-2.0)
     inp = synth.generate(wl)
     _check(inp, synth.output_grads(inp, 822))
+
+
+@pytest.mark.parametrize("name", ["wide_head", "small_state"])
+def test_full_workload_sampled_chains(name):
+    """The full workload (wide_head: B=4 H=16 T=4096 d=128 bf16; small_state:
+    B=8 H=16 T=4096 d=32, whose sweeps run in segments) in one call, in the
+    configuration bench.py --pass bwd times; the oracle checks two chains,
+    (first sequence, first head) and (last, last), every gradient."""
+    wl = synth.WORKLOADS[name]
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 1000 + wl.seed)
+    grads = _run(inp, og)
+    tol = TOL[wl.dtype]
+    for b, h in ((0, 0), (wl.B - 1, wl.H - 1)):
+        cut = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]
+        ref = bwd_seq(*(cut(inp.as_f64(n)) for n in ("q", "k", "v", "g", "beta")),
+                      None if inp.h0 is None else inp.as_f64("h0")[b:b + 1, h:h + 1], None,
+                      cut(og.as_f64("dout")),
+                      None if og.dhT is None else og.as_f64("dhT")[b:b + 1, h:h + 1])
+        errs = {n: _rel(host_f64(grads[n][b:b + 1, :, h:h + 1]), ref[n])
+                for n in ("dq", "dk", "dv", "dg", "dbeta")}
+        errs["dh0"] = _rel(host_f64(grads["dh0"][b:b + 1, h:h + 1]), ref["dh0"])
+        print(f"{name} chain ({b},{h}): " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+              flush=True)
+        for n, e in errs.items():
+            assert e <= tol, (n, e)
