@@ -15,7 +15,7 @@ import os
 
 __all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
            "gdn_bwd_workspace_size", "fwd", "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent",
-           "bwd", "GdnError", "lib_path", "load", "version"]
+           "bwd", "gated_delta_rule", "GdnError", "lib_path", "load", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -333,3 +333,41 @@ def bwd(q, k, v, g, beta, dout, h0=None, cu_seqlens=None, dhT=None, want_dh0=Tru
     if rc != 0:
         raise GdnError(rc, strerror(rc))
     return grads
+
+
+# -------------------------------------------------------------- autograd ---
+
+def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None):
+    """(out, hT) of ``fwd`` as a differentiable torch operation: the forward
+    runs gdn_fwd and the backward gdn_bwd (from the saved inputs), giving
+    gradients for q, k, v, g, beta and h0.  Arguments as for ``fwd``."""
+    return _gdr_function().apply(q, k, v, g, beta, h0, cu_seqlens)
+
+
+_GDR = None
+
+
+def _gdr_function():
+    global _GDR
+    if _GDR is None:
+        import torch
+
+        class _GatedDeltaRule(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, g, beta, h0, cu_seqlens):
+                out, hT = fwd(q, k, v, g, beta, h0, cu_seqlens)
+                ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens)
+                ctx.has_h0 = h0 is not None
+                return out, hT
+
+            @staticmethod
+            def backward(ctx, dout, dhT):
+                q, k, v, g, beta, h0, cu_seqlens = ctx.saved_tensors
+                dout = torch.zeros_like(v) if dout is None else dout.contiguous()
+                dhT = None if dhT is None else dhT.contiguous()
+                gr = bwd(q, k, v, g, beta, dout, h0=h0, cu_seqlens=cu_seqlens, dhT=dhT,
+                         want_dh0=ctx.has_h0)
+                return gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["dh0"], None
+
+        _GDR = _GatedDeltaRule
+    return _GDR

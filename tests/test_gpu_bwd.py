@@ -253,3 +253,24 @@ def test_full_workload_sampled_chains(name):
               flush=True)
         for n, e in errs.items():
             assert e <= tol, (n, e)
+
+
+def test_autograd_function():
+    """gated_delta_rule as a torch autograd operation: a scalar loss built
+    from out and hT back-propagates to every input (including h0) with the
+    oracle's gradients of the same loss."""
+    import gated_deltanet_recurrence_delta_amd as gdn
+
+    wl = synth.custom(name="bwd_autograd", seed=723, B=2, T=70, H=2, dk=64, dv=32,
+                      dtype="f32", h0_std=0.3)
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 823)
+    x = {n: dev(getattr(inp, n)).requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "h0")}
+    out, hT = gdn.gated_delta_rule(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    loss = (out * dev(og.dout)).sum() + (hT * dev(og.dhT)).sum()
+    loss.backward()
+    ref = _oracle(inp, og)
+    for n, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
+                     ("h0", "dh0")):
+        e = _rel(host_f64(x[n].grad), ref[gname])
+        assert e <= 1e-4, (gname, e)
