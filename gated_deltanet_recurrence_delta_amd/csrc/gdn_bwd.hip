@@ -649,7 +649,7 @@ struct GradLds {
 };
 
 template <typename TI, int DK>
-__global__ __launch_bounds__(NT, 2) void bwd_grad_kernel(
+__global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const TI* __restrict__ dO,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const float* __restrict__ wsT, const float* __restrict__ wsP, const float* __restrict__ wsM,
