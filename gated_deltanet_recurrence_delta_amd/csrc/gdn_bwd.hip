@@ -42,7 +42,8 @@
 // Four kernels, all in fp32, their products on the fp32 matrix cores (bf16
 // storage is widened on load, the token gradients rounded to nearest even on
 // store):
-//   prep     (chunk, head), parallel:  T and P of every chunk;
+//   prep     (chunk, head), parallel:  T and P of every chunk (T by 16 x 16
+//            blocks: two diagonal substitutions, then the off-diagonal block);
 //   states   (chain, 16-column tile), serial over chunks: the state at every
 //            chunk's entry, from h0;
 //   adjoint  (chain, 16-column tile), serial over chunks in reverse: the
@@ -297,14 +298,32 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(const TI* __restrict__ q, 
     }
   }
   __syncthreads();
-  // (I + A)^-1 by forward substitution, one column per thread
+  // (I + A)^-1 in 16 x 16 blocks: the two diagonal blocks by forward
+  // substitution (one column per thread), then T21 = -T22 (A21 T11).  The
+  // upper-right block of As, zero in A, holds A21 T11.
+  constexpr int HB = BC / 2;
   if (tid < BC) {
-    const int u = tid;
-    for (int t = 0; t < BC; ++t) {
+    const int o = HB * (tid / HB), u = tid % HB;
+    for (int t = 0; t < HB; ++t) {
       float x = t == u ? 1.f : 0.f;
-      for (int r = u; r < t; ++r) x = __builtin_fmaf(-As[t][r], Ts[r][u], x);
-      Ts[t][u] = x;
+      for (int r = u; r < t; ++r) x = __builtin_fmaf(-As[o + t][o + r], Ts[o + r][o + u], x);
+      Ts[o + t][o + u] = x;
+      Ts[t][HB + u] = 0.f;  // upper-right block of T
     }
+  }
+  __syncthreads();
+  {
+    const int i = tid / HB, j = tid % HB;  // NT = HB * HB
+    float x = 0.f;
+    for (int r = j; r < HB; ++r) x = __builtin_fmaf(As[HB + i][r], Ts[r][j], x);
+    As[i][HB + j] = x;
+  }
+  __syncthreads();
+  {
+    const int i = tid / HB, j = tid % HB;
+    float x = 0.f;
+    for (int r = 0; r <= i; ++r) x = __builtin_fmaf(Ts[HB + i][HB + r], As[r][HB + j], x);
+    Ts[HB + i][j] = -x;
   }
   __syncthreads();
   for (int e = tid; e < BC * BC; e += NT) wsT[base + e] = Ts[e / BC][e % BC];
