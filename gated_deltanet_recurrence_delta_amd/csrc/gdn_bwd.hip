@@ -239,6 +239,27 @@ __device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// acc + sum over the contraction of A B, in steps of four (the lane's
+// element of step kk is a(kk), b(kk)).  The operands of G steps are read
+// before their products are issued, so the LDS reads overlap the
+// matrix-core work instead of waiting in front of every product.
+template <int K, class FA, class FB>
+__device__ inline f32x4 mfma_chain(f32x4 acc, FA a, FB b) {
+  constexpr int G = K / 4 < 8 ? K / 4 : 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 4 * G) {
+    float av[G], bv[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      av[j] = a(k0 + 4 * j);
+      bv[j] = b(k0 + 4 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc = mfma4(av[j], bv[j], acc);
+  }
+  return acc;
+}
+
 constexpr int SC = BC + 8;  // row stride of the C x C arrays
 constexpr int ST = TW + 8;  // row stride of the tile arrays
 
@@ -747,9 +768,8 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
     // phase A.  waves 0, 1: Y = K M on row block rb, then X;
     //           waves 2, 3: KD = K dM' and P^T dO on row block rb, then dU.
     if (wave < 2) {
-      f32x4 y = zero;
-#pragma unroll
-      for (int kk = 0; kk < DK; kk += 4) y = mfma4(kf(r16, kk + lq), L.u.tile.Mt[kk + lq][ln], y);
+      const f32x4 y = mfma_chain<DK>(zero, [&](int kk) { return kf(r16, kk + lq); },
+                                     [&](int kk) { return L.u.tile.Mt[kk + lq][ln]; });
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int t = 16 * rb + 4 * lq + x;
@@ -757,11 +777,10 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
         L.Xt[t][ln] = L.bet[t] * (L.vt[t][ln] - ex(L.gam[t]) * y[x]);
       }
     } else {
-      f32x4 kd = zero, pd = zero;
-#pragma unroll
-      for (int kk = 0; kk < DK; kk += 4) kd = mfma4(kf(r16, kk + lq), L.u.tile.Dt[kk + lq][ln], kd);
-#pragma unroll
-      for (int kk = 0; kk < BC; kk += 4) pd = mfma4(L.Ps[kk + lq][r16], L.dot[kk + lq][ln], pd);
+      const f32x4 kd = mfma_chain<DK>(zero, [&](int kk) { return kf(r16, kk + lq); },
+                                      [&](int kk) { return L.u.tile.Dt[kk + lq][ln]; });
+      const f32x4 pd = mfma_chain<BC>(zero, [&](int kk) { return L.Ps[kk + lq][r16]; },
+                                      [&](int kk) { return L.dot[kk + lq][ln]; });
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int t = 16 * rb + 4 * lq + x;
@@ -772,9 +791,8 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
     __syncthreads();
     // phase B.  waves 0, 1: U = T X;  waves 2, 3: dX = T^T dU, dV.
     if (wave < 2) {
-      f32x4 uu = zero;
-#pragma unroll
-      for (int kk = 0; kk < BC; kk += 4) uu = mfma4(L.Ts[r16][kk + lq], L.Xt[kk + lq][ln], uu);
+      const f32x4 uu = mfma_chain<BC>(zero, [&](int kk) { return L.Ts[r16][kk + lq]; },
+                                      [&](int kk) { return L.Xt[kk + lq][ln]; });
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int t = 16 * rb + 4 * lq + x;
@@ -782,9 +800,8 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
         pB[x] = __builtin_fmaf(uu[x], L.KDt[t][ln], pB[x]);  // U . KD
       }
     } else {
-      f32x4 dx = zero;
-#pragma unroll
-      for (int kk = 0; kk < BC; kk += 4) dx = mfma4(L.Ts[kk + lq][r16], L.dUt[kk + lq][ln], dx);
+      const f32x4 dx = mfma_chain<BC>(zero, [&](int kk) { return L.Ts[kk + lq][r16]; },
+                                      [&](int kk) { return L.dUt[kk + lq][ln]; });
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int t = 16 * rb + 4 * lq + x;
@@ -804,23 +821,45 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
     // -diag(beta Gam) dX M^T + diag(w) U dM'^T (C x DK, blocks wave + 4 m).
     {
       const int cr = 16 * (wave >> 1) + ln, cc = 16 * (wave & 1) + ln;
+      float xa[TW / 4], oa[TW / 4], ub[TW / 4];
 #pragma unroll
-      for (int kk = 0; kk < TW; kk += 4) {
-        const float b = L.Ut[cc][kk + lq];
-        accXU = mfma4(L.dXt[cr][kk + lq], b, accXU);
-        accOU = mfma4(L.dot[cr][kk + lq], b, accOU);
+      for (int j = 0; j < TW / 4; ++j) {
+        xa[j] = L.dXt[cr][4 * j + lq];
+        oa[j] = L.dot[cr][4 * j + lq];
+        ub[j] = L.Ut[cc][4 * j + lq];
+      }
+#pragma unroll
+      for (int j = 0; j < TW / 4; ++j) {
+        accXU = mfma4(xa[j], ub[j], accXU);
+        accOU = mfma4(oa[j], ub[j], accOU);
       }
     }
-#pragma unroll
-    for (int m = 0; m < NB; ++m) {
-      const int blk = wave + 4 * m, br = 16 * (blk & 1) + ln, bc = 16 * (blk >> 1) + ln;
+    {
+      // the A operands' rows are the same for every block of this wave
+      const int br = 16 * (wave & 1) + ln;
       const float bg = -L.bet[br] * ex(L.gam[br]), w = ex(L.gam[BC - 1] - L.gam[br]);
+      float ao[TW / 4], ax[TW / 4], au[TW / 4];
 #pragma unroll
-      for (int kk = 0; kk < TW; kk += 4) {
-        const float mv = L.u.tile.Mt[bc][kk + lq], dd = L.u.tile.Dt[bc][kk + lq];
-        accQ[m] = mfma4(L.dot[br][kk + lq], mv, accQ[m]);
-        accK[m] = mfma4(bg * L.dXt[br][kk + lq], mv, accK[m]);
-        accK[m] = mfma4(w * L.Ut[br][kk + lq], dd, accK[m]);
+      for (int j = 0; j < TW / 4; ++j) {
+        ao[j] = L.dot[br][4 * j + lq];
+        ax[j] = bg * L.dXt[br][4 * j + lq];
+        au[j] = w * L.Ut[br][4 * j + lq];
+      }
+#pragma unroll
+      for (int m = 0; m < NB; ++m) {
+        const int bc = 16 * ((wave + 4 * m) >> 1) + ln;
+        float mv[TW / 4], dd[TW / 4];
+#pragma unroll
+        for (int j = 0; j < TW / 4; ++j) {
+          mv[j] = L.u.tile.Mt[bc][4 * j + lq];
+          dd[j] = L.u.tile.Dt[bc][4 * j + lq];
+        }
+#pragma unroll
+        for (int j = 0; j < TW / 4; ++j) {
+          accQ[m] = mfma4(ao[j], mv[j], accQ[m]);
+          accK[m] = mfma4(ax[j], mv[j], accK[m]);
+          accK[m] = mfma4(au[j], dd[j], accK[m]);
+        }
       }
     }
   }
@@ -866,9 +905,8 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
   if ((tid & 63) == 0) L.red[wave] = sGC;
   {  // K K^T on block `wave`, then dA, G, dP . E, Z and the second dbeta term
     const int tr0 = 16 * (wave >> 1), uc = 16 * (wave & 1) + ln;
-    f32x4 kk4 = zero;
-#pragma unroll
-    for (int kk = 0; kk < DK; kk += 4) kk4 = mfma4(kf(tr0 + ln, kk + lq), kf(uc, kk + lq), kk4);
+    const f32x4 kk4 = mfma_chain<DK>(zero, [&](int kk) { return kf(tr0 + ln, kk + lq); },
+                                     [&](int kk) { return kf(uc, kk + lq); });
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int t = tr0 + 4 * lq + x;
@@ -886,16 +924,30 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
   }
   __syncthreads();
   // dQ += (dP . E) K;  dK += (G + G^T) K + (dP . E)^T Q
+  // the A operands' rows are the same for every block of this wave
+  const int fbr = 16 * (wave & 1);
+  float fp[BC / 4], fg[BC / 4], ft[BC / 4];
+#pragma unroll
+  for (int j = 0; j < BC / 4; ++j) {
+    const int r = 4 * j + lq;
+    fp[j] = L.u.fin.dPs[fbr + ln][r];
+    fg[j] = L.u.fin.Gs[fbr + ln][r] + L.u.fin.Gs[r][fbr + ln];
+    ft[j] = L.u.fin.dPs[r][fbr + ln];
+  }
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
     const int blk = wave + 4 * m, br = 16 * (blk & 1), bc = 16 * (blk >> 1) + ln;
+    float kv[BC / 4], qv[BC / 4];
 #pragma unroll
-    for (int kk = 0; kk < BC; kk += 4) {
-      const int r = kk + lq;
-      const float kv = kf(r, bc), qv = qf(r, bc);
-      accQ[m] = mfma4(L.u.fin.dPs[br + ln][r], kv, accQ[m]);
-      accK[m] = mfma4(L.u.fin.Gs[br + ln][r] + L.u.fin.Gs[r][br + ln], kv, accK[m]);
-      accK[m] = mfma4(L.u.fin.dPs[r][br + ln], qv, accK[m]);
+    for (int j = 0; j < BC / 4; ++j) {
+      kv[j] = kf(4 * j + lq, bc);
+      qv[j] = qf(4 * j + lq, bc);
+    }
+#pragma unroll
+    for (int j = 0; j < BC / 4; ++j) {
+      accQ[m] = mfma4(fp[j], kv[j], accQ[m]);
+      accK[m] = mfma4(fg[j], kv[j], accK[m]);
+      accK[m] = mfma4(ft[j], qv[j], accK[m]);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -910,6 +962,7 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
   if (tid < BC) {  // per-token terms
     const int t = tid, last = Lc - 1;
     float rz = 0.f, cz = 0.f, b2 = 0.f;
+#pragma unroll
     for (int uu = 0; uu < BC; ++uu) {
       rz += L.u.fin.Zs[t][uu];
       cz += L.u.fin.Zs[uu][t];
@@ -930,9 +983,13 @@ __global__ __launch_bounds__(NT, sizeof(TI) == 2 ? 2 : 1) void bwd_grad_kernel(
   // when the decay is strong.
   if (tid < Lc) {
     const int t = tid;
+    // fixed trip counts (the reads do not wait on each other); adding the
+    // zeros of rows past the chunk's end first leaves the sum unchanged
     float acc = 0.f;
-    for (int uu = Lc - 1; uu >= t; --uu) acc += L.sgQ[0][uu];
-    for (int uu = 0; uu < t; ++uu) acc += L.sw[uu];
+#pragma unroll
+    for (int uu = BC - 1; uu >= 0; --uu) acc += (uu >= t && uu < Lc) ? L.sgQ[0][uu] : 0.f;
+#pragma unroll
+    for (int uu = 0; uu < BC; ++uu) acc += uu < t ? L.sw[uu] : 0.f;
     const long th = (row0 + t0 + t) * H + h;
     dg[th] = acc;
     dbeta[th] = L.sb1[t];
