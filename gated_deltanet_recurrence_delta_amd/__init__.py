@@ -23,6 +23,7 @@ _lib = None
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_FLAG_NO_SEGMENTS = 1
 
 
 class GdnError(RuntimeError):
@@ -46,7 +47,7 @@ def load():
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.gdn_fwd.restype = I
-        lib.gdn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I]
+        lib.gdn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I]
         lib.gdn_fwd_recurrent.restype = I
         lib.gdn_fwd_recurrent.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I]
         lib.gdn_diag_fwd.restype = I
@@ -74,11 +75,11 @@ def strerror(status: int) -> str:
 
 
 def gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
-            stream, dtype, chunk) -> int:
+            stream, dtype, chunk, flags=0) -> int:
     """Raw C call with integer pointers (0 = NULL).  Returns the status."""
     return load().gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT,
                           int(B), int(T), int(H), int(dk), int(dv),
-                          stream, int(dtype), int(chunk))
+                          stream, int(dtype), int(chunk), int(flags))
 
 
 def gdn_fwd_recurrent(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
@@ -90,17 +91,24 @@ def gdn_fwd_recurrent(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv
 
 
 def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
-        out=None, hT=None, stream=None):
+        out=None, hT=None, stream=None, segments: bool = True,
+        check_cu_seqlens: bool = False):
     """Gated-delta-rule forward on torch device tensors (chunkwise form).
 
     q, k: (B,T,H,dk); v: (B,T,H,dv); g, beta: (B,T,H) float32 (packed:
     drop B and pass int32 ``cu_seqlens`` of length B+1).  q/k/v share one
     dtype, float32 or bfloat16.  h0: (B,H,dk,dv) float32 or None.
     Returns (out, hT); out has q's dtype, hT is float32.  Runs on the
-    current stream (or ``stream``), asynchronously.
+    current stream (or ``stream``), asynchronously.  ``segments=False``
+    passes GDN_FLAG_NO_SEGMENTS (every chain runs from its start).
+    ``check_cu_seqlens=True`` copies cu_seqlens to the host (a
+    synchronisation) and checks that it starts at 0, never decreases and
+    ends at T before anything is launched.
     """
     a, out, hT = _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream)
-    rc = gdn_fwd(*a, chunk)
+    if check_cu_seqlens and cu_seqlens is not None:
+        check_offsets(cu_seqlens.cpu().numpy(), a[10])
+    rc = gdn_fwd(*a, chunk, 0 if segments else GDN_FLAG_NO_SEGMENTS)
     if rc != 0:
         raise GdnError(rc, strerror(rc))
     return out, hT
@@ -114,6 +122,35 @@ def fwd_recurrent(q, k, v, g, beta, h0=None, cu_seqlens=None, out=None, hT=None,
     if rc != 0:
         raise GdnError(rc, strerror(rc))
     return out, hT
+
+
+def check_offsets(cu, T: int) -> None:
+    """Host check of packed-batch offsets: cu[0] == 0, non-decreasing,
+    cu[-1] == T.  Raises ValueError otherwise."""
+    import numpy as np
+
+    cu = np.asarray(cu).reshape(-1)
+    if cu.size < 1:
+        raise ValueError("cu_seqlens must have at least one entry")
+    if int(cu[0]) != 0:
+        raise ValueError(f"cu_seqlens[0] must be 0, got {int(cu[0])}")
+    if cu.size > 1 and bool(np.any(np.diff(cu.astype(np.int64)) < 0)):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if int(cu[-1]) != int(T):
+        raise ValueError(f"cu_seqlens[-1] must equal the packed length {T}, got {int(cu[-1])}")
+
+
+def _check_outputs(out, hT, out_shape, out_dtype, state_shape):
+    """Caller-supplied outputs must have exactly the shapes and dtypes the
+    kernel writes: a smaller buffer would be written past its end."""
+    import torch
+
+    if out is not None and (tuple(out.shape) != tuple(out_shape) or out.dtype != out_dtype):
+        raise ValueError(f"out must be {out_dtype} of shape {tuple(out_shape)}, "
+                         f"got {out.dtype} {tuple(out.shape)}")
+    if hT is not None and (tuple(hT.shape) != tuple(state_shape) or hT.dtype != torch.float32):
+        raise ValueError(f"hT must be float32 of shape {tuple(state_shape)}, "
+                         f"got {hT.dtype} {tuple(hT.shape)}")
 
 
 def _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream):
@@ -132,13 +169,6 @@ def _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream):
     for name, t in (("g", g), ("beta", beta)):
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
-    tensors = [q, k, v, g, beta] + [x for x in (h0, cu_seqlens, out, hT) if x is not None]
-    dev = q.device
-    for t in tensors:
-        if t.device != dev or dev.type != "cuda":
-            raise ValueError("all tensors must be on the same GPU device")
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
@@ -159,6 +189,14 @@ def _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream):
         raise ValueError("g/beta must have q's shape without the last dimension")
     if h0 is not None and (h0.dtype != torch.float32 or tuple(h0.shape) != (B, H, dk, dv)):
         raise ValueError("h0 must be float32 (B, H, dk, dv)")
+    _check_outputs(out, hT, v.shape, v.dtype, (B, H, dk, dv))
+    tensors = [q, k, v, g, beta] + [x for x in (h0, cu_seqlens, out, hT) if x is not None]
+    dev = q.device
+    for t in tensors:
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=dev)
     if hT is None:
@@ -230,14 +268,6 @@ def _marshal_diag(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, strea
     for name, t in (("g", g), ("A_log", A_log), ("D", Dskip), ("gate", gate), ("h0", h0)):
         if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
-    tensors = [v, b, c, g, A_log] + [x for x in (Dskip, gate, h0, cu_seqlens, out, hT)
-                                     if x is not None]
-    dev = v.device
-    for t in tensors:
-        if t.device != dev or dev.type != "cuda":
-            raise ValueError("all tensors must be on the same GPU device")
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
@@ -263,6 +293,15 @@ def _marshal_diag(v, b, c, g, A_log, Dskip, gate, h0, cu_seqlens, out, hT, strea
         raise ValueError("D must be (H,)")
     if h0 is not None and tuple(h0.shape) != (B, H, S, D):
         raise ValueError("h0 must be (B, H, S, D)")
+    _check_outputs(out, hT, v.shape, v.dtype, (B, H, S, D))
+    tensors = [v, b, c, g, A_log] + [x for x in (Dskip, gate, h0, cu_seqlens, out, hT)
+                                     if x is not None]
+    dev = v.device
+    for t in tensors:
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=dev)
     if hT is None:

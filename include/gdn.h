@@ -37,6 +37,9 @@ extern "C" {
 #define GDN_F32 0
 #define GDN_BF16 1
 
+/* gdn_fwd flags. */
+#define GDN_FLAG_NO_SEGMENTS 1 /* never cut a sequence into segments (see gdn_fwd) */
+
 /*
  * gdn_fwd -- forward pass of the gated delta rule, chunkwise-parallel form.
  *
@@ -71,6 +74,7 @@ extern "C" {
  *        fp32 tiles exceed the 160 KB of LDS).  The result does not depend
  *        on the chunk length beyond floating-point rounding.
  * stream: a hipStream_t (NULL = the null stream).
+ * flags: 0 or GDN_FLAG_NO_SEGMENTS; any other bit is GDN_ERR_INVALID_ARG.
  *
  * Pointers: q, k, v, g, beta and out are required when T > 0 and may be
  * NULL when T == 0 (no tokens); hT is required when B > 0.
@@ -82,24 +86,32 @@ extern "C" {
  * The caller owns all buffers; the library allocates no device memory,
  * keeps no pointer after returning and holds no global mutable state
  * (re-entrant, thread-safe).  Identical inputs give bitwise-identical
- * outputs on one device (no atomics, fixed reduction order).  A dense
- * GDN_BF16 batch with fewer chains x 32-column tiles than the device has
- * CUs runs each sequence as segments: a segment starts from a zero state at
- * the latest chunk boundary behind it where the product of the per-token
- * transition norms exp(g) max(1, |1 - beta |k|^2|) is below e^-40 (or at
- * the sequence start, from h0), so it differs from the exact sequential
- * result by less than that factor of the state, beyond rounding; hT == h0
- * turns this off, and packed batches are never cut.  So a packed sequence's
- * slice equals the same sequence run alone bit for bit when that run is not
- * cut (fewer than 16 chunks, or at least as many chains x tiles as CUs), and
- * within rounding otherwise.  Arithmetic: bf16 operands
+ * outputs on one device (no atomics, fixed reduction order).
+ *
+ * Segments.  Unless flags holds GDN_FLAG_NO_SEGMENTS, a long sequence may
+ * run as several segments, one workgroup each: a segment starts from a
+ * zero state at the latest chunk boundary behind it where the product of
+ * the per-token transition norms exp(g) max(1, |1 - beta |k|^2|) is below
+ * e^-40 (or at the sequence start, from h0), so it differs from the exact
+ * sequential result by less than that factor of the state, beyond
+ * rounding.  With GDN_BF16, dk = dv = 128 and 64-token chunks, a sequence
+ * of n chunks is cut into ceil(n / 16) segments of equal length, whatever
+ * the batch and the device: a packed sequence's slice of out and hT then
+ * equals the same sequence run alone (same h0, same flags) bit for bit.
+ * Other GDN_BF16 shapes cut only dense batches with fewer chains x 32-column
+ * tiles than the device has CUs (the cut then depends on the device), and
+ * never cut packed batches.  GDN_F32 never cuts.  hT == h0 turns cutting
+ * off (a segment could read h0 after another wrote hT over it).  With
+ * GDN_FLAG_NO_SEGMENTS every chain runs from its start, and a run split at
+ * a chunk boundary (the second part taking the first part's hT as h0)
+ * equals the whole run bit for bit.  Arithmetic: bf16 operands
  * with fp32 accumulation for GDN_BF16, fp32 throughout for GDN_F32; the
  * state is carried in fp32.  Non-finite inputs propagate.
  */
 int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
             const float* beta, const float* h0, const int32_t* cu_seqlens,
             void* out, float* hT, int B, int T, int H, int dk, int dv,
-            void* stream, int dtype, int chunk);
+            void* stream, int dtype, int chunk, int flags);
 
 /*
  * gdn_fwd_recurrent -- the same operation in its token-by-token form, for

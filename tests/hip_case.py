@@ -74,6 +74,58 @@ def chain_slices(inp: synth.Inputs, c: int):
     return (b, slice(None), h), (b, h)
 
 
+def _ratio(num, den):
+    """max|err| / max|ref| with 0/0 -> 0 (elementwise over arrays)."""
+    num = np.asarray(num, dtype=np.float64)
+    den = np.asarray(den, dtype=np.float64)
+    out = np.zeros(np.broadcast(num, den).shape)
+    nz = num > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out[nz] = np.where(den[nz] > 0, num[nz] / np.where(den[nz] > 0, den[nz], 1.0), np.inf)
+    return out
+
+
+def per_chain_errors(inp: synth.Inputs, o, hT, o_ref, h_ref):
+    """Infinity-norm relative error of every chain on its own scale:
+    (e_out[B, H], e_hT[B, H]) with e = max|x - ref| / max|ref| over the
+    chain's slice of out (its tokens, its head) and of hT."""
+    B = hT.shape[0]
+    H = hT.shape[1]
+    dh = np.abs(hT - h_ref).max(axis=(2, 3))
+    rh = np.abs(h_ref).max(axis=(2, 3))
+    e_h = _ratio(dh, rh)
+    if inp.cu_seqlens is None:
+        if o.size:
+            do = np.abs(o - o_ref).max(axis=(1, 3))
+            ro = np.abs(o_ref).max(axis=(1, 3))
+            e_o = _ratio(do, ro)
+        else:
+            e_o = np.zeros((B, H))
+    else:
+        e_o = np.zeros((B, H))
+        for n in range(B):
+            s, e = synth.chain_bounds(inp, n)
+            if e > s:
+                e_o[n] = _ratio(np.abs(o[s:e] - o_ref[s:e]).max(axis=(0, 2)),
+                                np.abs(o_ref[s:e]).max(axis=(0, 2)))
+    return e_o, e_h
+
+
+def compare_all(inp: synth.Inputs, out_hip, hT_hip):
+    """The oracle on every chain; returns a dict with the whole-tensor
+    errors (out, hT) and the worst chain's own-scale errors with its
+    (sequence, head)."""
+    o_ref, h_ref = run_oracle(inp)
+    o = host_f64(out_hip)
+    hT = host_f64(hT_hip)
+    e_o, e_h = per_chain_errors(inp, o, hT, o_ref, h_ref)
+    worst = np.maximum(e_o, e_h)
+    b, h = np.unravel_index(int(np.argmax(worst)), worst.shape)
+    return {"out": oracle.rel_err(o, o_ref), "hT": oracle.rel_err(hT, h_ref),
+            "chain_out": float(e_o.max()), "chain_hT": float(e_h.max()),
+            "worst_chain": (int(b), int(h))}
+
+
 def compare(inp: synth.Inputs, out_hip, hT_hip, chains=None):
     """Max relative errors (out, hT) of the HIP result against the oracle,
     over all chains or over the listed chain ids."""

@@ -35,14 +35,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert gdn.version() == 100
+    assert gdn.version() == 200
     for code in (OK, INVALID, UNSUPPORTED, LAUNCH, 12345):
         assert isinstance(gdn.strerror(code), str) and gdn.strerror(code)
 
 
 def _call(**kw):
     a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, out=P, hT=P,
-             B=1, T=8, H=1, dk=32, dv=32, stream=None, dtype=1, chunk=64)
+             B=1, T=8, H=1, dk=32, dv=32, stream=None, dtype=1, chunk=64, flags=0)
     a.update(kw)
     return gdn.gdn_fwd(**a)
 
@@ -54,7 +54,7 @@ def test_null_required_pointer(name):
 
 @pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=0), dict(dk=0), dict(dv=-4),
                                 dict(dtype=2), dict(dtype=-1), dict(chunk=48), dict(chunk=128),
-                                dict(chunk=-64)])
+                                dict(chunk=-64), dict(flags=2), dict(flags=-1), dict(flags=3)])
 def test_invalid_sizes(kw):
     assert _call(**kw) == INVALID
 

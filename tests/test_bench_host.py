@@ -6,6 +6,7 @@ import subprocess
 import sys
 
 import bench
+import numpy as np
 import synth
 import synth.diag as sd
 
@@ -46,9 +47,30 @@ def test_backward_flops_count_chunks_per_sequence():
 def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("int f(int x) {\n  return x + 1;  // one\n}\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SRCS", [str(src)])
     h1 = bench.kernel_source_hash()
     src.write_text("/* a note */\nint f(int x)   {\n\n  return x + 1;  // changed comment\n}\n")
     assert bench.kernel_source_hash() == h1
     src.write_text("int f(int x) {\n  return x + 2;\n}\n")
     assert bench.kernel_source_hash() != h1
+
+
+def test_chain_errors_scale_each_chain_on_its_own():
+    """A chain whose outputs are 100x smaller than the tensor's largest is
+    judged against its own largest value, not the tensor's."""
+    inp = synth.generate(synth.custom(name="ce", seed=1, B=2, T=3, H=2, dk=2, dv=2))
+    o_ref = np.ones((2, 3, 2, 2))
+    o_ref[1, :, 0] = 0.01
+    h_ref = np.ones((2, 2, 2, 2))
+    o = o_ref.copy()
+    o[1, 2, 0, 1] += 0.001  # 0.1 % of the tensor's scale, 10 % of the chain's
+    co, ch, worst = bench.chain_errors(inp, o, h_ref.copy(), o_ref, h_ref)
+    assert abs(co - 0.1) < 1e-12 and ch == 0.0 and worst == (1, 0)
+
+
+def test_timing_record_settled_flag():
+    flat = np.full(40, 0.1)
+    r = bench.timing_record(flat, 5, 123.0)
+    assert r["clock_settled"] and r["settle_launches"] == 5 and r["cold_first_call_us"] == 123.0
+    ramp = np.concatenate([np.full(10, 0.12), np.full(30, 0.1)])
+    assert not bench.timing_record(ramp, 0, 1.0)["clock_settled"]
