@@ -12,6 +12,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -200,6 +201,16 @@ __device__ static inline void flag_release(int* f, int v) {
 __device__ static inline void copy_to_lds(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
+
+// 4 bytes per lane from the buffer at byte offset voff into LDS at
+// lds + 4 * lane.
+__device__ static inline void copy_to_lds4(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (and nothing else).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __device__ static inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

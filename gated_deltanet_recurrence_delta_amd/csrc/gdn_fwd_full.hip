@@ -45,9 +45,9 @@
 // Column permutation: state column position r of 16-column block cb holds
 // value column 2r + cb (relative to the wave's 32), so that a lane's v
 // values come as bf16 pairs and its eight output columns are contiguous
-// (one 16-byte store per token row).  State rows use the key order of the
-// bf16 kernel in gdn_fwd.hip (key_of below), which makes the transposing
-// reads of K conflict-free and the state's bf16 fragments natural-order.
+// (one 16-byte store per token row).  State rows are ordered (key_of below)
+// so that the state's bf16 fragments come straight from its accumulators in
+// natural key order.
 //
 // No atomics: results are deterministic and bitwise independent of the
 // workgroup schedule.
@@ -82,7 +82,7 @@ constexpr int NKR = 4, NQR = 3, NVEC = 3;  // ring depths: k, q, decay vectors
 constexpr int F_BETA = 0, F_LAM = 1, F_GAM = 2, F_W = 3, F_ER = 4, NF = 4 + NB;
 constexpr int AD_ROW = 20, AD_BLK = 16 * AD_ROW + 4;  // padded fp32 diagonal blocks
 constexpr int LDS = NKR * KQ_BYTES + NQR * KQ_BYTES + CC_BYTES + 2 * CC_BYTES + CC_BYTES +
-                    NVEC * NF * C * 4 + NB * AD_BLK * 4 + 64;
+                    NVEC * NF * C * 4 + NB * AD_BLK * 4 + 4 * C * 4 + 64;
 static_assert(LDS <= 160 * 1024, "LDS budget");
 static_assert(NB == 4 && NKS == 4 && NCW == 4, "shape");
 
@@ -90,9 +90,11 @@ static_assert(NB == 4 && NKS == 4 && NCW == 4, "shape");
 __host__ __device__ constexpr int own_tb(int o, int i) { return i == 0 ? o : NB - 1 - o; }
 
 // State row (key) held by accumulator block b, row r: of the 32 keys of
-// slab b >> 1, block b takes from each 8-key group the half (b ^ g) & 1.
+// slab b >> 1, block b takes the half b & 1 of each 8-key group, so that
+// two stacked blocks form a bf16 fragment whose positions are the natural
+// keys 32 s + 8 q .. 32 s + 8 q + 7 of lane group q.
 __device__ static inline int key_of(int b, int r) {
-  return 32 * (b >> 1) + 8 * (r >> 2) + 4 * ((b ^ (r >> 2)) & 1) + (r & 3);
+  return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3);
 }
 
 // Chunk count of a sequence and its segment layout.
@@ -119,10 +121,11 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   __shared__ __attribute__((aligned(16))) char sK[NKR * KQ_BYTES];
   __shared__ __attribute__((aligned(16))) char sQ[NQR * KQ_BYTES];
   __shared__ __attribute__((aligned(16))) char sAT[CC_BYTES];     // A (off-diagonal) and T_bb^T
-  __shared__ __attribute__((aligned(16))) char sT[2 * CC_BYTES];  // T^T of two chunks
+  __shared__ __attribute__((aligned(16))) char sT[2 * CC_BYTES];  // (T diag(beta))^T of two chunks
   __shared__ __attribute__((aligned(16))) char sP[CC_BYTES];      // P, lane-major fragments
   __shared__ __attribute__((aligned(16))) float sVEC[NVEC * NF * C];
   __shared__ __attribute__((aligned(16))) float sAD[NB * AD_BLK];
+  __shared__ __attribute__((aligned(16))) float sGB[2 * 2 * C];  // g, beta of two chunks
   // Flags, chunk index + 1: [0], [1] P published by P wave 0 / 1.
   __shared__ int sFLAG[4];
   __shared__ int sPICK[2];
@@ -238,14 +241,14 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     const int j = wave;  // value columns 32 j .. 32 j + 31
     const long sbase = (long)chain * DK * DV;
     // K^T (transposing reads): rows 32 s + 16 hi + 4 q4 + (src >> 2), the
-    // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 ((b^src)&1) .. +3.
+    // 8-byte piece holding keys 32 (b>>1) + 8 (src&3) + 4 (b&1) .. +3 (two
+    // lanes of each 32-lane half share a bank pair: 2-way conflicts).
     int kt_base[NKB / 2];
 #pragma unroll
     for (int bh = 0; bh < NKB / 2; ++bh) {
       const int r = 4 * q4 + (src >> 2);
-      kt_base[bh] = r * KQR + 16 * ((4 * bh + (src & 3)) ^ swz_kq<GR>(r)) + 8 * (src & 1);
+      kt_base[bh] = r * KQR + 16 * ((4 * bh + (src & 3)) ^ swz_kq<GR>(r));
     }
-    const int kt_flip = 8 - 16 * (src & 1);  // to the other half (odd blocks)
     // T as a row operand (transposing read of T^T): rows
     // 32 s + 16 hi + 4 q4 + (src >> 2), columns 16 tb + 4 (src & 3) .. +3.
     int tp_base[NB];
@@ -262,28 +265,30 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     const int o_lane = (int)(n16 * v_stride) + (32 * j + 8 * q4) * 2;
 
     // State: Macc[kb][cb] lane (n16, q4) element e = M[key_of(kb, 4 q4 + e)]
-    // [32 j + 2 n16 + cb].
+    // [32 j + 2 n16 + cb].  h0 comes through a buffer descriptor that is
+    // empty without an initial state (reads return zero), so the 32 loads go
+    // out back to back.
     f32x4 Macc[NKB][2];
+    {
+      const __amdgpu_buffer_rsrc_t rh =
+          make_rsrc(p.h0 ? p.h0 + sbase : p.hT, (p.h0 && use_h0) ? (long)DK * DV * 4 : 0);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f32x2 h = {0.f, 0.f};
-        if (p.h0 && use_h0)
-          h = *reinterpret_cast<const f32x2*>(p.h0 + sbase + (long)key_of(kb, 4 * q4 + e) * DV + 32 * j + 2 * n16);
-        Macc[kb][0][e] = h[0];
-        Macc[kb][1][e] = h[1];
-      }
+        for (int e = 0; e < 4; ++e) {
+          const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(
+              rh, (key_of(kb, 4 * q4 + e) * DV + 32 * j + 2 * n16) * 4, 0, 0);
+          Macc[kb][0][e] = __uint_as_float(h[0]);
+          Macc[kb][1][e] = __uint_as_float(h[1]);
+        }
+    }
+    // bf16 state fragments, natural key order 32 s + 8 q4 .. +7 (key_of).
     F Mf[NKS][2];
-    const bool odd = q4 & 1;
     auto make_mf = [&]() {
 #pragma unroll
       for (int s = 0; s < NKS; ++s)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const u32x4 u = __builtin_bit_cast(u32x4, MM::from_acc(Macc[2 * s][cb], Macc[2 * s + 1][cb]));
-          Mf[s][cb] = __builtin_bit_cast(F, u32x4{odd ? u[2] : u[0], odd ? u[3] : u[1], odd ? u[0] : u[2], odd ? u[1] : u[3]});
-        }
+        for (int cb = 0; cb < 2; ++cb) Mf[s][cb] = MM::from_acc(Macc[2 * s][cb], Macc[2 * s + 1][cb]);
     };
     make_mf();
 
@@ -298,15 +303,65 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           Vn[tb][e] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_lane, (int)((16 * tb + e) * v_stride), 0);
     };
 
-    // v of chunk c sits in Vb from the middle of step c+1 (right after the
-    // previous chunk's X consumed it) to its own X at step c+2.
-    uint32_t Vb[NB][4];
+    // v of chunk c + 1 is loaded into Vn first thing in chunk c's step (a
+    // step ahead of its use) and moved to Vb at the end of it.
+    uint32_t Vb[NB][4], Vn[NB][4];
+    // Chunk c.  Only full-depth (32-long) products are used: where a slab's
+    // upper half lies above the diagonal, the row operand holds zeros there.
+    // With Tb = T diag(beta), U = Tb (V - diag(Gam) K M).  The recurrence's
+    // own path is Y = K M -> Z = -diag(Gam) Y -> U = u + Tb Z ->
+    // W = diag(w) U -> M <- Gam_C M + K^T W -> bf16 state; u = Tb V,
+    // diag(Gam) Q M and the stores hang off it.
     auto process = [&](int c) {
       const char* sk = sK + (c % NKR) * KQ_BYTES;
       const char* sq = sQ + (c % NQR) * KQ_BYTES;
       const char* st = sT + (c & 1) * CC_BYTES;
       const float* vec = vec_of(c);
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      load_v(c + 1, Vn);  // unconditional: past the end the descriptor is empty
+      asm volatile("" ::: "memory");  // issued here, not later
+
+      // T (lower triangular) as row operands: slab s of row block tb is used
+      // for 2 s <= tb, its upper half only when 2 s + 1 <= tb.
+      F TPf[NB][NTS];
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int s = 0; 2 * s <= tb; ++s) {
+          const bf16x4 lo = lds_read_tr(st, tp_base[tb] + 32 * s * CCR);
+          F f{};
+          f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+          if (2 * s + 1 <= tb) {
+            const bf16x4 hi = lds_read_tr(st, tp_base[tb] + (32 * s + 16) * CCR);
+            f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+          }
+          TPf[tb][s] = f;
+        }
+      // u = T diag(beta) V (independent of the state): the bf16 pairs of v
+      // regroup into fragments by byte permutes (column 2 n16 + cb is the
+      // low half of each pair for cb = 0, the high half for cb = 1).
+      F XVf[NTS][2];
+#pragma unroll
+      for (int s = 0; s < NTS; ++s)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const uint32_t sel = cb ? 0x07060302u : 0x05040100u;
+          const u32x4 f = {__builtin_amdgcn_perm(Vb[2 * s][1], Vb[2 * s][0], sel),
+                           __builtin_amdgcn_perm(Vb[2 * s][3], Vb[2 * s][2], sel),
+                           __builtin_amdgcn_perm(Vb[2 * s + 1][1], Vb[2 * s + 1][0], sel),
+                           __builtin_amdgcn_perm(Vb[2 * s + 1][3], Vb[2 * s + 1][2], sel)};
+          XVf[s][cb] = __builtin_bit_cast(F, f);
+        }
+      f32x4 U[NB][2];
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          f32x4 u = zero4;
+#pragma unroll
+          for (int s = 0; 2 * s <= tb; ++s) u = MM::mma(TPf[tb][s], XVf[s][cb], u);
+          U[tb][cb] = u;
+        }
 
       // Y = K M (K read one row block ahead of its use).
       f32x4 Y[NB][2];
@@ -329,8 +384,52 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           }
         }
       }
-      // O^T = (M^T Q^T) diag(Gam): lane (token 16 tb + n16, q4) holds value
-      // columns 32 j + 2 (4 q4 + e) + cb.
+      // Z = -diag(Gam) Y, then U = u + T diag(beta) Z.
+      F Zf[NTS][2];
+#pragma unroll
+      for (int s = 0; s < NTS; ++s) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(vec + F_GAM * C + 32 * s + 4 * q4);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(vec + F_GAM * C + 32 * s + 16 + 4 * q4);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          f32x4 z0, z1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            z0[e] = -(g0[e] * Y[2 * s][cb][e]);
+            z1[e] = -(g1[e] * Y[2 * s + 1][cb][e]);
+          }
+          Zf[s][cb] = MM::from_acc(z0, z1);
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          f32x4 u = U[tb][cb];
+#pragma unroll
+          for (int s = 0; 2 * s <= tb; ++s) u = MM::mma(TPf[tb][s], Zf[s][cb], u);
+          U[tb][cb] = u;
+        }
+      F Uf[NTS][2], Wf[NTS][2];
+#pragma unroll
+      for (int s = 0; s < NTS; ++s) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + F_W * C + 32 * s + 4 * q4);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + F_W * C + 32 * s + 16 + 4 * q4);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          Uf[s][cb] = MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb]);
+          f32x4 a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = w0[e] * U[2 * s][cb][e];
+            b[e] = w1[e] * U[2 * s + 1][cb][e];
+          }
+          Wf[s][cb] = MM::from_acc(a, b);
+        }
+      }
+      // O^T = (M^T Q^T) diag(Gam), from the state before this chunk's
+      // update: lane (token 16 tb + n16, q4) holds value columns
+      // 32 j + 2 (4 q4 + e) + cb.
       f32x4 O[NB][2];
       {
         F Qf[2][NKS];
@@ -354,81 +453,14 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           }
         }
       }
-      // T (lower triangular) as row operands: slab s of row block tb is used
-      // for 2 s <= tb, its upper half only when 2 s + 1 <= tb.
-      F TPf[NB][NTS];
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb)
-#pragma unroll
-        for (int s = 0; 2 * s <= tb; ++s) {
-          const bf16x4 lo = lds_read_tr(st, tp_base[tb] + 32 * s * CCR);
-          F f{};
-          f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-          if (2 * s + 1 <= tb) {
-            const bf16x4 hi = lds_read_tr(st, tp_base[tb] + (32 * s + 16) * CCR);
-            f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-          }
-          TPf[tb][s] = f;
-        }
-      // X = diag(beta) (V - diag(Gam) Y), in place of Y.
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + F_BETA * C + 16 * tb + 4 * q4);
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(vec + F_GAM * C + 16 * tb + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v0 = __uint_as_float(Vb[tb][e] << 16), v1 = __uint_as_float(Vb[tb][e] & 0xffff0000u);
-          Y[tb][0][e] = bt[e] * (v0 - gm[e] * Y[tb][0][e]);
-          Y[tb][1][e] = bt[e] * (v1 - gm[e] * Y[tb][1][e]);
-        }
-      }
-      if (c + 1 < NC) load_v(c + 1, Vb);
-      F Xf[NTS][2];
-#pragma unroll
-      for (int s = 0; s < NTS; ++s)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) Xf[s][cb] = MM::from_acc(Y[2 * s][cb], Y[2 * s + 1][cb]);
-      // U = T X (full- and half-depth products accumulate apart, see mma16).
-      f32x4 U[NB][2];
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          f32x4 u = zero4, h = zero4;
-#pragma unroll
-          for (int s = 0; 2 * s <= tb; ++s) {
-            if (2 * s + 1 <= tb) u = MM::mma(TPf[tb][s], Xf[s][cb], u);
-            else h = MM::mma16(MM::lo(TPf[tb][s]), MM::lo(Xf[s][cb]), h);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) u[e] += h[e];
-          U[tb][cb] = u;
-        }
-      F Uf[NTS][2], Wf[NTS][2];
-#pragma unroll
-      for (int s = 0; s < NTS; ++s) {
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(vec + F_W * C + 32 * s + 4 * q4);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(vec + F_W * C + 32 * s + 16 + 4 * q4);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          Uf[s][cb] = MM::from_acc(U[2 * s][cb], U[2 * s + 1][cb]);
-          f32x4 a, b;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = w0[e] * U[2 * s][cb][e];
-            b[e] = w1[e] * U[2 * s + 1][cb][e];
-          }
-          Wf[s][cb] = MM::from_acc(a, b);
-        }
-      }
-      // M <- Gam_C M + K^T diag(w) U
+      // M <- Gam_C M + K^T diag(w) U, then the next chunk's bf16 state.
       const float gC = vec[F_GAM * C + C - 1];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         F KT[NTS];
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
-          const char* p0 = sk + kt_base[kb >> 1] + ((kb & 1) ? kt_flip : 0) + 32 * s * KQR;
+          const char* p0 = sk + kt_base[kb >> 1] + 8 * (kb & 1) + 32 * s * KQR;
           const bf16x4 lo = lds_read_tr(p0, 0);
           const bf16x4 hi = lds_read_tr(p0, 16 * KQR);
           KT[s] = F{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -443,6 +475,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           Macc[kb][cb] = m;
         }
       }
+      make_mf();
       // O^T += U^T P^T once the P waves have published P.
       flag_wait_lds(&sFLAG[0], c + 1);
       flag_wait_lds(&sFLAG[1], c + 1);
@@ -452,32 +485,44 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
                                                   c >= store_from ? (long)(len - c * C) * v_stride : 0);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
-        f32x4 h[2] = {zero4, zero4};
 #pragma unroll
         for (int s = 0; 2 * s <= tb; ++s) {
           const F pf = lds_at<F>(sP + ((tb * NTS + s) * 64 + lane) * 16);
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            if (2 * s + 1 <= tb) O[tb][cb] = MM::mma(Uf[s][cb], pf, O[tb][cb]);
-            else h[cb] = MM::mma16(MM::lo(Uf[s][cb]), MM::lo(pf), h[cb]);
-          }
+          for (int cb = 0; cb < 2; ++cb) O[tb][cb] = MM::mma(Uf[s][cb], pf, O[tb][cb]);
         }
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const __bf16 a = (__bf16)(O[tb][0][e] + h[0][e]);
-          const __bf16 b = (__bf16)(O[tb][1][e] + h[1][e]);
-          w[e] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-        }
+        for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)O[tb][0][e], (__bf16)O[tb][1][e]});
         __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_lane, (int)(16 * tb * v_stride), 0);
       }
-      make_mf();
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Vb[tb][e] = Vn[tb][e];
     };
 
-    for (int it = 0; it < NIT; ++it) {
-      if (it == 1) load_v(0, Vb);
-      if (it >= 2) process(it - 2);
+    // No branch around the loads of v: a load whose destination register
+    // meets another value at a control-flow join would have to complete
+    // there.  Steps 0 and 1 fill the pipeline, step c + 2 works chunk c.
+    if (NIT > 0) {
       lds_barrier();
+      load_v(0, Vb);
+      // Four stores that write nothing (empty descriptor), so that here, as
+      // at the end of every chunk, the loads of v are followed by four
+      // stores: the waits placed for v before its first use then count the
+      // same operations on both ways in, and never wait for the stores.
+      {
+        const __amdgpu_buffer_rsrc_t none = make_rsrc(p.out, 0);
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, o_lane, (int)(16 * tb * v_stride), 0);
+      }
+      lds_barrier();
+      for (int c = 0; c < NC; ++c) {
+        process(c);
+        lds_barrier();
+      }
     }
     if (write_hT) {
 #pragma unroll
@@ -498,20 +543,21 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       const int r = i * KQ_RPI + lane / GR;
       kq_src[i] = (int)(r * kq_stride) + 16 * ((lane % GR) ^ swz_kq<GR>(r));
     }
-    // g and beta: lane t reads token t of the chunk.
+    // g and beta: lane t copies token t of the chunk into sGB.
     const int gb_src = lane * H * 4;
-    // Every load and copy below is issued unconditionally: a chunk past the
-    // end gets empty descriptors (its loads read zeros and its copies fill
-    // ring slots no live chunk occupies), so each step issues the same
-    // number of memory operations and one counted wait per step leaves
-    // exactly that step's operations in flight.
-    auto load_gb = [&](int c, float& sg, float& sb) {
+    // Every copy below is issued unconditionally: a chunk past the end gets
+    // empty descriptors (nothing is read, and the ring slots they fill hold
+    // no live chunk), so each step issues the same number of memory
+    // operations and one counted wait per step leaves exactly that step's
+    // operations in flight.  Nothing is loaded into registers: a register
+    // load carried from one step to the next would be made to complete at
+    // the loop's control-flow joins.
+    auto issue_gb = [&](int c) {
       const long row0 = rowbase + (long)c * C;
       const long left = c < NC ? (long)(len - c * C) : 0;
-      const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + row0 * H + hh, left * H * 4);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0 * H + hh, left * H * 4);
-      sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, gb_src, 0, 0));
-      sb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, gb_src, 0, 0));
+      char* d = reinterpret_cast<char*>(sGB + (c & 1) * 2 * C);
+      copy_to_lds4(make_rsrc(p.g + row0 * H + hh, left * H * 4), d, gb_src);
+      copy_to_lds4(make_rsrc(p.beta + row0 * H + hh, left * H * 4), d + C * 4, gb_src);
     };
     // q of a halo chunk is not needed (its outputs are not stored): empty.
     auto issue = [&](const char* base, char* ring, int nring, int c, bool need) {
@@ -553,23 +599,25 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    float g0 = 0.f, b0 = 0.f, g1 = 0.f, b1 = 0.f;
     if (NIT > 0) {
-      load_gb(0, g0, b0);
+      issue_gb(0);
       issue(p.k, sK, NKR, 0, true);
     }
-    // Step it: vectors of chunk it (from the g and beta loaded one step
-    // earlier), g and beta of chunk it+1, k of chunk it+1, q of chunk it.
-    auto step = [&](int it, float& gu, float& bu, float& gl, float& bl) {
-      if (it < NC) make_vec(it, gu, bu);
-      load_gb(it + 1, gl, bl);
+    // Step it: the vectors of chunk it (its g and beta were copied one
+    // step earlier, first among that step's operations), g and beta of
+    // chunk it+1, k of chunk it+1, q of chunk it.
+    for (int it = 0; it < NIT; ++it) {
+      if (it == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(KQ_INS));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * KQ_INS));
+      asm volatile("" ::: "memory");
+      if (it < NC) {
+        const float* gb = sGB + (it & 1) * 2 * C;
+        make_vec(it, gb[lane], gb[C + lane]);
+      }
+      issue_gb(it + 1);
       issue(p.k, sK, NKR, it + 1, true);
       issue(p.q, sQ, NQR, it, it >= store_from);
       step_barrier();
-    };
-    for (int it = 0; it < NIT; it += 2) {
-      step(it, g0, b0, g1, b1);
-      if (it + 1 < NIT) step(it + 1, g1, b1, g0, b0);
     }
     // The last steps' copies (of chunks past the end) still write LDS: let
     // them land before this wave ends.
@@ -722,11 +770,20 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           RH[b][col] = cvt4(RT[b][col]);
         }
       }
+      // Published as T diag(beta): row j = 16 col + n16 of the transposed
+      // tile is column j of T, scaled by beta_j.
       char* tp = sT + (c & 1) * CC_BYTES;
 #pragma unroll
-      for (int col = 0; col < NB; ++col)
+      for (int col = 0; col < NB; ++col) {
+        const float bj = vec[F_BETA * C + 16 * col + n16];
 #pragma unroll
-        for (int b = col; b < NB; ++b) lds_st<bf16x4>(tp, tp_off(b, col), RH[b][col]);
+        for (int b = col; b < NB; ++b) {
+          f32x4 t;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[e] = RT[b][col][e] * bj;
+          lds_st<bf16x4>(tp, tp_off(b, col), cvt4(t));
+        }
+      }
     };
     for (int it = 0; it < NIT; ++it) {
       const int c = it - 1;
