@@ -18,7 +18,9 @@ __all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurre
            "bwd", "gated_delta_rule", "GdnError", "lib_path", "load", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIB_PATH names another build of the same library (the tests use it to
+# run the host-side checks against a sanitizer-instrumented build).
+_LIB_PATH = os.environ.get("GDN_LIB_PATH") or os.path.join(_HERE, "libgdn.so")
 _lib = None
 
 GDN_F32 = 0

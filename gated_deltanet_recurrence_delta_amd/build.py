@@ -29,15 +29,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the csrc/*.hip sources into libgdn.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SRCS, "-o", tmp]
+# Host-side instrumentation only (AddressSanitizer and UBSan on the C entry
+# points' argument checks and launch set-up); the device code is unchanged.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """Compile the csrc/*.hip sources into libgdn.so, or ``out`` (always
+    recompiles); ``sanitize`` adds host-side AddressSanitizer/UBSan."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(HOST_SANITIZE if sanitize else []), *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

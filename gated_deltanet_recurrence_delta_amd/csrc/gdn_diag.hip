@@ -57,8 +57,10 @@ template <typename TI, int S>
 __global__ __launch_bounds__(64 * RWAVES) void diag_recurrent_kernel(
     const TI* __restrict__ vp, const TI* __restrict__ bp, const TI* __restrict__ cp, const float* __restrict__ gp,
     const float* __restrict__ alog, const float* __restrict__ dskip, const float* __restrict__ gatep,
-    const float* __restrict__ h0, const int32_t* __restrict__ cu, TI* __restrict__ out, float* __restrict__ hT,
+    const float* h0, const int32_t* __restrict__ cu, TI* __restrict__ out, float* hT,
     const DShape p) {
+  // h0 and hT carry no restrict: hT may be h0 itself (each lane reads its
+  // column of h0 before the token loop and writes it back after).
   constexpr bool kHoist = S <= 64;
   const int lane = threadIdx.x & 63;
   const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * RWAVES + (threadIdx.x >> 6));

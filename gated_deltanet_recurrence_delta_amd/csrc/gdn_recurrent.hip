@@ -50,12 +50,14 @@ __device__ static inline float row_el(const TI* __restrict__ base, long row0, in
 
 // Read-only, non-aliased pointers as separate arguments: the loads of the
 // token's k, q, g and beta, whose addresses are the same in every lane,
-// then go through the scalar unit.
+// then go through the scalar unit.  h0 and hT carry no restrict: hT may be
+// h0 itself (an in-place state update; each lane reads its column of h0
+// before the token loop and writes it back after).
 template <typename TI, int DK>
 __global__ __launch_bounds__(64 * WAVES) void gdn_recurrent_kernel(
     const TI* __restrict__ qp, const TI* __restrict__ kp, const TI* __restrict__ vp, const float* __restrict__ gp,
-    const float* __restrict__ bp, const float* __restrict__ h0, const int32_t* __restrict__ cu, TI* __restrict__ out,
-    float* __restrict__ hT, const RShape p) {
+    const float* __restrict__ bp, const float* h0, const int32_t* __restrict__ cu, TI* __restrict__ out,
+    float* hT, const RShape p) {
   constexpr float kLog2e = 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
   const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + (threadIdx.x >> 6));

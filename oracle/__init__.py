@@ -36,20 +36,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+# GDN_ORACLE_LIB names another build of the C oracle (the tests use it to
+# run the pins against an AddressSanitizer/UBSan build).
+_LIB = os.environ.get("GDN_ORACLE_LIB") or os.path.join(_HERE, "libgdn_oracle.so")
 _lib = None
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+                  "-fno-sanitize-recover=undefined"]
 
 
-def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc into ``oracle/libgdn_oracle.so``."""
+def build(force: bool = True, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile the C oracle with gcc into ``oracle/libgdn_oracle.so`` (or
+    ``out``); ``sanitize`` instruments it with AddressSanitizer and UBSan."""
     global _lib
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+    target = out or _LIB
+    if force or not os.path.exists(target):
+        tmp = target + ".tmp"
+        flags = ["-O1", "-g"] + SANITIZE_FLAGS if sanitize else ["-O2"]
+        subprocess.check_call(["gcc", *flags, "-std=c99", "-fPIC", "-shared",
                                "-pthread", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-        _lib = None
-    return _LIB
+        os.replace(tmp, target)
+        if target == _LIB:
+            _lib = None
+    return target
 
 
 def _load():
