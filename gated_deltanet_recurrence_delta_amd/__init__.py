@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
-           "gdn_bwd_workspace_size", "fwd", "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent",
+           "gdn_bwd_workspace_size", "gdn_bwd_noalloc", "fwd", "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent",
            "bwd", "gated_delta_rule", "GdnError", "lib_path", "load", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,8 @@ def load():
         lib.gdn_diag_fwd_recurrent.argtypes = [P] * 11 + [I] * 5 + [P, I]
         lib.gdn_bwd.restype = I
         lib.gdn_bwd.argtypes = [P] * 16 + [ctypes.c_longlong] + [I] * 5 + [P, I]
+        lib.gdn_bwd_noalloc.restype = I
+        lib.gdn_bwd_noalloc.argtypes = [P] * 15 + [I] * 5 + [P, I]
         lib.gdn_bwd_workspace_size.restype = ctypes.c_longlong
         lib.gdn_bwd_workspace_size.argtypes = [I] * 6
         lib.gdn_strerror.restype = ctypes.c_char_p
@@ -374,6 +376,18 @@ def bwd(q, k, v, g, beta, dout, h0=None, cu_seqlens=None, dhT=None, want_dh0=Tru
     if rc != 0:
         raise GdnError(rc, strerror(rc))
     return grads
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gdn_bwd_noalloc(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, dh0,
+                    B, T, H, dk_, dv_, stream, dtype) -> int:
+    """Raw C call of the backward pass with the library's fixed per-GPU
+    scratch instead of a workspace (0 = NULL).  Returns the status."""
+    return load().gdn_bwd_noalloc(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
+                                  dbeta, dh0, int(B), int(T), int(H), int(dk_), int(dv_), stream,
+                                  int(dtype))
 
 
 # -------------------------------------------------------------- autograd ---

@@ -58,6 +58,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn.h"
 
 namespace {
@@ -1046,6 +1048,35 @@ bool bwd_sizes_ok(int B, int T, int H, int dk, int dv, int packed) {
 
 }  // namespace
 
+namespace {
+
+// Workspace of gdn_bwd_noalloc: one array per GPU, in the library's device
+// code object, held until the process ends.  Host code never passes this
+// name to a kernel; it passes the device address that hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+float* g_scratch[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+
+// The current device's scratch address (looked up once per device, with
+// that device current), or null if the lookup failed.
+float* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_rc[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[dev] = g_scratch_rc[dev] == hipSuccess ? static_cast<float*>(ptr) : nullptr;
+  });
+  return g_scratch[dev];
+}
+
+}  // namespace
+
 extern "C" long long gdn_bwd_workspace_size(int B, int T, int H, int dk, int dv, int packed) {
   if (!bwd_sizes_ok(B, T, H, dk, dv, packed)) return GDN_ERR_INVALID_ARG;
   if (H > 65535) return GDN_ERR_UNSUPPORTED;
@@ -1054,10 +1085,12 @@ extern "C" long long gdn_bwd_workspace_size(int B, int T, int H, int dk, int dv,
   return (long long)(ws_floats(slots_per_head(ttot, B), H, dk, dv) * sizeof(float));
 }
 
-extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                       const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT, void* dq,
-                       void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
-                       long long workspace_bytes, int B, int T, int H, int dkn, int dvn, void* stream, int dtype) {
+namespace {
+
+// Every host-side check of gdn_bwd except the workspace's.
+int bwd_check(const void* q, const void* k, const void* v, const float* g, const float* beta,
+              const int32_t* cu_seqlens, const void* dout, void* dq, void* dk, void* dv, float* dg,
+              float* dbeta, int B, int T, int H, int dkn, int dvn, int dtype) {
   if (!bwd_sizes_ok(B, T, H, dkn, dvn, cu_seqlens != nullptr)) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
@@ -1067,11 +1100,24 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
   const long ttot = cu_seqlens ? (long)T : (long)B * T;
   const size_t nslots = slots_per_head(ttot, B);
   if ((long long)(nslots * (size_t)H) > 0x7fffffffLL || nslots > 0x7fffffffULL) return GDN_ERR_UNSUPPORTED;
+  if ((long)B * H * (dvn / TW) > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT, void* dq,
+                       void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
+                       long long workspace_bytes, int B, int T, int H, int dkn, int dvn, void* stream, int dtype) {
+  const int rc = bwd_check(q, k, v, g, beta, cu_seqlens, dout, dq, dk, dv, dg, dbeta, B, T, H, dkn, dvn, dtype);
+  if (rc != GDN_OK) return rc;
+  const long ttot = cu_seqlens ? (long)T : (long)B * T;
+  const size_t nslots = slots_per_head(ttot, B);
   const size_t need = ws_floats(nslots, H, dkn, dvn) * sizeof(float);
   if (B > 0 && (!workspace || workspace_bytes < 0 || (size_t)workspace_bytes < need ||
                 (reinterpret_cast<uintptr_t>(workspace) & 3u)))
     return GDN_ERR_INVALID_ARG;
-  if ((long)B * H * (dvn / TW) > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   BShape p;
   p.B = B;
@@ -1105,4 +1151,20 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
                                                   dbeta, dh0, ws, p, st)
                            : launch_dtype<float>(dkn, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
                                                  dbeta, dh0, ws, p, st);
+}
+
+extern "C" int gdn_bwd_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT,
+                               void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, int B, int T,
+                               int H, int dkn, int dvn, void* stream, int dtype) {
+  const int rc = bwd_check(q, k, v, g, beta, cu_seqlens, dout, dq, dk, dv, dg, dbeta, B, T, H, dkn, dvn, dtype);
+  if (rc != GDN_OK) return rc;
+  const long long need = gdn_bwd_workspace_size(B, T, H, dkn, dvn, cu_seqlens != nullptr);
+  if (need < 0) return (int)need;
+  if ((unsigned long long)need > kScratchBytes) return GDN_ERR_SCRATCH;
+  if (B == 0) return GDN_OK;
+  float* ws = device_scratch();
+  if (!ws) return GDN_ERR_LAUNCH;
+  return gdn_bwd(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
+                 (long long)kScratchBytes, B, T, H, dkn, dvn, stream, dtype);
 }

@@ -1818,6 +1818,7 @@ const char* gdn_strerror(int status) {
     case GDN_ERR_INVALID_ARG: return "invalid argument";
     case GDN_ERR_UNSUPPORTED: return "unsupported shape, dtype or chunk length";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_SCRATCH: return "problem larger than the no-allocation entry point's scratch buffer";
     default: return "unknown status";
   }
 }

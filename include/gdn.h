@@ -32,6 +32,7 @@ extern "C" {
 #define GDN_ERR_INVALID_ARG (-1) /* null required pointer, bad size, bad dtype/chunk */
 #define GDN_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for      */
 #define GDN_ERR_LAUNCH (-3)      /* the HIP launch itself failed                      */
+#define GDN_ERR_SCRATCH (-4)     /* too large for gdn_bwd_noalloc's fixed scratch      */
 
 /* Storage dtype of q, k, v and out. */
 #define GDN_F32 0
@@ -269,6 +270,31 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* g,
  */
 long long gdn_bwd_workspace_size(int B, int T, int H, int dk, int dv,
                                  int packed);
+
+/*
+ * gdn_bwd_noalloc -- gdn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, which is instead a
+ * fixed scratch array inside the library's device code, one per GPU, of
+ * 64 MiB (67108864 bytes), held from the library's first use on that GPU
+ * until the process ends.  Its address is looked up once per
+ * GPU (hipGetSymbolAddress) on the first call there; no call allocates or
+ * frees anything.  Results are those of gdn_bwd on the same inputs.
+ *
+ * Errors: as gdn_bwd, plus GDN_ERR_SCRATCH when gdn_bwd_workspace_size(...)
+ * exceeds 64 MiB (nothing is launched; at dk = dv = 128 and H = 16 that is
+ * beyond about 900 tokens), and GDN_ERR_LAUNCH when the
+ * scratch address cannot be looked up.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (different streams, or
+ * different host threads without ordering) race and give wrong results;
+ * order them on one stream.  The scratch needs no contents on entry.
+ */
+int gdn_bwd_noalloc(const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, const float* h0,
+                    const int32_t* cu_seqlens, const void* dout,
+                    const float* dhT, void* dq, void* dk, void* dv, float* dg,
+                    float* dbeta, float* dh0, int B, int T, int H, int dk_,
+                    int dv_, void* stream, int dtype);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* gdn_strerror(int status);

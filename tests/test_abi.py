@@ -23,7 +23,7 @@ def _declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["gdn_bwd", "gdn_bwd_workspace_size", "gdn_diag_fwd",
+    assert _declared_functions() == ["gdn_bwd", "gdn_bwd_noalloc", "gdn_bwd_workspace_size", "gdn_diag_fwd",
                                      "gdn_diag_fwd_recurrent", "gdn_fwd", "gdn_fwd_recurrent",
                                      "gdn_strerror", "gdn_version"]
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert gdn.version() == 200
-    for code in (OK, INVALID, UNSUPPORTED, LAUNCH, 12345):
+    for code in (OK, INVALID, UNSUPPORTED, LAUNCH, -4, 12345):
         assert isinstance(gdn.strerror(code), str) and gdn.strerror(code)
 
 
@@ -226,3 +226,26 @@ def test_bwd_exact_workspace_accepted_without_launch():
     """The exact workspace size passes validation; B = 0 launches nothing."""
     need = gdn.gdn_bwd_workspace_size(0, 8, 1, 32, 32, 0)
     assert _bcall(B=0, workspace_bytes=need) == OK
+
+
+# ---------------------------------------------------- no-allocation backward --
+
+def _call_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, dout=P, dhT=0, dq=P, dk=P, dv=P,
+             dg=P, dbeta=P, dh0=0, B=1, T=8, H=1, dk_=32, dv_=32, stream=None, dtype=1)
+    a.update(kw)
+    return gdn.gdn_bwd_noalloc(**a)
+
+
+def test_noalloc_rejects_bad_args_before_any_device_call():
+    assert _call_noalloc(q=0) == INVALID
+    assert _call_noalloc(B=-1) == INVALID
+    assert _call_noalloc(dk_=48) == UNSUPPORTED
+    assert _call_noalloc(B=0) == OK  # nothing to do
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    # 4 x 4096 tokens, 16 heads, d = 128 needs about 1.15 GB of workspace
+    assert gdn.gdn_bwd_workspace_size(4, 4096, 16, 128, 128, 0) > gdn.NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(B=4, T=4096, H=16, dk_=128, dv_=128) == -4
+    assert "scratch" in gdn.strerror(-4)
