@@ -14,7 +14,9 @@ FP64 oracle timed on the host cores on the same workload.
 
 ``--workload decode`` (one token per sequence, B=128 H=16 d=128, nonzero
 state) times the token-by-token entry point gdn_fwd_recurrent instead;
-``--form`` picks the entry point for any workload.
+``--form`` picks the entry point for any workload; ``--form scan`` times
+gdn_fwd_scan (segments with exact entry states from the chunk-map scan:
+three launches per step, timed together).
 
 ``--pass bwd`` times the backward entry point gdn_bwd on the same workload
 (dq, dk, dv, dg, dbeta, dh0 from seeded output gradients dout ~ N(0,1),
@@ -498,7 +500,7 @@ def main():
 
     ap.add_argument("--workload", default="wide_head",
                     choices=sorted(synth.WORKLOADS) + sorted(sd.WORKLOADS))
-    ap.add_argument("--form", choices=("chunked", "recurrent"), default=None,
+    ap.add_argument("--form", choices=("chunked", "recurrent", "scan"), default=None,
                     help="entry point (default: recurrent for the decode workload, "
                          "chunked otherwise)")
     ap.add_argument("--pass", dest="direction", choices=("fwd", "bwd"), default="fwd",
@@ -547,6 +549,14 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    ws = None
+    if form == "scan":
+        # one workspace for every set: the calls are serialised on the stream
+        need = gdn.gdn_fwd_scan_workspace_size(
+            len(inp.cu_seqlens) - 1 if inp.cu_seqlens is not None else wl.B,
+            int(inp.cu_seqlens[-1]) if inp.cu_seqlens is not None else wl.T, wl.H, wl.dk, wl.dv,
+            inp.cu_seqlens is not None, gdn.GDN_BF16 if wl.dtype == "bf16" else gdn.GDN_F32, wl.chunk)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     # Validate once through the checked wrapper, then time the raw C entry
     # point with pre-extracted pointers so host overhead stays off the clock.
@@ -559,6 +569,9 @@ def main():
         if form == "recurrent":
             gdn.fwd_recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
                               out=d["out"], hT=d["hT"], stream=stream)
+        elif form == "scan":
+            gdn.fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
+                         chunk=wl.chunk, out=d["out"], hT=d["hT"], stream=stream, workspace=ws)
         else:
             gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
                     chunk=wl.chunk, out=d["out"], hT=d["hT"], stream=stream,
@@ -577,6 +590,9 @@ def main():
     if form == "recurrent":
         raw = gdn.load().gdn_fwd_recurrent
         tail = (B, T, wl.H, wl.dk, wl.dv, sh, dtype_code)
+    elif form == "scan":
+        raw = gdn.load().gdn_fwd_scan
+        tail = (B, T, wl.H, wl.dk, wl.dv, sh, dtype_code, wl.chunk, ws.data_ptr(), ws.numel())
     else:
         raw = gdn.load().gdn_fwd
         flags = gdn.GDN_FLAG_NO_SEGMENTS if args.no_segments else 0
@@ -646,12 +662,13 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
-                "beta=sigmoid(N(0,1)), g=-softplus(N(%g,1)))" % wl.g_mean,
+                "beta=sigmoid(N(0,1)), " + ("g=0)" if wl.no_decay else "g=-softplus(N(%g,1)))" % wl.g_mean),
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} dk={wl.dk} dv={wl.dv} "
-                               f"{wl.dtype} " + (f"chunk={wl.chunk}" if form == "chunked"
-                                                 else "token-by-token")
+                               f"{wl.dtype} " + ("token-by-token" if form == "recurrent"
+                                                 else f"chunk={wl.chunk}")
                                + (" varlen" if wl.varlen else ""),
-                   "entry_point": "gdn_fwd" if form == "chunked" else "gdn_fwd_recurrent",
+                   "entry_point": {"chunked": "gdn_fwd", "recurrent": "gdn_fwd_recurrent",
+                                   "scan": "gdn_fwd_scan"}[form],
                    "tokens_per_step": tokens, "rotated_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -13,7 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdn_fwd", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
+__all__ = ["gdn_fwd", "gdn_fwd_scan", "gdn_fwd_scan_workspace_size", "fwd_scan", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
            "gdn_bwd_workspace_size", "gdn_bwd_noalloc", "fwd", "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent",
            "bwd", "gated_delta_rule", "GdnError", "lib_path", "load", "version"]
 
@@ -50,6 +50,10 @@ def load():
         I = ctypes.c_int
         lib.gdn_fwd.restype = I
         lib.gdn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, I, I]
+        lib.gdn_fwd_scan.restype = I
+        lib.gdn_fwd_scan.argtypes = [P] * 9 + [I] * 5 + [P, I, I, P, ctypes.c_longlong]
+        lib.gdn_fwd_scan_workspace_size.restype = ctypes.c_longlong
+        lib.gdn_fwd_scan_workspace_size.argtypes = [I] * 8
         lib.gdn_fwd_recurrent.restype = I
         lib.gdn_fwd_recurrent.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I]
         lib.gdn_diag_fwd.restype = I
@@ -86,6 +90,20 @@ def gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
                           stream, int(dtype), int(chunk), int(flags))
 
 
+def gdn_fwd_scan_workspace_size(B, T, H, dk, dv, packed, dtype, chunk=0) -> int:
+    """Workspace bytes ``gdn_fwd_scan`` needs (negative: a status code)."""
+    return load().gdn_fwd_scan_workspace_size(int(B), int(T), int(H), int(dk), int(dv), int(packed),
+                                              int(dtype), int(chunk))
+
+
+def gdn_fwd_scan(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
+                 stream, dtype, chunk, workspace, workspace_bytes) -> int:
+    """Raw C call of the chunk-map scan form (0 = NULL).  Returns the status."""
+    return load().gdn_fwd_scan(q, k, v, g, beta, h0, cu_seqlens, out, hT,
+                               int(B), int(T), int(H), int(dk), int(dv),
+                               stream, int(dtype), int(chunk), workspace, int(workspace_bytes))
+
+
 def gdn_fwd_recurrent(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
                       stream, dtype) -> int:
     """Raw C call of the token-by-token form (0 = NULL).  Returns the status."""
@@ -113,6 +131,30 @@ def fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
     if check_cu_seqlens and cu_seqlens is not None:
         check_offsets(cu_seqlens.cpu().numpy(), a[10])
     rc = gdn_fwd(*a, chunk, 0 if segments else GDN_FLAG_NO_SEGMENTS)
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT
+
+
+def fwd_scan(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
+             out=None, hT=None, stream=None, workspace=None):
+    """``fwd`` with exact segment starts from the chunk-map scan
+    (``gdn_fwd_scan``): long sequences run as parallel segments whatever the
+    decay.  ``workspace``: a uint8 device tensor of at least
+    ``gdn_fwd_scan_workspace_size`` bytes, allocated here when None.
+    Returns (out, hT)."""
+    import torch
+
+    a, out, hT = _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream)
+    B, T, H, dk, dv, dtype = a[9], a[10], a[11], a[12], a[13], a[15]
+    need = gdn_fwd_scan_workspace_size(B, T, H, dk, dv, cu_seqlens is not None, dtype, chunk)
+    if need < 0:
+        raise GdnError(need, strerror(need))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be on q's device and hold {need} bytes")
+    rc = gdn_fwd_scan(*a, chunk, workspace.data_ptr(), workspace.numel() * workspace.element_size())
     if rc != 0:
         raise GdnError(rc, strerror(rc))
     return out, hT

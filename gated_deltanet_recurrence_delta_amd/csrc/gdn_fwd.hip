@@ -1727,16 +1727,17 @@ int by_dk(const Params& p, int nwg, hipStream_t s, int dk, int chunk) {
 
 extern "C" {
 
-int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-            const float* h0, const int32_t* cu_seqlens, void* out, float* hT, int B, int T, int H,
-            int dk, int dv, void* stream, int dtype, int chunk, int flags) {
+// Host-side checks of gdn_fwd's and gdn_fwd_scan's common arguments;
+// resolves chunk 0 to the dtype's default.
+static int fwd_check(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                     const void* out, const float* hT, const int32_t* cu_seqlens, int B, int T, int H,
+                     int dk, int dv, int dtype, int& chunk) {
   if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_INVALID_ARG;
   // Token tensors may be NULL only when there are no tokens; the state
   // output is required whenever there is at least one chain.
   if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID_ARG;
   if (B > 0 && !hT) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (flags & ~GDN_FLAG_NO_SEGMENTS) return GDN_ERR_INVALID_ARG;
   if (chunk == 0) chunk = dtype == GDN_BF16 ? 64 : 16;
   if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_INVALID_ARG;
   if ((dk != 32 && dk != 64 && dk != 128) || (dv != 32 && dv != 64 && dv != 128))
@@ -1744,30 +1745,51 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   if (dtype == GDN_BF16 && chunk == 16) return GDN_ERR_UNSUPPORTED;
   if (dtype == GDN_F32 && chunk == 64) return GDN_ERR_UNSUPPORTED;
   if (!cu_seqlens && (long)B * T > 0x7fffffffL) return GDN_ERR_UNSUPPORTED;  // token rows are 32-bit
+  return GDN_OK;
+}
+
+// The full-width kernel's shapes: bf16, dk = dv = 128, 64-token chunks.
+static bool full_width(int dtype, int dk, int dv, int chunk) {
+  return dtype == GDN_BF16 && dk == 128 && dv == 128 && chunk == 64;
+}
+
+static gdn_launch::FullParams full_params(const void* q, const void* k, const void* v, const float* g,
+                                          const float* beta, const float* h0, const int32_t* cu_seqlens,
+                                          void* out, float* hT, int B, int T, int H, int seg_max) {
+  gdn_launch::FullParams fp;
+  fp.q = static_cast<const char*>(q);
+  fp.k = static_cast<const char*>(k);
+  fp.v = static_cast<const char*>(v);
+  fp.g = g;
+  fp.beta = beta;
+  fp.h0 = h0;
+  fp.cu = cu_seqlens;
+  fp.out = static_cast<char*>(out);
+  fp.hT = hT;
+  fp.B = B;
+  fp.T = T;
+  fp.H = H;
+  fp.seg_max = seg_max;
+  fp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, seg_max);
+  return fp;
+}
+
+int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+            const float* h0, const int32_t* cu_seqlens, void* out, float* hT, int B, int T, int H,
+            int dk, int dv, void* stream, int dtype, int chunk, int flags) {
+  const int rc = fwd_check(q, k, v, g, beta, out, hT, cu_seqlens, B, T, H, dk, dv, dtype, chunk);
+  if (rc != GDN_OK) return rc;
+  if (flags & ~GDN_FLAG_NO_SEGMENTS) return GDN_ERR_INVALID_ARG;
   // A segment that starts at the sequence start reads h0; when hT aliases
   // h0 the last segment may already have written over it, so such calls
   // are never cut.
   const bool alias = h0 && static_cast<const void*>(h0) == static_cast<const void*>(hT);
   const bool may_cut = !(flags & GDN_FLAG_NO_SEGMENTS) && !alias;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == GDN_BF16 && dk == 128 && dv == 128 && chunk == 64) {
-    gdn_launch::FullParams fp;
-    fp.q = static_cast<const char*>(q);
-    fp.k = static_cast<const char*>(k);
-    fp.v = static_cast<const char*>(v);
-    fp.g = g;
-    fp.beta = beta;
-    fp.h0 = h0;
-    fp.cu = cu_seqlens;
-    fp.out = static_cast<char*>(out);
-    fp.hT = hT;
-    fp.B = B;
-    fp.T = T;
-    fp.H = H;
-    fp.seg_max = may_cut ? GDN_SEG_MAX_CHUNKS : 0;
-    fp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, fp.seg_max);
-    return gdn_launch::fwd_full(fp, s);
-  }
+  if (full_width(dtype, dk, dv, chunk))
+    return gdn_launch::fwd_full(full_params(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H,
+                                            may_cut ? GDN_SEG_MAX_CHUNKS : 0),
+                                s);
   const int ntile = dv / 32;
   const long nwg_l = (long)B * H * ntile;
   if (nwg_l > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
@@ -1810,6 +1832,35 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   const int nwg_all = nwg * p.nseg;
   p.nwg = nwg_all;
   return dtype == GDN_BF16 ? by_dk<__bf16>(p, nwg_all, s, dk, chunk) : by_dk<float>(p, nwg, s, dk, chunk);
+}
+
+long long gdn_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv, int packed, int dtype, int chunk) {
+  if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_INVALID_ARG;
+  if (chunk == 0) chunk = dtype == GDN_BF16 ? 64 : 16;
+  // Only the full-width kernel's shapes use the scan, and only sequences of
+  // more than GDN_SEG_MAX_CHUNKS chunks are cut.
+  if (!full_width(dtype, dk, dv, chunk) || T <= GDN_SEG_MAX_CHUNKS * 64) return 0;
+  return 4 * gdn_launch::scan_ws_floats(gdn_launch::full_slots(B, T, packed != 0, GDN_SEG_MAX_CHUNKS), H);
+}
+
+int gdn_fwd_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                 const float* h0, const int32_t* cu_seqlens, void* out, float* hT, int B, int T, int H,
+                 int dk, int dv, void* stream, int dtype, int chunk, void* workspace,
+                 long long workspace_bytes) {
+  const int rc = fwd_check(q, k, v, g, beta, out, hT, cu_seqlens, B, T, H, dk, dv, dtype, chunk);
+  if (rc != GDN_OK) return rc;
+  if (!full_width(dtype, dk, dv, chunk))
+    return gdn_fwd(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv, stream, dtype, chunk,
+                   GDN_FLAG_NO_SEGMENTS);
+  const long long need = gdn_fwd_scan_workspace_size(B, T, H, dk, dv, cu_seqlens != nullptr, dtype, chunk);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u)))
+    return GDN_ERR_INVALID_ARG;
+  gdn_launch::FullParams fp =
+      full_params(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, GDN_SEG_MAX_CHUNKS);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need == 0) return gdn_launch::fwd_full(fp, s);  // nothing is cut: one workgroup per chain
+  fp.ws = static_cast<float*>(workspace);
+  return gdn_launch::fwd_full_scan(fp, s);
 }
 
 const char* gdn_strerror(int status) {

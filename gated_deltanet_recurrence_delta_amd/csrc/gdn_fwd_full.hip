@@ -112,6 +112,11 @@ __device__ static inline void seg_layout(int len, int seg_max, int& nch, int& se
 
 }  // namespace fk
 
+// MAPS = false: outputs and hT.  MAPS = true: the affine map of one segment
+// (p.ws set; see the chunk-map scan below): the recurrence over the
+// segment's chunks from the identity with v = 0 (giving P) or from zero
+// (from h0 for the first segment) with the real v (giving Q), no outputs.
+template <bool MAPS>
 __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_launch::FullParams p) {
   using namespace fk;
   using MM = Mma<__bf16>;
@@ -138,7 +143,11 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   const int H = p.H;
 
   // ---------------------------------------------------- which segment
-  const int slot = blockIdx.x / H, hh = blockIdx.x % H;
+  // The maps pass has two workgroups per segment slot: even ones compose
+  // Q, odd ones P.
+  const int wslot = blockIdx.x / H, hh = blockIdx.x % H;
+  const int slot = MAPS ? wslot >> 1 : wslot;
+  const bool map_p = MAPS && (wslot & 1);
   int bseq, seg;
   long rowbase;
   int len;
@@ -185,11 +194,17 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   seg_layout(len, p.seg_max, nch, seg_len, nseg);
   const int c0 = seg * seg_len;
   const int c1 = min(c0 + seg_len, nch);
+  // Maps are needed for every segment but the last; P not for the first,
+  // whose Q starts from h0 and is already the next segment's entry state.
+  if (MAPS && (seg >= nseg - 1 || (seg == 0 && map_p))) return;  // uniform over the workgroup
+  // With the scan, a cut sequence's segments start exactly at c0 (from the
+  // scanned entry state); otherwise a segment starts at its halo.
+  const bool exact = p.ws != nullptr && nseg > 1;
   if (threadIdx.x < 4) sFLAG[threadIdx.x] = 0;
   if (wave == 0) {
     int cs = c0;
     float acc = 0.f;  // log of the transition-norm product over chunks [cs, c0)
-    while (cs > 0 && acc > -HALO_NATS) {
+    while (!exact && cs > 0 && acc > -HALO_NATS) {
       --cs;  // chunks before c0 are whole: every lane holds a token
       const long th = (rowbase + (long)cs * C + lane) * H + hh;
       const uint4* kr = reinterpret_cast<const uint4*>(p.k + th * KQR);
@@ -215,8 +230,27 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   }
   __syncthreads();
   const int cs = sSTART;
-  const bool use_h0 = cs == 0;
-  const bool write_hT = c1 >= nch;
+  const bool write_hT = !MAPS && c1 >= nch;
+  // This (segment slot, head)'s P, Q and entry state S in the workspace.
+  float* const wsm = p.ws ? p.ws + ((long)slot * H + hh) * 3 * DK * DV : nullptr;
+  // Where the recurrence's starting state comes from (an empty descriptor
+  // reads zeros): P starts from the identity (set below), the first
+  // segment's Q and an uncut or halo start at the sequence start from h0,
+  // an exact output start from the scanned state, anything else from zero.
+  const float* st_src = p.hT;
+  long st_bytes = 0;
+  if (MAPS) {
+    if (!map_p && seg == 0 && p.h0) {
+      st_src = p.h0 + (long)chain * DK * DV;
+      st_bytes = (long)DK * DV * 4;
+    }
+  } else if (exact) {
+    st_src = wsm + 2 * DK * DV;
+    st_bytes = (long)DK * DV * 4;
+  } else if (p.h0 && cs == 0) {
+    st_src = p.h0 + (long)chain * DK * DV;
+    st_bytes = (long)DK * DV * 4;
+  }
   const int store_from = c0 - cs;
   rowbase = __builtin_amdgcn_readfirstlane((int)(rowbase + (long)cs * C));
   len = __builtin_amdgcn_readfirstlane(min(len, c1 * C) - cs * C);
@@ -270,8 +304,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     // out back to back.
     f32x4 Macc[NKB][2];
     {
-      const __amdgpu_buffer_rsrc_t rh =
-          make_rsrc(p.h0 ? p.h0 + sbase : p.hT, (p.h0 && use_h0) ? (long)DK * DV * 4 : 0);
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(st_src, st_bytes);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -281,6 +314,17 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           Macc[kb][0][e] = __uint_as_float(h[0]);
           Macc[kb][1][e] = __uint_as_float(h[1]);
         }
+      if constexpr (MAPS) {
+        if (map_p) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                Macc[kb][cb][e] = key_of(kb, 4 * q4 + e) == 32 * j + 2 * n16 + cb ? 1.f : 0.f;
+        }
+      }
     }
     // bf16 state fragments, natural key order 32 s + 8 q4 .. +7 (key_of).
     F Mf[NKS][2];
@@ -292,10 +336,11 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     };
     make_mf();
 
+    // P's recurrence runs with v = 0: an empty descriptor.
     auto load_v = [&](int c, uint32_t (&Vn)[NB][4]) {
       const long row0 = rowbase + (long)c * C;
       const __amdgpu_buffer_rsrc_t rv =
-          make_rsrc(p.v + (row0 * H + hh) * DV * 2, c < NC ? (long)(len - c * C) * v_stride : 0);
+          make_rsrc(p.v + (row0 * H + hh) * DV * 2, c < NC && !map_p ? (long)(len - c * C) * v_stride : 0);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
@@ -431,7 +476,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       // update: lane (token 16 tb + n16, q4) holds value columns
       // 32 j + 2 (4 q4 + e) + cb.
       f32x4 O[NB][2];
-      {
+      if constexpr (!MAPS) {
         F Qf[2][NKS];
         auto read_q = [&](int tb) {
 #pragma unroll
@@ -476,25 +521,27 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         }
       }
       make_mf();
-      // O^T += U^T P^T once the P waves have published P.
-      flag_wait_lds(&sFLAG[0], c + 1);
-      flag_wait_lds(&sFLAG[1], c + 1);
-      const long row0 = rowbase + (long)c * C;
-      // a segment's halo chunks are computed but not stored (zero-size descriptor)
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + (row0 * H + hh) * DV * 2,
-                                                  c >= store_from ? (long)(len - c * C) * v_stride : 0);
+      if constexpr (!MAPS) {
+        // O^T += U^T P^T once the P waves have published P.
+        flag_wait_lds(&sFLAG[0], c + 1);
+        flag_wait_lds(&sFLAG[1], c + 1);
+        const long row0 = rowbase + (long)c * C;
+        // a segment's halo chunks are computed but not stored (zero-size descriptor)
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + (row0 * H + hh) * DV * 2,
+                                                    c >= store_from ? (long)(len - c * C) * v_stride : 0);
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
+        for (int tb = 0; tb < NB; ++tb) {
 #pragma unroll
-        for (int s = 0; 2 * s <= tb; ++s) {
-          const F pf = lds_at<F>(sP + ((tb * NTS + s) * 64 + lane) * 16);
+          for (int s = 0; 2 * s <= tb; ++s) {
+            const F pf = lds_at<F>(sP + ((tb * NTS + s) * 64 + lane) * 16);
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) O[tb][cb] = MM::mma(Uf[s][cb], pf, O[tb][cb]);
+            for (int cb = 0; cb < 2; ++cb) O[tb][cb] = MM::mma(Uf[s][cb], pf, O[tb][cb]);
+          }
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)O[tb][0][e], (__bf16)O[tb][1][e]});
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_lane, (int)(16 * tb * v_stride), 0);
         }
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)O[tb][0][e], (__bf16)O[tb][1][e]});
-        __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_lane, (int)(16 * tb * v_stride), 0);
       }
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb)
@@ -512,7 +559,8 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       // at the end of every chunk, the loads of v are followed by four
       // stores: the waits placed for v before its first use then count the
       // same operations on both ways in, and never wait for the stores.
-      {
+      // (The maps pass stores nothing in its chunks.)
+      if constexpr (!MAPS) {
         const __amdgpu_buffer_rsrc_t none = make_rsrc(p.out, 0);
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
@@ -524,12 +572,14 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         lds_barrier();
       }
     }
-    if (write_hT) {
+    // The final state: hT at the sequence end, or this segment's P or Q.
+    float* const dst = MAPS ? wsm + (map_p ? 0 : DK * DV) : (write_hT ? p.hT + sbase : nullptr);
+    if (dst) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<f32x2*>(p.hT + sbase + (long)key_of(kb, 4 * q4 + e) * DV + 32 * j + 2 * n16) =
+          *reinterpret_cast<f32x2*>(dst + (long)key_of(kb, 4 * q4 + e) * DV + 32 * j + 2 * n16) =
               f32x2{Macc[kb][0][e], Macc[kb][1][e]};
     }
   } else if (wave == W_L) {
@@ -616,7 +666,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       }
       issue_gb(it + 1);
       issue(p.k, sK, NKR, it + 1, true);
-      issue(p.q, sQ, NQR, it, it >= store_from);
+      issue(p.q, sQ, NQR, it, !MAPS && it >= store_from);
       step_barrier();
     }
     // The last steps' copies (of chunks past the end) still write LDS: let
@@ -841,8 +891,109 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         lds_barrier();
       }
     };
-    if (wave == W_P) p_wave(IC<0>{});
-    else p_wave(IC<1>{});
+    if constexpr (MAPS) {
+      for (int it = 0; it < NIT; ++it) lds_barrier();  // no outputs: nothing to form
+    } else if (wave == W_P) {
+      p_wave(IC<0>{});
+    } else {
+      p_wave(IC<1>{});
+    }
+  }
+}
+
+// ------------------------------------------------------------ the scan
+// Exact entry states of a cut sequence's segments.  Over a segment the rule
+// is affine in the state, M_end = P M_start + Q, and the maps pass above
+// leaves P (for segments 1 .. nseg-2) and Q (segments 0 .. nseg-2, the first
+// one from h0) in the workspace.  Here S_0 = h0, S_1 = Q_0 and
+// S_{s+1} = P_s S_s + Q_s, in fp32 on the matrix cores: the chunk-to-chunk
+// series of the chunked form ("Optimization Quartet", section 3.2) shrinks
+// to one dk x dk by dk x dv product per segment.  One workgroup per
+// (sequence, head, 16-column block); wave w owns state rows 16 w .. 16 w + 15.
+namespace sk {
+constexpr int NCB = fk::DV / 16;  // column blocks (workgroups per chain)
+constexpr int NWS = fk::DK / 16;  // waves, one per 16-row block
+constexpr int LD = fk::DK + 4;    // LDS pitch (floats) of a column of the state block
+}  // namespace sk
+
+__global__ __launch_bounds__(64 * sk::NWS, 1) void gdn_scan_kernel(const gdn_launch::FullParams p) {
+  using namespace fk;
+  // S_s of this column block, transposed (column-major), two steps.
+  __shared__ __attribute__((aligned(16))) float sS[2][16 * sk::LD];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4, n16 = lane & 15;
+  const int H = p.H;
+  const int item = xcd_remap(blockIdx.x, p.B * H * sk::NCB);
+  const int cb = item % sk::NCB, chain = item / sk::NCB;
+  const int hh = chain % H, n = chain / H;
+  int len = p.T, s0 = 0;
+  if (p.cu) {
+    s0 = p.cu[n];
+    len = p.cu[n + 1] - s0;
+  }
+  int nch, seg_len, nseg;
+  seg_layout(len, p.seg_max, nch, seg_len, nseg);
+  if (nseg <= 1) return;  // uniform over the workgroup
+  // First segment slot of the sequence (the same numbering as the kernel above).
+  const long slot0 = p.cu ? (long)(s0 / (p.seg_max * C)) + n : (long)n * nseg;
+  auto mat = [&](int s, int which) {  // which: 0 P, 1 Q, 2 S
+    return p.ws + (((slot0 + s) * H + hh) * 3 + which) * (long)(DK * DV);
+  };
+  // Result lane layout (16x16 fp32 accumulator): rows 16 w + 4 q4 + r,
+  // column 16 cb + n16.
+  const int col = 16 * cb + n16;
+  const int row = 16 * w + 4 * q4;
+  auto put = [&](int s, f32x4 d) {
+    float* S = mat(s, 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[(long)(row + r) * DV + col] = d[r];
+    *reinterpret_cast<f32x4*>(&sS[s & 1][n16 * sk::LD + row]) = d;
+  };
+  {
+    f32x4 h = {0.f, 0.f, 0.f, 0.f};
+    if (p.h0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = p.h0[((long)chain * DK + row + r) * DV + col];
+    }
+    put(0, h);
+    const float* Q0 = mat(0, 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = Q0[(long)(row + r) * DV + col];
+    put(1, h);
+  }
+  // A operand of step (a, t): P[16 w + n16][16 a + 4 q4 + t]; B operand:
+  // S[16 a + 4 q4 + t][col], one 16-byte LDS read per a.  The maps of
+  // segment s + 1 are loaded during step s (empty descriptors past the last).
+  f32x4 Pc[8], Qc, Pn[8], Qn;
+  auto load = [&](int s, f32x4 (&Pd)[8], f32x4& Qd) {
+    const bool live = s + 1 < nseg;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(mat(live ? s : 1, 0), live ? (long)DK * DV * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(mat(live ? s : 1, 1), live ? (long)DK * DV * 4 : 0);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+      Pd[a] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, ((16 * w + n16) * DV + 16 * a + 4 * q4) * 4, 0, 0));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      Qd[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rq, ((row + r) * DV + col) * 4, 0, 0));
+  };
+  load(1, Pc, Qc);
+  for (int s = 1; s + 1 < nseg; ++s) {
+    load(s + 1, Pn, Qn);
+    __syncthreads();  // S_s complete in sS[s & 1]; sS[(s + 1) & 1] no longer read
+    const float* Sb = sS[s & 1] + n16 * sk::LD + 4 * q4;
+    f32x4 d = Qc;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Sb + 16 * a);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) d = __builtin_amdgcn_mfma_f32_16x16x4f32(Pc[a][t], b[t], d, 0, 0, 0);
+    }
+    put(s + 1, d);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) Pc[a] = Pn[a];
+    Qc = Qn;
   }
 }
 
@@ -868,7 +1019,27 @@ int fwd_full(const FullParams& p, hipStream_t stream) {
   const long nwg = (long)p.nslot * p.H;
   if (nwg <= 0) return GDN_OK;
   if (nwg > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(gdn_full_kernel, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
+  hipLaunchKernelGGL(gdn_full_kernel<false>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+long long scan_ws_floats(int nslot, int H) { return (long long)nslot * H * 3 * fk::DK * fk::DV; }
+
+int fwd_full_scan(const FullParams& p, hipStream_t stream) {
+  const long nwg = (long)p.nslot * p.H;
+  if (nwg <= 0) return GDN_OK;
+  const long nscan = (long)p.B * p.H * sk::NCB;
+  if (!p.ws || 2 * nwg > 0x7fffffffL || nscan > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
+  // Only a sequence of more than seg_max chunks is cut.
+  const long seg_tokens = (long)p.seg_max * fk::C;
+  const bool cut = p.seg_max > 0 && p.T > seg_tokens;
+  if (cut) {
+    hipLaunchKernelGGL(gdn_full_kernel<true>, dim3((unsigned)(2 * nwg)), dim3(64 * fk::NW), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    hipLaunchKernelGGL(gdn_scan_kernel, dim3((unsigned)nscan), dim3(64 * sk::NWS), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(gdn_full_kernel<false>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

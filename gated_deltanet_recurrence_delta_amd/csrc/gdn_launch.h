@@ -27,12 +27,23 @@ struct FullParams {
   // on the sequence alone, never on the batch or the device.
   int seg_max;
   int nslot;  // segment slots per head (the grid is nslot x H)
+  // Chunk-map scan (fwd_full_scan): per (segment slot, head) three dk x dv
+  // fp32 matrices, row-major: the segment's map P and Q (M_end = P M_start
+  // + Q) and its exact entry state S.  Null: segments start from halos.
+  float* ws = nullptr;
 };
 
 // Number of segment slots per head for a call (see FullParams).
 __attribute__((visibility("hidden"))) int full_slots(int B, int T, bool packed, int seg_max);
 
 __attribute__((visibility("hidden"))) int fwd_full(const FullParams& p, hipStream_t stream);
+
+// Floats of workspace fwd_full_scan needs for nslot segment slots.
+__attribute__((visibility("hidden"))) long long scan_ws_floats(int nslot, int H);
+
+// Three launches: the maps of every segment but the last, the scan of the
+// maps into exact entry states, then the outputs from those states.
+__attribute__((visibility("hidden"))) int fwd_full_scan(const FullParams& p, hipStream_t stream);
 
 }  // namespace gdn_launch
 

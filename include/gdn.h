@@ -115,6 +115,59 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
             void* stream, int dtype, int chunk, int flags);
 
 /*
+ * gdn_fwd_scan -- gdn_fwd with exact segment starts: the chunk-map scan.
+ *
+ * Over any run of chunks the rule is affine in the state: with M = S^T,
+ * M_end = P M_start + Q, where P (dk x dk) depends on k, g and beta alone and
+ * Q (dk x dv) is the end state reached from zero.  The chunkwise form of the
+ * pages carries the state across chunks in series ("v1.0 Architecture &
+ * Design Spec", section 2.3; "Optimization Quartet", section 3.2); composing
+ * the chunks' maps lets a long sequence's segments run in parallel without
+ * any dependence on decay.  A sequence of n > 16 chunks is cut as in gdn_fwd
+ * (ceil(n / 16) segments of equal length) and run in three launches on
+ * `stream`:
+ *   1. every segment but the last composes its map -- the recurrence over
+ *      its chunks from the identity with v = 0 gives P, from zero with the
+ *      real v gives Q (the first segment's Q starts from h0 and so is the
+ *      second segment's entry state, and its P is not formed);
+ *   2. a scan per chain gives the exact entry states, S_0 = h0,
+ *      S_1 = Q_0, S_{s+1} = P_s S_s + Q_s (fp32, matrix cores);
+ *   3. every segment runs the forward pass from S_s and stores its outputs;
+ *      the last writes hT.
+ * Unlike gdn_fwd's halo segments, the result does not depend on the decay
+ * beyond rounding: a sequence with no decay at all is cut just the same.
+ * It costs about three passes over each cut sequence instead of one, so
+ * gdn_fwd is the faster choice when the decay makes halos short.
+ *
+ * Arguments, layouts, state semantics, error behaviour and determinism are
+ * gdn_fwd's (flags are not taken), plus:
+ *   workspace        DEVICE buffer of at least gdn_fwd_scan_workspace_size
+ *                    bytes, 16-byte aligned, owned by the caller and used
+ *                    only until the stream passes the call's last launch;
+ *                    may be NULL when that size is 0.
+ *   workspace_bytes  its size; too small (or a NULL / misaligned buffer
+ *                    when one is needed) is GDN_ERR_INVALID_ARG.
+ * After the call the workspace holds, for every segment slot sigma and head
+ * h, three fp32 dk x dv row-major matrices at float offset
+ * ((sigma * H + h) * 3 + m) * dk * dv: m = 0 the segment's P (m = 1 its Q,
+ * m = 2 its entry state S), written only for segments of cut sequences
+ * (P for segments 1 .. nseg-2, Q for 0 .. nseg-2, S for all).  Segment s of
+ * dense sequence b is slot b * nseg + s; of packed sequence n, slot
+ * floor(cu_seqlens[n] / 1024) + n + s.
+ * hT may alias h0 (h0 is read only by the first two launches).  A packed
+ * sequence's results equal the same sequence run alone bit for bit.
+ * Shapes other than GDN_BF16 with dk = dv = 128 and 64-token chunks need no
+ * workspace and run gdn_fwd with GDN_FLAG_NO_SEGMENTS (exact, uncut).
+ */
+long long gdn_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv,
+                                      int packed, int dtype, int chunk);
+int gdn_fwd_scan(const void* q, const void* k, const void* v, const float* g,
+                 const float* beta, const float* h0, const int32_t* cu_seqlens,
+                 void* out, float* hT, int B, int T, int H, int dk, int dv,
+                 void* stream, int dtype, int chunk, void* workspace,
+                 long long workspace_bytes);
+
+/*
  * gdn_fwd_recurrent -- the same operation in its token-by-token form, for
  * decoding and other short sequences: per token one rank-1 state update,
  *

@@ -45,6 +45,7 @@ class Workload:
     chunk: int
     h0_std: float = 0.0         # 0 -> no initial state (h0 = NULL)
     g_mean: float = 0.0         # g = -softplus(N(g_mean, 1))
+    no_decay: bool = False      # g = 0 (its draw is still taken, so the other draws are unchanged)
     varlen: bool = False
     len_lo: int = 0             # varlen: lengths ~ U[len_lo, len_hi] (inclusive)
     len_hi: int = 0
@@ -63,7 +64,7 @@ def _varlen(name, seed, nseq, lo, hi, H, dk, dv, dtype, chunk, **kw):
                     len_hi=hi, nseq=nseq, **kw)
 
 
-#: The five workloads, indexed by seed.
+#: The workloads, indexed by seed.
 WORKLOADS = {
     "tiny": Workload("tiny", 0, B=1, T=64, H=2, dk=32, dv=32, dtype=F32, chunk=16),
     "small_state": Workload("small_state", 1, B=8, T=4096, H=16, dk=32, dv=32,
@@ -74,6 +75,10 @@ WORKLOADS = {
                       dtype=BF16, chunk=64),
     "long_context": Workload("long_context", 4, B=1, T=32768, H=16, dk=128,
                              dv=128, dtype=BF16, chunk=64, g_mean=-2.0),
+    # long_context without any decay: a segment's halo would reach back to
+    # the sequence start, the case the chunk-map scan is for.
+    "long_context_nodecay": Workload("long_context_nodecay", 6, B=1, T=32768, H=16, dk=128,
+                                     dv=128, dtype=BF16, chunk=64, no_decay=True),
     # One decoding step at batch scale (the token-by-token entry point's
     # workload): the traffic is dominated by the state read and write.
     "decode": Workload("decode", 5, B=128, T=1, H=16, dk=128, dv=128, dtype=BF16,
@@ -82,7 +87,7 @@ WORKLOADS = {
 
 
 def custom(name="custom", seed=0, B=1, T=64, H=2, dk=32, dv=32, dtype=F32,
-           chunk=64, h0_std=0.0, g_mean=0.0, seq_lens=None) -> Workload:
+           chunk=64, h0_std=0.0, g_mean=0.0, seq_lens=None, no_decay=False) -> Workload:
     """A workload with the standard distributions at arbitrary sizes.
 
     ``seq_lens`` (a sequence of ints) makes it a packed varlen workload with
@@ -92,9 +97,9 @@ def custom(name="custom", seed=0, B=1, T=64, H=2, dk=32, dv=32, dtype=F32,
         lens = [int(x) for x in seq_lens]
         return Workload(name, seed, B=len(lens), T=sum(lens), H=H, dk=dk, dv=dv,
                         dtype=dtype, chunk=chunk, h0_std=h0_std, g_mean=g_mean,
-                        varlen=True, nseq=len(lens), seq_lens=tuple(lens))
+                        no_decay=no_decay, varlen=True, nseq=len(lens), seq_lens=tuple(lens))
     return Workload(name, seed, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype,
-                    chunk=chunk, h0_std=h0_std, g_mean=g_mean)
+                    chunk=chunk, h0_std=h0_std, g_mean=g_mean, no_decay=no_decay)
 
 
 # ---------------------------------------------------------------- casts ---
@@ -194,6 +199,8 @@ def generate(wl: Workload) -> Inputs:
     v = rng.standard_normal(lead + (H, dv))
     beta = _sigmoid(rng.standard_normal(lead + (H,)))
     g = -_softplus(rng.normal(wl.g_mean, 1.0, size=lead + (H,)))
+    if wl.no_decay:
+        g = np.zeros_like(g)
     h0 = None
     if wl.h0_std > 0:
         h0 = (rng.standard_normal((wl.B, H, dk, dv)) * wl.h0_std).astype(np.float32)

@@ -47,6 +47,19 @@ def run_hip(inp: synth.Inputs, chunk=None, d=None, **kw):
     return out, hT
 
 
+def run_hip_scan(inp: synth.Inputs, d=None, **kw):
+    """(out, hT) of the chunk-map scan entry point as torch device tensors."""
+    import torch
+
+    import gated_deltanet_recurrence_delta_amd as gdn
+
+    d = d or device_inputs(inp)
+    out, hT = gdn.fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
+                           chunk=inp.wl.chunk, **kw)
+    torch.cuda.synchronize()
+    return out, hT
+
+
 def run_hip_recurrent(inp: synth.Inputs, d=None, **kw):
     """(out, hT) of the token-by-token entry point as torch device tensors."""
     import torch

@@ -25,6 +25,7 @@ def _declared_functions():
 def test_header_declares_entry_points():
     assert _declared_functions() == ["gdn_bwd", "gdn_bwd_noalloc", "gdn_bwd_workspace_size", "gdn_diag_fwd",
                                      "gdn_diag_fwd_recurrent", "gdn_fwd", "gdn_fwd_recurrent",
+                                     "gdn_fwd_scan", "gdn_fwd_scan_workspace_size",
                                      "gdn_strerror", "gdn_version"]
 
 
@@ -87,6 +88,60 @@ def test_python_wrapper_rejects_cpu_tensors():
     g = torch.zeros(1, 4, 1)
     with pytest.raises(ValueError):
         gdn.fwd(q, q, q, g, g)
+
+
+# ------------------------------------------------------ chunk-map scan --
+
+def _call_scan(**kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, out=P, hT=P,
+             B=1, T=4096, H=2, dk=128, dv=128, stream=None, dtype=1, chunk=64,
+             workspace=P, workspace_bytes=1 << 40)
+    a.update(kw)
+    return gdn.gdn_fwd_scan(**a)
+
+
+def test_scan_workspace_size():
+    MAT = 128 * 128 * 4
+    # a dense 4,096-token sequence is cut into 4 segments: 4 slots x H x (P, Q, S)
+    assert gdn.gdn_fwd_scan_workspace_size(1, 4096, 2, 128, 128, 0, 1, 64) == 4 * 2 * 3 * MAT
+    assert gdn.gdn_fwd_scan_workspace_size(3, 4096, 2, 128, 128, 0, 1, 0) == 3 * 4 * 2 * 3 * MAT
+    # 17 chunks: 2 segments of 9 and 8 chunks
+    assert gdn.gdn_fwd_scan_workspace_size(1, 1025, 1, 128, 128, 0, 1, 64) == 2 * 3 * MAT
+    # packed: floor(T / 1024) + B slots
+    assert gdn.gdn_fwd_scan_workspace_size(5, 5000, 1, 128, 128, 1, 1, 64) == (4 + 5) * 3 * MAT
+    # nothing is cut at or below 16 chunks, and other shapes never use it
+    assert gdn.gdn_fwd_scan_workspace_size(8, 1024, 16, 128, 128, 0, 1, 64) == 0
+    assert gdn.gdn_fwd_scan_workspace_size(8, 1024, 16, 128, 128, 1, 1, 64) == 0
+    assert gdn.gdn_fwd_scan_workspace_size(1, 4096, 2, 32, 32, 0, 1, 64) == 0
+    assert gdn.gdn_fwd_scan_workspace_size(1, 4096, 2, 128, 128, 0, 1, 32) == 0
+    assert gdn.gdn_fwd_scan_workspace_size(1, 4096, 2, 128, 128, 0, 0, 32) == 0
+    assert gdn.gdn_fwd_scan_workspace_size(-1, 4096, 2, 128, 128, 0, 1, 64) == INVALID
+    assert gdn.gdn_fwd_scan_workspace_size(1, 4096, 0, 128, 128, 0, 1, 64) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(workspace=0), dict(workspace_bytes=4 * 2 * 3 * 65536 - 1),
+                                dict(workspace=P + 4), dict(workspace_bytes=-1)])
+def test_scan_rejects_bad_workspace(kw):
+    assert _call_scan(**kw) == INVALID
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "out", "hT"])
+def test_scan_null_required_pointer(name):
+    assert _call_scan(**{name: 0}) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(H=0), dict(dtype=2), dict(chunk=48)])
+def test_scan_invalid_sizes(kw):
+    assert _call_scan(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(dk=16), dict(dtype=0, chunk=64)])
+def test_scan_unsupported(kw):
+    assert _call_scan(**kw) == UNSUPPORTED
+
+
+def test_scan_no_chains_is_a_no_op():
+    assert _call_scan(B=0, workspace=0, workspace_bytes=0) == OK
 
 
 # -------------------------------------------------- token-by-token entry --
