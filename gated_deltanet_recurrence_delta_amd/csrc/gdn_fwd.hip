@@ -22,18 +22,20 @@
 //     O    = diag(Gam) Q M + ((Q K^T) * exp(gamma_i - gamma_j), j <= i) U
 //     M   <- Gam_C M + K^T diag(w) U
 //
-// Work decomposition: one workgroup per (chain, 32-wide value tile).  Value
-// columns never mix in the rule, so tiles are independent.  Per workgroup,
-// a three-stage pipeline over chunks (one LDS barrier per stage step):
-//   * the Gram wave loads chunk c+1 from HBM into registers while it stages
-//     chunk c (K, Q and this tile's V) into LDS, forms the decay vectors,
-//     the off-diagonal blocks of A and the masked decayed Q K^T;
-//   * one step later the solve wave forms the diagonal blocks of A and Tinv
-//     (16x16 diagonal inverses on the VALU, block merges on the MFMA);
-//   * one step after that the value waves (DVT/16 of them, 16 state columns
-//     each, M held in MFMA accumulators for the whole sequence) run the
-//     state-dependent part: K M, X, Tinv X, O, the state update.
-// One barrier per chunk.  No atomics: results are deterministic.
+// This file holds the C entry points (gdn_fwd, gdn_fwd_scan, gdn_strerror,
+// gdn_version) and the per-tile kernels.  Which kernel runs:
+//   * bf16 storage, dk = dv = 128, 64-token chunks: the full-width kernel of
+//     gdn_fwd_full.hip, one workgroup per (sequence segment, head) owning
+//     all value columns (also the three launches of gdn_fwd_scan);
+//   * other bf16 shapes: gdn_bf16_kernel below, one workgroup per (chain,
+//     32-column value tile), eight wave roles (loader, Gram, two solve, two
+//     state, two output) in a three-step software pipeline;
+//   * fp32 storage: gdn_fwd_kernel below, one workgroup per (chain,
+//     32-column value tile), a three-stage pipeline (Gram wave, solve wave,
+//     value waves holding the tile's state in MFMA accumulators).
+// Value columns never mix in the rule, so tiles are independent; each tile
+// recomputes its chunk's Gram matrix and solve.  No atomics: results are
+// deterministic.
 //
 // Operand conventions: a 16x16xSLAB MFMA "fragment" gives every lane
 // (l % 16 = row/column index, q = l / 16 = lane group) E consecutive

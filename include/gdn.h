@@ -154,8 +154,9 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
  * (P for segments 1 .. nseg-2, Q for 0 .. nseg-2, S for all).  Segment s of
  * dense sequence b is slot b * nseg + s; of packed sequence n, slot
  * floor(cu_seqlens[n] / 1024) + n + s.
- * hT may alias h0 (h0 is read only by the first two launches).  A packed
- * sequence's results equal the same sequence run alone bit for bit.
+ * hT may alias h0: a cut sequence reads h0 only in the first two launches,
+ * and an uncut one reads it in the same workgroup that later writes its hT.
+ * A packed sequence's results equal the same sequence run alone bit for bit.
  * Shapes other than GDN_BF16 with dk = dv = 128 and 64-token chunks need no
  * workspace and run gdn_fwd with GDN_FLAG_NO_SEGMENTS (exact, uncut).
  */
