@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", f) for f in ("gdn_fwd.hip", "gdn_fwd_full.hip", "gdn_recurrent.hip",
-                                                "gdn_diag.hip", "gdn_bwd.hip")]
+                                                "gdn_diag.hip", "gdn_bwd.hip", "gdn_bwd_full.hip")]
 LIB = os.path.join(HERE, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -61,6 +61,7 @@
 #include <mutex>
 
 #include "gdn.h"
+#include "gdn_launch.h"
 
 namespace {
 
@@ -1146,6 +1147,36 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
     }
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // bf16 with dk = dv = 128: the full-width kernels (gdn_bwd_full.hip), whose
+  // records fit in the workspace sized above (a 16-byte-aligned one).
+  if (dtype == GDN_BF16 && dkn == 128 && dvn == 128 && (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0 &&
+      (long long)need >= gdn_launch::bwd_full_ws_bytes(B, ttot, H)) {
+    gdn_launch::BwdParams bp;
+    bp.q = static_cast<const char*>(q);
+    bp.k = static_cast<const char*>(k);
+    bp.v = static_cast<const char*>(v);
+    bp.dO = static_cast<const char*>(dout);
+    bp.g = g;
+    bp.beta = beta;
+    bp.h0 = h0;
+    bp.dhT = dhT;
+    bp.cu = cu_seqlens;
+    bp.dq = static_cast<char*>(dq);
+    bp.dk = static_cast<char*>(dk);
+    bp.dv = static_cast<char*>(dv);
+    bp.dg = dg;
+    bp.dbeta = dbeta;
+    bp.dh0 = dh0;
+    bp.sv = static_cast<char*>(workspace);
+    bp.hT = dg;
+    bp.B = B;
+    bp.T = T;
+    bp.H = H;
+    bp.seg_max = gdn_launch::SEG_MAX_CHUNKS;
+    bp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, bp.seg_max);
+    bp.nchunk = (int)(ttot / 64 + B);
+    return gdn_launch::bwd_full(bp, st);
+  }
   float* ws = static_cast<float*>(workspace);
   return dtype == GDN_BF16 ? launch_dtype<__bf16>(dkn, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
                                                   dbeta, dh0, ws, p, st)

@@ -199,7 +199,7 @@ struct Params {
 
 // Longest segment, in chunks, of the full-width kernel (gdn_fwd_full.hip):
 // 16 chunks of 64 tokens cut a 4,096-token sequence into four workgroups.
-constexpr int GDN_SEG_MAX_CHUNKS = 16;
+constexpr int GDN_SEG_MAX_CHUNKS = gdn_launch::SEG_MAX_CHUNKS;
 
 // Largest packed batch whose sequences the bf16 kernel orders by length.
 constexpr int GDN_LPT_MAX = 512;

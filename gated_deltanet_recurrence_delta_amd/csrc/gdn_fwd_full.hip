@@ -57,67 +57,24 @@
 
 #include "gdn.h"
 #include "gdn_device.h"
+#include "gdn_full_common.h"
 #include "gdn_launch.h"
 
 namespace {
 
-namespace fk {
 
-constexpr int DK = 128, DV = 128, C = 64;
-constexpr int NB = C / 16, NTS = C / 32;    // 16-token blocks, 32-token slabs per chunk
-constexpr int NKB = DK / 16, NKS = DK / 32;  // 16-key blocks, 32-key slabs
-constexpr int NCW = DV / 32;                 // column waves
-constexpr int NW = NCW + 4;                  // + loader, Gram, two P waves
-constexpr int W_L = NCW, W_G = NCW + 1, W_P = NCW + 2;
-constexpr int KQR = DK * 2;       // bytes per q/k row
-constexpr int GR = KQR / 16;      // 16-byte granules per row
-constexpr int KQ_BYTES = C * KQR;  // one chunk of q or k
-constexpr int KQ_INS = KQ_BYTES / 1024, KQ_RPI = 1024 / KQR;  // copies per chunk, rows per copy
-constexpr int CCR = C * 2;        // bytes per row of a C x C bf16 tile
-constexpr int CC_BYTES = C * CCR;
-constexpr int NKR = 4, NQR = 3, NVEC = 3;  // ring depths: k, q, decay vectors
-// Per-token vectors (fp32, C each): beta, lambda = gamma*log2(e), Gam,
-// w = exp(gamma_C - gamma), exp(gamma_t - gamma at the start of t's block),
-// and for b = 1..NB-1, exp(gamma_{16 b} - gamma_t) (t < 16 b).
-constexpr int F_BETA = 0, F_LAM = 1, F_GAM = 2, F_W = 3, F_ER = 4, NF = 4 + NB;
-constexpr int AD_ROW = 20, AD_BLK = 16 * AD_ROW + 4;  // padded fp32 diagonal blocks
-constexpr int LDS = NKR * KQ_BYTES + NQR * KQ_BYTES + CC_BYTES + 2 * CC_BYTES + CC_BYTES +
-                    NVEC * NF * C * 4 + NB * AD_BLK * 4 + 4 * C * 4 + 64;
-static_assert(LDS <= 160 * 1024, "LDS budget");
-static_assert(NB == 4 && NKS == 4 && NCW == 4, "shape");
-
-// P wave o owns the 16-row blocks {o, 3 - o} (equal MFMA work).
-__host__ __device__ constexpr int own_tb(int o, int i) { return i == 0 ? o : NB - 1 - o; }
-
-// State row (key) held by accumulator block b, row r: of the 32 keys of
-// slab b >> 1, block b takes the half b & 1 of each 8-key group, so that
-// two stacked blocks form a bf16 fragment whose positions are the natural
-// keys 32 s + 8 q .. 32 s + 8 q + 7 of lane group q.
-__device__ static inline int key_of(int b, int r) {
-  return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3);
-}
-
-// Chunk count of a sequence and its segment layout.
-__device__ static inline void seg_layout(int len, int seg_max, int& nch, int& seg_len, int& nseg) {
-  nch = (len + C - 1) / C;
-  if (seg_max <= 0 || nch <= seg_max) {
-    seg_len = nch > 0 ? nch : 1;
-    nseg = 1;
-    return;
-  }
-  const int n0 = (nch + seg_max - 1) / seg_max;
-  seg_len = (nch + n0 - 1) / n0;
-  nseg = (nch + seg_len - 1) / seg_len;
-}
-
-}  // namespace fk
-
-// MAPS = false: outputs and hT.  MAPS = true: the affine map of one segment
+// MODE 0: outputs and hT.  MODE 1 (maps): the affine map of one segment
 // (p.ws set; see the chunk-map scan below): the recurrence over the
 // segment's chunks from the identity with v = 0 (giving P) or from zero
 // (from h0 for the first segment) with the real v (giving Q), no outputs.
-template <bool MAPS>
+// MODE 2 (states for the backward pass, p.sv set): the recurrence as in
+// MODE 0 without outputs; every chunk's entry state M and its U are saved
+// in bf16 (see gdn_launch.h).
+template <int MODE>
 __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_launch::FullParams p) {
+  constexpr bool MAPS = MODE == 1;
+  constexpr bool SAVE = MODE == 2;
+  constexpr bool NOOUT = MODE != 0;  // no outputs: no q, no P waves
   using namespace fk;
   using MM = Mma<__bf16>;
   using F = bf16x8;
@@ -187,6 +144,8 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   seg = __builtin_amdgcn_readfirstlane(seg);
   len = __builtin_amdgcn_readfirstlane(len);
   const int chain = bseq * H + hh;
+  // Chunk slot of the sequence's first chunk (backward records).
+  const long cslot0 = rowbase / C + bseq;
 
   // Segment range [c0, c1) of chunks whose outputs this workgroup stores,
   // and where its recurrence starts (cs <= c0).
@@ -230,7 +189,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   }
   __syncthreads();
   const int cs = sSTART;
-  const bool write_hT = !MAPS && c1 >= nch;
+  const bool write_hT = MODE == 0 && c1 >= nch;
   // This (segment slot, head)'s P, Q and entry state S in the workspace.
   float* const wsm = p.ws ? p.ws + ((long)slot * H + hh) * 3 * DK * DV : nullptr;
   // Where the recurrence's starting state comes from (an empty descriptor
@@ -358,6 +317,22 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     // W = diag(w) U -> M <- Gam_C M + K^T W -> bf16 state; u = Tb V,
     // diag(Gam) Q M and the stores hang off it.
     auto process = [&](int c) {
+      // States pass: this chunk's record (empty for halo chunks).
+      __amdgpu_buffer_rsrc_t rrec;
+      if constexpr (SAVE) {
+        rrec = make_rsrc(p.sv + ((cslot0 + cs + c) * H + hh) * gdn_launch::BWD_REC_BYTES,
+                         c >= store_from ? gdn_launch::BWD_REC_BYTES : 0);
+        // entry state, transposed (value rows of 128 keys): lane (n16, q4)
+        // holds the four consecutive keys key_of(kb, 4 q4) .. +3 of value
+        // column 32 j + 2 n16 + cb
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(u32x2, cvt4(Macc[kb][cb])), rrec,
+                (int)(gdn_launch::BWD_OFF_M + ((32 * j + 2 * n16 + cb) * DK + key_of(kb, 4 * q4)) * 2), 0, 0);
+      }
       const char* sk = sK + (c % NKR) * KQ_BYTES;
       const char* sq = sQ + (c % NQR) * KQ_BYTES;
       const char* st = sT + (c & 1) * CC_BYTES;
@@ -455,6 +430,16 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
           for (int s = 0; 2 * s <= tb; ++s) u = MM::mma(TPf[tb][s], Zf[s][cb], u);
           U[tb][cb] = u;
         }
+      if constexpr (SAVE) {
+        // U, bf16 row-major: tokens 16 tb + 4 q4 + e, value columns 32 j + 2 n16 + {0, 1}
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, bf16x2{(__bf16)U[tb][0][e], (__bf16)U[tb][1][e]}), rrec,
+                (int)(gdn_launch::BWD_OFF_U + ((16 * tb + 4 * q4 + e) * DV + 32 * j + 2 * n16) * 2), 0, 0);
+      }
       F Uf[NTS][2], Wf[NTS][2];
 #pragma unroll
       for (int s = 0; s < NTS; ++s) {
@@ -476,7 +461,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       // update: lane (token 16 tb + n16, q4) holds value columns
       // 32 j + 2 (4 q4 + e) + cb.
       f32x4 O[NB][2];
-      if constexpr (!MAPS) {
+      if constexpr (!NOOUT) {
         F Qf[2][NKS];
         auto read_q = [&](int tb) {
 #pragma unroll
@@ -521,7 +506,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         }
       }
       make_mf();
-      if constexpr (!MAPS) {
+      if constexpr (!NOOUT) {
         // O^T += U^T P^T once the P waves have published P.
         flag_wait_lds(&sFLAG[0], c + 1);
         flag_wait_lds(&sFLAG[1], c + 1);
@@ -559,8 +544,8 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       // at the end of every chunk, the loads of v are followed by four
       // stores: the waits placed for v before its first use then count the
       // same operations on both ways in, and never wait for the stores.
-      // (The maps pass stores nothing in its chunks.)
-      if constexpr (!MAPS) {
+      // (The maps and states passes store nothing here in their chunks.)
+      if constexpr (!NOOUT) {
         const __amdgpu_buffer_rsrc_t none = make_rsrc(p.out, 0);
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
@@ -666,7 +651,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       }
       issue_gb(it + 1);
       issue(p.k, sK, NKR, it + 1, true);
-      issue(p.q, sQ, NQR, it, !MAPS && it >= store_from);
+      issue(p.q, sQ, NQR, it, !NOOUT && it >= store_from);
       step_barrier();
     }
     // The last steps' copies (of chunks past the end) still write LDS: let
@@ -891,7 +876,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         lds_barrier();
       }
     };
-    if constexpr (MAPS) {
+    if constexpr (NOOUT) {
       for (int it = 0; it < NIT; ++it) lds_barrier();  // no outputs: nothing to form
     } else if (wave == W_P) {
       p_wave(IC<0>{});
@@ -1019,7 +1004,15 @@ int fwd_full(const FullParams& p, hipStream_t stream) {
   const long nwg = (long)p.nslot * p.H;
   if (nwg <= 0) return GDN_OK;
   if (nwg > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(gdn_full_kernel<false>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
+  hipLaunchKernelGGL(gdn_full_kernel<0>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int fwd_full_save(const FullParams& p, hipStream_t stream) {
+  const long nwg = (long)p.nslot * p.H;
+  if (nwg <= 0) return GDN_OK;
+  if (nwg > 0x7fffffffL || !p.sv) return GDN_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(gdn_full_kernel<2>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -1034,12 +1027,12 @@ int fwd_full_scan(const FullParams& p, hipStream_t stream) {
   const long seg_tokens = (long)p.seg_max * fk::C;
   const bool cut = p.seg_max > 0 && p.T > seg_tokens;
   if (cut) {
-    hipLaunchKernelGGL(gdn_full_kernel<true>, dim3((unsigned)(2 * nwg)), dim3(64 * fk::NW), 0, stream, p);
+    hipLaunchKernelGGL(gdn_full_kernel<1>, dim3((unsigned)(2 * nwg)), dim3(64 * fk::NW), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
     hipLaunchKernelGGL(gdn_scan_kernel, dim3((unsigned)nscan), dim3(64 * sk::NWS), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(gdn_full_kernel<false>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
+  hipLaunchKernelGGL(gdn_full_kernel<0>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -9,6 +9,9 @@
 
 namespace gdn_launch {
 
+// Longest sequence segment, in 64-token chunks, of the full-width kernels.
+constexpr int SEG_MAX_CHUNKS = 16;
+
 // One workgroup per (sequence segment, head), all dv = 128 value columns,
 // dk = 128, 64-token chunks, bf16 storage.
 struct FullParams {
@@ -31,7 +34,48 @@ struct FullParams {
   // fp32 matrices, row-major: the segment's map P and Q (M_end = P M_start
   // + Q) and its exact entry state S.  Null: segments start from halos.
   float* ws = nullptr;
+  // Backward-pass records (gdn_full_kernel<2> writes M and U, the adjoint
+  // kernel dM and dX): one record of BWD_REC_BYTES per (chunk slot, head),
+  // chunk c of the sequence whose tokens start at s taking chunk slot
+  // floor(s / 64) + (sequence index) + c.  Each part is bf16 row-major.
+  char* sv = nullptr;
 };
+
+// A backward record: M^T and dM^T (the chunk's entry state and the
+// gradient reaching its exit state, transposed: dv rows of dk keys), then
+// U and dX (C token rows of dv values), at these byte offsets.
+constexpr long BWD_OFF_M = 0, BWD_OFF_DM = 128 * 128 * 2, BWD_OFF_U = 2 * 128 * 128 * 2,
+               BWD_OFF_DX = 2 * 128 * 128 * 2 + 64 * 128 * 2, BWD_REC_BYTES = 2 * 128 * 128 * 2 + 2 * 64 * 128 * 2;
+
+// Backward pass, bf16, dk = dv = 128, 64-token chunks (gdn_bwd_full.hip).
+struct BwdParams {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* dO;
+  const float* g;
+  const float* beta;
+  const float* h0;
+  const float* dhT;
+  const int32_t* cu;
+  char* dq;
+  char* dk;
+  char* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  char* sv;   // records, as FullParams::sv
+  float* hT;  // any valid float buffer (the states pass writes no hT)
+  int B, T, H;
+  int seg_max, nslot;  // sequence segments of the two sweeps (as FullParams)
+  int nchunk;          // chunk slots per head
+};
+
+// Bytes of records the full-width backward needs.
+__attribute__((visibility("hidden"))) long long bwd_full_ws_bytes(int B, long ttot, int H);
+
+// The states pass, the adjoint sweep and the gradient kernel.
+__attribute__((visibility("hidden"))) int bwd_full(const BwdParams& p, hipStream_t stream);
 
 // Number of segment slots per head for a call (see FullParams).
 __attribute__((visibility("hidden"))) int full_slots(int B, int T, bool packed, int seg_max);
@@ -44,6 +88,10 @@ __attribute__((visibility("hidden"))) long long scan_ws_floats(int nslot, int H)
 // Three launches: the maps of every segment but the last, the scan of the
 // maps into exact entry states, then the outputs from those states.
 __attribute__((visibility("hidden"))) int fwd_full_scan(const FullParams& p, hipStream_t stream);
+
+// The forward recurrence saving every chunk's entry state and U into p.sv
+// (no outputs, no hT).
+__attribute__((visibility("hidden"))) int fwd_full_save(const FullParams& p, hipStream_t stream);
 
 }  // namespace gdn_launch
 
