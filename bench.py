@@ -20,8 +20,9 @@ three launches per step, timed together).
 
 ``--pass bwd`` times the backward entry point gdn_bwd on the same workload
 (dq, dk, dv, dg, dbeta, dh0 from seeded output gradients dout ~ N(0,1),
-dhT ~ N(0,1)); its roofline is fp32 vector arithmetic (the backward's four
-kernels compute in fp32 on the VALU).
+dhT ~ N(0,1)); its roofline is the matrix cores' bf16 rate for bf16 storage
+with dk = dv = 128 (three full-width kernels, 64-token chunks) and fp32
+arithmetic otherwise (four fp32 kernels, 32-token chunks).
 
 ``--workload hymo`` / ``hymo_decode`` time the diagonal-decay additive
 recurrence with its epilogue (gdn_diag_fwd / gdn_diag_fwd_recurrent) on the
@@ -53,6 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wide_head.json")
 COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
 METRIC_BWD = "gated-delta-rule bwd tokens/s + achieved fp32 TFLOP/s (% roofline), 1 MI355X"
 FP32_PEAK_TFLOPS = 157.3
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores (no sparsity)
 METRIC_DIAG = ("diagonal-decay recurrence (HyMo GDN layer) fwd tokens/s + achieved HBM GB/s "
                "(% roofline), 1 MI355X")
 
@@ -343,6 +345,29 @@ def diag_main(args):
     print(json.dumps(rec), flush=True)
 
 
+def bwd_full_width(wl: synth.Workload) -> bool:
+    """gdn_bwd runs the full-width bf16 kernels (64-token chunks) for these shapes."""
+    return wl.dtype == "bf16" and wl.dk == 128 and wl.dv == 128
+
+
+def bwd_flops_full(wl: synth.Workload, lens) -> int:
+    """Floating-point operations of one full-width gdn_bwd call (bf16, dk = dv
+    = d = 128, C = 64-token chunks; 2 per multiply-add; products with a
+    triangular factor counted at half).  Per chunk and head:
+      states   K K^T (C^2 d / 2), the triangular inverse (C^3 / 6), K M and
+               K^T diag(w) U (2 C d^2), T diag(beta) X (C^2 d / 2)
+      adjoint  K K^T and Q K^T (C^2 d), the inverse (C^3 / 6), K dM',
+               Q^T (Gam dO), K^T W (3 C d^2), P^T dO and T^T dU (C^2 d)
+      grad     K K^T, Q K^T, dX U^T, dO U^T (2 C^2 d), dO M^T, dX M^T,
+               U dM'^T (3 C d^2), (dP.E) K, G K, G^T K, (dP.E)^T Q (2 C^2 d)."""
+    C, d = 64, wl.dk
+    per_chunk = (C * C * d // 2 + C ** 3 // 6 + 2 * C * d * d + C * C * d // 2
+                 + C * C * d + C ** 3 // 6 + 3 * C * d * d + C * C * d
+                 + 2 * C * C * d + 3 * C * d * d + 2 * C * C * d)
+    chunks = sum((int(n) + C - 1) // C for n in lens)
+    return 2 * per_chunk * chunks * wl.H
+
+
 def bwd_flops(wl: synth.Workload, lens) -> int:
     """Floating-point operations of one gdn_bwd call as its four kernels
     compute it (32-token chunks; 2 per multiply-add).  Per chunk of L <= 32
@@ -421,7 +446,9 @@ def bwd_main(args):
     launch_ms = np.array([a.elapsed_time(e) for a, e in zip(starts, ends)])
     ms_per_step = wall * 1e3 / args.steps
     mean_s = float(launch_ms.mean()) / 1e3
-    flops = bwd_flops(wl, lens)
+    full = bwd_full_width(wl)
+    flops = bwd_flops_full(wl, lens) if full else bwd_flops(wl, lens)
+    peak = BF16_PEAK_TFLOPS if full else FP32_PEAK_TFLOPS
     achieved = flops / mean_s / 1e12
     rec = {
         "metric": METRIC_BWD,
@@ -438,13 +465,14 @@ def bwd_main(args):
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
                 "g=-softplus(N(%g,1)), dout N(0,1), dhT N(0,1))" % wl.g_mean,
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} dk={wl.dk} dv={wl.dv} "
-                               f"{wl.dtype} backward, 32-token chunks"
+                               f"{wl.dtype} backward, " + ("64-token chunks" if full else "32-token chunks")
                                + (" varlen" if wl.varlen else ""),
                    "entry_point": "gdn_bwd", "tokens_per_step": wl.tokens,
                    "rotated_sets": len(sets), "workspace_bytes": need},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "gdn_bwd, all four kernels of one call",
+        "roofline": {"bound": "mfma" if full else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "kernel": ("gdn_bwd, its three kernels (states, adjoint, grad) of one call, bf16 matrix cores"
+                                if full else "gdn_bwd, all four kernels of one call"),
                      "algorithmic_flops": flops, "mean_launch_us": mean_s * 1e6,
                      "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
                      "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,

@@ -246,13 +246,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
                                                     r >= r_store ? gdn_launch::BWD_REC_BYTES : 0);
       // The gradient reaching this chunk's exit, transposed (value rows of
       // 128 keys, four consecutive keys per lane and column).
+      {
+        const int dt_lane = ((32 * j + 2 * n16) * DK + 8 * q4) * 2;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          __builtin_amdgcn_raw_buffer_store_b64(
-              __builtin_bit_cast(u32x2, cvt4(Dacc[kb][cb])), rrec,
-              (int)(gdn_launch::BWD_OFF_DM + ((32 * j + 2 * n16 + cb) * DK + key_of(kb, 4 * q4)) * 2), 0, 0);
+          for (int cb = 0; cb < 2; ++cb)
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(Dacc[kb][cb])), rrec,
+                                                  dt_lane + (cb * DK + 32 * (kb >> 1) + 4 * (kb & 1)) * 2,
+                                                  (int)gdn_launch::BWD_OFF_DM, 0);
+      }
 
       // dO as B fragments (byte permutes of the bf16 pairs), and Gam dO.
       F dOf[NTS][2], GdOf[NTS][2];
@@ -369,13 +372,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
         }
       }
       // dX saved (bf16 token rows); W = -diag(Gam beta) dX.
+      {
+        const int x_lane = (4 * q4 * DV + 32 * j + 2 * n16) * 2;
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb)
+        for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __builtin_bit_cast(uint32_t, bf16x2{(__bf16)dX[tb][0][e], (__bf16)dX[tb][1][e]}), rrec,
-              (int)(gdn_launch::BWD_OFF_DX + ((16 * tb + 4 * q4 + e) * DV + 32 * j + 2 * n16) * 2), 0, 0);
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, bf16x2{(__bf16)dX[tb][0][e], (__bf16)dX[tb][1][e]}), rrec, x_lane,
+                (int)gdn_launch::BWD_OFF_DX + (16 * tb + e) * DV * 2, 0);
+      }
       F Wf[NTS][2];
 #pragma unroll
       for (int s = 0; s < NTS; ++s) {
@@ -750,7 +756,7 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
   __shared__ __attribute__((aligned(16))) float sGB[2 * C];
   __shared__ float sZr[NB * NB][16], sZc[NB * NB][16], sBr[NB * NB][16];
   __shared__ float sSum[3][2][C];  // dO M^T . q, dX M^T . k, U dM'^T . k per token, per key half
-  __shared__ float sXV[C], sGC[gk::NWG], sDG[2][C];
+  __shared__ float sXV[C], sGC[gk::NWG];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1121,19 +1127,22 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
     const float sWv = sSum[2][0][t] + sSum[2][1][t];
     const float dGam = __builtin_fmaf(-bt, sXv, sQv) + (t == last ? gc : 0.f);
     const float dbeta = __builtin_fmaf(-Gt, sXv, sXV[t]) + b2;
-    sDG[0][t] = __builtin_fmaf(dGam, Gt, rz - cz);  // dgamma without the w terms
-    sDG[1][t] = sWv * wt;                           // dw . w
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, read across lanes below
+    const float dgam = t < Lc ? __builtin_fmaf(dGam, Gt, rz - cz) : 0.f;  // dgamma without the w terms
+    const float dww = t < Lc ? sWv * wt : 0.f;                              // dw . w
     // dg_t = sum_{u >= t} dgamma_u; the w terms (-dw_u w_u at every token,
     // +sum_u dw_u w_u at the last) enter as they add up after the reverse
     // sum, sum_{u < t} dw_u w_u, which cancels nothing large under strong
-    // decay.  Fixed trip counts; the zeros past the chunk's end are added
-    // first and change nothing.
-    float acc = 0.f;
-#pragma unroll
-    for (int u = C - 1; u >= 0; --u) acc += (u >= t && u < Lc) ? sDG[0][u] : 0.f;
-#pragma unroll
-    for (int u = 0; u < C; ++u) acc += u < t ? sDG[1][u] : 0.f;
+    // decay.  The suffix sum is a prefix sum over the lanes in reverse
+    // order, the exclusive prefix sum an inclusive one moved up a lane:
+    // neither subtracts a total (fixed addition order: deterministic).
+    const float rev = __shfl(dgam, C - 1 - t);
+    const float suf = __shfl(wave_prefix_sum(rev, t), C - 1 - t);
+    const float inc = wave_prefix_sum(dww, t);
+    // every lane takes part in the cross-lane read (a lane left out of it
+    // would not supply its value to the next one), then lane 0 drops it
+    const float prev = __shfl(inc, (t + C - 1) & (C - 1));
+    const float exc = t > 0 ? prev : 0.f;
+    const float acc = suf + exc;
     if (t < Lc) {
       const long th = (t0 + t) * H + hh;
       p.dg[th] = acc;

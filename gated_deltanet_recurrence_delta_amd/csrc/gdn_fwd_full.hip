@@ -325,13 +325,14 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         // entry state, transposed (value rows of 128 keys): lane (n16, q4)
         // holds the four consecutive keys key_of(kb, 4 q4) .. +3 of value
         // column 32 j + 2 n16 + cb
+        // (one lane base; the rest is a per-instruction constant)
+        const int mt_lane = (int)gdn_launch::BWD_OFF_M + ((32 * j + 2 * n16) * DK + 8 * q4) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(u32x2, cvt4(Macc[kb][cb])), rrec,
-                (int)(gdn_launch::BWD_OFF_M + ((32 * j + 2 * n16 + cb) * DK + key_of(kb, 4 * q4)) * 2), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(Macc[kb][cb])), rrec,
+                                                  mt_lane + (cb * DK + 32 * (kb >> 1) + 4 * (kb & 1)) * 2, 0, 0);
       }
       const char* sk = sK + (c % NKR) * KQ_BYTES;
       const char* sq = sQ + (c % NQR) * KQ_BYTES;
@@ -432,13 +433,14 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
         }
       if constexpr (SAVE) {
         // U, bf16 row-major: tokens 16 tb + 4 q4 + e, value columns 32 j + 2 n16 + {0, 1}
+        const int u_lane = (4 * q4 * DV + 32 * j + 2 * n16) * 2;
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             __builtin_amdgcn_raw_buffer_store_b32(
-                __builtin_bit_cast(uint32_t, bf16x2{(__bf16)U[tb][0][e], (__bf16)U[tb][1][e]}), rrec,
-                (int)(gdn_launch::BWD_OFF_U + ((16 * tb + 4 * q4 + e) * DV + 32 * j + 2 * n16) * 2), 0, 0);
+                __builtin_bit_cast(uint32_t, bf16x2{(__bf16)U[tb][0][e], (__bf16)U[tb][1][e]}), rrec, u_lane,
+                (int)gdn_launch::BWD_OFF_U + (16 * tb + e) * DV * 2, 0);
       }
       F Uf[NTS][2], Wf[NTS][2];
 #pragma unroll

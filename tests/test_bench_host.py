@@ -44,6 +44,18 @@ def test_backward_flops_count_chunks_per_sequence():
     assert bench.bwd_flops(wl, [33]) == 2 * bench.bwd_flops(wl, [32])
 
 
+def test_full_width_backward_flops():
+    """bf16 with dk = dv = 128 runs the 64-token full-width kernels; per
+    chunk and head: 8 C d^2 (dense products), 7 C^2 d (chunk-square ones,
+    triangular ones at half) and C^3 / 3 (two triangular inverses)."""
+    wl = synth.WORKLOADS["wide_head"]
+    assert bench.bwd_full_width(wl) and not bench.bwd_full_width(synth.WORKLOADS["small_state"])
+    C, d = 64, 128
+    per = 8 * C * d * d + 7 * C * C * d + 2 * (C ** 3 // 6)
+    assert bench.bwd_flops_full(wl, [wl.T] * wl.B) == 2 * per * 64 * wl.B * wl.H
+    assert bench.bwd_flops_full(wl, [65]) == 2 * bench.bwd_flops_full(wl, [64])
+
+
 def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("int f(int x) {\n  return x + 1;  // one\n}\n")
