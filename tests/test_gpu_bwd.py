@@ -305,3 +305,16 @@ def test_adjoint_identity_full_workload(name):
     print(f"{name}: <dout,out>+<dhT,hT> {lhs:.6e}  <dv,v>+<dh0,h0> {rhs:.6e}  "
           f"rel to sum |terms| {abs(lhs - rhs) / scale:.2e}", flush=True)
     assert abs(lhs - rhs) <= 5e-5 * scale
+
+
+@pytest.mark.parametrize("T", [70, 200, 136])
+def test_partial_last_chunk_slow_decay(T):
+    """bf16 d = 128 (the 64-token full-width kernels) with a ragged last
+    chunk and slow decay, so that every exit-decay factor w of the partial
+    chunk is far from zero and each token's dg takes the w terms of all the
+    tokens before it (a defect in how one lane's term reached the next
+    showed here and not under the default decay)."""
+    wl = synth.custom(name=f"bwd_tail{T}", seed=730 + T, B=2, T=T, H=2, dk=128, dv=128,
+                      dtype="bf16", h0_std=0.3, g_mean=-4.0)
+    inp = synth.generate(wl)
+    _check(inp, synth.output_grads(inp, 830 + T))
