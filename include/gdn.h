@@ -294,12 +294,25 @@ int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c,
  * workspace when B > 0.  No output may alias an input or another output.
  *
  * Behaviour: host-side arguments are validated first; on any error a
- * negative status is returned and nothing is launched.  Four kernels are
- * queued on `stream` (chunk matrices, chunk-entry states, the state
- * gradient swept backwards over the chunks, the per-chunk token gradients);
- * results are valid once the stream has been synchronised.  Arithmetic is
- * fp32 throughout; results are bitwise reproducible on one device (no
- * atomics).  A dense batch with fewer chains x 16-column tiles than twice
+ * negative status is returned and nothing is launched.  Results are valid
+ * once the stream has been synchronised, and bitwise reproducible on one
+ * device (no atomics).
+ *
+ * GDN_BF16 with dk = dv = 128 and a 16-byte-aligned workspace: three
+ * kernels with 64-token chunks, every product on the bf16 matrix cores with
+ * fp32 accumulation: the forward recurrence saving each chunk's entry state
+ * and U, the state gradient swept backwards over the chunks saving each
+ * chunk's exit gradient and dX, then the per-chunk token gradients.  The
+ * sweeps run as gdn_fwd's sequence segments (at most 16 chunks each, halos
+ * bounded as there; a packed sequence equals the same sequence alone bit for
+ * bit).  The saved matrices are bf16, so the gradients carry bf16-level
+ * rounding (about 5e-3 of their scale); the workspace use is a prefix of
+ * 96 KB per (64-token chunk, head).
+ *
+ * Other shapes and GDN_F32: four kernels with 32-token chunks (chunk
+ * matrices, chunk-entry states, the state gradient swept backwards, the
+ * per-chunk token gradients), arithmetic fp32 throughout (bf16 storage is
+ * widened on load).  A dense batch with fewer chains x 16-column tiles than twice
  * the device's CUs, and at least 16 chunks per sequence, runs the two
  * sweeps as sequence segments: a segment's state sweep starts from zero at
  * the latest chunk boundary behind it where the product of the per-token
