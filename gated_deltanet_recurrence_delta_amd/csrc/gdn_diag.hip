@@ -14,6 +14,7 @@
 // Every value column of the state evolves on its own: column d only ever
 // meets v_t[d].  That is what both forms below exploit.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "gdn.h"
@@ -237,24 +238,44 @@ struct ChunkParams {
   int T, H, nchain, nseg, seg_chunks;
 };
 
-// Per-wave LDS region (≈16.8 KB; four waves and the shared part fit twice
+// Per-wave LDS region (≈17.8 KB; four waves and the shared part fit twice
 // in a CU's 160 KB).
+//
+// The chunk rows of b, c and v are token-major, 64 bytes per token, with
+// the four 16-byte granules of row r permuted: granule g sits at
+// g ^ swz(r), swz(r) = the two bits of (r >> 2) & 3 reversed.  That puts
+// the column reads of the c rows (sixteen rows, 8 bytes each) and the
+// transposing reads of b and v (eight rows) on distinct banks.
+//
+// The decay-product tables of a sub-chunk are one contiguous block: the
+// per-token decays e^{A_s g_t} (fp16, row t at 15 - t, i.e. stored last
+// row first), 15 zero rows, then the b rows in fp16 (row t at t).  Rows
+// -1 ... -15 of either table fall into the zero rows, which is what lets
+// every lane walk the same number of steps (see phase B).
+constexpr int PROW = 80;  // bytes per row of P (bf16, column tau at 16 + tau)
 struct WaveLds {
-  alignas(16) char b[CC * ROWB];     // chunk rows of b (bf16, token-major)
+  alignas(16) char b[CC * ROWB];     // chunk rows of b (bf16, token-major, granules permuted)
   alignas(16) char c[CC * ROWB];
   alignas(16) char v[CC * ROWB];
-  alignas(16) _Float16 at[16 * CS];  // e^{A_s g_t} of the current sub-chunk (fp16); output staging after P
-  alignas(16) _Float16 ct[16 * CS];  // c rows of the current sub-chunk (fp16)
-  alignas(16) float p[16 * 16];      // P of the current sub-chunk, [t][tau]
+  alignas(16) _Float16 ta[16 * CS];  // e^{A_s g_t}, last row first; output staging after P
+  alignas(16) _Float16 tz[15 * CS];  // zeros
+  alignas(16) _Float16 tb[16 * CS];  // b rows of the sub-chunk (fp16)
+  alignas(16) char p[16 * PROW];     // P of the sub-chunk (bf16), row t, column tau at 16 + tau
   alignas(16) float ex[5 * CS];      // per-row decays: sub-chunk k at [32 k + s], chunk at [128 + s]
   alignas(16) float gam[CC];         // chunk-relative inclusive cumsum of g
   alignas(16) float graw[CC];
   alignas(16) float gate[CC];
 };
+static_assert(offsetof(WaveLds, tz) == offsetof(WaveLds, ta) + 16 * CS * 2, "tables are contiguous");
+static_assert(offsetof(WaveLds, tb) == offsetof(WaveLds, tz) + 15 * CS * 2, "tables are contiguous");
+
+// Granule permutation of the chunk rows (see WaveLds).
+__device__ static inline int swz(int row) { return ((row >> 2) & 1) << 1 | ((row >> 3) & 1); }
 
 struct ChunkLds {
   WaveLds w[CW];
-  alignas(16) float state[2][CS * CD];  // entry states, lane-major (16 floats per lane)
+  // entry states: element i of the lane's f32x4 number j at [j][lane][i]
+  alignas(16) float state[2][CS * CD];
   alignas(16) float a2[CS];             // A_s log2(e)
   int ready;                            // index of the latest entry state in `state`
   int cstart;                           // first chunk this workgroup runs
@@ -378,7 +399,7 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
       }
     }
     // lane holds rows 16*mt + 4q + i, column 16*nt + n  (accumulator layout)
-    float* slot = L.state[cs & 1] + 16 * lane;
+    float* slot = L.state[cs & 1] + 4 * lane;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -387,13 +408,20 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * mt + 4 * q + i, d = 16 * nt + n;
           const float x = (p.h0 && cs == 0) ? p.h0[sbase + s * CD + d] : 0.f;
-          slot[8 * mt + 4 * nt + i] = x;
+          slot[256 * (2 * mt + nt) + i] = x;
           if (nch == 0) p.hT[sbase + s * CD + d] = x;
         }
     if (lane == 0) {
       L.ready = cs;
       L.cstart = cs;
     }
+  }
+  // the zero rows of the decay tables and the never-written part of P
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (lane < 60) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tz) + 16 * lane) = z;
+    *reinterpret_cast<u32x4*>(W.p + 16 * lane) = z;
+    if (lane < 16) *reinterpret_cast<u32x4*>(W.p + 1024 + 16 * lane) = z;
   }
   __syncthreads();
   const int cs = L.cstart;
@@ -447,11 +475,14 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
     const int nn = ln & 15, qq = ln >> 4, m4 = ln & 3, hi4 = ln >> 2;
 
     // ---- this chunk's rows into LDS; fetch the wave's next chunk ----------
+    {
+      const int wo = 64 * hi4 + 16 * (m4 ^ swz(hi4));  // row 16 i + hi4, granule m4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(W.b + 1024 * i + 16 * ln) = pf[i];
-      *reinterpret_cast<u32x4*>(W.c + 1024 * i + 16 * ln) = pf[4 + i];
-      *reinterpret_cast<u32x4*>(W.v + 1024 * i + 16 * ln) = pf[8 + i];
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<u32x4*>(W.b + 1024 * i + wo) = pf[i];
+        *reinterpret_cast<u32x4*>(W.c + 1024 * i + wo) = pf[4 + i];
+        *reinterpret_cast<u32x4*>(W.v + 1024 * i + wo) = pf[8 + i];
+      }
     }
     const float gt = pg, gate_t = pgate;
     if (c + CW < c1) prefetch(c + CW);
@@ -476,8 +507,12 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) dH[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int trow0 = 4 * qq + (nn >> 2);  // source row of the transposing reads
-    const int tcol = 4 * (ln & 3);         // source column of the transposing reads
+    // Source row and the byte offsets of value/key columns 16 h + 4 (ln & 3)
+    // (h = 0, 1) of the transposing reads; the row's granule permutation is
+    // swz(trow0) = swz(4 qq).
+    const int trow0 = 4 * qq + (nn >> 2);
+    const int tcol0 = 16 * (((ln & 3) >> 1) ^ swz(4 * qq)) + 8 * (ln & 1);
+    const int tcol1 = 16 * ((2 + ((ln & 3) >> 1)) ^ swz(4 * qq)) + 8 * (ln & 1);
     bf16x4 bsub[4][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -486,10 +521,10 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
       const f32x4 g4 = *reinterpret_cast<const f32x4*>(&W.gam[t0 + 4 * qq]);
       bf16x4 vf[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + 2 * (16 * nt + tcol));
+      for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + (nt ? tcol1 : tcol0));
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x4 braw = lds_read_tr(W.b + (t0 + trow0) * ROWB + 2 * (16 * mt + tcol));
+        const bf16x4 braw = lds_read_tr(W.b + (t0 + trow0) * ROWB + (mt ? tcol1 : tcol0));
         const float a2r = mt ? a2n1 : a2n0;
         const float f = __builtin_amdgcn_exp2f(a2r * (gend - gsub));
         f32x4 bt, btc;
@@ -534,11 +569,11 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
     wait_ready(&L.ready, c);
     f32x4 hs[2][2];  // state at the start of the current sub-chunk
     {
-      const f32x4* src = reinterpret_cast<const f32x4*>(L.state[c & 1] + 16 * ln);
+      const f32x4* src = reinterpret_cast<const f32x4*>(L.state[c & 1]) + ln;
       hs[0][0] = src[0];
-      hs[0][1] = src[1];
-      hs[1][0] = src[2];
-      hs[1][1] = src[3];
+      hs[0][1] = src[64];
+      hs[1][0] = src[128];
+      hs[1][1] = src[192];
     }
     {
       f32x4 hn[2][2];
@@ -549,11 +584,11 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
           for (int i = 0; i < 4; ++i) hn[mt][nt][i] = __builtin_fmaf(ec[4 * mt + i], hs[mt][nt][i], dH[mt][nt][i]);
       if (c + 1 < c1) {
-        f32x4* dst = reinterpret_cast<f32x4*>(L.state[(c + 1) & 1] + 16 * ln);
+        f32x4* dst = reinterpret_cast<f32x4*>(L.state[(c + 1) & 1]) + ln;
         dst[0] = hn[0][0];
-        dst[1] = hn[0][1];
-        dst[2] = hn[1][0];
-        dst[3] = hn[1][1];
+        dst[64] = hn[0][1];
+        dst[128] = hn[1][0];
+        dst[192] = hn[1][1];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         if (ln == 0) __hip_atomic_store(&L.ready, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       } else if (write_hT) {
@@ -573,28 +608,36 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
     for (int k = 0; k < 4; ++k) {
       const int t0 = 16 * k;
       const float gref = k ? W.gam[t0 - 1] : 0.f;
-      // tables for P in fp16: e^{A_s g_t} and c; lane -> (token hi4, rows 8*m4 + j)
+      // Tables for P in fp16, lane -> (token hi4, key rows 8*m4 + j): the
+      // per-token decays e^{A_s g_t} (row t at 15 - t) and b (row t at t).
+      // The lane keeps its own token's c.  (swz(t0 + hi4) = swz(hi4).)
+      h16x2 d[4];
       {
+        const int gsw = 16 * (m4 ^ swz(hi4));
         const float gu = W.graw[t0 + hi4];
         h16x8 x;
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = (_Float16)__builtin_amdgcn_exp2f(a2g[j] * gu);
-        *reinterpret_cast<h16x8*>(&W.at[hi4 * CS + 8 * m4]) = x;
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + 16 * m4);
+        *reinterpret_cast<h16x8*>(reinterpret_cast<char*>(W.ta) + 64 * (15 - hi4) + 16 * m4) = x;
+        const u32x4 bw = *reinterpret_cast<const u32x4*>(W.b + (t0 + hi4) * ROWB + gsw);
         h16x8 y;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          y[2 * j] = (_Float16)bf_lo(cw[j]);
-          y[2 * j + 1] = (_Float16)bf_hi(cw[j]);
+          y[2 * j] = (_Float16)bf_lo(bw[j]);
+          y[2 * j + 1] = (_Float16)bf_hi(bw[j]);
         }
-        *reinterpret_cast<h16x8*>(&W.ct[hi4 * CS + 8 * m4]) = y;
+        *reinterpret_cast<h16x8*>(reinterpret_cast<char*>(W.tb) + 64 * hi4 + 16 * m4) = y;
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + gsw);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = h16x2{(_Float16)bf_lo(cw[j]), (_Float16)bf_hi(cw[j])};
       }
       // Qt = c (.) e^{x_t - x_ref}: row t0 + nn, key rows sigma(qq, j)
       bf16x8 Qt;
       {
         const float gt_n = W.gam[t0 + nn];
-        const u32x2 c0 = *reinterpret_cast<const u32x2*>(W.c + (t0 + nn) * ROWB + 8 * qq);
-        const u32x2 c1 = *reinterpret_cast<const u32x2*>(W.c + (t0 + nn) * ROWB + 32 + 8 * qq);
+        const int sq = swz(nn), h8 = 8 * (qq & 1);
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(W.c + (t0 + nn) * ROWB + 16 * ((qq >> 1) ^ sq) + h8);
+        const u32x2 c1 = *reinterpret_cast<const u32x2*>(W.c + (t0 + nn) * ROWB + 16 * ((2 + (qq >> 1)) ^ sq) + h8);
         const float cv[8] = {bf_lo(c0[0]), bf_hi(c0[0]), bf_lo(c0[1]), bf_hi(c0[1]),
                              bf_lo(c1[0]), bf_hi(c1[0]), bf_lo(c1[1]), bf_hi(c1[1])};
         f32x4 lo, hi;
@@ -608,60 +651,63 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
       // v fragments and the sub-chunk's own write, decayed to its end
       bf16x4 vf[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + 2 * (16 * nt + tcol));
+      for (int nt = 0; nt < 2; ++nt) vf[nt] = lds_read_tr(W.v + (t0 + trow0) * ROWB + (nt ? tcol1 : tcol0));
       f32x4 dk[2][2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bsub[k][mt], vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
       wave_lds_sync();  // tables written above are visible to every lane
-      // P[t][tau]; lane -> (tau = hi4, key rows 8*m4 + j).  The running
-      // product r = b_tau (.) prod_{j = tau+1..t} e^{A g_j} (zero before
-      // t = tau) and the sum over the lane's eight rows use packed fp16
-      // operands with fp32 accumulation (two rows per dot-product
-      // instruction); every lane walks the same token t, so the table
-      // reads are broadcasts at constant offsets.
+      // P[t][tau], tau <= t; lane -> (t = hi4, key rows 8*m4 + j).  The lane
+      // walks tau = t, t - 1, ..., t - 15 carrying r = c_t (.) prod_{j =
+      // tau+1..t} e^{A g_j}: step l multiplies r by the decays of token
+      // t - l + 1 and dots it with b_{t - l}, in packed fp16 with fp32
+      // accumulation (two rows per dot-product instruction), so every factor
+      // stays in [0, 1] however fast a row decays.  Steps that pass the
+      // sub-chunk's first token read the zero rows below both tables; their
+      // sums are zero and land in P's unused left columns.  Every lane thus
+      // runs the same 16 steps, at constant offsets from its own row.
       {
-        const int tau = hi4;
-        const u32x4 bw = *reinterpret_cast<const u32x4*>(W.b + (t0 + tau) * ROWB + 16 * m4);
-        h16x2 bb2[4], r[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bb2[j] = h16x2{(_Float16)bf_lo(bw[j]), (_Float16)bf_hi(bw[j])};
-          r[j] = h16x2{(_Float16)0.f, (_Float16)0.f};
-        }
-        const _Float16* arow = &W.at[8 * m4];
-        const _Float16* crow = &W.ct[8 * m4];
+        const char* arow = reinterpret_cast<const char*>(W.tz) - 128 - 64 * hi4 + 16 * m4;  // + 64 l
+        const char* brow = reinterpret_cast<const char*>(W.tb) - 960 + 64 * hi4 + 16 * m4;  // + 64 (15 - l)
         float pt[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const h16x8 a = *reinterpret_cast<const h16x8*>(arow + t * CS);
-          const bool start = t == tau;
+        for (int l = 0; l < 16; ++l) {
+          if (l > 0) {
+            const h16x8 a = *reinterpret_cast<const h16x8*>(arow + 64 * l);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) r[j] = start ? bb2[j] : r[j] * h16x2{a[2 * j], a[2 * j + 1]};
-          const h16x8 cc = *reinterpret_cast<const h16x8*>(crow + t * CS);
+            for (int j = 0; j < 4; ++j) d[j] = d[j] * h16x2{a[2 * j], a[2 * j + 1]};
+          }
+          const h16x8 bq = *reinterpret_cast<const h16x8*>(brow + 64 * (15 - l));
           float acc = 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{cc[2 * j], cc[2 * j + 1]}, r[j], acc, false);
-          pt[t] = acc;
+          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{bq[2 * j], bq[2 * j + 1]}, d[j], acc, false);
+          pt[l] = acc;
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          pt[t] += dpp_xor1(pt[t]);
-          pt[t] += dpp_xor2(pt[t]);
+        for (int l = 0; l < 16; ++l) {
+          pt[l] += dpp_xor1(pt[l]);
+          pt[l] += dpp_xor2(pt[l]);
         }
         // the four lanes of a quad hold the same sums; one of them stores
+        // P[t][t - l] (bf16, the MFMA operand's precision)
         if (m4 == 0) {
+          char* prow = W.p + (PROW + 2) * hi4 + 2;  // + 2 (15 - l): column t - l of row t
 #pragma unroll
-          for (int t = 0; t < 16; ++t) W.p[t * 16 + tau] = pt[t];
+          for (int l = 0; l < 16; l += 2) {
+            *reinterpret_cast<__bf16*>(prow + 2 * (15 - l)) = (__bf16)pt[l];
+            *reinterpret_cast<__bf16*>(prow + 2 * (14 - l)) = (__bf16)pt[l + 1];
+          }
         }
       }
       wave_lds_sync();
-      // O = Qt H_start + P V, then the epilogue and 16-byte stores
+      // O = Qt H_start + P V, then the epilogue; the output tile is staged
+      // in bf16 rows of 32 values whose 16-byte granule g of row t sits at
+      // g ^ (2 ((t >> 2) & 1)), for 16-byte stores
       {
-        const f32x4 pr = *reinterpret_cast<const f32x4*>(&W.p[nn * 16 + 4 * qq]);
-        const bf16x4 pa = pack4(pr);
+        const bf16x4 pa = *reinterpret_cast<const bf16x4*>(W.p + PROW * nn + 32 + 8 * qq);
         const f32x4 gt4 = *reinterpret_cast<const f32x4*>(&W.gate[t0 + 4 * qq]);
+        __bf16* const stg = reinterpret_cast<__bf16*>(W.ta);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           // Two accumulators, added on the VALU: a 16-deep MFMA that takes a
@@ -669,11 +715,12 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
           // later can read the register before that result lands.
           const f32x4 qh = mma32(Qt, pack8(hs[0][nt], hs[1][nt]), f32x4{0.f, 0.f, 0.f, 0.f});
           const f32x4 pv = mma16(pa, vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+          const int col = 8 * ((2 * nt + (nn >> 3)) ^ (2 * (qq & 1))) + (nn & 7);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float y = qh[i] + pv[i];
             if (p.dskip) y = __builtin_fmaf(dh, (float)vf[nt][i], y);
-            reinterpret_cast<__bf16*>(W.at)[(4 * qq + i) * CD + 16 * nt + nn] = (__bf16)(y * gt4[i]);
+            stg[(4 * qq + i) * CD + col] = (__bf16)(y * gt4[i]);
           }
         }
       }
@@ -691,7 +738,8 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
       }
       wave_lds_sync();
       {
-        const u32x4 ow = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(W.at) + 16 * ln);
+        const u32x4 ow = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(W.ta) + 64 * hi4 +
+                                                          16 * (m4 ^ (2 * ((hi4 >> 2) & 1))));
         const int orow = c * CC + t0 + hi4;
         __builtin_amdgcn_raw_buffer_store_b128(ow, ro, (int)((long)orow * tok_stride) + 16 * m4, 0, 0);
       }
