@@ -249,17 +249,20 @@ struct ChunkParams {
 //
 // The decay-product tables of a sub-chunk are one contiguous block: the
 // per-token decays e^{A_s g_t} (fp16, row t at 15 - t, i.e. stored last
-// row first), 15 zero rows, then the b rows in fp16 (row t at t).  Rows
-// -1 ... -15 of either table fall into the zero rows, which is what lets
-// every lane walk the same number of steps (see phase B).
+// row first), 7 zero rows, the b rows 0..7 in fp16, 7 zero rows, the b rows
+// 8..15.  Rows -1 ... -6 of the decay table fall into the first zero rows,
+// and so do rows -1 ... -7 of each half of b, which is what lets every
+// lane walk the same number of steps (see phase B).
 constexpr int PROW = 80;  // bytes per row of P (bf16, column tau at 16 + tau)
 struct WaveLds {
   alignas(16) char b[CC * ROWB];     // chunk rows of b (bf16, token-major, granules permuted)
   alignas(16) char c[CC * ROWB];
   alignas(16) char v[CC * ROWB];
-  alignas(16) _Float16 ta[16 * CS];  // e^{A_s g_t}, last row first; output staging after P
-  alignas(16) _Float16 tz[15 * CS];  // zeros
-  alignas(16) _Float16 tb[16 * CS];  // b rows of the sub-chunk (fp16)
+  alignas(16) _Float16 ta[16 * CS];   // e^{A_s g_t}, last row first; output staging after P
+  alignas(16) _Float16 tz[7 * CS];    // zeros
+  alignas(16) _Float16 tb0[8 * CS];   // b rows 0..7 of the sub-chunk (fp16)
+  alignas(16) _Float16 tz1[7 * CS];   // zeros
+  alignas(16) _Float16 tb1[8 * CS];   // b rows 8..15
   alignas(16) char p[16 * PROW];     // P of the sub-chunk (bf16), row t, column tau at 16 + tau
   alignas(16) float ex[5 * CS];      // per-row decays: sub-chunk k at [32 k + s], chunk at [128 + s]
   alignas(16) float gam[CC];         // chunk-relative inclusive cumsum of g
@@ -267,7 +270,9 @@ struct WaveLds {
   alignas(16) float gate[CC];
 };
 static_assert(offsetof(WaveLds, tz) == offsetof(WaveLds, ta) + 16 * CS * 2, "tables are contiguous");
-static_assert(offsetof(WaveLds, tb) == offsetof(WaveLds, tz) + 15 * CS * 2, "tables are contiguous");
+static_assert(offsetof(WaveLds, tb0) == offsetof(WaveLds, tz) + 7 * CS * 2, "tables are contiguous");
+static_assert(offsetof(WaveLds, tz1) == offsetof(WaveLds, tb0) + 8 * CS * 2, "tables are contiguous");
+static_assert(offsetof(WaveLds, tb1) == offsetof(WaveLds, tz1) + 7 * CS * 2, "tables are contiguous");
 
 // Granule permutation of the chunk rows (see WaveLds).
 __device__ static inline int swz(int row) { return ((row >> 2) & 1) << 1 | ((row >> 3) & 1); }
@@ -281,9 +286,6 @@ struct ChunkLds {
   int cstart;                           // first chunk this workgroup runs
 };
 
-__device__ static inline f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 __device__ static inline f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
                                                    0, 0);
@@ -296,6 +298,14 @@ __device__ static inline bf16x4 lds_read_tr(const char* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)(p));
   return __builtin_bit_cast(bf16x4, r);
+}
+
+// a.x b.x + a.y b.y in fp32 (packed fp16 operands): the three-operand
+// form with an inline zero, which needs no zeroed accumulator register.
+__device__ static inline float dot2_first(h16x2 a, h16x2 b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 __device__ static inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -320,12 +330,29 @@ __device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-__device__ static inline bf16x8 pack8(f32x4 lo, f32x4 hi) {
-  return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
-                (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+// Pairs are converted as two-element vectors: that gives one packed
+// conversion per pair, where a four-element vector (or one built element by
+// element) is converted a value at a time and merged with permutes.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ static inline uint32_t cvt_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 __device__ static inline bf16x4 pack4(f32x4 x) {
-  return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  return __builtin_bit_cast(bf16x4, u32x2{cvt_pair(x[0], x[1]), cvt_pair(x[2], x[3])});
+}
+
+// Issue priority of the calling wave from the number r of chunks it still
+// has after the current one (r is the same in every lane).  Two workgroups
+// share each CU; with equal priorities the older wave of a SIMD wins every
+// issue conflict, so the younger workgroup would lag and finish its last
+// chunks alone.  A wave that falls behind the other wave of its SIMD by a
+// chunk outranks it until it catches up.
+__device__ static inline void set_prio_remaining(int r) {
+  if (r >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (r == 2) __builtin_amdgcn_s_setprio(2);
+  else if (r == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // Wait until the LDS counter holds at least v (bounded: a wait that runs
@@ -419,7 +446,10 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
   // the zero rows of the decay tables and the never-written part of P
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if (lane < 60) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tz) + 16 * lane) = z;
+    if (lane < 28) {
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tz) + 16 * lane) = z;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tz1) + 16 * lane) = z;
+    }
     *reinterpret_cast<u32x4*>(W.p + 16 * lane) = z;
     if (lane < 16) *reinterpret_cast<u32x4*>(W.p + 1024 + 16 * lane) = z;
   }
@@ -428,12 +458,14 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
   if (cs + wave >= c1) return;
 
   // Decay rates in the lane's layouts: rows sigma(q, j) (= accumulator rows
-  // 16*mt + 4q + i), rows n and n + 16, and the group 8*(lane & 3) + j.
-  float a2s[8], a2g[8];
+  // 16*mt + 4q + i), rows n and n + 16, and the groups 8*(lane & 3) + j and
+  // 8*q + j.
+  float a2s[8], a2g[8], a2q[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     a2s[j] = L.a2[(j < 4 ? 0 : 16) + 4 * q + (j & 3)];
     a2g[j] = L.a2[8 * (lane & 3) + j];
+    a2q[j] = L.a2[8 * q + j];
   }
   const float a2n0 = L.a2[n], a2n1 = L.a2[n + 16];
   const float dh = p.dskip ? p.dskip[hh] : 0.f;
@@ -470,6 +502,7 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
   for (int c = cs + wave; c < c1; c += CW) {
     // Lane-dependent offsets are re-derived in each iteration instead of
     // being held in registers across the whole loop.
+    set_prio_remaining((c1 - 1 - c) / CW);
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int nn = ln & 15, qq = ln >> 4, m4 = ln & 3, hi4 = ln >> 2;
@@ -609,7 +642,8 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
       const int t0 = 16 * k;
       const float gref = k ? W.gam[t0 - 1] : 0.f;
       // Tables for P in fp16, lane -> (token hi4, key rows 8*m4 + j): the
-      // per-token decays e^{A_s g_t} (row t at 15 - t) and b (row t at t).
+      // per-token decays e^{A_s g_t} (row t at 15 - t) and b (row t in the
+      // half of its token).
       // The lane keeps its own token's c.  (swz(t0 + hi4) = swz(hi4).)
       h16x2 d[4];
       {
@@ -626,13 +660,14 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
           y[2 * j] = (_Float16)bf_lo(bw[j]);
           y[2 * j + 1] = (_Float16)bf_hi(bw[j]);
         }
-        *reinterpret_cast<h16x8*>(reinterpret_cast<char*>(W.tb) + 64 * hi4 + 16 * m4) = y;
+        *reinterpret_cast<h16x8*>(reinterpret_cast<char*>(W.tb0) + 64 * hi4 + 448 * (hi4 >> 3) + 16 * m4) = y;
         const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + gsw);
 #pragma unroll
         for (int j = 0; j < 4; ++j) d[j] = h16x2{(_Float16)bf_lo(cw[j]), (_Float16)bf_hi(cw[j])};
       }
-      // Qt = c (.) e^{x_t - x_ref}: row t0 + nn, key rows sigma(qq, j)
-      bf16x8 Qt;
+      // Qt = c (.) e^{x_t - x_ref}: row t0 + nn, key rows 4 qq + j (Qlo) and
+      // 16 + 4 qq + j (Qhi)
+      bf16x4 Qlo, Qhi;
       {
         const float gt_n = W.gam[t0 + nn];
         const int sq = swz(nn), h8 = 8 * (qq & 1);
@@ -646,7 +681,8 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
           lo[j] = cv[j] * __builtin_amdgcn_exp2f(a2s[j] * (gt_n - gref));
           hi[j] = cv[j + 4] * __builtin_amdgcn_exp2f(a2s[j + 4] * (gt_n - gref));
         }
-        Qt = pack8(lo, hi);
+        Qlo = pack4(lo);
+        Qhi = pack4(hi);
       }
       // v fragments and the sub-chunk's own write, decayed to its end
       bf16x4 vf[2];
@@ -658,47 +694,75 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bsub[k][mt], vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
       wave_lds_sync();  // tables written above are visible to every lane
-      // P[t][tau], tau <= t; lane -> (t = hi4, key rows 8*m4 + j).  The lane
-      // walks tau = t, t - 1, ..., t - 15 carrying r = c_t (.) prod_{j =
+      // P[t][tau] for t and tau in the same half of the sub-chunk (tokens
+      // 0..7 or 8..15), tau <= t; lane -> (t = hi4, key rows 8*m4 + j).  The
+      // lane walks tau = t, t - 1, ..., t - 7 carrying r = c_t (.) prod_{j =
       // tau+1..t} e^{A g_j}: step l multiplies r by the decays of token
       // t - l + 1 and dots it with b_{t - l}, in packed fp16 with fp32
       // accumulation (two rows per dot-product instruction), so every factor
       // stays in [0, 1] however fast a row decays.  Steps that pass the
-      // sub-chunk's first token read the zero rows below both tables; their
-      // sums are zero and land in P's unused left columns.  Every lane thus
-      // runs the same 16 steps, at constant offsets from its own row.
+      // half's first token read zero rows of b (and decays of earlier tokens
+      // or zero rows, all in [0, 1]); their sums are zero and land in P's
+      // columns left of the half.  Every lane thus runs the same 8 steps,
+      // at constant offsets from its own row.
       {
         const char* arow = reinterpret_cast<const char*>(W.tz) - 128 - 64 * hi4 + 16 * m4;  // + 64 l
-        const char* brow = reinterpret_cast<const char*>(W.tb) - 960 + 64 * hi4 + 16 * m4;  // + 64 (15 - l)
-        float pt[16];
+        const char* brow = reinterpret_cast<const char*>(W.tb0) - 448 + 64 * hi4 + 448 * (hi4 >> 3) +
+                           16 * m4;  // + 64 (7 - l)
+        float pt[8];
 #pragma unroll
-        for (int l = 0; l < 16; ++l) {
+        for (int l = 0; l < 8; ++l) {
           if (l > 0) {
             const h16x8 a = *reinterpret_cast<const h16x8*>(arow + 64 * l);
 #pragma unroll
             for (int j = 0; j < 4; ++j) d[j] = d[j] * h16x2{a[2 * j], a[2 * j + 1]};
           }
-          const h16x8 bq = *reinterpret_cast<const h16x8*>(brow + 64 * (15 - l));
-          float acc = 0.f;
+          const h16x8 bq = *reinterpret_cast<const h16x8*>(brow + 64 * (7 - l));
+          float acc = dot2_first(h16x2{bq[0], bq[1]}, d[0]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{bq[2 * j], bq[2 * j + 1]}, d[j], acc, false);
+          for (int j = 1; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{bq[2 * j], bq[2 * j + 1]}, d[j], acc, false);
           pt[l] = acc;
         }
 #pragma unroll
-        for (int l = 0; l < 16; ++l) {
+        for (int l = 0; l < 8; ++l) {
           pt[l] += dpp_xor1(pt[l]);
           pt[l] += dpp_xor2(pt[l]);
         }
         // the four lanes of a quad hold the same sums; one of them stores
         // P[t][t - l] (bf16, the MFMA operand's precision)
         if (m4 == 0) {
-          char* prow = W.p + (PROW + 2) * hi4 + 2;  // + 2 (15 - l): column t - l of row t
+          char* prow = W.p + (PROW + 2) * hi4 + 18;  // + 2 (7 - l): column t - l of row t
 #pragma unroll
-          for (int l = 0; l < 16; l += 2) {
-            *reinterpret_cast<__bf16*>(prow + 2 * (15 - l)) = (__bf16)pt[l];
-            *reinterpret_cast<__bf16*>(prow + 2 * (14 - l)) = (__bf16)pt[l + 1];
+          for (int l = 0; l < 8; l += 2) {
+            const uint32_t w = cvt_pair(pt[l + 1], pt[l]);  // columns t - l - 1, t - l
+            *reinterpret_cast<uint16_t*>(prow + 2 * (6 - l)) = (uint16_t)w;
+            *reinterpret_cast<uint16_t*>(prow + 2 * (7 - l)) = (uint16_t)(w >> 16);
           }
         }
+      }
+      // The block t >= 8 > tau on the matrix unit.  With the sub-chunk's
+      // token 7 as the reference, P[t][tau] = sum_s X[t][s] X[tau][s] for
+      // X[x] = c_x (.) e^{x_x - x_7} (x >= 8) and b_x (.) e^{x_7 - x_x}
+      // (x < 8): both factors lie in [0, 1], so the split is exact.  The
+      // product X X^T (16x16x32, fp16 operands) leaves P[t][4 qq + i] in lane
+      // (t = nn, qq), the layout of P V's row operand; entries with t < 8 or
+      // tau >= 8 pair tokens on one side of the reference and are dropped.
+      bf16x4 poff;
+      {
+        const float dg = fabsf(W.gam[t0 + nn] - W.gam[t0 + 7]);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>((nn < 8 ? W.b : W.c) + (t0 + nn) * ROWB +
+                                                          16 * (qq ^ swz(nn)));
+        h16x8 xv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xv[2 * j] = (_Float16)(bf_lo(raw[j]) * __builtin_amdgcn_exp2f(a2q[2 * j] * dg));
+          xv[2 * j + 1] = (_Float16)(bf_hi(raw[j]) * __builtin_amdgcn_exp2f(a2q[2 * j + 1] * dg));
+        }
+        f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, xv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const bool keep = nn >= 8 && qq < 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = keep ? x[i] : 0.f;
+        poff = pack4(x);
       }
       wave_lds_sync();
       // O = Qt H_start + P V, then the epilogue; the output tile is staged
@@ -710,17 +774,28 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
         __bf16* const stg = reinterpret_cast<__bf16*>(W.ta);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          // Two accumulators, added on the VALU: a 16-deep MFMA that takes a
-          // 32-deep MFMA's result as its accumulator a few instructions
-          // later can read the register before that result lands.
-          const f32x4 qh = mma32(Qt, pack8(hs[0][nt], hs[1][nt]), f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 pv = mma16(pa, vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+          // One accumulator through four 16-deep products (key rows
+          // 4 qq + j, then 16 + 4 qq + j, then P V for the two parts of P).  Products of one depth
+          // only: a 16-deep MFMA that takes a 32-deep MFMA's result as its
+          // accumulator a few instructions later can read the register
+          // before that result lands.
+          f32x4 acc = mma16(Qlo, pack4(hs[0][nt]), f32x4{0.f, 0.f, 0.f, 0.f});
+          acc = mma16(Qhi, pack4(hs[1][nt]), acc);
+          acc = mma16(pa, vf[nt], acc);
+          acc = mma16(poff, vf[nt], acc);
           const int col = 8 * ((2 * nt + (nn >> 3)) ^ (2 * (qq & 1))) + (nn & 7);
+          float y[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float y = qh[i] + pv[i];
-            if (p.dskip) y = __builtin_fmaf(dh, (float)vf[nt][i], y);
-            stg[(4 * qq + i) * CD + col] = (__bf16)(y * gt4[i]);
+            y[i] = acc[i];
+            if (p.dskip) y[i] = __builtin_fmaf(dh, (float)vf[nt][i], y[i]);
+            y[i] *= gt4[i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const uint32_t w = cvt_pair(y[i], y[i + 1]);  // rows 4 qq + i, 4 qq + i + 1
+            reinterpret_cast<uint16_t*>(stg)[(4 * qq + i) * CD + col] = (uint16_t)w;
+            reinterpret_cast<uint16_t*>(stg)[(4 * qq + i + 1) * CD + col] = (uint16_t)(w >> 16);
           }
         }
       }
