@@ -249,30 +249,27 @@ struct ChunkParams {
 //
 // The decay-product tables of a sub-chunk are one contiguous block: the
 // per-token decays e^{A_s g_t} (fp16, row t at 15 - t, i.e. stored last
-// row first), 7 zero rows, the b rows 0..7 in fp16, 7 zero rows, the b rows
-// 8..15.  Rows -1 ... -6 of the decay table fall into the first zero rows,
-// and so do rows -1 ... -7 of each half of b, which is what lets every
-// lane walk the same number of steps (see phase B).
+// row first), then for each quarter of the sub-chunk (tokens 4 u .. 4 u + 3)
+// 3 zero rows and its 4 b rows in fp16.  Rows -1 and -2 of the decay table
+// fall into the first zero rows, and rows -1 ... -3 of each quarter of b
+// into the zero rows before it, which is what lets every lane walk the same
+// number of steps (see phase B).
 constexpr int PROW = 80;  // bytes per row of P (bf16, column tau at 16 + tau)
 struct WaveLds {
   alignas(16) char b[CC * ROWB];     // chunk rows of b (bf16, token-major, granules permuted)
   alignas(16) char c[CC * ROWB];
   alignas(16) char v[CC * ROWB];
   alignas(16) _Float16 ta[16 * CS];   // e^{A_s g_t}, last row first; output staging after P
-  alignas(16) _Float16 tz[7 * CS];    // zeros
-  alignas(16) _Float16 tb0[8 * CS];   // b rows 0..7 of the sub-chunk (fp16)
-  alignas(16) _Float16 tz1[7 * CS];   // zeros
-  alignas(16) _Float16 tb1[8 * CS];   // b rows 8..15
+  alignas(16) _Float16 tb[28 * CS];   // per quarter: 3 zero rows, then its b rows (fp16)
   alignas(16) char p[16 * PROW];     // P of the sub-chunk (bf16), row t, column tau at 16 + tau
   alignas(16) float ex[5 * CS];      // per-row decays: sub-chunk k at [32 k + s], chunk at [128 + s]
   alignas(16) float gam[CC];         // chunk-relative inclusive cumsum of g
   alignas(16) float graw[CC];
   alignas(16) float gate[CC];
 };
-static_assert(offsetof(WaveLds, tz) == offsetof(WaveLds, ta) + 16 * CS * 2, "tables are contiguous");
-static_assert(offsetof(WaveLds, tb0) == offsetof(WaveLds, tz) + 7 * CS * 2, "tables are contiguous");
-static_assert(offsetof(WaveLds, tz1) == offsetof(WaveLds, tb0) + 8 * CS * 2, "tables are contiguous");
-static_assert(offsetof(WaveLds, tb1) == offsetof(WaveLds, tz1) + 7 * CS * 2, "tables are contiguous");
+static_assert(offsetof(WaveLds, tb) == offsetof(WaveLds, ta) + 16 * CS * 2, "tables are contiguous");
+// byte offset in tb of b row t of the sub-chunk
+__device__ static inline int tb_row(int t) { return 64 * (3 + t + 3 * (t >> 2)); }
 
 // Granule permutation of the chunk rows (see WaveLds).
 __device__ static inline int swz(int row) { return ((row >> 2) & 1) << 1 | ((row >> 3) & 1); }
@@ -446,10 +443,8 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
   // the zero rows of the decay tables and the never-written part of P
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if (lane < 28) {
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tz) + 16 * lane) = z;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tz1) + 16 * lane) = z;
-    }
+    // zero rows of tb: rows 7 u .. 7 u + 2, 12 granules per quarter u
+    if (lane < 48) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(W.tb) + 448 * (lane / 12) + 16 * (lane % 12)) = z;
     *reinterpret_cast<u32x4*>(W.p + 16 * lane) = z;
     if (lane < 16) *reinterpret_cast<u32x4*>(W.p + 1024 + 16 * lane) = z;
   }
@@ -643,7 +638,7 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
       const float gref = k ? W.gam[t0 - 1] : 0.f;
       // Tables for P in fp16, lane -> (token hi4, key rows 8*m4 + j): the
       // per-token decays e^{A_s g_t} (row t at 15 - t) and b (row t in the
-      // half of its token).
+      // quarter of its token).
       // The lane keeps its own token's c.  (swz(t0 + hi4) = swz(hi4).)
       h16x2 d[4];
       {
@@ -660,7 +655,7 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
           y[2 * j] = (_Float16)bf_lo(bw[j]);
           y[2 * j + 1] = (_Float16)bf_hi(bw[j]);
         }
-        *reinterpret_cast<h16x8*>(reinterpret_cast<char*>(W.tb0) + 64 * hi4 + 448 * (hi4 >> 3) + 16 * m4) = y;
+        *reinterpret_cast<h16x8*>(reinterpret_cast<char*>(W.tb) + tb_row(hi4) + 16 * m4) = y;
         const u32x4 cw = *reinterpret_cast<const u32x4*>(W.c + (t0 + hi4) * ROWB + gsw);
 #pragma unroll
         for (int j = 0; j < 4; ++j) d[j] = h16x2{(_Float16)bf_lo(cw[j]), (_Float16)bf_hi(cw[j])};
@@ -694,75 +689,84 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) dk[mt][nt] = mma16(bsub[k][mt], vf[nt], f32x4{0.f, 0.f, 0.f, 0.f});
       wave_lds_sync();  // tables written above are visible to every lane
-      // P[t][tau] for t and tau in the same half of the sub-chunk (tokens
-      // 0..7 or 8..15), tau <= t; lane -> (t = hi4, key rows 8*m4 + j).  The
-      // lane walks tau = t, t - 1, ..., t - 7 carrying r = c_t (.) prod_{j =
+      // P[t][tau] for t and tau in the same quarter of the sub-chunk (tokens
+      // 4 u .. 4 u + 3), tau <= t; lane -> (t = hi4, key rows 8*m4 + j).  The
+      // lane walks tau = t, t - 1, t - 2, t - 3 carrying r = c_t (.) prod_{j =
       // tau+1..t} e^{A g_j}: step l multiplies r by the decays of token
       // t - l + 1 and dots it with b_{t - l}, in packed fp16 with fp32
       // accumulation (two rows per dot-product instruction), so every factor
       // stays in [0, 1] however fast a row decays.  Steps that pass the
-      // half's first token read zero rows of b (and decays of earlier tokens
-      // or zero rows, all in [0, 1]); their sums are zero and land in P's
-      // columns left of the half.  Every lane thus runs the same 8 steps,
-      // at constant offsets from its own row.
+      // quarter's first token read zero rows of b (and decays of earlier
+      // tokens or zero rows, all in [0, 1]); their sums are zero and land in
+      // P's columns left of the quarter.  Every lane thus runs the same 4
+      // steps, at constant offsets from its own row.
       {
-        const char* arow = reinterpret_cast<const char*>(W.tz) - 128 - 64 * hi4 + 16 * m4;  // + 64 l
-        const char* brow = reinterpret_cast<const char*>(W.tb0) - 448 + 64 * hi4 + 448 * (hi4 >> 3) +
-                           16 * m4;  // + 64 (7 - l)
-        float pt[8];
+        const char* arow = reinterpret_cast<const char*>(W.tb) - 128 - 64 * hi4 + 16 * m4;  // + 64 l
+        const char* brow = reinterpret_cast<const char*>(W.tb) + tb_row(hi4) - 192 + 16 * m4;  // + 64 (3 - l)
+        float pt[4];
 #pragma unroll
-        for (int l = 0; l < 8; ++l) {
+        for (int l = 0; l < 4; ++l) {
           if (l > 0) {
             const h16x8 a = *reinterpret_cast<const h16x8*>(arow + 64 * l);
 #pragma unroll
             for (int j = 0; j < 4; ++j) d[j] = d[j] * h16x2{a[2 * j], a[2 * j + 1]};
           }
-          const h16x8 bq = *reinterpret_cast<const h16x8*>(brow + 64 * (7 - l));
+          const h16x8 bq = *reinterpret_cast<const h16x8*>(brow + 64 * (3 - l));
           float acc = dot2_first(h16x2{bq[0], bq[1]}, d[0]);
 #pragma unroll
           for (int j = 1; j < 4; ++j) acc = __builtin_amdgcn_fdot2(h16x2{bq[2 * j], bq[2 * j + 1]}, d[j], acc, false);
           pt[l] = acc;
         }
 #pragma unroll
-        for (int l = 0; l < 8; ++l) {
+        for (int l = 0; l < 4; ++l) {
           pt[l] += dpp_xor1(pt[l]);
           pt[l] += dpp_xor2(pt[l]);
         }
         // the four lanes of a quad hold the same sums; one of them stores
         // P[t][t - l] (bf16, the MFMA operand's precision)
         if (m4 == 0) {
-          char* prow = W.p + (PROW + 2) * hi4 + 18;  // + 2 (7 - l): column t - l of row t
+          char* prow = W.p + (PROW + 2) * hi4 + 26;  // + 2 (3 - l): column t - l of row t
 #pragma unroll
-          for (int l = 0; l < 8; l += 2) {
+          for (int l = 0; l < 4; l += 2) {
             const uint32_t w = cvt_pair(pt[l + 1], pt[l]);  // columns t - l - 1, t - l
-            *reinterpret_cast<uint16_t*>(prow + 2 * (6 - l)) = (uint16_t)w;
-            *reinterpret_cast<uint16_t*>(prow + 2 * (7 - l)) = (uint16_t)(w >> 16);
+            *reinterpret_cast<uint16_t*>(prow + 2 * (2 - l)) = (uint16_t)w;
+            *reinterpret_cast<uint16_t*>(prow + 2 * (3 - l)) = (uint16_t)(w >> 16);
           }
         }
       }
-      // The block t >= 8 > tau on the matrix unit.  With the sub-chunk's
-      // token 7 as the reference, P[t][tau] = sum_s X[t][s] X[tau][s] for
-      // X[x] = c_x (.) e^{x_x - x_7} (x >= 8) and b_x (.) e^{x_7 - x_x}
-      // (x < 8): both factors lie in [0, 1], so the split is exact.  The
-      // product X X^T (16x16x32, fp16 operands) leaves P[t][4 qq + i] in lane
-      // (t = nn, qq), the layout of P V's row operand; entries with t < 8 or
-      // tau >= 8 pair tokens on one side of the reference and are dropped.
+      // The rest of P on the matrix unit, split at reference tokens so that
+      // every factor lies in [0, 1] and the split is exact:
+      //   t in 8..15, tau in 0..7 (reference 7), and within each half
+      //   t in 4 u' + 4 .. 4 u' + 7, tau in 4 u' .. 4 u' + 3 (reference 4 u' + 3),
+      // P[t][tau] = sum_s X[t][s] X[tau][s] with X[x] = c_x (.) e^{x_x - x_r}
+      // on the later side of the reference r and b_x (.) e^{x_r - x_x} on
+      // the earlier side.  Each product X X^T (16x16x32, fp16 operands) leaves
+      // P[t][4 qq + i] in lane (t = nn, qq), the layout of P V's row operand;
+      // its entries that do not pair the two sides of one reference are
+      // dropped.
       bf16x4 poff;
       {
-        const float dg = fabsf(W.gam[t0 + nn] - W.gam[t0 + 7]);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>((nn < 8 ? W.b : W.c) + (t0 + nn) * ROWB +
-                                                          16 * (qq ^ swz(nn)));
-        h16x8 xv;
+        f32x4 x8, x4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xv[2 * j] = (_Float16)(bf_lo(raw[j]) * __builtin_amdgcn_exp2f(a2q[2 * j] * dg));
-          xv[2 * j + 1] = (_Float16)(bf_hi(raw[j]) * __builtin_amdgcn_exp2f(a2q[2 * j + 1] * dg));
+        for (int lev = 0; lev < 2; ++lev) {
+          const int r = lev ? 4 * (nn >> 2 & ~1) + 3 : 7;  // the lane token's reference
+          const bool late = lev ? (nn >> 2) & 1 : nn >= 8;
+          const float dg = fabsf(W.gam[t0 + nn] - W.gam[t0 + r]);
+          const u32x4 raw = *reinterpret_cast<const u32x4*>((late ? W.c : W.b) + (t0 + nn) * ROWB +
+                                                            16 * (qq ^ swz(nn)));
+          h16x8 xv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xv[2 * j] = (_Float16)(bf_lo(raw[j]) * __builtin_amdgcn_exp2f(a2q[2 * j] * dg));
+            xv[2 * j + 1] = (_Float16)(bf_hi(raw[j]) * __builtin_amdgcn_exp2f(a2q[2 * j + 1] * dg));
+          }
+          (lev ? x4 : x8) = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, xv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
-        f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, xv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const bool keep = nn >= 8 && qq < 2;
+        const bool keep8 = nn >= 8 && qq < 2;
+        const bool keep4 = ((nn >> 2) & 1) && qq == 2 * (nn >> 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = keep ? x[i] : 0.f;
-        poff = pack4(x);
+        for (int i = 0; i < 4; ++i) x8[i] = keep8 ? x8[i] : (keep4 ? x4[i] : 0.f);
+        poff = pack4(x8);
       }
       wave_lds_sync();
       // O = Qt H_start + P V, then the epilogue; the output tile is staged
@@ -787,9 +791,8 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
           float y[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            y[i] = acc[i];
-            if (p.dskip) y[i] = __builtin_fmaf(dh, (float)vf[nt][i], y[i]);
-            y[i] *= gt4[i];
+            // dh = 0 without the skip term: one form, no lane selects
+            y[i] = __builtin_fmaf(dh, (float)vf[nt][i], acc[i]) * gt4[i];
           }
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {

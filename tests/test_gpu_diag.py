@@ -274,6 +274,19 @@ def test_chunked_segments(decay):
     check(inp, "chunked")
 
 
+# Six chains of 21 chunks, the last one partial, each with its own initial
+# state: 5 segments of 5 chunks per sequence, the last one ragged.
+@pytest.mark.parametrize("decay", ["default", "slow", "none"])
+def test_chunked_segments_ragged_with_state(decay):
+    inp = sd.generate(sd.custom(f"chunk_win_{decay}", seed=28, B=2, T=1307, H=3, dtype="bf16",
+                                h0_std=0.3))
+    if decay == "slow":
+        inp = dataclasses.replace(inp, A_log=np.full_like(inp.A_log, -4.0))
+    elif decay == "none":
+        inp = dataclasses.replace(inp, g=np.zeros_like(inp.g))
+    check(inp, "chunked")
+
+
 def test_chunked_segments_hymo_heads_alias_fallback():
     """hT aliasing h0 turns segments off; the result still matches."""
     import torch
