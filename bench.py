@@ -48,9 +48,13 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "gated-delta-rule fwd tokens/s + achieved HBM GB/s (% roofline), 1 MI355X"
 CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_delta_amd", "csrc")
-# the sources of the kernel that runs the wide_head workload
-KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gdn_fwd_full.hip", "gdn_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wide_head.json")
+# the sources of the kernel each workload's traffic counters were taken on
+KERNEL_SRCS = {
+    "wide_head": [os.path.join(CSRC, f) for f in ("gdn_fwd_full.hip", "gdn_device.h", "gdn_full_common.h",
+                                                  "gdn_launch.h")],
+    "hymo": [os.path.join(CSRC, "gdn_diag.hip")],
+}
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
 METRIC_BWD = "gated-delta-rule bwd tokens/s + achieved fp32 TFLOP/s (% roofline), 1 MI355X"
 FP32_PEAK_TFLOPS = 157.3
@@ -89,14 +93,14 @@ def algorithmic_bytes(wl: synth.Workload, has_h0: bool) -> int:
     return wl.tokens * wl.H * per_token_head + state * (2 if has_h0 else 1)
 
 
-def kernel_source_hash() -> str:
-    """sha256[:16] of the kernel sources' code: comments and whitespace are
-    dropped first, so that editing a comment does not disown counter runs
-    taken on the same code."""
+def kernel_source_hash(workload: str = "wide_head") -> str:
+    """sha256[:16] of the code of the kernel sources behind ``workload``:
+    comments and whitespace are dropped first, so that editing a comment does
+    not disown counter runs taken on the same code."""
     import re
 
     text = ""
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[workload]:
         with open(path) as f:
             text += f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -105,17 +109,35 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs
+    (profiles/traffic_<workload>.json), if they were taken on the current
+    kernel source; else None."""
+    if workload not in KERNEL_SRCS:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("kernel_sha256_16") != kernel_source_hash():
+    if d.get("kernel_sha256_16") != kernel_source_hash(workload):
         return None
     return d.get("bytes_per_launch")
+
+
+def copy_calibration():
+    """Three plain device-to-device copies of COPY_BYTES each, before the
+    warm-up: under rocprofv3 --pmc their FETCH_SIZE / WRITE_SIZE readings
+    give the bytes per counted KiB."""
+    import torch
+
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def copy_reference(nbytes: int, stream) -> float:
@@ -274,6 +296,8 @@ def diag_main(args):
             raise SystemExit(f"diagonal-decay {form} entry point failed with status {rc}")
 
     alg = diag_algorithmic_bytes(wl, inp.h0 is not None, inp.gate is not None)
+    if args.copy_calibration:
+        copy_calibration()
     copy_gbs = copy_reference(alg, stream)
     torch.cuda.synchronize()
     for i in range(args.warmup):
@@ -313,7 +337,8 @@ def diag_main(args):
                    "entry_point": "gdn_diag_fwd" if form == "chunked" else "gdn_diag_fwd_recurrent",
                    "tokens_per_step": wl.tokens, "rotated_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload) if form == "chunked" else None,
                      "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
                      "algorithmic_bytes": alg, "mean_launch_us": mean_launch_s * 1e6,
                      "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
@@ -632,13 +657,7 @@ def main():
             raise SystemExit(f"{form} entry point failed with status {rc}")
 
     if args.copy_calibration:
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     copy_gbs = copy_reference(algorithmic_bytes(wl, inp.h0 is not None), stream)
 
@@ -675,7 +694,7 @@ def main():
     alg = algorithmic_bytes(wl, inp.h0 is not None)
     mean_launch_s = float(launch_ms.mean()) / 1e3
     achieved = alg / mean_launch_s / 1e9
-    traffic = measured_traffic() if (args.workload == "wide_head" and form == "chunked") else None
+    traffic = measured_traffic(args.workload) if form == "chunked" else None
 
     rec = {
         "metric": METRIC,

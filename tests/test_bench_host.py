@@ -59,7 +59,7 @@ def test_full_width_backward_flops():
 def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("int f(int x) {\n  return x + 1;  // one\n}\n")
-    monkeypatch.setattr(bench, "KERNEL_SRCS", [str(src)])
+    monkeypatch.setattr(bench, "KERNEL_SRCS", {"wide_head": [str(src)]})
     h1 = bench.kernel_source_hash()
     src.write_text("/* a note */\nint f(int x)   {\n\n  return x + 1;  // changed comment\n}\n")
     assert bench.kernel_source_hash() == h1
