@@ -214,8 +214,15 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 
 __device__ static inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four values to bf16 (round to nearest even) as two packed pair
+// conversions.  (A vector built element by element, or a four-element
+// vector conversion feeding a bit cast, is converted a value at a time and
+// merged with permutes.)
+__device__ static inline uint32_t cvt_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 __device__ static inline bf16x4 cvt4(f32x4 v) {
-  return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  return __builtin_bit_cast(bf16x4, u32x2{cvt_pair(v[0], v[1]), cvt_pair(v[2], v[3])});
 }
 
 // Raw buffer descriptor over [base, base + bytes); accesses at or past the
