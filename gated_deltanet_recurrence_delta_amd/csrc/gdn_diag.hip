@@ -186,8 +186,9 @@ int diag_validate(const void* v, const void* b, const void* c, const float* g, c
 // a factor that underflows to zero stands for a contribution below 1e-38 of
 // its neighbours.
 //
-// Mapping: one workgroup per chain (sequence, head), 8 waves; wave w takes
-// chunks w, w+8, ...; neighbouring chains run on one XCD.  Per chunk:
+// Mapping: one workgroup per (chain, segment), 4 waves, two workgroups per
+// CU; wave w takes chunks w, w+4, ... of its range; neighbouring chains run
+// on one XCD.  Per chunk:
 //   phase A (needs no state): the chunk's own write to the next state,
 //     dH = sum_tau (e^{x_63 - x_tau} (.) b_tau) v_tau^T, with each key first
 //     decayed to the end of its 16-token sub-chunk (kept for phase B); the
@@ -198,14 +199,17 @@ int diag_validate(const void* v, const void* b, const void* c, const float* g, c
 //   phase B: the outputs, sub-chunk by sub-chunk with the running state Hs
 //     (Hs = H_c at the first): O = Qt Hs + P V with Qt = c (.) e^{x_t -
 //     x_ref} (ref = the token before the sub-chunk) and the 16x16 matrix
-//     P[t][tau] = sum_s c_t[s] b_tau[s] prod_{j = tau+1..t} e^{A_s g_j},
-//     tau <= t, whose decay is formed by multiplication so that every factor
-//     stays in [0, 1] even for rows that decay by e^-40 per token; then the
-//     epilogue and Hs <- E_k (.) Hs + Bt_k^T V_k.
-// Products with a contraction go to the bf16 MFMA (fp32 accumulation):
-// Bt^T V and P V with the 16-deep form, Qt Hs with the 32-deep form; the
-// state is rounded to bf16 only as an MFMA operand and carried in fp32.  P
-// is formed in packed fp16 with fp32-accumulating dot products.
+//     P[t][tau] = sum_s c_t[s] b_tau[s] e^{x_t[s] - x_tau[s]}, tau <= t;
+//     then the epilogue and Hs <- E_k (.) Hs + Bt_k^T V_k.
+// P is split at reference tokens so that no factor exceeds 1 even for rows
+// that decay by e^-40 per token: pairs on the two sides of token 7, or of
+// token 3 or 11 inside a half, are products X X^T of keys and queries
+// decayed to the reference (fp16 matrix core); pairs inside one 4-token
+// quarter are formed exactly by products of per-token decays in packed
+// fp16 with fp32-accumulating dot products.  The other contractions (Bt^T V,
+// Qt Hs, P V) run on the bf16 matrix core with fp32 accumulation, in one
+// 16-deep accumulation chain for the outputs; the state is rounded to bf16
+// only as an operand and carried in fp32.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -238,7 +242,7 @@ struct ChunkParams {
   int T, H, nchain, nseg, seg_chunks;
 };
 
-// Per-wave LDS region (≈17.8 KB; four waves and the shared part fit twice
+// Per-wave LDS region (≈17.6 KB; four waves and the shared part fit twice
 // in a CU's 160 KB).
 //
 // The chunk rows of b, c and v are token-major, 64 bytes per token, with
