@@ -86,3 +86,26 @@ def test_timing_record_settled_flag():
     assert r["clock_settled"] and r["settle_launches"] == 5 and r["cold_first_call_us"] == 123.0
     ramp = np.concatenate([np.full(10, 0.12), np.full(30, 0.1)])
     assert not bench.timing_record(ramp, 0, 1.0)["clock_settled"]
+
+
+def test_measured_traffic_follows_each_workloads_sources(tmp_path, monkeypatch):
+    """A counter file counts only while its hash matches that workload's
+    sources; other workloads and unknown names report None."""
+    import json
+
+    srcs = {}
+    for w in ("wide_head", "hymo"):
+        f = tmp_path / f"{w}.hip"
+        f.write_text(f"int {w}_kernel() {{ return 1; }}\n")
+        srcs[w] = [str(f)]
+    monkeypatch.setattr(bench, "KERNEL_SRCS", srcs)
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    for w, nbytes in (("wide_head", 300.0), ("hymo", 190.0)):
+        (tmp_path / f"traffic_{w}.json").write_text(
+            json.dumps({"kernel_sha256_16": bench.kernel_source_hash(w), "bytes_per_launch": nbytes}))
+    assert bench.measured_traffic("wide_head") == 300.0
+    assert bench.measured_traffic("hymo") == 190.0
+    assert bench.measured_traffic("varlen") is None
+    (tmp_path / "hymo.hip").write_text("int hymo_kernel() { return 2; }\n")  # the code changed
+    assert bench.measured_traffic("hymo") is None
+    assert bench.measured_traffic("wide_head") == 300.0
