@@ -254,6 +254,34 @@ def test_recurrent_packed_equals_per_sequence_bitwise():
         assert torch.equal(o1[0], out[s:e]) and torch.equal(h1[0], hT[n])
 
 
+def test_chunked_packed_equals_per_sequence_bitwise():
+    """Each sequence's slice of a packed run equals that sequence run alone,
+    both packed by itself (cu_seqlens = [0, L]) and, where the dense batch
+    is too short to split into segments, as a dense B = 1 batch."""
+    import torch
+
+    lens = [70, 0, 130, 1, 64 * 9 + 5, 33, 64]
+    inp = sd.generate(sd.custom("chunk_bitwise", seed=29, H=3, dtype="bf16", h0_std=0.3,
+                                seq_lens=lens))
+    out, hT = run(inp, "chunked")
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        packed = dataclasses.replace(
+            inp, wl=sd.custom("one", seed=0, H=3, dtype="bf16", seq_lens=[e - s]),
+            v=inp.v[s:e], b=inp.b[s:e], c=inp.c[s:e], g=inp.g[s:e], gate=inp.gate[s:e],
+            h0=inp.h0[n:n + 1], cu_seqlens=np.array([0, e - s], dtype=np.int32))
+        o1, h1 = run(packed, "chunked")
+        assert torch.equal(o1, out[s:e]) and torch.equal(h1[0], hT[n]), n
+        if (e - s + 63) // 64 < 8:  # fewer than 8 chunks: never split
+            dense = dataclasses.replace(
+                packed, wl=sd.custom("one", seed=0, B=1, T=e - s, H=3, dtype="bf16"),
+                v=inp.v[None, s:e], b=inp.b[None, s:e], c=inp.c[None, s:e], g=inp.g[None, s:e],
+                gate=inp.gate[None, s:e], cu_seqlens=None)
+            o2, h2 = run(dense, "chunked")
+            assert torch.equal(o2[0], out[s:e]) and torch.equal(h2[0], hT[n]), n
+
+
 # Dense batches with fewer chains than two workgroups per CU run each
 # sequence as segments that start from a zero state where the decay since
 # then is below e^-40 (or at the sequence start).  Two chains and 32 chunks
