@@ -484,12 +484,12 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
   // Lane -> row 16*i + (lane >> 2) of the chunk, 16-byte granule lane & 3.
   u32x4 pf[12];
   float pg = 0.f, pgate = 1.f;
-  auto prefetch = [&](int c) {
+  // b, v and the gates first (phase A needs them), c last (phase B only).
+  auto prefetch_bv = [&](int c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int voff = (int)(((long)(c * CC + 16 * i + (lane >> 2))) * tok_stride) + 16 * (lane & 3);
       pf[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0);
-      pf[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0);
       pf[8 + i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
     }
     const int tok = c * CC + lane;
@@ -497,7 +497,15 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
     pg = tok < len ? p.g[th] : 0.f;
     pgate = (tok < len && p.gate) ? p.gate[th] : 1.f;
   };
-  prefetch(cs + wave);
+  auto prefetch_c = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int voff = (int)(((long)(c * CC + 16 * i + (lane >> 2))) * tok_stride) + 16 * (lane & 3);
+      pf[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0);
+    }
+  };
+  prefetch_bv(cs + wave);
+  prefetch_c(cs + wave);
   for (int c = cs + wave; c < c1; c += CW) {
     // Lane-dependent offsets are re-derived in each iteration instead of
     // being held in registers across the whole loop.
@@ -512,12 +520,11 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         *reinterpret_cast<u32x4*>(W.b + 1024 * i + wo) = pf[i];
-        *reinterpret_cast<u32x4*>(W.c + 1024 * i + wo) = pf[4 + i];
         *reinterpret_cast<u32x4*>(W.v + 1024 * i + wo) = pf[8 + i];
       }
     }
     const float gt = pg, gate_t = pgate;
-    if (c + CW < c1) prefetch(c + CW);
+    if (c + CW < c1) prefetch_bv(c + CW);
     float gam = gt;  // inclusive scan of g over the chunk (lane = token)
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -571,6 +578,14 @@ __global__ __launch_bounds__(64 * CW, 2) void diag_chunk_kernel(const ChunkParam
         for (int nt = 0; nt < 2; ++nt) dH[mt][nt] = mma16(bb, vf[nt], dH[mt][nt]);
       }
     }
+    // This chunk's c rows into LDS (made visible by the sync below), then
+    // the next chunk's c.
+    {
+      const int wo = 64 * hi4 + 16 * (m4 ^ swz(hi4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(W.c + 1024 * i + wo) = pf[4 + i];
+    }
+    if (c + CW < c1) prefetch_c(c + CW);
     // Per-row decays over each sub-chunk (E_k) and over the chunk (e^{x_63}),
     // one exponential per lane and value.
     float* const ex = W.ex;
