@@ -187,6 +187,27 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     }
     if (lane == 0) sSTART = cs;
   }
+  // The loader requests the first chunk's k, g and beta while the start is
+  // still being searched for, assuming the start the search usually finds:
+  // c0 itself without a search, else the chunk before it (one chunk of
+  // decay reaches e^-HALO_NATS).  Another start requests them again below.
+  const int cs_guess = (exact || c0 == 0) ? c0 : c0 - 1;
+  if (wave == W_L) {
+    const int rb = (int)(rowbase + (long)cs_guess * C);
+    const long ln = (long)min(len, c1 * C) - (long)cs_guess * C;
+    if (ln > 0) {
+      const long kq_stride = (long)H * KQR;
+      char* d = reinterpret_cast<char*>(sGB);
+      copy_to_lds4(make_rsrc(p.g + (long)rb * H + hh, ln * H * 4), d, lane * H * 4);
+      copy_to_lds4(make_rsrc(p.beta + (long)rb * H + hh, ln * H * 4), d + C * 4, lane * H * 4);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(p.k + (long)rb * kq_stride + hh * KQR, ln * kq_stride);
+#pragma unroll
+      for (int i = 0; i < KQ_INS; ++i) {
+        const int rr = i * KQ_RPI + lane / GR;
+        copy_to_lds(r, sK + i * 1024, (int)(rr * kq_stride) + 16 * ((lane % GR) ^ swz_kq<GR>(rr)));
+      }
+    }
+  }
   __syncthreads();
   const int cs = sSTART;
   const bool write_hT = MODE == 0 && c1 >= nch;
@@ -636,7 +657,8 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    if (NIT > 0) {
+    if (NIT > 0 && cs != cs_guess) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the early copies have landed
       issue_gb(0);
       issue(p.k, sK, NKR, 0, true);
     }
