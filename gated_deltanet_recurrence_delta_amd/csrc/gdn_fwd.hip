@@ -1695,6 +1695,28 @@ int launch16(const Params& p, int nwg, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+// Workgroups of gdn_bf16_kernel<DK, C> that fit on one CU at once (LDS and
+// registers), 1 when the runtime cannot tell.
+template <int DK, int C>
+int occupancy16() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gdn_bf16_kernel<DK, C>, 64 * Cfg16<DK, C>::NW, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+static int occupancy_bf16(int dk, int chunk) {
+  switch (dk * 1000 + chunk) {
+    case 32064: return occupancy16<32, 64>();
+    case 32032: return occupancy16<32, 32>();
+    case 64064: return occupancy16<64, 64>();
+    case 64032: return occupancy16<64, 32>();
+    case 128064: return occupancy16<128, 64>();
+    case 128032: return occupancy16<128, 32>();
+    default: return 1;
+  }
+}
+
 template <typename TI, int DK, int DVT, int C>
 int launch(const Params& p, int nwg, hipStream_t stream) {
   using CF = Cfg<TI, DK, DVT, C>;
@@ -1823,7 +1845,10 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
     const int nchunks = (T + chunk - 1) / chunk;
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && nwg < ncu) {
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+      ncu *= occupancy_bf16(dk, chunk);  // workgroup slots
+    }
+    if (ncu > 0 && nwg < ncu) {
       int nseg = ncu / nwg < nchunks / 8 ? ncu / nwg : nchunks / 8;
       if (nseg >= 2) {
         p.seg_chunks = (nchunks + nseg - 1) / nseg;
