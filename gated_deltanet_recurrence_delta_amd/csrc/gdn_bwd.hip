@@ -1173,7 +1173,8 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
     bp.T = T;
     bp.H = H;
     bp.seg_max = gdn_launch::SEG_MAX_CHUNKS;
-    bp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, bp.seg_max);
+    bp.seg_cap = gdn_launch::seg_cap_for(H);
+    bp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, bp.seg_max, bp.seg_cap);
     bp.nchunk = (int)(ttot / 64 + B);
     return gdn_launch::bwd_full(bp, st);
   }

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
     for (int t = threadIdx.x; t < p.B; t += blockDim.x) {
       const int s0 = p.cu[t], s1 = p.cu[t + 1];
       int nch, seg_len, nseg;
-      seg_layout(s1 - s0, p.seg_max, nch, seg_len, nseg);
+      seg_layout(s1 - s0, p.seg_max, p.seg_cap, nch, seg_len, nseg);
       const long f = (segt > 0 ? s0 / segt : 0) + t;
       if (slot >= f && slot < f + nseg) {
         sPICK[0] = t;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
     len = p.cu[bseq + 1] - p.cu[bseq];
   } else {
     int nch, seg_len, nseg;
-    seg_layout(p.T, p.seg_max, nch, seg_len, nseg);
+    seg_layout(p.T, p.seg_max, p.seg_cap, nch, seg_len, nseg);
     bseq = slot / nseg;
     seg = slot % nseg;
     if (bseq >= p.B) return;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
   const long cslot0 = rowbase / C + bseq;  // chunk slot of the sequence's first chunk
 
   int nch, seg_len, nseg;
-  seg_layout(len, p.seg_max, nch, seg_len, nseg);
+  seg_layout(len, p.seg_max, p.seg_cap, nch, seg_len, nseg);
   const int c0 = seg * seg_len;
   const int c1 = min(c0 + seg_len, nch);
   if (threadIdx.x < 4) sFLAG[threadIdx.x] = 0;
@@ -1176,6 +1176,7 @@ int bwd_full(const BwdParams& p, hipStream_t stream) {
   fp.T = p.T;
   fp.H = p.H;
   fp.seg_max = p.seg_max;
+  fp.seg_cap = p.seg_cap;
   fp.nslot = p.nslot;
   fp.sv = p.sv;
   const long nwg = (long)p.nslot * p.H;

@@ -45,15 +45,19 @@ __device__ static inline int key_of(int b, int r) {
   return 32 * (b >> 1) + 8 * (r >> 2) + 4 * (b & 1) + (r & 3);
 }
 
-// Chunk count of a sequence and its segment layout.
-__device__ static inline void seg_layout(int len, int seg_max, int& nch, int& seg_len, int& nseg) {
+// Chunk count of a sequence and its segment layout: ceil(nch / seg_max)
+// segments of equal length (the last one shorter), at most seg_cap of them
+// when seg_cap > 0.
+__host__ __device__ static inline void seg_layout(int len, int seg_max, int seg_cap, int& nch, int& seg_len,
+                                                  int& nseg) {
   nch = (len + C - 1) / C;
   if (seg_max <= 0 || nch <= seg_max) {
     seg_len = nch > 0 ? nch : 1;
     nseg = 1;
     return;
   }
-  const int n0 = (nch + seg_max - 1) / seg_max;
+  int n0 = (nch + seg_max - 1) / seg_max;
+  if (seg_cap > 0 && n0 > seg_cap) n0 = seg_cap;
   seg_len = (nch + n0 - 1) / n0;
   nseg = (nch + seg_len - 1) / seg_len;
 }

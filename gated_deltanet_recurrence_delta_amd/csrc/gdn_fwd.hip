@@ -1794,7 +1794,8 @@ static gdn_launch::FullParams full_params(const void* q, const void* k, const vo
   fp.T = T;
   fp.H = H;
   fp.seg_max = seg_max;
-  fp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, seg_max);
+  fp.seg_cap = seg_max > 0 ? gdn_launch::seg_cap_for(H) : 0;
+  fp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, seg_max, fp.seg_cap);
   return fp;
 }
 
@@ -1865,9 +1866,10 @@ long long gdn_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv, int p
   if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_INVALID_ARG;
   if (chunk == 0) chunk = dtype == GDN_BF16 ? 64 : 16;
   // Only the full-width kernel's shapes use the scan, and only sequences of
-  // more than GDN_SEG_MAX_CHUNKS chunks are cut.
+  // more than GDN_SEG_MAX_CHUNKS chunks are cut; the slots without a
+  // segment cap bound those of any device.
   if (!full_width(dtype, dk, dv, chunk) || T <= GDN_SEG_MAX_CHUNKS * 64) return 0;
-  return 4 * gdn_launch::scan_ws_floats(gdn_launch::full_slots(B, T, packed != 0, GDN_SEG_MAX_CHUNKS), H);
+  return 4 * gdn_launch::scan_ws_floats(gdn_launch::full_slots(B, T, packed != 0, GDN_SEG_MAX_CHUNKS, 0), H);
 }
 
 int gdn_fwd_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     for (int t = threadIdx.x; t < p.B; t += blockDim.x) {
       const int s0 = p.cu[t], s1 = p.cu[t + 1];
       int nch, seg_len, nseg;
-      seg_layout(s1 - s0, p.seg_max, nch, seg_len, nseg);
+      seg_layout(s1 - s0, p.seg_max, p.seg_cap, nch, seg_len, nseg);
       const long f = (segt > 0 ? s0 / segt : 0) + t;
       if (slot >= f && slot < f + nseg) {
         sPICK[0] = t;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
     len = p.cu[bseq + 1] - p.cu[bseq];
   } else {
     int nch, seg_len, nseg;
-    seg_layout(p.T, p.seg_max, nch, seg_len, nseg);
+    seg_layout(p.T, p.seg_max, p.seg_cap, nch, seg_len, nseg);
     bseq = slot / nseg;
     seg = slot % nseg;
     if (bseq >= p.B) return;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   // Segment range [c0, c1) of chunks whose outputs this workgroup stores,
   // and where its recurrence starts (cs <= c0).
   int nch, seg_len, nseg;
-  seg_layout(len, p.seg_max, nch, seg_len, nseg);
+  seg_layout(len, p.seg_max, p.seg_cap, nch, seg_len, nseg);
   const int c0 = seg * seg_len;
   const int c1 = min(c0 + seg_len, nch);
   // Maps are needed for every segment but the last; P not for the first,
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(64 * sk::NWS, 1) void gdn_scan_kernel(const gdn_lau
     len = p.cu[n + 1] - s0;
   }
   int nch, seg_len, nseg;
-  seg_layout(len, p.seg_max, nch, seg_len, nseg);
+  seg_layout(len, p.seg_max, p.seg_cap, nch, seg_len, nseg);
   if (nseg <= 1) return;  // uniform over the workgroup
   // First segment slot of the sequence (the same numbering as the kernel above).
   const long slot0 = p.cu ? (long)(s0 / (p.seg_max * C)) + n : (long)n * nseg;
@@ -1010,18 +1010,23 @@ __global__ __launch_bounds__(64 * sk::NWS, 1) void gdn_scan_kernel(const gdn_lau
 
 namespace gdn_launch {
 
-int full_slots(int B, int T, bool packed, int seg_max) {
+int full_slots(int B, int T, bool packed, int seg_max, int seg_cap) {
   if (!packed) {
-    const int nch = (T + 63) / 64;
-    int nseg = 1;
-    if (seg_max > 0 && nch > seg_max) {
-      const int n0 = (nch + seg_max - 1) / seg_max;
-      const int seg_len = (nch + n0 - 1) / n0;
-      nseg = (nch + seg_len - 1) / seg_len;
-    }
+    int nch, seg_len, nseg;
+    fk::seg_layout(T, seg_max, seg_cap, nch, seg_len, nseg);
     return B * nseg;
   }
+  // sequence n takes slots [floor(start_n / (seg_max * 64)) + n, + its
+  // segments), never more than ceil(length_n / (seg_max * 64)) of them
   return (seg_max > 0 ? T / (seg_max * 64) : 0) + B;
+}
+
+int seg_cap_for(int H) {
+  int dev = 0, ncu = 0;
+  if (H < 1 || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+    return 0;
+  return ncu / H > 1 ? ncu / H : 1;
 }
 
 int fwd_full(const FullParams& p, hipStream_t stream) {

@@ -26,9 +26,11 @@ struct FullParams {
   float* hT;
   int B, T, H;
   // A sequence of n chunks is cut into ceil(n / seg_max) segments of equal
-  // length (the last one shorter); seg_max = 0 never cuts.  The cut depends
-  // on the sequence alone, never on the batch or the device.
+  // length (the last one shorter), but into at most seg_cap of them when
+  // seg_cap > 0; seg_max = 0 never cuts.  The cut depends on the sequence,
+  // H and the device (seg_cap is the CUs per head), never on the batch.
   int seg_max;
+  int seg_cap = 0;
   int nslot;  // segment slots per head (the grid is nslot x H)
   // Chunk-map scan (fwd_full_scan): per (segment slot, head) three dk x dv
   // fp32 matrices, row-major: the segment's map P and Q (M_end = P M_start
@@ -67,7 +69,7 @@ struct BwdParams {
   char* sv;   // records, as FullParams::sv
   float* hT;  // any valid float buffer (the states pass writes no hT)
   int B, T, H;
-  int seg_max, nslot;  // sequence segments of the two sweeps (as FullParams)
+  int seg_max, seg_cap, nslot;  // sequence segments of the two sweeps (as FullParams)
   int nchunk;          // chunk slots per head
 };
 
@@ -78,7 +80,11 @@ __attribute__((visibility("hidden"))) long long bwd_full_ws_bytes(int B, long tt
 __attribute__((visibility("hidden"))) int bwd_full(const BwdParams& p, hipStream_t stream);
 
 // Number of segment slots per head for a call (see FullParams).
-__attribute__((visibility("hidden"))) int full_slots(int B, int T, bool packed, int seg_max);
+__attribute__((visibility("hidden"))) int full_slots(int B, int T, bool packed, int seg_max, int seg_cap);
+
+// The segment cap for H heads on the current device: its CUs per head (at
+// least 1), or 0 when the device cannot be queried (no cap).
+__attribute__((visibility("hidden"))) int seg_cap_for(int H);
 
 __attribute__((visibility("hidden"))) int fwd_full(const FullParams& p, hipStream_t stream);
 

@@ -96,12 +96,13 @@ extern "C" {
  * e^-40 (or at the sequence start, from h0), so it differs from the exact
  * sequential result by less than that factor of the state, beyond
  * rounding.  With GDN_BF16, dk = dv = 128 and 64-token chunks, a sequence
- * of n chunks is cut into ceil(n / 16) segments of equal length, whatever
- * the batch and the device: a packed sequence's slice of out and hT then
- * equals the same sequence run alone (same h0, same flags) bit for bit.
- * Other GDN_BF16 shapes cut only dense batches with fewer chains x 32-column
- * tiles than the device has CUs (the cut then depends on the device), and
- * never cut packed batches.  GDN_F32 never cuts.  hT == h0 turns cutting
+ * of n chunks is cut into ceil(n / 16) segments of equal length, but into
+ * no more segments than the device has CUs per head (CUs / H, at least 1),
+ * whatever the batch: a packed sequence's slice of out and hT then equals
+ * the same sequence run alone (same H, h0 and flags, same device) bit for
+ * bit.  Other GDN_BF16 shapes cut only dense batches with fewer chains x
+ * 32-column tiles than the device has workgroup slots (the cut then depends
+ * on the device), and never cut packed batches.  GDN_F32 never cuts.  hT == h0 turns cutting
  * off (a segment could read h0 after another wrote hT over it).  With
  * GDN_FLAG_NO_SEGMENTS every chain runs from its start, and a run split at
  * a chunk boundary (the second part taking the first part's hT as h0)
@@ -124,7 +125,8 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
  * Design Spec", section 2.3; "Optimization Quartet", section 3.2); composing
  * the chunks' maps lets a long sequence's segments run in parallel without
  * any dependence on decay.  A sequence of n > 16 chunks is cut as in gdn_fwd
- * (ceil(n / 16) segments of equal length) and run in three launches on
+ * (ceil(n / 16) segments of equal length, at most CUs / H of them) and run
+ * in three launches on
  * `stream`:
  *   1. every segment but the last composes its map -- the recurrence over
  *      its chunks from the identity with v = 0 gives P, from zero with the
@@ -153,7 +155,8 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g,
  * m = 2 its entry state S), written only for segments of cut sequences
  * (P for segments 1 .. nseg-2, Q for 0 .. nseg-2, S for all).  Segment s of
  * dense sequence b is slot b * nseg + s; of packed sequence n, slot
- * floor(cu_seqlens[n] / 1024) + n + s.
+ * floor(cu_seqlens[n] / 1024) + n + s (the workspace size counts the slots
+ * without the CUs-per-head cap, so it does not depend on the device).
  * hT may alias h0: a cut sequence reads h0 only in the first two launches,
  * and an uncut one reads it in the same workgroup that later writes its hT.
  * A packed sequence's results equal the same sequence run alone bit for bit.
@@ -303,8 +306,8 @@ int gdn_diag_fwd_recurrent(const void* v, const void* b, const void* c,
  * fp32 accumulation: the forward recurrence saving each chunk's entry state
  * and U, the state gradient swept backwards over the chunks saving each
  * chunk's exit gradient and dX, then the per-chunk token gradients.  The
- * sweeps run as gdn_fwd's sequence segments (at most 16 chunks each, halos
- * bounded as there; a packed sequence equals the same sequence alone bit for
+ * sweeps run as gdn_fwd's sequence segments (cut as there, halos bounded
+ * as there; a packed sequence equals the same sequence alone bit for
  * bit).  The saved matrices are bf16, so the gradients carry bf16-level
  * rounding (about 5e-3 of their scale); the workspace use is a prefix of
  * 96 KB per (64-token chunk, head).

@@ -108,9 +108,9 @@ def test_maps_and_entry_states_against_oracle(decay):
 
 @pytest.mark.parametrize("name", ["long_context_nodecay", "long_context"])
 def test_long_context_every_chain(name):
-    """B=1 H=16 T=32,768 d=128: 512 chunks in 32 segments per chain, every
-    chain against the oracle -- with no decay at all (where the halo
-    segments of gdn_fwd reach back to the sequence start) and with
+    """B=1 H=16 T=32,768 d=128: 512 chunks in 16 segments per chain on 256
+    CUs, every chain against the oracle -- with no decay at all (where the
+    halo segments of gdn_fwd reach back to the sequence start) and with
     long_context's slow decay."""
     _check(synth.generate(synth.WORKLOADS[name]))
 
