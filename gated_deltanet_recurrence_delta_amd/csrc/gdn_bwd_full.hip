@@ -786,26 +786,22 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
   const char* rec = p.sv + (sigma * H + hh) * gdn_launch::BWD_REC_BYTES;
 
   // ---------------------------------------------------- phase 0: loads
+  // In order: q and k (16 copies each; wave w issues [4 w, 4 w + 4) of the
+  // 32), g and beta, this wave's operands in registers, then M^T and dM'^T
+  // (32 copies each; wave w issues [8 w, 8 w + 8) of the 64), which only
+  // phase 2 reads: phase 1 starts once all but those last GK_LATE copies
+  // of each wave have landed.
+  constexpr int GK_QK = 2 * KQ_INS / gk::NWG, GK_LATE = 2 * gk::MT_INS / gk::NWG;
+  static_assert(GK_QK * gk::NWG == 2 * KQ_INS && GK_LATE * gk::NWG == 2 * gk::MT_INS, "copies per wave");
   {
-    // q, k (16 copies each), M^T, dM'^T (32 each): wave w issues copies
-    // [12 w, 12 w + 12) of the 96.
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (t0 * H + hh) * KQR, (long)Lc * kq_stride);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (t0 * H + hh) * KQR, (long)Lc * kq_stride);
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(rec, gdn_launch::BWD_OFF_U);
 #pragma unroll
-    for (int x = 0; x < 12; ++x) {
-      const int i = 12 * wave + x;
-      if (i < 2 * KQ_INS) {
-        const int ii = i % KQ_INS, r = ii * KQ_RPI + lane / GR;
-        const int so = (int)(r * kq_stride) + 16 * ((lane % GR) ^ swz_kq<GR>(r));
-        copy_to_lds(i < KQ_INS ? rq : rk, (i < KQ_INS ? sQ : sK) + ii * 1024, so);
-      } else {
-        const int ii = (i - 2 * KQ_INS) % gk::MT_INS, r = ii * KQ_RPI + lane / GR;
-        const bool dm = i - 2 * KQ_INS >= gk::MT_INS;
-        const int so = (int)(dm ? gdn_launch::BWD_OFF_DM : gdn_launch::BWD_OFF_M) + r * KQR +
-                       16 * ((lane % GR) ^ swz_m(r));
-        copy_to_lds(rm, (dm ? sDT : sMT) + ii * 1024, so);
-      }
+    for (int x = 0; x < GK_QK; ++x) {
+      const int i = GK_QK * wave + x;
+      const int ii = i % KQ_INS, r = ii * KQ_RPI + lane / GR;
+      const int so = (int)(r * kq_stride) + 16 * ((lane % GR) ^ swz_kq<GR>(r));
+      copy_to_lds(i < KQ_INS ? rq : rk, (i < KQ_INS ? sQ : sK) + ii * 1024, so);
     }
     if (wave == 0) {
       copy_to_lds4(make_rsrc(p.g + t0 * H + hh, (long)Lc * H * 4), reinterpret_cast<char*>(sGB), lane * H * 4);
@@ -847,8 +843,22 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
                                              rr, (int)gdn_launch::BWD_OFF_U + jrow * DV * 2 + (32 * s + 8 * q4) * 2, 0, 0));
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  {
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(rec, gdn_launch::BWD_OFF_U);
+#pragma unroll
+    for (int x = 0; x < GK_LATE; ++x) {
+      const int i = GK_LATE * wave + x;
+      const int ii = i % gk::MT_INS, r = ii * KQ_RPI + lane / GR;
+      const bool dm = i >= gk::MT_INS;
+      const int so = (int)(dm ? gdn_launch::BWD_OFF_DM : gdn_launch::BWD_OFF_M) + r * KQR +
+                     16 * ((lane % GR) ^ swz_m(r));
+      copy_to_lds(rm, (dm ? sDT : sMT) + ii * 1024, so);
+    }
+  }
+  // everything but the M^T / dM'^T copies has landed, in every wave (a
+  // plain barrier: an LDS fence would also wait for those copies)
+  static_assert(GK_LATE <= 15, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(GK_LATE) : "memory");
   if (wave == 0) {
     // per-token vectors (as the forward's loader)
     const float lam = wave_prefix_sum(sGB[lane] * kLog2e, lane);
@@ -868,24 +878,7 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
 #pragma unroll
     for (int b = 1; b < NB; ++b) sVEC[(F_ER + b) * C + lane] = lane < 16 * b ? exp2_fast(lb[b] - lam) : 0.f;
   }
-  {
-    // <M, dM'> over the whole state (the last token's Gam_C term)
-    float acc = 0.f;
-    const int base = threadIdx.x * 64;  // 64 bytes of each tile per thread
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const u32x4 a = lds_ld<u32x4>(sMT, base + 16 * x), b = lds_ld<u32x4>(sDT, base + 16 * x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
-        acc = __builtin_fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    if (lane == 0) sGC[wave] = acc;
-  }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const float* vec = sVEC;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -966,7 +959,25 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       }
     }
   }
-  __syncthreads();
+  // the M^T / dM'^T copies of every wave have landed
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  {
+    // <M, dM'> over the whole state (the last token's Gam_C term)
+    float acc = 0.f;
+    const int base = threadIdx.x * 64;  // 64 bytes of each tile per thread
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const u32x4 a = lds_ld<u32x4>(sMT, base + 16 * x), b = lds_ld<u32x4>(sDT, base + 16 * x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+        acc = __builtin_fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+    if (lane == 0) sGC[wave] = acc;
+  }
 
   // ---------------------------------------------------- phase 2
   {
