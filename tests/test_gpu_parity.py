@@ -197,6 +197,23 @@ def test_varlen_workload_packed_equals_per_sequence_bitwise(segments, with_h0):
         assert torch.equal(_bits(hT[n]), _bits(h1[0])), f"sequence {n} ({e - s} tokens) hT"
 
 
+def test_capped_segments_packed_equals_per_sequence_bitwise():
+    """With H = 128 heads a sequence is cut into at most CUs / 128 segments
+    (two on 256 CUs): the 40-chunk sequence runs as two 20-chunk segments,
+    not three of 14.  Every chain matches the oracle, and each sequence's
+    slice of the packed run equals the sequence run alone bit for bit."""
+    inp = synth.generate(synth.custom(name="cap_packed", seed=47, H=128, dk=128, dv=128, dtype="bf16",
+                                      chunk=64, h0_std=0.2, g_mean=-2.0, seq_lens=[2560, 500, 1, 1100]))
+    out, hT = _check(inp)
+    d = device_inputs(inp)
+    cu = inp.cu_seqlens
+    for n in range(len(cu) - 1):
+        s, e = int(cu[n]), int(cu[n + 1])
+        o1, h1 = run_hip(inp, d=_alone(d, s, e, d["h0"][n:n + 1].contiguous()))
+        assert torch.equal(_bits(out[s:e]), _bits(o1[0])), f"sequence {n} out"
+        assert torch.equal(_bits(hT[n]), _bits(h1[0])), f"sequence {n} hT"
+
+
 def test_causality_bitwise():
     wl = synth.custom(name="causal", seed=32, B=1, T=256, H=2, dk=128, dv=128, dtype="bf16",
                       chunk=64, h0_std=0.2)
