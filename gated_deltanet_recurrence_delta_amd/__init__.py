@@ -13,7 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdn_fwd", "gdn_fwd_scan", "gdn_fwd_scan_workspace_size", "fwd_scan", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
+__all__ = ["gdn_fwd", "gdn_fwd_train", "gdn_bwd_saved", "fwd_train", "gdn_fwd_scan", "gdn_fwd_scan_workspace_size", "fwd_scan", "gdn_fwd_recurrent", "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_bwd",
            "gdn_bwd_workspace_size", "gdn_bwd_noalloc", "fwd", "fwd_recurrent", "diag_fwd", "diag_fwd_recurrent",
            "bwd", "gated_delta_rule", "GdnError", "lib_path", "load", "version"]
 
@@ -60,8 +60,12 @@ def load():
         lib.gdn_diag_fwd.argtypes = [P] * 11 + [I] * 5 + [P, I, I]
         lib.gdn_diag_fwd_recurrent.restype = I
         lib.gdn_diag_fwd_recurrent.argtypes = [P] * 11 + [I] * 5 + [P, I]
+        lib.gdn_fwd_train.restype = I
+        lib.gdn_fwd_train.argtypes = [P] * 9 + [I] * 5 + [P, I, I, P, ctypes.c_longlong]
         lib.gdn_bwd.restype = I
         lib.gdn_bwd.argtypes = [P] * 16 + [ctypes.c_longlong] + [I] * 5 + [P, I]
+        lib.gdn_bwd_saved.restype = I
+        lib.gdn_bwd_saved.argtypes = [P] * 16 + [ctypes.c_longlong] + [I] * 5 + [P, I]
         lib.gdn_bwd_noalloc.restype = I
         lib.gdn_bwd_noalloc.argtypes = [P] * 15 + [I] * 5 + [P, I]
         lib.gdn_bwd_workspace_size.restype = ctypes.c_longlong
@@ -102,6 +106,14 @@ def gdn_fwd_scan(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
     return load().gdn_fwd_scan(q, k, v, g, beta, h0, cu_seqlens, out, hT,
                                int(B), int(T), int(H), int(dk), int(dv),
                                stream, int(dtype), int(chunk), workspace, int(workspace_bytes))
+
+
+def gdn_fwd_train(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
+                  stream, dtype, chunk, workspace, workspace_bytes) -> int:
+    """Raw C call of the training forward (0 = NULL).  Returns the status."""
+    return load().gdn_fwd_train(q, k, v, g, beta, h0, cu_seqlens, out, hT, int(B), int(T), int(H),
+                                int(dk), int(dv), stream, int(dtype), int(chunk), workspace,
+                                int(workspace_bytes))
 
 
 def gdn_fwd_recurrent(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, dk, dv,
@@ -375,15 +387,60 @@ def gdn_bwd(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, 
                           int(dk_), int(dv_), stream, int(dtype))
 
 
+def gdn_bwd_saved(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, dh0,
+                  workspace, workspace_bytes, B, T, H, dk_, dv_, stream, dtype) -> int:
+    """Raw C call of the backward pass from records gdn_fwd_train left in the
+    workspace (0 = NULL).  Returns the status."""
+    return load().gdn_bwd_saved(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta,
+                                dh0, workspace, int(workspace_bytes), int(B), int(T), int(H),
+                                int(dk_), int(dv_), stream, int(dtype))
+
+
+def train_records_supported(q, k, v, chunk: int = 0) -> bool:
+    """Whether gdn_fwd_train / gdn_bwd_saved have records for this shape:
+    bf16 storage, dk = dv = 128 and 64-token chunks (chunk 0 or 64)."""
+    import torch
+
+    return (q.dtype == torch.bfloat16 and q.shape[-1] == 128 and v.shape[-1] == 128
+            and chunk in (0, 64))
+
+
+def fwd_train(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk: int = 0,
+              out=None, hT=None, workspace=None, stream=None):
+    """``fwd`` that also leaves the backward pass's per-chunk records in a
+    workspace (``gdn_fwd_train``), for ``bwd(..., saved=True)`` on the same
+    inputs.  Only for bf16 with dk = dv = 128 and 64-token chunks
+    (``train_records_supported``).  ``workspace``: a uint8 device tensor of
+    at least ``gdn_bwd_workspace_size`` bytes, allocated here when None.
+    Returns (out, hT, workspace)."""
+    import torch
+
+    a, out, hT = _marshal(q, k, v, g, beta, h0, cu_seqlens, out, hT, stream)
+    B, T, H, dk, dv = a[9:14]
+    need = gdn_bwd_workspace_size(B, T, H, dk, dv, cu_seqlens is not None)
+    if need < 0:
+        raise GdnError(need, strerror(need))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be on q's device and hold {need} bytes")
+    rc = gdn_fwd_train(*a, chunk, workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    if rc != 0:
+        raise GdnError(rc, strerror(rc))
+    return out, hT, workspace
+
+
 def bwd(q, k, v, g, beta, dout, h0=None, cu_seqlens=None, dhT=None, want_dh0=True,
-        workspace=None, stream=None):
+        workspace=None, stream=None, saved=False):
     """Gradients of <dout, out> + <dhT, hT> for ``fwd``'s outputs (out, hT).
 
     Arguments as for ``fwd``; dout has out's shape and dtype, dhT is
     (B,H,dk,dv) float32 or None (zero).  Returns a dict with dq, dk, dv (the
     inputs' dtype), dg, dbeta (float32) and dh0 (float32, or None when
     ``want_dh0`` is false).  ``workspace``: a uint8 device tensor of at least
-    ``gdn_bwd_workspace_size`` bytes, allocated here when None.
+    ``gdn_bwd_workspace_size`` bytes, allocated here when None.  ``saved``:
+    the workspace holds the records ``fwd_train`` wrote for these inputs
+    (``gdn_bwd_saved``, which skips recomputing them).
     """
     import torch
 
@@ -402,6 +459,8 @@ def bwd(q, k, v, g, beta, dout, h0=None, cu_seqlens=None, dhT=None, want_dh0=Tru
     need = gdn_bwd_workspace_size(B, T, H, dk_, dv_, cu_seqlens is not None)
     if need < 0:
         raise GdnError(need, strerror(need))
+    if saved and workspace is None:
+        raise ValueError("saved=True needs the workspace fwd_train filled")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.numel() * workspace.element_size() < need:
@@ -411,10 +470,11 @@ def bwd(q, k, v, g, beta, dout, h0=None, cu_seqlens=None, dhT=None, want_dh0=Tru
              "dh0": torch.empty((B, H, dk_, dv_), dtype=torch.float32, device=dev)
              if want_dh0 else None}
     ptr = lambda t: 0 if t is None else t.data_ptr()
-    rc = gdn_bwd(a[0], a[1], a[2], a[3], a[4], a[5], a[6], ptr(dout), ptr(dhT),
-                 ptr(grads["dq"]), ptr(grads["dk"]), ptr(grads["dv"]), ptr(grads["dg"]),
-                 ptr(grads["dbeta"]), ptr(grads["dh0"]), ptr(workspace),
-                 workspace.numel() * workspace.element_size(), B, T, H, dk_, dv_, strm, dtype)
+    call = gdn_bwd_saved if saved else gdn_bwd
+    rc = call(a[0], a[1], a[2], a[3], a[4], a[5], a[6], ptr(dout), ptr(dhT),
+              ptr(grads["dq"]), ptr(grads["dk"]), ptr(grads["dv"]), ptr(grads["dg"]),
+              ptr(grads["dbeta"]), ptr(grads["dh0"]), ptr(workspace),
+              workspace.numel() * workspace.element_size(), B, T, H, dk_, dv_, strm, dtype)
     if rc != 0:
         raise GdnError(rc, strerror(rc))
     return grads
@@ -437,7 +497,9 @@ def gdn_bwd_noalloc(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
 def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None):
     """(out, hT) of ``fwd`` as a differentiable torch operation: the forward
     runs gdn_fwd and the backward gdn_bwd (from the saved inputs), giving
-    gradients for q, k, v, g, beta and h0.  Arguments as for ``fwd``."""
+    gradients for q, k, v, g, beta and h0.  Where the training records exist
+    (bf16, dk = dv = 128) the forward runs gdn_fwd_train instead and keeps
+    its workspace for gdn_bwd_saved.  Arguments as for ``fwd``."""
     return _gdr_function().apply(q, k, v, g, beta, h0, cu_seqlens)
 
 
@@ -452,7 +514,11 @@ def _gdr_function():
         class _GatedDeltaRule(torch.autograd.Function):
             @staticmethod
             def forward(ctx, q, k, v, g, beta, h0, cu_seqlens):
-                out, hT = fwd(q, k, v, g, beta, h0, cu_seqlens)
+                ctx.workspace = None
+                if train_records_supported(q, k, v):
+                    out, hT, ctx.workspace = fwd_train(q, k, v, g, beta, h0, cu_seqlens)
+                else:
+                    out, hT = fwd(q, k, v, g, beta, h0, cu_seqlens)
                 ctx.save_for_backward(q, k, v, g, beta, h0, cu_seqlens)
                 ctx.has_h0 = h0 is not None
                 return out, hT
@@ -463,7 +529,9 @@ def _gdr_function():
                 dout = torch.zeros_like(v) if dout is None else dout.contiguous()
                 dhT = None if dhT is None else dhT.contiguous()
                 gr = bwd(q, k, v, g, beta, dout, h0=h0, cu_seqlens=cu_seqlens, dhT=dhT,
-                         want_dh0=ctx.has_h0)
+                         want_dh0=ctx.has_h0, workspace=ctx.workspace,
+                         saved=ctx.workspace is not None)
+                ctx.workspace = None
                 return gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["dh0"], None
 
         _GDR = _GatedDeltaRule

@@ -1107,6 +1107,65 @@ int bwd_check(const void* q, const void* k, const void* v, const float* g, const
 
 }  // namespace
 
+// The full-width backward (bf16, dk = dv = 128, a 16-byte-aligned workspace
+// of gdn_bwd_workspace_size bytes): states (unless states_saved), adjoint
+// and gradient kernels of gdn_bwd_full.hip.
+static int bwd_full_path(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT, void* dq,
+                         void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace, int B, int T,
+                         int H, long ttot, bool states_saved, hipStream_t st) {
+  gdn_launch::BwdParams bp;
+  bp.q = static_cast<const char*>(q);
+  bp.k = static_cast<const char*>(k);
+  bp.v = static_cast<const char*>(v);
+  bp.dO = static_cast<const char*>(dout);
+  bp.g = g;
+  bp.beta = beta;
+  bp.h0 = h0;
+  bp.dhT = dhT;
+  bp.cu = cu_seqlens;
+  bp.dq = static_cast<char*>(dq);
+  bp.dk = static_cast<char*>(dk);
+  bp.dv = static_cast<char*>(dv);
+  bp.dg = dg;
+  bp.dbeta = dbeta;
+  bp.dh0 = dh0;
+  bp.sv = static_cast<char*>(workspace);
+  bp.hT = dg;
+  bp.B = B;
+  bp.T = T;
+  bp.H = H;
+  bp.seg_max = gdn_launch::SEG_MAX_CHUNKS;
+  bp.seg_cap = gdn_launch::seg_cap_for(H);
+  bp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, bp.seg_max, bp.seg_cap);
+  bp.nchunk = (int)(ttot / 64 + B);
+  bp.states_saved = states_saved ? 1 : 0;
+  return gdn_launch::bwd_full(bp, st);
+}
+
+// Whether gdn_bwd takes the full-width kernels for these arguments.
+static bool bwd_full_width(int dtype, int dkn, int dvn, const void* workspace, size_t need, int B, long ttot, int H) {
+  return dtype == GDN_BF16 && dkn == 128 && dvn == 128 && (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0 &&
+         (long long)need >= gdn_launch::bwd_full_ws_bytes(B, ttot, H);
+}
+
+extern "C" int gdn_bwd_saved(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT,
+                             void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
+                             long long workspace_bytes, int B, int T, int H, int dkn, int dvn, void* stream,
+                             int dtype) {
+  const int rc = bwd_check(q, k, v, g, beta, cu_seqlens, dout, dq, dk, dv, dg, dbeta, B, T, H, dkn, dvn, dtype);
+  if (rc != GDN_OK) return rc;
+  const long ttot = cu_seqlens ? (long)T : (long)B * T;
+  const size_t need = ws_floats(slots_per_head(ttot, B), H, dkn, dvn) * sizeof(float);
+  if (B > 0 && (!workspace || workspace_bytes < 0 || (size_t)workspace_bytes < need))
+    return GDN_ERR_INVALID_ARG;
+  if (!bwd_full_width(dtype, dkn, dvn, workspace, need, B, ttot, H)) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  return bwd_full_path(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, dh0, workspace, B, T, H,
+                       ttot, true, static_cast<hipStream_t>(stream));
+}
+
 extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                        const float* h0, const int32_t* cu_seqlens, const void* dout, const float* dhT, void* dq,
                        void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
@@ -1149,35 +1208,9 @@ extern "C" int gdn_bwd(const void* q, const void* k, const void* v, const float*
   hipStream_t st = static_cast<hipStream_t>(stream);
   // bf16 with dk = dv = 128: the full-width kernels (gdn_bwd_full.hip), whose
   // records fit in the workspace sized above (a 16-byte-aligned one).
-  if (dtype == GDN_BF16 && dkn == 128 && dvn == 128 && (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0 &&
-      (long long)need >= gdn_launch::bwd_full_ws_bytes(B, ttot, H)) {
-    gdn_launch::BwdParams bp;
-    bp.q = static_cast<const char*>(q);
-    bp.k = static_cast<const char*>(k);
-    bp.v = static_cast<const char*>(v);
-    bp.dO = static_cast<const char*>(dout);
-    bp.g = g;
-    bp.beta = beta;
-    bp.h0 = h0;
-    bp.dhT = dhT;
-    bp.cu = cu_seqlens;
-    bp.dq = static_cast<char*>(dq);
-    bp.dk = static_cast<char*>(dk);
-    bp.dv = static_cast<char*>(dv);
-    bp.dg = dg;
-    bp.dbeta = dbeta;
-    bp.dh0 = dh0;
-    bp.sv = static_cast<char*>(workspace);
-    bp.hT = dg;
-    bp.B = B;
-    bp.T = T;
-    bp.H = H;
-    bp.seg_max = gdn_launch::SEG_MAX_CHUNKS;
-    bp.seg_cap = gdn_launch::seg_cap_for(H);
-    bp.nslot = gdn_launch::full_slots(B, T, cu_seqlens != nullptr, bp.seg_max, bp.seg_cap);
-    bp.nchunk = (int)(ttot / 64 + B);
-    return gdn_launch::bwd_full(bp, st);
-  }
+  if (bwd_full_width(dtype, dkn, dvn, workspace, need, B, ttot, H))
+    return bwd_full_path(q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg, dbeta, dh0, workspace, B, T,
+                         H, ttot, false, st);
   float* ws = static_cast<float*>(workspace);
   return dtype == GDN_BF16 ? launch_dtype<__bf16>(dkn, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, dq, dk, dv, dg,
                                                   dbeta, dh0, ws, p, st)

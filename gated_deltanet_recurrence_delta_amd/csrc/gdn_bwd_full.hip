@@ -1194,8 +1194,10 @@ int bwd_full(const BwdParams& p, hipStream_t stream) {
   const long ngrad = (long)p.nchunk;
   if (nwg > 0x7fffffffL || ngrad > 0x7fffffffL || p.H > 65535) return GDN_ERR_INVALID_ARG;
   if (nwg > 0) {
-    const int rc = fwd_full_save(fp, stream);
-    if (rc != GDN_OK) return rc;
+    if (!p.states_saved) {
+      const int rc = fwd_full_save(fp, stream);
+      if (rc != GDN_OK) return rc;
+    }
     hipLaunchKernelGGL(gdn_adjoint_kernel, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
   }

@@ -1862,6 +1862,27 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* g, const f
   return dtype == GDN_BF16 ? by_dk<__bf16>(p, nwg_all, s, dk, chunk) : by_dk<float>(p, nwg, s, dk, chunk);
 }
 
+int gdn_fwd_train(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* h0, const int32_t* cu_seqlens, void* out, float* hT, int B, int T, int H,
+                  int dk, int dv, void* stream, int dtype, int chunk, void* workspace,
+                  long long workspace_bytes) {
+  const int rc = fwd_check(q, k, v, g, beta, out, hT, cu_seqlens, B, T, H, dk, dv, dtype, chunk);
+  if (rc != GDN_OK) return rc;
+  if (!full_width(dtype, dk, dv, chunk)) return GDN_ERR_UNSUPPORTED;
+  const long long need = gdn_bwd_workspace_size(B, T, H, dk, dv, cu_seqlens != nullptr);
+  if (need < 0) return (int)need;
+  if (B > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u)))
+    return GDN_ERR_INVALID_ARG;
+  const long ttot = cu_seqlens ? (long)T : (long)B * T;
+  if (need < gdn_launch::bwd_full_ws_bytes(B, ttot, H)) return GDN_ERR_UNSUPPORTED;
+  // cut as gdn_fwd cuts (not when hT aliases h0)
+  const bool alias = h0 && static_cast<const void*>(h0) == static_cast<const void*>(hT);
+  gdn_launch::FullParams fp =
+      full_params(q, k, v, g, beta, h0, cu_seqlens, out, hT, B, T, H, alias ? 0 : GDN_SEG_MAX_CHUNKS);
+  fp.sv = static_cast<char*>(workspace);
+  return gdn_launch::fwd_full_train(fp, static_cast<hipStream_t>(stream));
+}
+
 long long gdn_fwd_scan_workspace_size(int B, int T, int H, int dk, int dv, int packed, int dtype, int chunk) {
   if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_INVALID_ARG;
   if (chunk == 0) chunk = dtype == GDN_BF16 ? 64 : 16;
@@ -1903,6 +1924,6 @@ const char* gdn_strerror(int status) {
   }
 }
 
-int gdn_version(void) { return 200; }
+int gdn_version(void) { return 300; }
 
 }  // extern "C"

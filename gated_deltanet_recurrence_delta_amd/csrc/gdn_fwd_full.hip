@@ -67,14 +67,16 @@ namespace {
 // (p.ws set; see the chunk-map scan below): the recurrence over the
 // segment's chunks from the identity with v = 0 (giving P) or from zero
 // (from h0 for the first segment) with the real v (giving Q), no outputs.
+// MODE 3 (training forward, p.sv set): MODE 0 and MODE 2 at once -- the
+// outputs and hT, and every chunk's saved state and U.
 // MODE 2 (states for the backward pass, p.sv set): the recurrence as in
 // MODE 0 without outputs; every chunk's entry state M and its U are saved
 // in bf16 (see gdn_launch.h).
 template <int MODE>
 __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_launch::FullParams p) {
   constexpr bool MAPS = MODE == 1;
-  constexpr bool SAVE = MODE == 2;
-  constexpr bool NOOUT = MODE != 0;  // no outputs: no q, no P waves
+  constexpr bool SAVE = MODE == 2 || MODE == 3;
+  constexpr bool NOOUT = MODE == 1 || MODE == 2;  // no outputs: no q, no P waves
   using namespace fk;
   using MM = Mma<__bf16>;
   using F = bf16x8;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
   }
   __syncthreads();
   const int cs = sSTART;
-  const bool write_hT = MODE == 0 && c1 >= nch;
+  const bool write_hT = (MODE == 0 || MODE == 3) && c1 >= nch;
   // This (segment slot, head)'s P, Q and entry state S in the workspace.
   float* const wsm = p.ws ? p.ws + ((long)slot * H + hh) * 3 * DK * DV : nullptr;
   // Where the recurrence's starting state comes from (an empty descriptor
@@ -1034,6 +1036,14 @@ int fwd_full(const FullParams& p, hipStream_t stream) {
   if (nwg <= 0) return GDN_OK;
   if (nwg > 0x7fffffffL) return GDN_ERR_INVALID_ARG;
   hipLaunchKernelGGL(gdn_full_kernel<0>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int fwd_full_train(const FullParams& p, hipStream_t stream) {
+  const long nwg = (long)p.nslot * p.H;
+  if (nwg <= 0) return GDN_OK;
+  if (nwg > 0x7fffffffL || !p.sv) return GDN_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(gdn_full_kernel<3>, dim3((unsigned)nwg), dim3(64 * fk::NW), 0, stream, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

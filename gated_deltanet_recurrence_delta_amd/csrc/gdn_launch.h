@@ -70,6 +70,7 @@ struct BwdParams {
   float* hT;  // any valid float buffer (the states pass writes no hT)
   int B, T, H;
   int seg_max, seg_cap, nslot;  // sequence segments of the two sweeps (as FullParams)
+  int states_saved = 0;         // the records of M and U are already in sv (a training forward wrote them)
   int nchunk;          // chunk slots per head
 };
 
@@ -98,6 +99,9 @@ __attribute__((visibility("hidden"))) int fwd_full_scan(const FullParams& p, hip
 // The forward recurrence saving every chunk's entry state and U into p.sv
 // (no outputs, no hT).
 __attribute__((visibility("hidden"))) int fwd_full_save(const FullParams& p, hipStream_t stream);
+
+// fwd_full and fwd_full_save in one pass: outputs, hT and the records.
+__attribute__((visibility("hidden"))) int fwd_full_train(const FullParams& p, hipStream_t stream);
 
 }  // namespace gdn_launch
 

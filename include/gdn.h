@@ -334,6 +334,50 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* g,
             void* stream, int dtype);
 
 /*
+ * gdn_fwd_train -- gdn_fwd for training: the same outputs (out and hT equal
+ * gdn_fwd's bit for bit, with flags 0), and in the same pass the per-chunk
+ * records gdn_bwd's first kernel would otherwise recompute -- each 64-token
+ * chunk's entry state and its corrected values U (bf16) -- written into
+ * workspace, so that gdn_bwd_saved can skip that kernel.  The pages'
+ * fused kernel likewise keeps the forward's states for its backward instead
+ * of recomputing them, at the price of extra HBM writes ("Model Architecture
+ * Walkthrough", sections 6.5 and 6.8); here one state per 64-token chunk is
+ * kept, not one per token.
+ *
+ * Arguments as gdn_fwd's, without flags, plus workspace / workspace_bytes:
+ * a DEVICE buffer of at least gdn_bwd_workspace_size(B, T, H, dk, dv,
+ * cu_seqlens != NULL) bytes, 16-byte aligned, owned by the caller; its
+ * records stay valid for gdn_bwd_saved on the same inputs until the buffer
+ * is written again.  Only the full-width shapes have records: GDN_BF16 with
+ * dk = dv = 128 and 64-token chunks (chunk 0 or 64); other valid requests
+ * return GDN_ERR_UNSUPPORTED and launch nothing (use gdn_fwd and gdn_bwd).
+ * Errors and the rest of the behaviour are gdn_fwd's.
+ */
+int gdn_fwd_train(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  void* out, float* hT, int B, int T, int H, int dk, int dv,
+                  void* stream, int dtype, int chunk, void* workspace,
+                  long long workspace_bytes);
+
+/*
+ * gdn_bwd_saved -- gdn_bwd for a workspace that already holds the records
+ * gdn_fwd_train wrote for the same q, k, v, g, beta, h0 and cu_seqlens (the
+ * caller's promise: other inputs give wrong gradients): gdn_bwd without its
+ * first kernel.  Arguments, layouts and results are gdn_bwd's; the
+ * gradients equal gdn_bwd's bit for bit, except after a gdn_fwd_train call
+ * whose hT aliased h0 (its records then come from an uncut recurrence and
+ * the gradients differ within rounding).  Only the full-width shapes
+ * (GDN_BF16, dk = dv = 128, a 16-byte-aligned workspace) are accepted;
+ * other valid requests return GDN_ERR_UNSUPPORTED and launch nothing.
+ */
+int gdn_bwd_saved(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  const void* dout, const float* dhT, void* dq, void* dk, void* dv,
+                  float* dg, float* dbeta, float* dh0, void* workspace,
+                  long long workspace_bytes, int B, int T, int H, int dk_, int dv_,
+                  void* stream, int dtype);
+
+/*
  * gdn_bwd_workspace_size -- bytes of workspace gdn_bwd needs for these sizes
  * (packed != 0: T is the total token count of a packed batch of B
  * sequences).  Returns a negative status for sizes gdn_bwd rejects.

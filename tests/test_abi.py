@@ -23,9 +23,9 @@ def _declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["gdn_bwd", "gdn_bwd_noalloc", "gdn_bwd_workspace_size", "gdn_diag_fwd",
-                                     "gdn_diag_fwd_recurrent", "gdn_fwd", "gdn_fwd_recurrent",
-                                     "gdn_fwd_scan", "gdn_fwd_scan_workspace_size",
+    assert _declared_functions() == ["gdn_bwd", "gdn_bwd_noalloc", "gdn_bwd_saved", "gdn_bwd_workspace_size",
+                                     "gdn_diag_fwd", "gdn_diag_fwd_recurrent", "gdn_fwd", "gdn_fwd_recurrent",
+                                     "gdn_fwd_scan", "gdn_fwd_scan_workspace_size", "gdn_fwd_train",
                                      "gdn_strerror", "gdn_version"]
 
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert gdn.version() == 200
+    assert gdn.version() == 300
     for code in (OK, INVALID, UNSUPPORTED, LAUNCH, -4, 12345):
         assert isinstance(gdn.strerror(code), str) and gdn.strerror(code)
 
@@ -281,6 +281,48 @@ def test_bwd_exact_workspace_accepted_without_launch():
     """The exact workspace size passes validation; B = 0 launches nothing."""
     need = gdn.gdn_bwd_workspace_size(0, 8, 1, 32, 32, 0)
     assert _bcall(B=0, workspace_bytes=need) == OK
+
+
+# -------------------------------------------- training forward / saved bwd --
+
+def _tcall(**kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, out=P, hT=P, B=1, T=8, H=1, dk=128,
+             dv=128, stream=None, dtype=1, chunk=0, workspace=P, workspace_bytes=1 << 40)
+    a.update(kw)
+    return gdn.gdn_fwd_train(**a)
+
+
+def test_fwd_train_only_for_the_full_width_shapes():
+    """Records exist for bf16 with dk = dv = 128 and 64-token chunks only;
+    every other valid request is refused before anything is launched."""
+    assert _tcall(dtype=0, chunk=16) == UNSUPPORTED
+    assert _tcall(dk=64, dv=64) == UNSUPPORTED
+    assert _tcall(chunk=32) == UNSUPPORTED
+    assert _tcall(B=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [(dict(q=0), INVALID), (dict(hT=0), INVALID), (dict(B=-1), INVALID),
+                                     (dict(workspace=0), INVALID), (dict(workspace=P + 8), INVALID),
+                                     (dict(workspace_bytes=gdn.gdn_bwd_workspace_size(1, 8, 1, 128, 128, 0) - 1),
+                                      INVALID), (dict(chunk=48), INVALID)])
+def test_fwd_train_rejects(kw, code):
+    assert _tcall(**kw) == code
+
+
+def test_bwd_saved_only_for_the_full_width_shapes():
+    a = dict(dk_=128, dv_=128, workspace_bytes=1 << 40)
+    assert gdn.gdn_bwd_saved(**{**_bargs(), **a, "dtype": 0}) == UNSUPPORTED
+    assert gdn.gdn_bwd_saved(**{**_bargs(), "dk_": 64, "dv_": 64}) == UNSUPPORTED
+    assert gdn.gdn_bwd_saved(**{**_bargs(), **a, "workspace": P + 8}) == UNSUPPORTED
+    assert gdn.gdn_bwd_saved(**{**_bargs(), **a, "workspace": 0}) == INVALID
+    assert gdn.gdn_bwd_saved(**{**_bargs(), **a, "q": 0}) == INVALID
+    assert gdn.gdn_bwd_saved(**{**_bargs(), **a, "B": 0}) == OK
+
+
+def _bargs():
+    return dict(q=P, k=P, v=P, g=P, beta=P, h0=0, cu_seqlens=0, dout=P, dhT=0, dq=P, dk=P, dv=P,
+                dg=P, dbeta=P, dh0=0, workspace=P, workspace_bytes=1 << 40, B=1, T=8, H=1, dk_=32,
+                dv_=32, stream=None, dtype=1)
 
 
 # ---------------------------------------------------- no-allocation backward --
