@@ -45,6 +45,14 @@ def load():
         if not os.path.exists(_LIB_PATH):
             raise OSError(f"{_LIB_PATH} is missing: build it with "
                           "`python -m gated_deltanet_recurrence_delta_amd.build`")
+        # torch first: libgdn.so names the HIP runtime by its soname, and the
+        # process must hold one runtime.  Loaded before torch, the library
+        # would bring in the system ROCm's copy next to torch's own, and its
+        # launches fail.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int

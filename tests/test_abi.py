@@ -301,11 +301,14 @@ def test_fwd_train_only_for_the_full_width_shapes():
     assert _tcall(B=0) == OK
 
 
+# (parameters hold no library calls: nothing may load libgdn.so while the
+# tests are collected, before torch has brought up its HIP runtime)
 @pytest.mark.parametrize("kw,code", [(dict(q=0), INVALID), (dict(hT=0), INVALID), (dict(B=-1), INVALID),
                                      (dict(workspace=0), INVALID), (dict(workspace=P + 8), INVALID),
-                                     (dict(workspace_bytes=gdn.gdn_bwd_workspace_size(1, 8, 1, 128, 128, 0) - 1),
-                                      INVALID), (dict(chunk=48), INVALID)])
+                                     (dict(workspace_bytes="one short"), INVALID), (dict(chunk=48), INVALID)])
 def test_fwd_train_rejects(kw, code):
+    if kw.get("workspace_bytes") == "one short":
+        kw = dict(kw, workspace_bytes=gdn.gdn_bwd_workspace_size(1, 8, 1, 128, 128, 0) - 1)
     assert _tcall(**kw) == code
 
 
