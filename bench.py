@@ -496,7 +496,7 @@ def bwd_main(args):
                    "rotated_sets": len(sets), "workspace_bytes": need},
         "roofline": {"bound": "mfma" if full else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                     "kernel": ("gdn_bwd, its three kernels (states, adjoint, grad) of one call, bf16 matrix cores"
+                     "kernel": ("gdn_bwd, its four kernels (states, adjoint, grad, dg and dbeta) of one call, bf16 matrix cores"
                                 if full else "gdn_bwd, all four kernels of one call"),
                      "algorithmic_flops": flops, "mean_launch_us": mean_s * 1e6,
                      "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,

@@ -244,16 +244,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
       asm volatile("" ::: "memory");
       const __amdgpu_buffer_rsrc_t rrec = make_rsrc(p.sv + ((cslot0 + c) * H + hh) * gdn_launch::BWD_REC_BYTES,
                                                     r >= r_store ? gdn_launch::BWD_REC_BYTES : 0);
-      // The gradient reaching this chunk's exit, transposed (value rows of
-      // 128 keys, four consecutive keys per lane and column).
+      // The gradient reaching this chunk's exit, key-major (key rows of 128
+      // values; one bf16 pair of adjacent value columns per lane and key).
       {
-        const int dt_lane = ((32 * j + 2 * n16) * DK + 8 * q4) * 2;
+        const int d_lane = (8 * q4 * DV + 32 * j + 2 * n16) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(Dacc[kb][cb])), rrec,
-                                                  dt_lane + (cb * DK + 32 * (kb >> 1) + 4 * (kb & 1)) * 2,
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(cvt_pair(Dacc[kb][0][e], Dacc[kb][1][e]), rrec,
+                                                  d_lane + (32 * (kb >> 1) + 4 * (kb & 1) + e) * DV * 2,
                                                   (int)gdn_launch::BWD_OFF_DM, 0);
       }
 
@@ -715,58 +715,40 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
 }
 
 // ====================================================================
-// gradient kernel
+// gradient kernels
 //
-// One workgroup per (chunk slot, head), eight waves.  From the saved M^T,
-// dM'^T (staged in LDS), U and dX (read as operands from the record), and
-// the chunk's q, k (LDS), v and dO:
-//   phase 1 (64 x 64 blocks of the lower triangle): S = K K^T, Q K^T,
-//       dX U^T and dO U^T; then G = dA . E . beta_i and dP . E (bf16 tiles,
-//       rows in pi order), and the row and column sums of Z and the row sums
-//       of dA . (S . E) per block;
-//   phase 2 (dq and dk, transposed 16 x 16 tiles: keys by tokens): wave w
-//       takes the tokens of row block w & 3 and the keys of column blocks
-//       4 (w >> 2) .. +3;
-//   phase 3: the per-token sums, dg (a reverse sum over the chunk) and dbeta.
-// A key-side operand (rows = keys) comes from LDS by transposing reads, a
-// token-side one (rows = tokens) from the record, v and dO (natural value
-// order) or from the bf16 tiles (pi token order).
+// gdn_grad_kernel: one workgroup per (chunk slot, head), four waves, wave w
+// owning the tokens of row block w.  From the saved M and dM' (key-major,
+// read as operands from the record), U and dX (read as operands), and the
+// chunk's q, k (LDS), v and dO:
+//   phase 1 (the 64 x 64 blocks (w, b) of the lower triangle, b <= w): S =
+//       K K^T, Q K^T, dX U^T and dO U^T; then G = dA . E . beta_i and
+//       dP . E (bf16 tiles, rows in pi order), and the row and column sums
+//       of Z and the row sums of dA . (S . E) per block;
+//   phase 2 (dq and dk as transposed 16 x 16 tiles, keys by tokens, over
+//       the eight key blocks; M and dM' fragments loaded a block ahead),
+//       dv, and the per-token sums over the keys.
+// The per-token sums go to a small block per (chunk slot, head) after the
+// backward records; gdn_grad_sums_kernel forms dg (a reverse sum over the
+// chunk) and dbeta from them.  A key-side operand (rows = keys) comes from
+// the record (M, dM') or from LDS by transposing reads (q, k); a token-side
+// one (rows = tokens) from the record, v and dO (natural value order) or
+// from the bf16 tiles (pi token order).
+//
+// Two workgroups share a CU (51 KB of LDS and at most 256 VGPRs per wave):
+// one's loads overlap the other's products.
 namespace gk {
-constexpr int NWG = 8;
-constexpr int MT_BYTES = DV * DK * 2;  // M^T or dM'^T, value rows of 256 bytes
-constexpr int MT_INS = MT_BYTES / 1024;
+constexpr int NWG = 4;  // waves per gradient workgroup
+constexpr int NSW = 4;  // waves (heads) per dg / dbeta workgroup
 }  // namespace gk
 
-// Granule permutation of the M^T / dM'^T tiles: the transposing reads take
-// eight rows 32 s + 8 q + (0..3 or 4..7) of two lane groups; this keeps
-// their sixteen granules distinct.
-__device__ static inline int swz_m(int r) { return swz_kq<GR>(r & 7) ^ (2 * ((r >> 3) & 1)); }
-
-__global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_launch::BwdParams p) {
-  using MM = Mma<__bf16>;
-  using F = bf16x8;
-  constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ __attribute__((aligned(16))) char sQ[KQ_BYTES];
-  __shared__ __attribute__((aligned(16))) char sK[KQ_BYTES];
-  __shared__ __attribute__((aligned(16))) char sMT[gk::MT_BYTES];
-  __shared__ __attribute__((aligned(16))) char sDT[gk::MT_BYTES];
-  __shared__ __attribute__((aligned(16))) char sPE[CC_BYTES];  // dP . E, rows in pi order
-  __shared__ __attribute__((aligned(16))) char sG[CC_BYTES];   // G = dA . E . beta_i, rows in pi order
-  __shared__ __attribute__((aligned(16))) float sVEC[NF * C];
-  __shared__ __attribute__((aligned(16))) float sGB[2 * C];
-  __shared__ float sZr[NB * NB][16], sZc[NB * NB][16], sBr[NB * NB][16];
-  __shared__ float sSum[3][2][C];  // dO M^T . q, dX M^T . k, U dM'^T . k per token, per key half
-  __shared__ float sXV[C], sGC[gk::NWG];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int q4 = lane >> 4, n16 = lane & 15;
-  const int H = p.H, hh = blockIdx.y;
-  const long sigma = blockIdx.x;
-
-  // ---------------------------------------------------- which chunk
-  // the sequence n owning slot sigma: the largest n with
-  // floor(start_n / C) + n <= sigma (slots of a sequence are consecutive)
+// The chunk that slot sigma holds: sequence n is the largest with
+// floor(start_n / C) + n <= sigma (slots of a sequence are consecutive).
+struct SlotChunk {
+  long t0;   // first token row
+  int Lc;    // tokens of the chunk (0: a slot no chunk uses)
+};
+__device__ static inline SlotChunk slot_chunk(const gdn_launch::BwdParams& p, long sigma) {
   auto start_of = [&](int n) { return p.cu ? (long)p.cu[n] : (long)n * p.T; };
   int lo = 0, hi = p.B - 1;
   while (lo < hi) {
@@ -778,21 +760,42 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
   const long start = start_of(n);
   const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
   const int c = (int)(sigma - (start / C + n));
-  if (c < 0 || (long)c * C >= len) return;  // a slot no chunk uses (uniform)
-  const long t0 = start + (long)c * C;     // first token row
-  const int Lc = min(C, len - c * C);      // tokens of this chunk
+  if (c < 0 || (long)c * C >= len) return SlotChunk{0, 0};
+  return SlotChunk{start + (long)c * C, min(C, len - c * C)};
+}
+
+__global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_launch::BwdParams p) {
+  using MM = Mma<__bf16>;
+  using F = bf16x8;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) char sQ[KQ_BYTES];
+  __shared__ __attribute__((aligned(16))) char sK[KQ_BYTES];
+  __shared__ __attribute__((aligned(16))) char sPE[CC_BYTES];  // dP . E, rows in pi order
+  __shared__ __attribute__((aligned(16))) char sG[CC_BYTES];   // G = dA . E . beta_i, rows in pi order
+  __shared__ __attribute__((aligned(16))) float sVEC[NF * C];
+  __shared__ __attribute__((aligned(16))) float sGB[2 * C];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4, n16 = lane & 15;
+  const int H = p.H, hh = blockIdx.y;
+  const long sigma = blockIdx.x;
+  const SlotChunk sc = slot_chunk(p, sigma);
+  if (sc.Lc == 0) return;  // a slot no chunk uses (uniform)
+  const long t0 = sc.t0;
+  const int Lc = sc.Lc;
   const long kq_stride = (long)H * KQR;
   const long v_stride = (long)H * DV * 2;
   const char* rec = p.sv + (sigma * H + hh) * gdn_launch::BWD_REC_BYTES;
+  float* sums = reinterpret_cast<float*>(p.sv + (long)p.nchunk * H * gdn_launch::BWD_REC_BYTES) +
+                (sigma * H + hh) * gdn_launch::BWD_SUM_FLOATS;
 
   // ---------------------------------------------------- phase 0: loads
-  // In order: q and k (16 copies each; wave w issues [4 w, 4 w + 4) of the
-  // 32), g and beta, this wave's operands in registers, then M^T and dM'^T
-  // (32 copies each; wave w issues [8 w, 8 w + 8) of the 64), which only
-  // phase 2 reads: phase 1 starts once all but those last GK_LATE copies
-  // of each wave have landed.
-  constexpr int GK_QK = 2 * KQ_INS / gk::NWG, GK_LATE = 2 * gk::MT_INS / gk::NWG;
-  static_assert(GK_QK * gk::NWG == 2 * KQ_INS && GK_LATE * gk::NWG == 2 * gk::MT_INS, "copies per wave");
+  // q and k (16 copies each; wave w issues [8 w, 8 w + 8) of the 32), g and
+  // beta, then this wave's operands in registers: phase 1 starts once the
+  // copies have landed in every wave.
+  constexpr int GK_QK = 2 * KQ_INS / gk::NWG;
+  static_assert(GK_QK * gk::NWG == 2 * KQ_INS, "copies per wave");
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (t0 * H + hh) * KQR, (long)Lc * kq_stride);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (t0 * H + hh) * KQR, (long)Lc * kq_stride);
@@ -809,15 +812,14 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
                    lane * H * 4);
     }
   }
+  asm volatile("" ::: "memory");  // the register loads below are issued after the copies
   // token-side operands of this wave: rows 16 ib + n16, values 32 s + 8 q4 .. +7
-  const int ib = wave & 3, half = wave >> 2;
+  const int ib = wave;
   const int irow = 16 * ib + n16;
   F dOr[NKS], dXr[NKS], Ur[NKS];
-  uint32_t Vr[NKS][4];
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, gdn_launch::BWD_REC_BYTES);
   {
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + (t0 * H + hh) * DV * 2, (long)Lc * v_stride);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (t0 * H + hh) * DV * 2, (long)Lc * v_stride);
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, gdn_launch::BWD_REC_BYTES);
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int col = (32 * s + 8 * q4) * 2;
@@ -826,39 +828,34 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
           F, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)gdn_launch::BWD_OFF_DX + irow * DV * 2 + col, 0, 0));
       Ur[s] = __builtin_bit_cast(
           F, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)gdn_launch::BWD_OFF_U + irow * DV * 2 + col, 0, 0));
-      const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(irow * v_stride) + col, 0, 0);
-      Vr[s][0] = vv[0]; Vr[s][1] = vv[1]; Vr[s][2] = vv[2]; Vr[s][3] = vv[3];
     }
   }
-  // U rows of the phase-1 column blocks b2 in {half, half + 2}, b2 <= ib
-  F Uc[2][NKS];
-  {
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, gdn_launch::BWD_REC_BYTES);
+  // U rows of the phase-1 column blocks b2 < ib (past the record's end,
+  // reading zeros without a fetch, for b2 >= ib; block ib is Ur)
+  F Uc[NB - 1][NKS];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int jrow = 16 * (half + 2 * x) + n16;
+  for (int b2 = 0; b2 < NB - 1; ++b2) {
+    const int base = b2 < ib ? (int)gdn_launch::BWD_OFF_U + (16 * b2 + n16) * DV * 2 : (int)gdn_launch::BWD_REC_BYTES;
 #pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        Uc[x][s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rr, (int)gdn_launch::BWD_OFF_U + jrow * DV * 2 + (32 * s + 8 * q4) * 2, 0, 0));
-    }
+    for (int s = 0; s < NKS; ++s)
+      Uc[b2][s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rr, base + (32 * s + 8 * q4) * 2, 0, 0));
   }
-  {
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(rec, gdn_launch::BWD_OFF_U);
+  // key-side M and dM' rows of phase 2's first key block
+  F Mc[NKS], Dc[NKS];
+  auto load_md = [&](int ab) {
 #pragma unroll
-    for (int x = 0; x < GK_LATE; ++x) {
-      const int i = GK_LATE * wave + x;
-      const int ii = i % gk::MT_INS, r = ii * KQ_RPI + lane / GR;
-      const bool dm = i >= gk::MT_INS;
-      const int so = (int)(dm ? gdn_launch::BWD_OFF_DM : gdn_launch::BWD_OFF_M) + r * KQR +
-                     16 * ((lane % GR) ^ swz_m(r));
-      copy_to_lds(rm, (dm ? sDT : sMT) + ii * 1024, so);
+    for (int s = 0; s < NKS; ++s) {
+      const int off = ((16 * ab + n16) * DV + 32 * s + 8 * q4) * 2;
+      Mc[s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)gdn_launch::BWD_OFF_M + off, 0, 0));
+      Dc[s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)gdn_launch::BWD_OFF_DM + off, 0, 0));
     }
-  }
-  // everything but the M^T / dM'^T copies has landed, in every wave (a
-  // plain barrier: an LDS fence would also wait for those copies)
-  static_assert(GK_LATE <= 15, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(GK_LATE) : "memory");
+  };
+  load_md(0);
+  // the copies have landed, in every wave; the register loads (3 NKS + (NB
+  // - 1) NKS + 2 NKS of them) may still be in flight
+  constexpr int GK_REG = (3 + NB - 1 + 2) * NKS;
+  static_assert(GK_REG <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(GK_REG) : "memory");
   if (wave == 0) {
     // per-token vectors (as the forward's loader)
     const float lam = wave_prefix_sum(sGB[lane] * kLog2e, lane);
@@ -897,17 +894,17 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       Qb1[s] = lds_at<F>(sQ + kq_frag[s] + 16 * KQR * b1);
     }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int b2 = half + 2 * x;
+    for (int b2 = 0; b2 < NB; ++b2) {
       if (b2 > b1) continue;
       f32x4 S = zero4, QK = zero4, XU = zero4, OU = zero4;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         const F kb2 = lds_at<F>(sK + kq_frag[s] + 16 * KQR * b2);
+        const F ub = (b2 == NB - 1 || b2 == b1) ? Ur[s] : Uc[b2 < NB - 1 ? b2 : 0][s];
         S = MM::mma(kb2, Kb1[s], S);
         QK = MM::mma(kb2, Qb1[s], QK);
-        XU = MM::mma(Uc[x][s], dXr[s], XU);
-        OU = MM::mma(Uc[x][s], dOr[s], OU);
+        XU = MM::mma(ub, dXr[s], XU);
+        OU = MM::mma(ub, dOr[s], OU);
       }
       // lane: row i, columns j = 16 b2 + 4 q4 + e
       f32x4 E;
@@ -938,46 +935,31 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       const int toff = i * CCR + 16 * ((4 * (b2 >> 1) + q4) ^ swz_cc<C>(i)) + 8 * (b2 & 1);
       lds_st<bf16x4>(sPE, toff, cvt4(PEv));
       lds_st<bf16x4>(sG, toff, cvt4(Gv));
-      // row sums over the block's 16 columns (the four lane groups), column
-      // sums over its 16 rows (the sixteen lanes of a group)
-      zr += __shfl_xor(zr, 16);
-      zr += __shfl_xor(zr, 32);
-      br += __shfl_xor(br, 16);
-      br += __shfl_xor(br, 32);
+      {
+        // row sums over the block's 16 columns (the four lane groups), column
+        // sums over its 16 rows (the sixteen lanes of a group)
+        zr += __shfl_xor(zr, 16);
+        zr += __shfl_xor(zr, 32);
+        br += __shfl_xor(br, 16);
+        br += __shfl_xor(br, 32);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int d = 1; d < 16; d <<= 1) zc[e] += __shfl_xor(zc[e], d);
-      const int blk = b1 * NB + b2;
-      if (q4 == 0) {
-        sZr[blk][n16] = zr;
-        sBr[blk][n16] = br;
-      }
-      if (n16 == 0) {
+          for (int d = 1; d < 16; d <<= 1) zc[e] += __shfl_xor(zc[e], d);
+        const int blk = b1 * NB + b2;
+        if (q4 == 0) {
+          sums[gdn_launch::BWD_SUM_ZR + blk * 16 + n16] = zr;
+          sums[gdn_launch::BWD_SUM_BR + blk * 16 + n16] = br;
+        }
+        if (n16 == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sZc[blk][4 * q4 + e] = zc[e];
+          for (int e = 0; e < 4; ++e) sums[gdn_launch::BWD_SUM_ZC + blk * 16 + 4 * q4 + e] = zc[e];
+        }
       }
     }
   }
-  // the M^T / dM'^T copies of every wave have landed
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  {
-    // <M, dM'> over the whole state (the last token's Gam_C term)
-    float acc = 0.f;
-    const int base = threadIdx.x * 64;  // 64 bytes of each tile per thread
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const u32x4 a = lds_ld<u32x4>(sMT, base + 16 * x), b = lds_ld<u32x4>(sDT, base + 16 * x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
-        acc = __builtin_fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    if (lane == 0) sGC[wave] = acc;
-  }
+  // the tiles are complete
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // ---------------------------------------------------- phase 2
   {
@@ -1016,28 +998,27 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       GTr[ts] = gt;
     }
     const float gi = vec[F_GAM * C + irow], wi = vec[F_W * C + irow], bgi = vec[F_BETA * C + irow] * gi;
-    float sq_ = 0.f, sx_ = 0.f, sw_ = 0.f;
+    float sq_ = 0.f, sx_ = 0.f, sw_ = 0.f, gc = 0.f;
     const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dq + (t0 * H + hh) * KQR, (long)Lc * kq_stride);
     const __amdgpu_buffer_rsrc_t rdk = make_rsrc(p.dk + (t0 * H + hh) * KQR, (long)Lc * kq_stride);
+#pragma unroll 1
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int ab = 4 * half + m;
-      // key-side operands, rows a = 16 ab + n16 (transposing reads)
-      const int mg = 2 * ab + ((n16 & 3) >> 1), mh = 8 * (n16 & 1);
+    for (int m = 0; m < NKB / 2; ++m) {
+      const int ab = NKB / 2 * hf + m;
+      // key-side operands, rows a = 16 ab + n16: M and dM' (loaded a block
+      // ahead), k and q (transposing reads)
       F MTa[NKS], DTa[NKS], KTa[NTS], QTa[NTS];
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const int v0 = 32 * s + 8 * q4 + (n16 >> 2), v1 = v0 + 4;
-        const bf16x4 m0 = lds_read_tr(sMT, v0 * KQR + 16 * (mg ^ swz_m(v0)) + mh);
-        const bf16x4 m1 = lds_read_tr(sMT, v1 * KQR + 16 * (mg ^ swz_m(v1)) + mh);
-        const bf16x4 d0 = lds_read_tr(sDT, v0 * KQR + 16 * (mg ^ swz_m(v0)) + mh);
-        const bf16x4 d1 = lds_read_tr(sDT, v1 * KQR + 16 * (mg ^ swz_m(v1)) + mh);
-        MTa[s] = F{m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-        DTa[s] = F{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        MTa[s] = Mc[s];
+        DTa[s] = Dc[s];
       }
+      if (ab + 1 < NKB) load_md(ab + 1);
 #pragma unroll
       for (int ts = 0; ts < NTS; ++ts) {
         const int jl = 32 * ts + 4 * q4 + (n16 >> 2), jh = jl + 16;
+        const int mg = 2 * ab + ((n16 & 3) >> 1), mh = 8 * (n16 & 1);
         const bf16x4 kl = lds_read_tr(sK, jl * KQR + 16 * (mg ^ swz_kq<GR>(jl)) + mh);
         const bf16x4 kh = lds_read_tr(sK, jh * KQR + 16 * (mg ^ swz_kq<GR>(jh)) + mh);
         const bf16x4 ql = lds_read_tr(sQ, jl * KQR + 16 * (mg ^ swz_kq<GR>(jl)) + mh);
@@ -1051,6 +1032,13 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
         aQ = MM::mma(MTa[s], dOr[s], aQ);
         aXM = MM::mma(MTa[s], dXr[s], aXM);
         aUD = MM::mma(DTa[s], Ur[s], aUD);
+      }
+      if (m == ib) {
+        // <M, dM'> over this wave's 32 keys (all four waves: all 128)
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gc = __builtin_fmaf((float)MTa[s][e], (float)DTa[s][e], gc);
       }
       // lane: token irow, keys 16 ab + 4 q4 + e; q and k of them
       const int kgo = irow * KQR + 16 * ((2 * ab + (q4 >> 1)) ^ swz_kq<GR>(irow)) + 8 * (q4 & 1);
@@ -1079,7 +1067,7 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(aQ)), rdq, so, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(aK)), rdk, so, 0, 0);
     }
-    // per-token sums: over the four lane groups, then one value per half
+    // per-token sums over the keys: over the four lane groups
 #pragma unroll
     for (int d = 16; d <= 32; d <<= 1) {
       sq_ += __shfl_xor(sq_, d);
@@ -1087,12 +1075,23 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       sw_ += __shfl_xor(sw_, d);
     }
     if (q4 == 0) {
-      sSum[0][half][irow] = sq_;
-      sSum[1][half][irow] = sx_;
-      sSum[2][half][irow] = sw_;
+      float* s3 = sums + gdn_launch::BWD_SUM_S3;
+      s3[irow] = sq_;
+      s3[C + irow] = sx_;
+      s3[2 * C + irow] = sw_;
     }
-    if (half == 0) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) gc += __shfl_xor(gc, d);
+    if (lane == 0) sums[gdn_launch::BWD_SUM_GC + ib] = gc;
+    {
       // dv = diag(beta) dX (rows irow, values 32 s + 8 q4 .. +7), and dX . v
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (t0 * H + hh) * DV * 2, (long)Lc * v_stride);
+      uint32_t Vr[NKS][4];
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(irow * v_stride) + (32 * s + 8 * q4) * 2, 0, 0);
+        Vr[s][0] = vv[0]; Vr[s][1] = vv[1]; Vr[s][2] = vv[2]; Vr[s][3] = vv[3];
+      }
       const float bt = vec[F_BETA * C + irow];
       const __amdgpu_buffer_rsrc_t rdv = make_rsrc(p.dv + (t0 * H + hh) * DV * 2, (long)Lc * v_stride);
       float xv = 0.f;
@@ -1112,53 +1111,69 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
       }
       xv += __shfl_xor(xv, 16);
       xv += __shfl_xor(xv, 32);
-      if (q4 == 0) sXV[irow] = xv;
+      if (q4 == 0) sums[gdn_launch::BWD_SUM_XV + irow] = xv;
     }
   }
-  __syncthreads();
+}
 
-  // ---------------------------------------------------- phase 3
-  if (wave == 0) {
-    const int t = lane, tb = t >> 4, tr = t & 15, last = Lc - 1;
-    float rz = 0.f, cz = 0.f, b2 = 0.f;
+// dg and dbeta: one wave per (chunk slot, head), from the gradient kernel's
+// per-token sums and the chunk's g and beta.  Fixed addition order
+// throughout: deterministic.
+__global__ __launch_bounds__(64 * gk::NSW) void gdn_grad_sums_kernel(const gdn_launch::BwdParams p) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int t = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = p.H, hh = blockIdx.y * gk::NSW + wave;
+  const long sigma = blockIdx.x;
+  if (hh >= H) return;  // uniform per wave; no barrier below
+  const SlotChunk sc = slot_chunk(p, sigma);
+  if (sc.Lc == 0) return;
+  const long t0 = sc.t0;
+  const int Lc = sc.Lc;
+  const float* sums = reinterpret_cast<const float*>(p.sv + (long)p.nchunk * H * gdn_launch::BWD_REC_BYTES) +
+                      (sigma * H + hh) * gdn_launch::BWD_SUM_FLOATS;
+  const long th = (t0 + t) * H + hh;
+  const float gt = t < Lc ? p.g[th] : 0.f;
+  const float bt = t < Lc ? p.beta[th] : 0.f;
+  const float lam = wave_prefix_sum(gt * kLog2e, t);
+  const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), C - 1));
+  const float Gt = exp2_fast(lam), wt = exp2_fast(lamC - lam);
+  const int tb = t >> 4, tr = t & 15, last = Lc - 1;
+  float rz = 0.f, cz = 0.f, b2 = 0.f;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b <= tb) {
-        rz += sZr[tb * NB + b][tr];
-        b2 += sBr[tb * NB + b][tr];
-      }
-      if (b >= tb) cz += sZc[b * NB + tb][tr];
+  for (int b = 0; b < NB; ++b) {
+    if (b <= tb) {
+      rz += sums[gdn_launch::BWD_SUM_ZR + (tb * NB + b) * 16 + tr];
+      b2 += sums[gdn_launch::BWD_SUM_BR + (tb * NB + b) * 16 + tr];
     }
-    float gc = 0.f;
+    if (b >= tb) cz += sums[gdn_launch::BWD_SUM_ZC + (b * NB + tb) * 16 + tr];
+  }
+  float gc = 0.f;
 #pragma unroll
-    for (int w = 0; w < gk::NWG; ++w) gc += sGC[w];
-    const float Gt = vec[F_GAM * C + t], wt = vec[F_W * C + t], bt = vec[F_BETA * C + t];
-    const float sQv = sSum[0][0][t] + sSum[0][1][t];
-    const float sXv = sSum[1][0][t] + sSum[1][1][t];
-    const float sWv = sSum[2][0][t] + sSum[2][1][t];
-    const float dGam = __builtin_fmaf(-bt, sXv, sQv) + (t == last ? gc : 0.f);
-    const float dbeta = __builtin_fmaf(-Gt, sXv, sXV[t]) + b2;
-    const float dgam = t < Lc ? __builtin_fmaf(dGam, Gt, rz - cz) : 0.f;  // dgamma without the w terms
-    const float dww = t < Lc ? sWv * wt : 0.f;                              // dw . w
-    // dg_t = sum_{u >= t} dgamma_u; the w terms (-dw_u w_u at every token,
-    // +sum_u dw_u w_u at the last) enter as they add up after the reverse
-    // sum, sum_{u < t} dw_u w_u, which cancels nothing large under strong
-    // decay.  The suffix sum is a prefix sum over the lanes in reverse
-    // order, the exclusive prefix sum an inclusive one moved up a lane:
-    // neither subtracts a total (fixed addition order: deterministic).
-    const float rev = __shfl(dgam, C - 1 - t);
-    const float suf = __shfl(wave_prefix_sum(rev, t), C - 1 - t);
-    const float inc = wave_prefix_sum(dww, t);
-    // every lane takes part in the cross-lane read (a lane left out of it
-    // would not supply its value to the next one), then lane 0 drops it
-    const float prev = __shfl(inc, (t + C - 1) & (C - 1));
-    const float exc = t > 0 ? prev : 0.f;
-    const float acc = suf + exc;
-    if (t < Lc) {
-      const long th = (t0 + t) * H + hh;
-      p.dg[th] = acc;
-      p.dbeta[th] = dbeta;
-    }
+  for (int w = 0; w < gk::NWG; ++w) gc += sums[gdn_launch::BWD_SUM_GC + w];
+  const float* s3 = sums + gdn_launch::BWD_SUM_S3;
+  const float sQv = s3[t], sXv = s3[C + t], sWv = s3[2 * C + t];
+  const float dGam = __builtin_fmaf(-bt, sXv, sQv) + (t == last ? gc : 0.f);
+  const float dbeta = __builtin_fmaf(-Gt, sXv, sums[gdn_launch::BWD_SUM_XV + t]) + b2;
+  const float dgam = t < Lc ? __builtin_fmaf(dGam, Gt, rz - cz) : 0.f;  // dgamma without the w terms
+  const float dww = t < Lc ? sWv * wt : 0.f;                              // dw . w
+  // dg_t = sum_{u >= t} dgamma_u; the w terms (-dw_u w_u at every token,
+  // +sum_u dw_u w_u at the last) enter as they add up after the reverse
+  // sum, sum_{u < t} dw_u w_u, which cancels nothing large under strong
+  // decay.  The suffix sum is a prefix sum over the lanes in reverse
+  // order, the exclusive prefix sum an inclusive one moved up a lane:
+  // neither subtracts a total (fixed addition order: deterministic).
+  const float rev = __shfl(dgam, C - 1 - t);
+  const float suf = __shfl(wave_prefix_sum(rev, t), C - 1 - t);
+  const float inc = wave_prefix_sum(dww, t);
+  // every lane takes part in the cross-lane read (a lane left out of it
+  // would not supply its value to the next one), then lane 0 drops it
+  const float prev = __shfl(inc, (t + C - 1) & (C - 1));
+  const float exc = t > 0 ? prev : 0.f;
+  const float acc = suf + exc;
+  if (t < Lc) {
+    p.dg[th] = acc;
+    p.dbeta[th] = dbeta;
   }
 }
 
@@ -1167,7 +1182,7 @@ __global__ __launch_bounds__(64 * gk::NWG, 1) void gdn_grad_kernel(const gdn_lau
 namespace gdn_launch {
 
 long long bwd_full_ws_bytes(int B, long ttot, int H) {
-  return (long long)((ttot / fk::C) + B) * H * BWD_REC_BYTES;
+  return (long long)((ttot / fk::C) + B) * H * (BWD_REC_BYTES + BWD_SUM_FLOATS * 4);
 }
 
 int bwd_full(const BwdParams& p, hipStream_t stream) {
@@ -1203,6 +1218,9 @@ int bwd_full(const BwdParams& p, hipStream_t stream) {
   }
   if (ngrad > 0) {
     hipLaunchKernelGGL(gdn_grad_kernel, dim3((unsigned)ngrad, (unsigned)p.H), dim3(64 * gk::NWG), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
+    hipLaunchKernelGGL(gdn_grad_sums_kernel, dim3((unsigned)ngrad, (unsigned)((p.H + gk::NSW - 1) / gk::NSW)),
+                       dim3(64 * gk::NSW), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
   }
   return GDN_OK;

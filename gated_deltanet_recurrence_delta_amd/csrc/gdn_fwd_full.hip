@@ -345,17 +345,17 @@ __global__ __launch_bounds__(64 * fk::NW, 1) void gdn_full_kernel(const gdn_laun
       if constexpr (SAVE) {
         rrec = make_rsrc(p.sv + ((cslot0 + cs + c) * H + hh) * gdn_launch::BWD_REC_BYTES,
                          c >= store_from ? gdn_launch::BWD_REC_BYTES : 0);
-        // entry state, transposed (value rows of 128 keys): lane (n16, q4)
-        // holds the four consecutive keys key_of(kb, 4 q4) .. +3 of value
-        // column 32 j + 2 n16 + cb
+        // entry state, key-major (key rows of 128 values): lane (n16, q4)
+        // holds keys key_of(kb, 4 q4) .. +3 of value columns 32 j + 2 n16
+        // (block cb = 0) and the next one (cb = 1), one bf16 pair per key
         // (one lane base; the rest is a per-instruction constant)
-        const int mt_lane = (int)gdn_launch::BWD_OFF_M + ((32 * j + 2 * n16) * DK + 8 * q4) * 2;
+        const int m_lane = (int)gdn_launch::BWD_OFF_M + (8 * q4 * DV + 32 * j + 2 * n16) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(Macc[kb][cb])), rrec,
-                                                  mt_lane + (cb * DK + 32 * (kb >> 1) + 4 * (kb & 1)) * 2, 0, 0);
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(cvt_pair(Macc[kb][0][e], Macc[kb][1][e]), rrec,
+                                                  m_lane + (32 * (kb >> 1) + 4 * (kb & 1) + e) * DV * 2, 0, 0);
       }
       const char* sk = sK + (c % NKR) * KQ_BYTES;
       const char* sq = sQ + (c % NQR) * KQ_BYTES;

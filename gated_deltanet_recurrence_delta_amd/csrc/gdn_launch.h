@@ -36,18 +36,26 @@ struct FullParams {
   // fp32 matrices, row-major: the segment's map P and Q (M_end = P M_start
   // + Q) and its exact entry state S.  Null: segments start from halos.
   float* ws = nullptr;
-  // Backward-pass records (gdn_full_kernel<2> writes M and U, the adjoint
-  // kernel dM and dX): one record of BWD_REC_BYTES per (chunk slot, head),
+  // Backward-pass records (gdn_full_kernel<2> and <3> write M and U, the
+  // adjoint kernel dM and dX): one record of BWD_REC_BYTES per (chunk slot, head),
   // chunk c of the sequence whose tokens start at s taking chunk slot
   // floor(s / 64) + (sequence index) + c.  Each part is bf16 row-major.
   char* sv = nullptr;
 };
 
-// A backward record: M^T and dM^T (the chunk's entry state and the
-// gradient reaching its exit state, transposed: dv rows of dk keys), then
-// U and dX (C token rows of dv values), at these byte offsets.
+// A backward record: M and dM (the chunk's entry state and the gradient
+// reaching its exit state, key-major: dk rows of dv values), then U and dX
+// (C token rows of dv values), at these byte offsets.
 constexpr long BWD_OFF_M = 0, BWD_OFF_DM = 128 * 128 * 2, BWD_OFF_U = 2 * 128 * 128 * 2,
                BWD_OFF_DX = 2 * 128 * 128 * 2 + 64 * 128 * 2, BWD_REC_BYTES = 2 * 128 * 128 * 2 + 2 * 64 * 128 * 2;
+// After all records (nchunk x H of them), one block of BWD_SUM_FLOATS fp32
+// per (chunk slot, head): the gradient kernel's per-token partial sums for
+// dg and dbeta, at these float offsets: the row sums of Z, its column sums
+// and the row sums of dA . (S . E) for each 16 x 16 block (b1, b2), 16 each;
+// the per-token sums dO M^T . q, dX M^T . k and U dM^T . k (64 each); dX . v
+// per token; <M, dM> over each wave's keys (4).
+constexpr int BWD_SUM_ZR = 0, BWD_SUM_ZC = 256, BWD_SUM_BR = 512, BWD_SUM_S3 = 768, BWD_SUM_XV = 960,
+              BWD_SUM_GC = 1024, BWD_SUM_FLOATS = 1040;
 
 // Backward pass, bf16, dk = dv = 128, 64-token chunks (gdn_bwd_full.hip).
 struct BwdParams {
