@@ -21,8 +21,11 @@ three launches per step, timed together).
 ``--pass bwd`` times the backward entry point gdn_bwd on the same workload
 (dq, dk, dv, dg, dbeta, dh0 from seeded output gradients dout ~ N(0,1),
 dhT ~ N(0,1)); its roofline is the matrix cores' bf16 rate for bf16 storage
-with dk = dv = 128 (three full-width kernels, 64-token chunks) and fp32
-arithmetic otherwise (four fp32 kernels, 32-token chunks).
+with dk = dv = 128 (four full-width kernels, 64-token chunks) and fp32
+arithmetic otherwise (four fp32 kernels, 32-token chunks).  ``--pass train``
+times a training step for those full-width shapes: gdn_fwd_train (outputs
+plus the backward's per-chunk records) followed by gdn_bwd_saved, the
+forward's and the backward's products counted together.
 
 ``--workload hymo`` / ``hymo_decode`` time the diagonal-decay additive
 recurrence with its epilogue (gdn_diag_fwd / gdn_diag_fwd_recurrent) on the
@@ -57,6 +60,7 @@ KERNEL_SRCS = {
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
 METRIC_BWD = "gated-delta-rule bwd tokens/s + achieved fp32 TFLOP/s (% roofline), 1 MI355X"
+METRIC_TRAIN = "gated-delta-rule training step (fwd + bwd) tokens/s + achieved bf16 TFLOP/s (% roofline), 1 MI355X"
 FP32_PEAK_TFLOPS = 157.3
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores (no sparsity)
 METRIC_DIAG = ("diagonal-decay recurrence (HyMo GDN layer) fwd tokens/s + achieved HBM GB/s "
@@ -393,6 +397,16 @@ def bwd_flops_full(wl: synth.Workload, lens) -> int:
     return 2 * per_chunk * chunks * wl.H
 
 
+def fwd_flops_full(wl: synth.Workload, lens) -> int:
+    """Floating-point operations of the full-width forward (64-token chunks):
+    per chunk and head 3 C d^2 multiply-adds (K M, Q M and the state update
+    K^T W), 2 C^2 d (K K^T, Q K^T, T X and P U, each triangular, at half) and
+    C^3 / 6 (one triangular inverse); a partial chunk counts as a whole one."""
+    C, d = 64, wl.dk
+    per = 3 * C * d * wl.dv + 2 * C * C * d + C ** 3 // 6
+    return 2 * per * sum((int(n) + C - 1) // C for n in lens) * wl.H
+
+
 def bwd_flops(wl: synth.Workload, lens) -> int:
     """Floating-point operations of one gdn_bwd call as its four kernels
     compute it (32-token chunks; 2 per multiply-add).  Per chunk of L <= 32
@@ -416,12 +430,17 @@ def bwd_flops(wl: synth.Workload, lens) -> int:
 def bwd_main(args):
     """The backward pass: same protocol as ``main`` (rotated sets, HIP events
     on the launch stream around each gdn_bwd call, a CPU oracle leg on two
-    chains whose results also check those chains)."""
+    chains whose results also check those chains).  ``--pass train`` times a
+    training step instead: gdn_fwd_train (outputs and the backward's
+    records) then gdn_bwd_saved, bf16 with dk = dv = 128 only."""
     import torch
 
     import gated_deltanet_recurrence_delta_amd as gdn
 
     wl = synth.WORKLOADS[args.workload]
+    train = args.direction == "train"
+    if train and not bwd_full_width(wl):
+        raise SystemExit("--pass train needs bf16 storage with dk = dv = 128")
     inp = synth.generate(wl)
     og = synth.output_grads(inp, 1000 + wl.seed)
     B = len(inp.cu_seqlens) - 1 if inp.cu_seqlens is not None else wl.B
@@ -436,20 +455,34 @@ def bwd_main(args):
         for n, like in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta")):
             d[n] = torch.empty_like(d[like])
         d["dh0"] = torch.empty((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+        d["out"] = torch.empty_like(d["v"])
+        d["hT"] = torch.empty((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
         sets.append(d)
     stream = torch.cuda.current_stream()
-    first = gdn.bwd(sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["g"], sets[0]["beta"],
-                    sets[0]["dout"], h0=sets[0]["h0"], cu_seqlens=sets[0]["cu_seqlens"],
-                    dhT=sets[0]["dhT"], workspace=ws, stream=stream)
+    d0 = sets[0]
+    if train:
+        gdn.fwd_train(d0["q"], d0["k"], d0["v"], d0["g"], d0["beta"], d0["h0"], d0["cu_seqlens"],
+                      out=d0["out"], hT=d0["hT"], workspace=ws, stream=stream)
+    first = gdn.bwd(d0["q"], d0["k"], d0["v"], d0["g"], d0["beta"], d0["dout"], h0=d0["h0"],
+                    cu_seqlens=d0["cu_seqlens"], dhT=d0["dhT"], workspace=ws, stream=stream,
+                    saved=train)
     ptr = lambda t: 0 if t is None else t.data_ptr()
     names = ("q", "k", "v", "g", "beta", "h0", "cu_seqlens", "dout", "dhT", "dq", "dk", "dv",
              "dg", "dbeta", "dh0")
     calls = [tuple(ptr(d[n]) for n in names) for d in sets]
     dtype_code = gdn.GDN_BF16 if wl.dtype == "bf16" else gdn.GDN_F32
-    raw = gdn.load().gdn_bwd
+    raw = gdn.load().gdn_bwd_saved if train else gdn.load().gdn_bwd
     tail = (ws.data_ptr(), need, B, T, wl.H, wl.dk, wl.dv, stream.cuda_stream, dtype_code)
+    fnames = ("q", "k", "v", "g", "beta", "h0", "cu_seqlens", "out", "hT")
+    fcalls = [tuple(ptr(d[n]) for n in fnames) for d in sets]
+    raw_fwd = gdn.load().gdn_fwd_train
+    ftail = (B, T, wl.H, wl.dk, wl.dv, stream.cuda_stream, dtype_code, 0, ws.data_ptr(), need)
 
     def step(i):
+        if train:
+            rc = raw_fwd(*fcalls[i % len(fcalls)], *ftail)
+            if rc != 0:
+                raise SystemExit(f"gdn_fwd_train failed with status {rc}")
         rc = raw(*calls[i % len(calls)], *tail)
         if rc != 0:
             raise SystemExit(f"gdn_bwd failed with status {rc}")
@@ -473,10 +506,12 @@ def bwd_main(args):
     mean_s = float(launch_ms.mean()) / 1e3
     full = bwd_full_width(wl)
     flops = bwd_flops_full(wl, lens) if full else bwd_flops(wl, lens)
+    if train:
+        flops += fwd_flops_full(wl, lens)
     peak = BF16_PEAK_TFLOPS if full else FP32_PEAK_TFLOPS
     achieved = flops / mean_s / 1e12
     rec = {
-        "metric": METRIC_BWD,
+        "metric": METRIC_TRAIN if train else METRIC_BWD,
         "value": wl.tokens / (ms_per_step / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -490,14 +525,19 @@ def bwd_main(args):
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
                 "g=-softplus(N(%g,1)), dout N(0,1), dhT N(0,1))" % wl.g_mean,
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} dk={wl.dk} dv={wl.dv} "
-                               f"{wl.dtype} backward, " + ("64-token chunks" if full else "32-token chunks")
+                               f"{wl.dtype} " + ("training step (forward with records, backward from them), "
+                                                 if train else "backward, ")
+                               + ("64-token chunks" if full else "32-token chunks")
                                + (" varlen" if wl.varlen else ""),
-                   "entry_point": "gdn_bwd", "tokens_per_step": wl.tokens,
+                   "entry_point": "gdn_fwd_train + gdn_bwd_saved" if train else "gdn_bwd",
+                   "tokens_per_step": wl.tokens,
                    "rotated_sets": len(sets), "workspace_bytes": need},
         "roofline": {"bound": "mfma" if full else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                     "kernel": ("gdn_bwd, its four kernels (states, adjoint, grad, dg and dbeta) of one call, bf16 matrix cores"
-                                if full else "gdn_bwd, all four kernels of one call"),
+                     "kernel": ("gdn_fwd_train and gdn_bwd_saved, their four kernels (forward with records, "
+                                "adjoint, grad, dg and dbeta) of one step, bf16 matrix cores" if train else
+                                "gdn_bwd, its four kernels (states, adjoint, grad, dg and dbeta) of one call, "
+                                "bf16 matrix cores" if full else "gdn_bwd, all four kernels of one call"),
                      "algorithmic_flops": flops, "mean_launch_us": mean_s * 1e6,
                      "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
                      "p50_us": float(np.percentile(launch_ms, 50)) * 1e3,
@@ -556,7 +596,7 @@ def main():
     ap.add_argument("--form", choices=("chunked", "recurrent", "scan"), default=None,
                     help="entry point (default: recurrent for the decode workload, "
                          "chunked otherwise)")
-    ap.add_argument("--pass", dest="direction", choices=("fwd", "bwd"), default="fwd",
+    ap.add_argument("--pass", dest="direction", choices=("fwd", "bwd", "train"), default="fwd",
                     help="forward (default) or backward entry point")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -580,10 +620,10 @@ def main():
         sys.exit(2)
 
     if args.workload in sd.WORKLOADS:
-        if args.direction == "bwd":
+        if args.direction != "fwd":
             raise SystemExit("the diagonal-decay form has no backward entry point")
         return diag_main(args)
-    if args.direction == "bwd":
+    if args.direction in ("bwd", "train"):
         return bwd_main(args)
 
     import torch

@@ -109,3 +109,20 @@ def test_measured_traffic_follows_each_workloads_sources(tmp_path, monkeypatch):
     (tmp_path / "hymo.hip").write_text("int hymo_kernel() { return 2; }\n")  # the code changed
     assert bench.measured_traffic("hymo") is None
     assert bench.measured_traffic("wide_head") == 300.0
+
+
+def test_full_width_forward_flops():
+    """The training-step line adds the full-width forward: per chunk and
+    head 3 C d^2 dense products, four triangular C^2 d ones at half, and one
+    triangular inverse (C^3 / 6)."""
+    wl = synth.WORKLOADS["wide_head"]
+    C, d = 64, 128
+    per = 3 * C * d * d + 2 * C * C * d + C ** 3 // 6
+    assert bench.fwd_flops_full(wl, [wl.T] * wl.B) == 2 * per * 64 * wl.B * wl.H
+    assert bench.fwd_flops_full(wl, [1]) == bench.fwd_flops_full(wl, [64])
+
+
+def test_train_pass_needs_the_full_width_shapes():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pass", "train",
+                        "--workload", "small_state"], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "dk = dv = 128" in r.stderr
