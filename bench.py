@@ -21,7 +21,7 @@ three launches per step, timed together).
 ``--pass bwd`` times the backward entry point gdn_bwd on the same workload
 (dq, dk, dv, dg, dbeta, dh0 from seeded output gradients dout ~ N(0,1),
 dhT ~ N(0,1)); its roofline is the matrix cores' bf16 rate for bf16 storage
-with dk = dv = 128 (four full-width kernels, 64-token chunks) and fp32
+with dk = dv = 128 (three full-width kernels, 64-token chunks) and fp32
 arithmetic otherwise (four fp32 kernels, 32-token chunks).  ``--pass train``
 times a training step for those full-width shapes: gdn_fwd_train (outputs
 plus the backward's per-chunk records) followed by gdn_bwd_saved, the
@@ -534,9 +534,9 @@ def bwd_main(args):
                    "rotated_sets": len(sets), "workspace_bytes": need},
         "roofline": {"bound": "mfma" if full else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                     "kernel": ("gdn_fwd_train and gdn_bwd_saved, their four kernels (forward with records, "
-                                "adjoint, grad, dg and dbeta) of one step, bf16 matrix cores" if train else
-                                "gdn_bwd, its four kernels (states, adjoint, grad, dg and dbeta) of one call, "
+                     "kernel": ("gdn_fwd_train and gdn_bwd_saved, their three kernels (forward with records, "
+                                "adjoint, grad) of one step, bf16 matrix cores" if train else
+                                "gdn_bwd, its three kernels (states, adjoint, grad) of one call, "
                                 "bf16 matrix cores" if full else "gdn_bwd, all four kernels of one call"),
                      "algorithmic_flops": flops, "mean_launch_us": mean_s * 1e6,
                      "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,

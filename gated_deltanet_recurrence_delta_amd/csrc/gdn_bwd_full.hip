@@ -727,19 +727,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
 //       of Z and the row sums of dA . (S . E) per block;
 //   phase 2 (dq and dk as transposed 16 x 16 tiles, keys by tokens, over
 //       the eight key blocks; M and dM' fragments loaded a block ahead),
-//       dv, and the per-token sums over the keys.
-// The per-token sums go to a small block per (chunk slot, head) after the
-// backward records; gdn_grad_sums_kernel forms dg (a reverse sum over the
-// chunk) and dbeta from them.  A key-side operand (rows = keys) comes from
+//       dv, and the per-token sums over the keys;
+//   phase 3 (one wave): dg (a reverse sum over the chunk) and dbeta from
+//       those sums.
+// A key-side operand (rows = keys) comes from
 // the record (M, dM') or from LDS by transposing reads (q, k); a token-side
 // one (rows = tokens) from the record, v and dO (natural value order) or
 // from the bf16 tiles (pi token order).
 //
-// Two workgroups share a CU (51 KB of LDS and at most 256 VGPRs per wave):
+// Two workgroups share a CU (56 KB of LDS and at most 256 VGPRs per wave):
 // one's loads overlap the other's products.
 namespace gk {
 constexpr int NWG = 4;  // waves per gradient workgroup
-constexpr int NSW = 4;  // waves (heads) per dg / dbeta workgroup
+// Per-token partial sums for dg and dbeta (LDS, fp32 offsets): the row sums
+// of Z, its column sums and the row sums of dA . (S . E) for each 16 x 16
+// block (b1, b2), 16 each; the per-token sums dO M^T . q, dX M^T . k and
+// U dM'^T . k (64 each); dX . v per token; <M, dM'> over each wave's keys.
+constexpr int SUM_ZR = 0, SUM_ZC = 256, SUM_BR = 512, SUM_S3 = 768, SUM_XV = 960, SUM_GC = 1024,
+              SUM_FLOATS = 1028;
 }  // namespace gk
 
 // The chunk that slot sigma holds: sequence n is the largest with
@@ -774,6 +779,7 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
   __shared__ __attribute__((aligned(16))) char sG[CC_BYTES];   // G = dA . E . beta_i, rows in pi order
   __shared__ __attribute__((aligned(16))) float sVEC[NF * C];
   __shared__ __attribute__((aligned(16))) float sGB[2 * C];
+  __shared__ float sums[gk::SUM_FLOATS];  // per-token partial sums for dg and dbeta
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -787,8 +793,6 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
   const long kq_stride = (long)H * KQR;
   const long v_stride = (long)H * DV * 2;
   const char* rec = p.sv + (sigma * H + hh) * gdn_launch::BWD_REC_BYTES;
-  float* sums = reinterpret_cast<float*>(p.sv + (long)p.nchunk * H * gdn_launch::BWD_REC_BYTES) +
-                (sigma * H + hh) * gdn_launch::BWD_SUM_FLOATS;
 
   // ---------------------------------------------------- phase 0: loads
   // q and k (16 copies each; wave w issues [8 w, 8 w + 8) of the 32), g and
@@ -948,12 +952,12 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
           for (int d = 1; d < 16; d <<= 1) zc[e] += __shfl_xor(zc[e], d);
         const int blk = b1 * NB + b2;
         if (q4 == 0) {
-          sums[gdn_launch::BWD_SUM_ZR + blk * 16 + n16] = zr;
-          sums[gdn_launch::BWD_SUM_BR + blk * 16 + n16] = br;
+          sums[gk::SUM_ZR + blk * 16 + n16] = zr;
+          sums[gk::SUM_BR + blk * 16 + n16] = br;
         }
         if (n16 == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sums[gdn_launch::BWD_SUM_ZC + blk * 16 + 4 * q4 + e] = zc[e];
+          for (int e = 0; e < 4; ++e) sums[gk::SUM_ZC + blk * 16 + 4 * q4 + e] = zc[e];
         }
       }
     }
@@ -1075,14 +1079,14 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
       sw_ += __shfl_xor(sw_, d);
     }
     if (q4 == 0) {
-      float* s3 = sums + gdn_launch::BWD_SUM_S3;
+      float* s3 = sums + gk::SUM_S3;
       s3[irow] = sq_;
       s3[C + irow] = sx_;
       s3[2 * C + irow] = sw_;
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) gc += __shfl_xor(gc, d);
-    if (lane == 0) sums[gdn_launch::BWD_SUM_GC + ib] = gc;
+    if (lane == 0) sums[gk::SUM_GC + ib] = gc;
     {
       // dv = diag(beta) dX (rows irow, values 32 s + 8 q4 .. +7), and dX . v
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (t0 * H + hh) * DV * 2, (long)Lc * v_stride);
@@ -1111,69 +1115,54 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
       }
       xv += __shfl_xor(xv, 16);
       xv += __shfl_xor(xv, 32);
-      if (q4 == 0) sums[gdn_launch::BWD_SUM_XV + irow] = xv;
+      if (q4 == 0) sums[gk::SUM_XV + irow] = xv;
     }
   }
-}
+  // every wave's sums are in LDS (no wait for the global stores)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-// dg and dbeta: one wave per (chunk slot, head), from the gradient kernel's
-// per-token sums and the chunk's g and beta.  Fixed addition order
-// throughout: deterministic.
-__global__ __launch_bounds__(64 * gk::NSW) void gdn_grad_sums_kernel(const gdn_launch::BwdParams p) {
-  constexpr float kLog2e = 1.4426950408889634f;
-  const int t = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int H = p.H, hh = blockIdx.y * gk::NSW + wave;
-  const long sigma = blockIdx.x;
-  if (hh >= H) return;  // uniform per wave; no barrier below
-  const SlotChunk sc = slot_chunk(p, sigma);
-  if (sc.Lc == 0) return;
-  const long t0 = sc.t0;
-  const int Lc = sc.Lc;
-  const float* sums = reinterpret_cast<const float*>(p.sv + (long)p.nchunk * H * gdn_launch::BWD_REC_BYTES) +
-                      (sigma * H + hh) * gdn_launch::BWD_SUM_FLOATS;
-  const long th = (t0 + t) * H + hh;
-  const float gt = t < Lc ? p.g[th] : 0.f;
-  const float bt = t < Lc ? p.beta[th] : 0.f;
-  const float lam = wave_prefix_sum(gt * kLog2e, t);
-  const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), C - 1));
-  const float Gt = exp2_fast(lam), wt = exp2_fast(lamC - lam);
-  const int tb = t >> 4, tr = t & 15, last = Lc - 1;
-  float rz = 0.f, cz = 0.f, b2 = 0.f;
+  // ---------------------------------------------------- phase 3
+  if (wave == 0) {
+    const int t = lane;
+    const long th = (t0 + t) * H + hh;
+    const float Gt = vec[F_GAM * C + t], wt = vec[F_W * C + t], bt = vec[F_BETA * C + t];
+    const int tb = t >> 4, tr = t & 15, last = Lc - 1;
+    float rz = 0.f, cz = 0.f, b2 = 0.f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (b <= tb) {
-      rz += sums[gdn_launch::BWD_SUM_ZR + (tb * NB + b) * 16 + tr];
-      b2 += sums[gdn_launch::BWD_SUM_BR + (tb * NB + b) * 16 + tr];
+    for (int b = 0; b < NB; ++b) {
+      if (b <= tb) {
+        rz += sums[gk::SUM_ZR + (tb * NB + b) * 16 + tr];
+        b2 += sums[gk::SUM_BR + (tb * NB + b) * 16 + tr];
+      }
+      if (b >= tb) cz += sums[gk::SUM_ZC + (b * NB + tb) * 16 + tr];
     }
-    if (b >= tb) cz += sums[gdn_launch::BWD_SUM_ZC + (b * NB + tb) * 16 + tr];
-  }
-  float gc = 0.f;
+    float gc = 0.f;
 #pragma unroll
-  for (int w = 0; w < gk::NWG; ++w) gc += sums[gdn_launch::BWD_SUM_GC + w];
-  const float* s3 = sums + gdn_launch::BWD_SUM_S3;
-  const float sQv = s3[t], sXv = s3[C + t], sWv = s3[2 * C + t];
-  const float dGam = __builtin_fmaf(-bt, sXv, sQv) + (t == last ? gc : 0.f);
-  const float dbeta = __builtin_fmaf(-Gt, sXv, sums[gdn_launch::BWD_SUM_XV + t]) + b2;
-  const float dgam = t < Lc ? __builtin_fmaf(dGam, Gt, rz - cz) : 0.f;  // dgamma without the w terms
-  const float dww = t < Lc ? sWv * wt : 0.f;                              // dw . w
-  // dg_t = sum_{u >= t} dgamma_u; the w terms (-dw_u w_u at every token,
-  // +sum_u dw_u w_u at the last) enter as they add up after the reverse
-  // sum, sum_{u < t} dw_u w_u, which cancels nothing large under strong
-  // decay.  The suffix sum is a prefix sum over the lanes in reverse
-  // order, the exclusive prefix sum an inclusive one moved up a lane:
-  // neither subtracts a total (fixed addition order: deterministic).
-  const float rev = __shfl(dgam, C - 1 - t);
-  const float suf = __shfl(wave_prefix_sum(rev, t), C - 1 - t);
-  const float inc = wave_prefix_sum(dww, t);
-  // every lane takes part in the cross-lane read (a lane left out of it
-  // would not supply its value to the next one), then lane 0 drops it
-  const float prev = __shfl(inc, (t + C - 1) & (C - 1));
-  const float exc = t > 0 ? prev : 0.f;
-  const float acc = suf + exc;
-  if (t < Lc) {
-    p.dg[th] = acc;
-    p.dbeta[th] = dbeta;
+    for (int w = 0; w < gk::NWG; ++w) gc += sums[gk::SUM_GC + w];
+    const float* s3 = sums + gk::SUM_S3;
+    const float sQv = s3[t], sXv = s3[C + t], sWv = s3[2 * C + t];
+    const float dGam = __builtin_fmaf(-bt, sXv, sQv) + (t == last ? gc : 0.f);
+    const float dbeta = __builtin_fmaf(-Gt, sXv, sums[gk::SUM_XV + t]) + b2;
+    const float dgam = t < Lc ? __builtin_fmaf(dGam, Gt, rz - cz) : 0.f;  // dgamma without the w terms
+    const float dww = t < Lc ? sWv * wt : 0.f;                              // dw . w
+    // dg_t = sum_{u >= t} dgamma_u; the w terms (-dw_u w_u at every token,
+    // +sum_u dw_u w_u at the last) enter as they add up after the reverse
+    // sum, sum_{u < t} dw_u w_u, which cancels nothing large under strong
+    // decay.  The suffix sum is a prefix sum over the lanes in reverse
+    // order, the exclusive prefix sum an inclusive one moved up a lane:
+    // neither subtracts a total (fixed addition order: deterministic).
+    const float rev = __shfl(dgam, C - 1 - t);
+    const float suf = __shfl(wave_prefix_sum(rev, t), C - 1 - t);
+    const float inc = wave_prefix_sum(dww, t);
+    // every lane takes part in the cross-lane read (a lane left out of it
+    // would not supply its value to the next one), then lane 0 drops it
+    const float prev = __shfl(inc, (t + C - 1) & (C - 1));
+    const float exc = t > 0 ? prev : 0.f;
+    const float acc = suf + exc;
+    if (t < Lc) {
+      p.dg[th] = acc;
+      p.dbeta[th] = dbeta;
+    }
   }
 }
 
@@ -1182,7 +1171,7 @@ __global__ __launch_bounds__(64 * gk::NSW) void gdn_grad_sums_kernel(const gdn_l
 namespace gdn_launch {
 
 long long bwd_full_ws_bytes(int B, long ttot, int H) {
-  return (long long)((ttot / fk::C) + B) * H * (BWD_REC_BYTES + BWD_SUM_FLOATS * 4);
+  return (long long)((ttot / fk::C) + B) * H * BWD_REC_BYTES;
 }
 
 int bwd_full(const BwdParams& p, hipStream_t stream) {
@@ -1218,9 +1207,6 @@ int bwd_full(const BwdParams& p, hipStream_t stream) {
   }
   if (ngrad > 0) {
     hipLaunchKernelGGL(gdn_grad_kernel, dim3((unsigned)ngrad, (unsigned)p.H), dim3(64 * gk::NWG), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
-    hipLaunchKernelGGL(gdn_grad_sums_kernel, dim3((unsigned)ngrad, (unsigned)((p.H + gk::NSW - 1) / gk::NSW)),
-                       dim3(64 * gk::NSW), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_LAUNCH;
   }
   return GDN_OK;

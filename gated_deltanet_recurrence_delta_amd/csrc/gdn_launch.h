@@ -48,14 +48,6 @@ struct FullParams {
 // (C token rows of dv values), at these byte offsets.
 constexpr long BWD_OFF_M = 0, BWD_OFF_DM = 128 * 128 * 2, BWD_OFF_U = 2 * 128 * 128 * 2,
                BWD_OFF_DX = 2 * 128 * 128 * 2 + 64 * 128 * 2, BWD_REC_BYTES = 2 * 128 * 128 * 2 + 2 * 64 * 128 * 2;
-// After all records (nchunk x H of them), one block of BWD_SUM_FLOATS fp32
-// per (chunk slot, head): the gradient kernel's per-token partial sums for
-// dg and dbeta, at these float offsets: the row sums of Z, its column sums
-// and the row sums of dA . (S . E) for each 16 x 16 block (b1, b2), 16 each;
-// the per-token sums dO M^T . q, dX M^T . k and U dM^T . k (64 each); dX . v
-// per token; <M, dM> over each wave's keys (4).
-constexpr int BWD_SUM_ZR = 0, BWD_SUM_ZC = 256, BWD_SUM_BR = 512, BWD_SUM_S3 = 768, BWD_SUM_XV = 960,
-              BWD_SUM_GC = 1024, BWD_SUM_FLOATS = 1040;
 
 // Backward pass, bf16, dk = dv = 128, 64-token chunks (gdn_bwd_full.hip).
 struct BwdParams {
