@@ -719,23 +719,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gdn_adjoint_kernel(const gdn_launc
 //
 // gdn_grad_kernel: one workgroup per (chunk slot, head), four waves, wave w
 // owning the tokens of row block w.  From the saved M and dM' (key-major,
-// read as operands from the record), U and dX (read as operands), and the
+// staged in LDS a key block at a time), U and dX (read as operands), and the
 // chunk's q, k (LDS), v and dO:
 //   phase 1 (the 64 x 64 blocks (w, b) of the lower triangle, b <= w): S =
 //       K K^T, Q K^T, dX U^T and dO U^T; then G = dA . E . beta_i and
 //       dP . E (bf16 tiles, rows in pi order), and the row and column sums
 //       of Z and the row sums of dA . (S . E) per block;
 //   phase 2 (dq and dk as transposed 16 x 16 tiles, keys by tokens, over
-//       the eight key blocks; M and dM' fragments loaded a block ahead),
+//       the eight key blocks; each block's M and dM' rows copied to LDS
+//       while the previous block is worked),
 //       dv, and the per-token sums over the keys;
 //   phase 3 (one wave): dg (a reverse sum over the chunk) and dbeta from
 //       those sums.
 // A key-side operand (rows = keys) comes from
-// the record (M, dM') or from LDS by transposing reads (q, k); a token-side
+// LDS, by plain reads (M, dM') or transposing ones (q, k); a token-side
 // one (rows = tokens) from the record, v and dO (natural value order) or
 // from the bf16 tiles (pi token order).
 //
-// Two workgroups share a CU (56 KB of LDS and at most 256 VGPRs per wave):
+// Two workgroups share a CU (72 KB of LDS and at most 256 VGPRs per wave):
 // one's loads overlap the other's products.
 namespace gk {
 constexpr int NWG = 4;  // waves per gradient workgroup
@@ -780,6 +781,9 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
   __shared__ __attribute__((aligned(16))) float sVEC[NF * C];
   __shared__ __attribute__((aligned(16))) float sGB[2 * C];
   __shared__ float sums[gk::SUM_FLOATS];  // per-token partial sums for dg and dbeta
+  // M and dM' rows of one key block (16 rows of 256 bytes each, granules
+  // permuted as in the q / k tiles), double-buffered over the key blocks
+  __shared__ __attribute__((aligned(16))) char sMD[2][2 * 16 * KQR];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -844,20 +848,24 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
     for (int s = 0; s < NKS; ++s)
       Uc[b2][s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rr, base + (32 * s + 8 * q4) * 2, 0, 0));
   }
-  // key-side M and dM' rows of phase 2's first key block
-  F Mc[NKS], Dc[NKS];
-  auto load_md = [&](int ab) {
+  // M and dM' rows of key block ab into buffer b: eight 1 KB copies (four
+  // rows each), two per wave
+  auto issue_md = [&](int ab, int b) {
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const int off = ((16 * ab + n16) * DV + 32 * s + 8 * q4) * 2;
-      Mc[s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)gdn_launch::BWD_OFF_M + off, 0, 0));
-      Dc[s] = __builtin_bit_cast(F, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)gdn_launch::BWD_OFF_DM + off, 0, 0));
+    for (int x = 0; x < 2; ++x) {
+      const int i = 2 * wave + x, part = i >> 2, ii = i & 3;
+      const int r = ii * KQ_RPI + lane / GR;
+      const int so = (int)(part ? gdn_launch::BWD_OFF_DM : gdn_launch::BWD_OFF_M) + (16 * ab + r) * KQR +
+                     16 * ((lane % GR) ^ swz_kq<GR>(r));
+      copy_to_lds(rr, sMD[b] + part * 16 * KQR + ii * 1024, so);
     }
   };
-  load_md(0);
-  // the copies have landed, in every wave; the register loads (3 NKS + (NB
-  // - 1) NKS + 2 NKS of them) may still be in flight
-  constexpr int GK_REG = (3 + NB - 1 + 2) * NKS;
+  static_assert(2 * gk::NWG * 1024 == 2 * 16 * KQR, "copies per key block");
+  issue_md(0, 0);
+  // the q / k copies have landed, in every wave; the register loads (3 NKS
+  // + (NB - 1) NKS of them) and the first key block's two copies may still
+  // be in flight
+  constexpr int GK_REG = (3 + NB - 1) * NKS + 2;
   static_assert(GK_REG <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(GK_REG) : "memory");
   if (wave == 0) {
@@ -1010,15 +1018,22 @@ __global__ __launch_bounds__(64 * gk::NWG, 2) void gdn_grad_kernel(const gdn_lau
 #pragma unroll
     for (int m = 0; m < NKB / 2; ++m) {
       const int ab = NKB / 2 * hf + m;
-      // key-side operands, rows a = 16 ab + n16: M and dM' (loaded a block
-      // ahead), k and q (transposing reads)
+      // key block ab's copies have landed in every wave (after them each
+      // wave issued only the previous block's two stores), and every wave
+      // is done with the other buffer; then the next block's copies go out
+      const int buf = m & 1;
+      if (ab == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+      if (ab + 1 < NKB) issue_md(ab + 1, buf ^ 1);
+      // key-side operands, rows a = 16 ab + n16: M and dM' (LDS), k and q
+      // (transposing reads)
       F MTa[NKS], DTa[NKS], KTa[NTS], QTa[NTS];
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        MTa[s] = Mc[s];
-        DTa[s] = Dc[s];
+        const int fo = n16 * KQR + 16 * ((4 * s + q4) ^ swz_kq<GR>(n16));
+        MTa[s] = lds_at<F>(sMD[buf] + fo);
+        DTa[s] = lds_at<F>(sMD[buf] + 16 * KQR + fo);
       }
-      if (ab + 1 < NKB) load_md(ab + 1);
 #pragma unroll
       for (int ts = 0; ts < NTS; ++ts) {
         const int jl = 32 * ts + 4 * q4 + (n16 >> 2), jh = jl + 16;
