@@ -1,5 +1,6 @@
 """Seeded sweep of random configurations against the FP64 oracles (forward,
-diagonal-decay and backward entry points): shapes,
+diagonal-decay and backward entry points, and the training pair against the
+plain forward and backward): shapes,
 dtypes, chunk lengths, dense or packed batches (with empty and ragged
 sequences), with or without an initial state, lengths that do and do not
 trigger sequence segments.  Every case is fixed by its seed."""
@@ -96,3 +97,53 @@ def test_bwd_random_configuration(seed):
     inp = synth.generate(wl)
     print(wl, flush=True)
     _check(inp, synth.output_grads(inp, 4000 + seed, dh))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_train_random_configuration(seed):
+    """The training pair on random full-width cases (bf16, dk = dv = 128):
+    gdn_fwd_train's out and hT equal gdn_fwd's bit for bit, and gdn_bwd_saved
+    from its records equals gdn_bwd bit for bit, dense (lengths that are and
+    are not cut into segments) and packed (with empty and ragged sequences);
+    small cases also against the FP64 oracle."""
+    import torch
+
+    import gated_deltanet_recurrence_delta_amd as gdn
+    from hip_case import dev, host_f64
+    from test_gpu_bwd import NAMES, _oracle, _rel
+
+    rng = np.random.default_rng(5000 + seed)
+    H = int(rng.integers(1, 5))
+    h0 = float(rng.choice([0.0, 0.2]))
+    g_mean = float(rng.choice([0.0, -2.0, -4.0]))
+    dh = float(rng.choice([0.0, 1.0]))
+    if rng.random() < 0.4:
+        lens = [int(x) for x in rng.integers(0, 1400, size=int(rng.integers(1, 5)))]
+        wl = synth.custom(name=f"train_sweep{seed}", seed=seed, H=H, dk=128, dv=128, dtype="bf16",
+                          h0_std=h0, g_mean=g_mean, seq_lens=lens)
+    else:
+        T = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(1024, 2200))]))
+        wl = synth.custom(name=f"train_sweep{seed}", seed=seed, B=int(rng.integers(1, 3)), T=T, H=H,
+                          dk=128, dv=128, dtype="bf16", h0_std=h0, g_mean=g_mean)
+    inp = synth.generate(wl)
+    og = synth.output_grads(inp, 6000 + seed, dh)
+    print(wl, flush=True)
+    d = {n: dev(getattr(inp, n)) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"])
+    out1, hT1 = gdn.fwd(*args)
+    out2, hT2, ws = gdn.fwd_train(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(hT1.view(torch.int32), hT2.view(torch.int32))
+    kw = dict(h0=d["h0"], cu_seqlens=d["cu_seqlens"], dhT=dev(og.dhT))
+    g1 = gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dev(og.dout), **kw)
+    g2 = gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dev(og.dout), workspace=ws, saved=True, **kw)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        if g1[n] is not None:
+            assert torch.equal(g1[n], g2[n]), n
+    if wl.tokens * H <= 3000:
+        ref = _oracle(inp, og)
+        for n in NAMES:
+            e = _rel(host_f64(g2[n]), ref[n])
+            assert e <= TOL["bf16"], (n, e)
